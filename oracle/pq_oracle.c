@@ -1,0 +1,474 @@
+/*
+ * pq_oracle.c -- plain, slow, CPU reference ("the oracle") for the ParetoQ
+ * quantized linear layer: alpha init, forward fake-quantization at
+ * 1 / 1.58 / 2 / 3 / 4 bits, the straight-through backward with the per-row
+ * scale gradient, 2-bit / 4-bit export packing and the packed-weight GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or constant with the GPU library, and the GPU library never
+ * calls it.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [Note]     "ParetoQ, the strongest low-bit QAT I could find"
+ *              (sections "QAT versus PTQ", "Finding 3", "The 2-bit recipe,
+ *              in full", "Paper vs. code").
+ *   [Rebuttal] "ParetoQ: Improving Scaling Laws in Extremely Low-bit LLM
+ *              Quantization" (the authors' OpenReview replies; part
+ *              "Regarding more discussion on why SEQ is better than LSQ").
+ *   [News]     "Meta's ParetoQ compares five bit widths and puts the accuracy
+ *              cliff at 1 bit" (speed and storage paragraphs).
+ *   [Abstract] "ParetoQ: Scaling Laws in Extremely Low-bit LLM Quantization".
+ *
+ * Arithmetic: every float expression below is one IEEE binary32 operation
+ * rounded to nearest-even.  Build with -O2 -ffp-contract=off, no fast-math, on
+ * x86-64 SSE (no x87 excess precision, no flush-to-zero).  Sums that the
+ * method leaves to the implementation are taken in binary64, sequentially in
+ * column order.
+ *
+ * Parity unpinned (no page fixes them; each is a documented reading):
+ *   - the 1-bit quantizer as a whole (the pages name the width only);
+ *   - the ternary alpha-gradient value for clipped weights (+-2/3);
+ *   - n and Qp of the 1/sqrt(n*Qp) gradient scale (only the default value).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Bit-width modes, in the order the pages list the widths ([Abstract]). */
+enum {
+    PQO_W1_BINARY = 0,        /* 1 bit                                   */
+    PQO_W158_SEQ_TERNARY = 1, /* 1.58 bit, SEQ                           */
+    PQO_W2_SEQ = 2,           /* 2 bit, SEQ                              */
+    PQO_W3_LSQ = 3,           /* 3 bit, LSQ integer grid                 */
+    PQO_W4_LSQ = 4            /* 4 bit, LSQ integer grid                 */
+};
+
+/* [Note] "Paper vs. code", first bullet: the shipped clip is 1 - 1e-2, which
+ * removes the fifth level (+1.25 alpha) that clipping to +-1 would create. */
+static const float CLIP_SHIPPED = 0.99f;
+/* Guard against alpha <= 0 (the pages are silent): divide by max(alpha, 1e-5). */
+static const float ALPHA_FLOOR = 1e-5f;
+/* [Note] "Finding 3": ternary SEQ levels are {-2/3, 0, +2/3} alpha. */
+static const float TWO_THIRDS = (float)(2.0 / 3.0);
+
+static int valid_mode(int mode) { return mode >= PQO_W1_BINARY && mode <= PQO_W4_LSQ; }
+
+/* Bits per stored code: 1 for binary, 2 for ternary and 2-bit SEQ (the
+ * [News] storage paragraph notes ternary is often kept as 2-bit integers),
+ * a 4-bit nibble for 3- and 4-bit LSQ. */
+int pqo_code_bits(int mode)
+{
+    switch (mode) {
+    case PQO_W1_BINARY: return 1;
+    case PQO_W158_SEQ_TERNARY: return 2;
+    case PQO_W2_SEQ: return 2;
+    case PQO_W3_LSQ: return 4;
+    case PQO_W4_LSQ: return 4;
+    }
+    return -1;
+}
+
+/* LSQ integer grid [Note] "Finding 3": levels -2^(b-1) .. 2^(b-1)-1. */
+static int lsq_bits(int mode) { return mode == PQO_W3_LSQ ? 3 : 4; }
+static float lsq_qn(int mode) { return -(float)(1 << (lsq_bits(mode) - 1)); }
+static float lsq_qp(int mode) { return (float)((1 << (lsq_bits(mode) - 1)) - 1); }
+
+/* Smallest step index r of each grid; the stored code is r - r_min. */
+static int r_min_of(int mode)
+{
+    switch (mode) {
+    case PQO_W1_BINARY: return -1;
+    case PQO_W158_SEQ_TERNARY: return -1;
+    case PQO_W2_SEQ: return -2;
+    default: return (int)lsq_qn(mode);
+    }
+}
+
+/* Stored code of step index r: offset-binary r - r_min on the multi-level
+ * grids; for the two 1-bit levels -1, +1 the code is 0, 1. */
+static unsigned code_of(int mode, int r)
+{
+    if (mode == PQO_W1_BINARY) return r > 0 ? 1u : 0u;
+    return (unsigned)(r - r_min_of(mode));
+}
+
+static int step_of_code(int mode, unsigned code)
+{
+    if (mode == PQO_W1_BINARY) return code ? 1 : -1;
+    return (int)code + r_min_of(mode);
+}
+
+float pqo_clip_value(void) { return CLIP_SHIPPED; }
+
+/* bf16 round-to-nearest-even of a finite binary32 value: keep the top 16
+ * bits, adding half an ulp of the result (plus one if the kept part is odd). */
+uint16_t pqo_bf16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7FFFu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+float pqo_bf16_to_f32(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* ---------------------------------------------------------------------------
+ * One weight through the quantizer.  Returns the step index r and writes the
+ * fake-quantized binary32 value q (before the bf16 cast) and x = w / alpha.
+ * ------------------------------------------------------------------------- */
+
+/* 2-bit SEQ, [Note] "Paper vs. code" (SEQ formula row):
+ *   q = alpha * (round(Clip(w/alpha) * k/2 - 0.5) + 0.5) / k * 2,  k = 4,
+ * with round = half-to-even and the clip bound `clip` (0.99 as shipped; the
+ * test suite also evaluates the literal +-1 of the paper's equation). */
+int pqo_seq2_quantize(float w, float alpha, float clip, float *q_out, float *x_out)
+{
+    float a = alpha > ALPHA_FLOOR ? alpha : ALPHA_FLOOR;
+    float x = w / a;                          /* w / alpha               */
+    float xc = fmaxf(x, -clip);               /* Clip(., -clip, clip)    */
+    xc = fminf(xc, clip);
+    float z = xc * 2.0f;                      /* * k/2 with k = 4        */
+    z = z - 0.5f;                             /* - 0.5                   */
+    float rf = rintf(z);                      /* round half-to-even      */
+    int r = (int)rf;
+    float t = (float)r + 0.5f;                /* + 0.5                   */
+    float q = a * t;                          /* alpha * (...)           */
+    q = q / 4.0f;                             /* / k                     */
+    q = q * 2.0f;                             /* * 2                     */
+    if (q_out) *q_out = q;
+    if (x_out) *x_out = x;
+    return r;
+}
+
+/* Ternary SEQ, [Rebuttal] 1.58-bit bullet: the clipped ratio is stretched to
+ * [-1.5, 1.5] and cut into three equal-width bins [-1.5,-0.5], [-0.5,0.5],
+ * [0.5,1.5] -> -1, 0, +1 (ties at +-0.5 go to the even index 0); the level of
+ * bin r is r * 2/3 of alpha ([Note] "Finding 3"). */
+static int ternary_quantize(float w, float alpha, float *q_out, float *x_out)
+{
+    float a = alpha > ALPHA_FLOOR ? alpha : ALPHA_FLOOR;
+    float x = w / a;
+    float xc = fmaxf(x, -CLIP_SHIPPED);
+    xc = fminf(xc, CLIP_SHIPPED);
+    float v = xc * 1.5f;                      /* stretch to [-1.5, 1.5]  */
+    float rf = rintf(v);                      /* nearest bin centre      */
+    int r = (int)rf;
+    float level = (float)r * TWO_THIRDS;      /* -2/3, 0, +2/3           */
+    float q = a * level;
+    if (q_out) *q_out = q;
+    if (x_out) *x_out = x;
+    return r;
+}
+
+/* LSQ at 3/4 bits: q = alpha * round(clamp(w/alpha, Qn, Qp)) on the integer
+ * grid Qn = -2^(b-1) .. Qp = 2^(b-1)-1 ([Note] "Finding 3"; the dispatch row
+ * of "Paper vs. code" sends 3 and 4 bits to LSQ). */
+static int lsq_quantize(int mode, float w, float alpha, float *q_out, float *x_out)
+{
+    float a = alpha > ALPHA_FLOOR ? alpha : ALPHA_FLOOR;
+    float x = w / a;
+    float xc = fmaxf(x, lsq_qn(mode));
+    xc = fminf(xc, lsq_qp(mode));
+    float rf = rintf(xc);
+    int r = (int)rf;
+    float q = a * (float)r;
+    if (q_out) *q_out = q;
+    if (x_out) *x_out = x;
+    return r;
+}
+
+/* 1 bit: q = alpha * sign(w), sign(0) taken as +1 so exactly two levels exist.
+ * The pages give the width only; this is the sign / mean-|W| binarizer of
+ * XNOR-Net, which [Rebuttal] cites as binary prior work. */
+static int binary_quantize(float w, float alpha, float *q_out, float *x_out)
+{
+    float a = alpha > ALPHA_FLOOR ? alpha : ALPHA_FLOOR;
+    float x = w / a;
+    int r = (w >= 0.0f) ? 1 : -1;
+    float q = a * (float)r;
+    if (q_out) *q_out = q;
+    if (x_out) *x_out = x;
+    return r;
+}
+
+int pqo_quantize_scalar(int mode, float w, float alpha, float *q_out, float *x_out)
+{
+    switch (mode) {
+    case PQO_W1_BINARY: return binary_quantize(w, alpha, q_out, x_out);
+    case PQO_W158_SEQ_TERNARY: return ternary_quantize(w, alpha, q_out, x_out);
+    case PQO_W2_SEQ: return pqo_seq2_quantize(w, alpha, CLIP_SHIPPED, q_out, x_out);
+    case PQO_W3_LSQ:
+    case PQO_W4_LSQ: return lsq_quantize(mode, w, alpha, q_out, x_out);
+    }
+    return 0;
+}
+
+/* Level of step index r in units of alpha, as a binary64 value. */
+static double level_of(int mode, int r)
+{
+    switch (mode) {
+    case PQO_W2_SEQ: return ((double)r + 0.5) / 2.0;        /* +-0.25, +-0.75 */
+    case PQO_W158_SEQ_TERNARY: return (double)((float)r * TWO_THIRDS);
+    default: return (double)r;                               /* LSQ, binary    */
+    }
+}
+
+/* Write `code` (cw bits) as element j of a row's LSB-first bit stream. */
+static void put_code(uint8_t *row, int64_t j, int cw, unsigned code)
+{
+    int64_t bit = j * cw;
+    row[bit >> 3] |= (uint8_t)((code & ((1u << cw) - 1u)) << (bit & 7));
+}
+
+static unsigned get_code(const uint8_t *row, int64_t j, int cw)
+{
+    int64_t bit = j * cw;
+    return (row[bit >> 3] >> (bit & 7)) & ((1u << cw) - 1u);
+}
+
+int64_t pqo_code_row_bytes(int mode, int64_t cols)
+{
+    return (cols * pqo_code_bits(mode) + 7) / 8;
+}
+
+void pqo_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int pqo_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ---------------------------------------------------------------------------
+ * alpha initialisation, per output row.
+ *   2-bit SEQ and ternary: max|w| ([Note] "The 2-bit recipe" table and the
+ *   scale-init row of "Paper vs. code").
+ *   LSQ: max|w| / (2^(b-1) - 1), one binary32 division (same row).
+ *   1 bit: mean|w|, summed in binary64 in column order, divided in binary64,
+ *   rounded once to binary32.
+ * Returns 0, or -1 on a bad argument.
+ * ------------------------------------------------------------------------- */
+int pqo_alpha_init(int mode, int64_t rows, int64_t cols, const float *W, float *alpha)
+{
+    if (!valid_mode(mode) || rows < 0 || cols <= 0 || !W || !alpha) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i) {
+        const float *w = W + i * cols;
+        if (mode == PQO_W1_BINARY) {
+            double s = 0.0;
+            for (int64_t j = 0; j < cols; ++j) s += (double)fabsf(w[j]);
+            alpha[i] = (float)(s / (double)cols);
+        } else {
+            float m = 0.0f;
+            for (int64_t j = 0; j < cols; ++j) {
+                float v = fabsf(w[j]);
+                if (v > m) m = v;
+            }
+            if (mode == PQO_W3_LSQ || mode == PQO_W4_LSQ) m = m / lsq_qp(mode);
+            alpha[i] = m;
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Forward.  For every weight: the mode's quantizer above; the binary32 value
+ * is cast to bf16 (round to nearest-even) because the layer casts the
+ * fake-quantized weight to the activation dtype ([Note] "Paper vs. code",
+ * last bullet).  Outputs are optional (NULL skips them):
+ *   wq_bf16 [rows, cols] bf16 bits, wq_f32 [rows, cols], codes [rows,
+ *   code_row_bytes] (code_of above), LSB-first.
+ * ------------------------------------------------------------------------- */
+int pqo_quantize_fwd(int mode, int64_t rows, int64_t cols, const float *W,
+                     const float *alpha, uint16_t *wq_bf16, float *wq_f32,
+                     uint8_t *codes)
+{
+    if (!valid_mode(mode) || rows < 0 || cols <= 0 || !W || !alpha) return -1;
+    const int cw = pqo_code_bits(mode);
+    const int64_t rb = pqo_code_row_bytes(mode, cols);
+    if (codes) memset(codes, 0, (size_t)(rows * rb));
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i) {
+        for (int64_t j = 0; j < cols; ++j) {
+            float q;
+            int r = pqo_quantize_scalar(mode, W[i * cols + j], alpha[i], &q, NULL);
+            if (wq_bf16) wq_bf16[i * cols + j] = pqo_bf16_rne(q);
+            if (wq_f32) wq_f32[i * cols + j] = q;
+            if (codes) put_code(codes + i * rb, j, cw, code_of(mode, r));
+        }
+    }
+    return 0;
+}
+
+/* Qp used in the 1/sqrt(n * Qp) scale of the alpha gradient ([Note]
+ * "Paper vs. code", LSQ-gradient row): 2^(b-1) - 1 for 3 and 4 bits,
+ * floored at 1 for the widths where that count is below one. */
+static double grad_qp(int mode)
+{
+    switch (mode) {
+    case PQO_W3_LSQ: return 3.0;
+    case PQO_W4_LSQ: return 7.0;
+    default: return 1.0;
+    }
+}
+
+/* Default gradient scale 1/sqrt(n * Qp), n = number of weights in the matrix
+ * (LSQ's count of the weights the scale serves). */
+double pqo_default_grad_scale(int mode, int64_t rows, int64_t cols)
+{
+    return 1.0 / sqrt((double)rows * (double)cols * grad_qp(mode));
+}
+
+/* ---------------------------------------------------------------------------
+ * Backward.  G is dL/d(fake-quantized weight), binary32 (g_is_bf16 = 0) or
+ * bf16 bits (g_is_bf16 = 1).  Per weight, with x = w / alpha:
+ *   inside = x lies in the clip range, bounds included: [-0.99, 0.99] for SEQ
+ *            and ternary, [Qn, Qp] for LSQ, [-1, 1] for 1 bit;
+ *   dW     = G where inside, exactly +0 elsewhere ([Note] "QAT versus PTQ"
+ *            and the STE paragraph of "The 2-bit recipe, in full");
+ *   s      = d q / d alpha with round() (sign() at 1 bit) passed straight
+ *            through: level - x inside; the boundary level (the level of the
+ *            clipped value) outside, which keeps a gradient flowing to alpha
+ *            from clipped weights (same paragraph);
+ *   dalpha = grad_scale * sum_j s * G, summed in binary64, rounded once
+ *            ([Note] "Paper vs. code", LSQ-gradient row).
+ * mask_bits (optional) gets `inside` per weight, LSB-first, ceil(cols/8)
+ * bytes per row.
+ * ------------------------------------------------------------------------- */
+int pqo_quantize_bwd(int mode, int64_t rows, int64_t cols, const float *W,
+                     const float *alpha, const void *G, int g_is_bf16,
+                     double grad_scale, float *dW, float *dalpha,
+                     uint8_t *mask_bits)
+{
+    if (!valid_mode(mode) || rows < 0 || cols <= 0 || !W || !alpha || !G) return -1;
+    const int64_t mb = (cols + 7) / 8;
+    if (mask_bits) memset(mask_bits, 0, (size_t)(rows * mb));
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < cols; ++j) {
+            int64_t e = i * cols + j;
+            float g = g_is_bf16 ? pqo_bf16_to_f32(((const uint16_t *)G)[e])
+                                : ((const float *)G)[e];
+            float x;
+            int r = pqo_quantize_scalar(mode, W[e], alpha[i], NULL, &x);
+            int inside;
+            double s;
+            if (mode == PQO_W1_BINARY) {
+                /* sign(w) plays the part of round(): level - x inside
+                 * [-1, 1], the boundary level sign(w) outside. */
+                inside = (x >= -1.0f) && (x <= 1.0f);
+                if (inside) s = (double)r - (double)x;
+                else s = (double)r;
+            } else if (mode == PQO_W3_LSQ || mode == PQO_W4_LSQ) {
+                float qn = lsq_qn(mode), qp = lsq_qp(mode);
+                inside = (x >= qn) && (x <= qp);
+                if (inside) s = (double)r - (double)x;
+                else s = (x < qn) ? (double)qn : (double)qp;
+            } else {
+                inside = (x >= -CLIP_SHIPPED) && (x <= CLIP_SHIPPED);
+                /* Outside, r is the index of the clipped value, so level_of(r)
+                 * is the boundary level +-0.75 (2 bit) or +-2/3 (ternary). */
+                if (inside) s = level_of(mode, r) - (double)x;
+                else s = level_of(mode, r);
+            }
+            if (dW) dW[e] = inside ? g : 0.0f;
+            if (mask_bits && inside) mask_bits[i * mb + (j >> 3)] |= (uint8_t)(1u << (j & 7));
+            acc += s * (double)g;
+        }
+        if (dalpha) dalpha[i] = (float)(grad_scale * acc);
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Export: the codes the forward emits for W (2-bit SEQ or 4-bit LSQ) and the
+ * per-row scale rounded to bf16.  Memory savings exist only after such an
+ * export ([Note] "Paper vs. code", last bullet).
+ * ------------------------------------------------------------------------- */
+int pqo_pack(int mode, int64_t rows, int64_t cols, const float *W, const float *alpha,
+             uint8_t *packed, uint16_t *alpha_bf16)
+{
+    if (mode != PQO_W2_SEQ && mode != PQO_W4_LSQ) return -1;
+    if (pqo_quantize_fwd(mode, rows, cols, W, alpha, NULL, NULL, packed) != 0) return -1;
+    if (alpha_bf16)
+        for (int64_t i = 0; i < rows; ++i) alpha_bf16[i] = pqo_bf16_rne(alpha[i]);
+    return 0;
+}
+
+/* Dequantized level of a stored code, in units of alpha. */
+static double code_level(int mode, unsigned code)
+{
+    return level_of(mode, step_of_code(mode, code));
+}
+
+/* ---------------------------------------------------------------------------
+ * Deployment GEMM reference, binary64: Y[m,n] = sum_k X[m,k] * alpha[n] *
+ * level(code[n,k]) -- a plain matmul of the activations with the dequantized
+ * packed weight (the deployed layer of the [News] speed paragraph, whose
+ * 2-bit-weight kernel is timed against FP16 and 4-bit GEMMs; the layer has no
+ * bias, [Note] "Paper vs. code").  X is [M,K] bf16 bits, packed is
+ * [N, code_row_bytes(K)], alpha_bf16 is [N].
+ * pqo_gemm_ref fills all of Y [M,N]; pqo_gemm_ref_at only the listed (m, n).
+ * ------------------------------------------------------------------------- */
+static double gemm_one(int mode, int64_t K, const uint16_t *xrow, const uint8_t *crow,
+                       double a)
+{
+    const int cw = pqo_code_bits(mode);
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double w = a * code_level(mode, get_code(crow, k, cw));
+        acc += (double)pqo_bf16_to_f32(xrow[k]) * w;
+    }
+    return acc;
+}
+
+int pqo_gemm_ref(int mode, int64_t M, int64_t N, int64_t K, const uint16_t *X,
+                 const uint8_t *packed, const uint16_t *alpha_bf16, double *Y)
+{
+    if (mode != PQO_W2_SEQ && mode != PQO_W4_LSQ) return -1;
+    const int64_t rb = pqo_code_row_bytes(mode, K);
+#pragma omp parallel for schedule(static) collapse(2)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            Y[m * N + n] = gemm_one(mode, K, X + m * K, packed + n * rb,
+                                    (double)pqo_bf16_to_f32(alpha_bf16[n]));
+    return 0;
+}
+
+int pqo_gemm_ref_at(int mode, int64_t M, int64_t N, int64_t K, const uint16_t *X,
+                    const uint8_t *packed, const uint16_t *alpha_bf16,
+                    const int64_t *ms, const int64_t *ns, int64_t count, double *out)
+{
+    if (mode != PQO_W2_SEQ && mode != PQO_W4_LSQ) return -1;
+    const int64_t rb = pqo_code_row_bytes(mode, K);
+    for (int64_t t = 0; t < count; ++t)
+        if (ms[t] < 0 || ms[t] >= M || ns[t] < 0 || ns[t] >= N) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < count; ++t)
+        out[t] = gemm_one(mode, K, X + ms[t] * K, packed + ns[t] * rb,
+                          (double)pqo_bf16_to_f32(alpha_bf16[ns[t]]));
+    return 0;
+}
