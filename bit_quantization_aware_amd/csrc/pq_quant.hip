@@ -1,0 +1,668 @@
+// pq_quant.hip -- gfx950 kernels and C entry points for the per-row weight
+// quantizer: alpha init, forward fake-quantization, straight-through backward
+// with the scale gradient, and export packing.
+//
+// Sources (web pages, cited by title and section):
+//   [Note]     "ParetoQ, the strongest low-bit QAT I could find"
+//   [Rebuttal] "ParetoQ: Improving Scaling Laws in Extremely Low-bit LLM
+//              Quantization" (authors' OpenReview replies)
+//   [News]     "Meta's ParetoQ compares five bit widths and puts the accuracy
+//              cliff at 1 bit"
+//
+// Work mapping.  The whole pass is HBM-bound elementwise work with one scalar
+// (alpha) and one reduction (init statistic or alpha gradient) per row.  A
+// "team" of WPR wavefronts owns one row: WPR = 1 (four rows per 256-thread
+// block) when the stack has enough rows to fill the chip, WPR = 4 (one row
+// per block) otherwise.  Each lane handles quads of 4 consecutive weights;
+// the quads of one wave instruction are contiguous, so every 128-bit load
+// and every 64-bit bf16 store is fully coalesced.  1-bit codes and mask bits
+// (a nibble per quad) are paired with the neighbouring lane into bytes.
+// Row reductions: a butterfly over the wave (ds_bpermute), then LDS across
+// the team's waves, in a fixed order, so results are run-to-run identical.
+//
+// Arithmetic.  Every float step is one IEEE binary32 operation (built with
+// -ffp-contract=off): x = w / a with the correctly rounded division, clamp,
+// the SEQ shift, rint (v_rndne_f32, half-to-even), q = a * level with the
+// level exact in binary32, bf16 by v_cvt_pk_bf16_f32 (nearest-even).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pq_common.hpp"
+
+namespace pq {
+namespace {
+
+// [Note] "Paper vs. code", first bullet: clip w/alpha to +-(1 - 1e-2).
+constexpr float kClip = 0.99f;
+// alpha <= 1e-5 is used as 1e-5 (the pages are silent; keeps 0/0 away).
+constexpr float kAlphaFloor = 1e-5f;
+// [Note] "Finding 3": ternary levels are {-2/3, 0, +2/3} alpha.
+constexpr float kTwoThirds = static_cast<float>(2.0 / 3.0);
+
+template <int MODE> struct Mode;
+template <> struct Mode<PQ_W1_BINARY> {
+    static constexpr int cw = 1;
+    static constexpr float lo = -1.0f, hi = 1.0f;
+};
+template <> struct Mode<PQ_W158_SEQ_TERNARY> {
+    static constexpr int cw = 2;
+    static constexpr float lo = -kClip, hi = kClip;
+};
+template <> struct Mode<PQ_W2_SEQ> {
+    static constexpr int cw = 2;
+    static constexpr float lo = -kClip, hi = kClip;
+};
+template <> struct Mode<PQ_W3_LSQ> {
+    static constexpr int cw = 4;
+    static constexpr float lo = -4.0f, hi = 3.0f;  // LSQ grid -2^(b-1) .. 2^(b-1)-1
+};
+template <> struct Mode<PQ_W4_LSQ> {
+    static constexpr int cw = 4;
+    static constexpr float lo = -8.0f, hi = 7.0f;
+};
+
+// One weight: returns its code; writes the level (binary32, exact) and x = w/a.
+template <int MODE>
+__device__ __forceinline__ uint32_t quant1(float w, float a, float &lvl, float &x)
+{
+    x = w / a;
+    if constexpr (MODE == PQ_W2_SEQ) {
+        // [Note] "Paper vs. code", SEQ row: round(Clip(x) * k/2 - 0.5) + 0.5, k = 4;
+        // the level (r + 0.5) * 2/k is exact, so alpha * level equals the
+        // page's alpha * (r + 0.5) / k * 2 bit for bit.
+        float xc = fminf(fmaxf(x, -kClip), kClip);
+        float z = xc * 2.0f;
+        z = z - 0.5f;
+        float rf = __builtin_rintf(z);
+        lvl = (rf + 0.5f) * 0.5f;
+        return static_cast<uint32_t>(static_cast<int>(rf) + 2);
+    } else if constexpr (MODE == PQ_W158_SEQ_TERNARY) {
+        // [Rebuttal] 1.58-bit bullet: stretch to [-1.5, 1.5], three equal bins.
+        float xc = fminf(fmaxf(x, -kClip), kClip);
+        float v = xc * 1.5f;
+        int r = static_cast<int>(__builtin_rintf(v));
+        lvl = static_cast<float>(r) * kTwoThirds;
+        return static_cast<uint32_t>(r + 1);
+    } else if constexpr (MODE == PQ_W3_LSQ || MODE == PQ_W4_LSQ) {
+        // LSQ integer grid: round(clamp(x, Qn, Qp)).
+        float xc = fminf(fmaxf(x, Mode<MODE>::lo), Mode<MODE>::hi);
+        int r = static_cast<int>(__builtin_rintf(xc));
+        lvl = static_cast<float>(r);
+        return static_cast<uint32_t>(r - static_cast<int>(Mode<MODE>::lo));
+    } else {
+        // 1 bit: sign(w) with sign(0) = +1.
+        bool pos = w >= 0.0f;
+        lvl = pos ? 1.0f : -1.0f;
+        return pos ? 1u : 0u;
+    }
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// Team-wide reductions.  WPR == 1: the wave butterfly; WPR == 4: the four wave
+// results go through LDS and are combined in wave order by every thread.
+template <int WPR>
+__device__ __forceinline__ float team_max(float v, float *lds4)
+{
+    v = wave_max(v);
+    if constexpr (WPR == 1) {
+        return v;
+    } else {
+        const int wave = threadIdx.x >> 6;
+        if ((threadIdx.x & 63) == 0) lds4[wave] = v;
+        __syncthreads();
+        float r = fmaxf(fmaxf(lds4[0], lds4[1]), fmaxf(lds4[2], lds4[3]));
+        __syncthreads();
+        return r;
+    }
+}
+
+template <int WPR>
+__device__ __forceinline__ double team_sum(double v, double *lds4)
+{
+    v = wave_sum(v);
+    if constexpr (WPR == 1) {
+        return v;
+    } else {
+        const int wave = threadIdx.x >> 6;
+        if ((threadIdx.x & 63) == 0) lds4[wave] = v;
+        __syncthreads();
+        double r = ((lds4[0] + lds4[1]) + lds4[2]) + lds4[3];
+        __syncthreads();
+        return r;
+    }
+}
+
+// Quads handled per lane per batch (loads are issued for the whole batch
+// before any math, to keep U * 16 bytes per lane in flight).
+constexpr int kUnroll = 4;
+
+enum : unsigned { OUT_BF16 = 1, OUT_F32 = 2, OUT_CODES = 4, OUT_ALPHA_BF16 = 8 };
+
+// Forward: optional alpha init, then per quad: quantize, emit bf16 / fp32 /
+// codes.  OUT_ALPHA_BF16 (export) also writes bf16(alpha) per row.
+template <int MODE, bool INIT, int WPR, unsigned OUTS>
+__global__ __launch_bounds__(256) void k_quant_fwd(LaunchTable lt, void *alpha_bf16_single)
+{
+    constexpr int RPB = 4 / WPR;
+    constexpr int TEAM = 64 * WPR;
+    constexpr int CW = Mode<MODE>::cw;
+    __shared__ float lds_f[4];
+    __shared__ double lds_d[4];
+
+    const int wave = threadIdx.x >> 6;
+    const int tl = (wave % WPR) * 64 + (threadIdx.x & 63);
+    const int b = blockIdx.x;
+    const int k = find_matrix(lt, b);
+    const pq_mat m = lt.table ? lt.table[k] : lt.single;
+    const int64_t row = static_cast<int64_t>(b - lt.block_start[k]) * RPB + wave / WPR;
+    if (row >= m.rows) return;  // only when WPR == 1 (RPB rows per block)
+
+    const int64_t cols = m.cols;
+    const int nq = static_cast<int>(cols >> 2);
+    const float4 *wr = reinterpret_cast<const float4 *>(m.W + row * cols);
+
+    float alpha_raw;
+    if constexpr (INIT) {
+        // [Note] "The 2-bit recipe" table / scale-init row of "Paper vs. code".
+        if constexpr (MODE == PQ_W1_BINARY) {
+            double s = 0.0;
+            for (int q = tl; q < nq; q += TEAM) {
+                float4 v = wr[q];
+                s += static_cast<double>(fabsf(v.x));
+                s += static_cast<double>(fabsf(v.y));
+                s += static_cast<double>(fabsf(v.z));
+                s += static_cast<double>(fabsf(v.w));
+            }
+            s = team_sum<WPR>(s, lds_d);
+            alpha_raw = static_cast<float>(s / static_cast<double>(cols));
+        } else {
+            float mx = 0.0f;
+            for (int q = tl; q < nq; q += TEAM) {
+                float4 v = wr[q];
+                mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            }
+            mx = team_max<WPR>(mx, lds_f);
+            if constexpr (MODE == PQ_W3_LSQ || MODE == PQ_W4_LSQ) mx = mx / Mode<MODE>::hi;
+            alpha_raw = mx;
+        }
+        if (tl == 0) m.alpha[row] = alpha_raw;
+    } else {
+        alpha_raw = m.alpha[row];
+    }
+    const float a = alpha_raw > kAlphaFloor ? alpha_raw : kAlphaFloor;
+
+    if constexpr ((OUTS & OUT_ALPHA_BF16) != 0) {
+        if (tl == 0) {
+            __bf16 h = static_cast<__bf16>(alpha_raw);
+            static_cast<uint16_t *>(alpha_bf16_single)[row] = __builtin_bit_cast(uint16_t, h);
+        }
+    }
+
+    uint2 *wq16 = (OUTS & OUT_BF16) ? reinterpret_cast<uint2 *>(static_cast<uint16_t *>(m.wq_bf16) + row * cols) : nullptr;
+    float4 *wq32 = (OUTS & OUT_F32) ? reinterpret_cast<float4 *>(m.wq_f32 + row * cols) : nullptr;
+    uint8_t *crow = (OUTS & OUT_CODES) ? m.codes + row * (cols * CW / 8) : nullptr;
+
+    for (int base = 0; base < nq; base += TEAM * kUnroll) {
+        float4 v[kUnroll] = {};
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int q = base + u * TEAM + tl;
+            if (q < nq) v[u] = wr[q];
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int q = base + u * TEAM + tl;
+            const bool act = q < nq;
+            float l0, l1, l2, l3, x;
+            const uint32_t c0 = quant1<MODE>(v[u].x, a, l0, x);
+            const uint32_t c1 = quant1<MODE>(v[u].y, a, l1, x);
+            const uint32_t c2 = quant1<MODE>(v[u].z, a, l2, x);
+            const uint32_t c3 = quant1<MODE>(v[u].w, a, l3, x);
+            const float q0 = a * l0, q1 = a * l1, q2 = a * l2, q3 = a * l3;
+            if constexpr ((OUTS & OUT_BF16) != 0) {
+                if (act) wq16[q] = make_uint2(pack_bf16x2(q0, q1), pack_bf16x2(q2, q3));
+            }
+            if constexpr ((OUTS & OUT_F32) != 0) {
+                if (act) wq32[q] = make_float4(q0, q1, q2, q3);
+            }
+            if constexpr ((OUTS & OUT_CODES) != 0) {
+                if constexpr (CW == 2) {
+                    if (act) crow[q] = static_cast<uint8_t>(c0 | (c1 << 2) | (c2 << 4) | (c3 << 6));
+                } else if constexpr (CW == 4) {
+                    if (act)
+                        reinterpret_cast<uint16_t *>(crow)[q] =
+                            static_cast<uint16_t>(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
+                } else {
+                    // 1 bit: a nibble per quad; even lane takes its odd neighbour's.
+                    const uint32_t nib = c0 | (c1 << 1) | (c2 << 2) | (c3 << 3);
+                    const uint32_t hi = __shfl_down(nib, 1);
+                    if (act && (tl & 1) == 0) crow[q >> 1] = static_cast<uint8_t>(nib | (hi << 4));
+                }
+            }
+        }
+    }
+}
+
+// Backward: per weight the forward's x and level (bit-identical), the clip
+// gate, dW = inside ? G : +0, and the binary64 alpha-gradient partial
+// (level - x inside, the boundary level outside).
+template <int MODE, int WPR, bool GBF16, bool WDW, bool WMASK>
+__global__ __launch_bounds__(256) void k_quant_bwd(LaunchTable lt)
+{
+    constexpr int RPB = 4 / WPR;
+    constexpr int TEAM = 64 * WPR;
+    __shared__ double lds_d[4];
+
+    const int wave = threadIdx.x >> 6;
+    const int tl = (wave % WPR) * 64 + (threadIdx.x & 63);
+    const int b = blockIdx.x;
+    const int k = find_matrix(lt, b);
+    const pq_mat m = lt.table ? lt.table[k] : lt.single;
+    const int64_t row = static_cast<int64_t>(b - lt.block_start[k]) * RPB + wave / WPR;
+    if (row >= m.rows) return;
+
+    const int64_t cols = m.cols;
+    const int nq = static_cast<int>(cols >> 2);
+    const float4 *wr = reinterpret_cast<const float4 *>(m.W + row * cols);
+    const float4 *gr32 = GBF16 ? nullptr : reinterpret_cast<const float4 *>(static_cast<const float *>(m.G) + row * cols);
+    const uint2 *gr16 = GBF16 ? reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(m.G) + row * cols) : nullptr;
+    float4 *dwr = WDW ? reinterpret_cast<float4 *>(m.dW + row * cols) : nullptr;
+    uint8_t *mrow = WMASK ? m.mask_bits + row * (cols >> 3) : nullptr;
+
+    const float alpha_raw = m.alpha[row];
+    const float a = alpha_raw > kAlphaFloor ? alpha_raw : kAlphaFloor;
+    constexpr float lo = Mode<MODE>::lo, hi = Mode<MODE>::hi;
+    double acc = 0.0;
+
+    for (int base = 0; base < nq; base += TEAM * kUnroll) {
+        float4 wv[kUnroll] = {}, gv[kUnroll] = {};
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int q = base + u * TEAM + tl;
+            if (q < nq) {
+                wv[u] = wr[q];
+                if constexpr (GBF16) {
+                    const uint2 h = gr16[q];
+                    gv[u] = make_float4(bf16_to_f32(h.x & 0xFFFFu), bf16_to_f32(h.x >> 16),
+                                        bf16_to_f32(h.y & 0xFFFFu), bf16_to_f32(h.y >> 16));
+                } else {
+                    gv[u] = gr32[q];
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int q = base + u * TEAM + tl;
+            const bool act = q < nq;
+            const float w4[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+            const float g4[4] = {gv[u].x, gv[u].y, gv[u].z, gv[u].w};
+            float d4[4];
+            uint32_t nib = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float lvl, x;
+                quant1<MODE>(w4[e], a, lvl, x);
+                const bool inside = (x >= lo) && (x <= hi);
+                d4[e] = inside ? g4[e] : 0.0f;
+                nib |= static_cast<uint32_t>(inside) << e;
+                const double s = static_cast<double>(lvl) - (inside ? static_cast<double>(x) : 0.0);
+                if (act) acc += s * static_cast<double>(g4[e]);
+            }
+            if constexpr (WDW) {
+                if (act) dwr[q] = make_float4(d4[0], d4[1], d4[2], d4[3]);
+            }
+            if constexpr (WMASK) {
+                const uint32_t hi4 = __shfl_down(nib, 1);
+                if (act && (tl & 1) == 0) mrow[q >> 1] = static_cast<uint8_t>(nib | (hi4 << 4));
+            }
+        }
+    }
+    acc = team_sum<WPR>(acc, lds_d);
+    if (tl == 0) m.dalpha[row] = static_cast<float>(m.grad_scale * acc);
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+// Rows a launch needs before one wave per row fills the chip
+// (256 CUs x 4 SIMDs x 4 waves).
+constexpr int64_t kWaveRowsThreshold = 4096;
+
+pq_status check_mat(const pq_mat &m, bool need_w)
+{
+    if (m.rows < 0) return PQ_ERR_SHAPE;
+    if (!valid_cols(m.cols)) return PQ_ERR_SHAPE;
+    if (need_w && (!m.W || !m.alpha)) return PQ_ERR_NULL;
+    return PQ_OK;
+}
+
+bool ptr_ok(const void *p) { return p == nullptr || aligned16(p); }
+
+template <typename F>
+pq_status launch_grouped(int count, const pq_mat *host, const pq_mat *dev, hipStream_t stream,
+                         F &&launch_one)
+{
+    int64_t total_rows = 0;
+    for (int i = 0; i < count; ++i) total_rows += host[i].rows;
+    const int wpr = total_rows >= kWaveRowsThreshold ? 1 : 4;
+    const int rpb = 4 / wpr;
+    for (int start = 0; start < count; start += kMaxGroup) {
+        const int n = count - start < kMaxGroup ? count - start : kMaxGroup;
+        LaunchTable lt;
+        lt.table = dev ? dev + start : nullptr;
+        lt.single = host[start];
+        lt.count = n;
+        int64_t blocks = 0;
+        for (int i = 0; i < n; ++i) {
+            lt.block_start[i] = static_cast<int32_t>(blocks);
+            blocks += (host[start + i].rows + rpb - 1) / rpb;
+            if (blocks > INT32_MAX) return PQ_ERR_SHAPE;
+        }
+        lt.block_start[n] = static_cast<int32_t>(blocks);
+        if (blocks == 0) continue;
+        launch_one(lt, static_cast<int>(blocks), wpr, stream);
+        if (hipGetLastError() != hipSuccess) return PQ_ERR_HIP;
+    }
+    (void)total_rows;
+    return PQ_OK;
+}
+
+template <int MODE, bool INIT, unsigned OUTS>
+void launch_fwd_t(const LaunchTable &lt, int blocks, int wpr, hipStream_t s, void *abf)
+{
+    if (wpr == 1)
+        hipLaunchKernelGGL((k_quant_fwd<MODE, INIT, 1, OUTS>), dim3(blocks), dim3(256), 0, s, lt, abf);
+    else
+        hipLaunchKernelGGL((k_quant_fwd<MODE, INIT, 4, OUTS>), dim3(blocks), dim3(256), 0, s, lt, abf);
+}
+
+template <int MODE, bool INIT>
+void launch_fwd_outs(unsigned outs, const LaunchTable &lt, int blocks, int wpr, hipStream_t s)
+{
+    switch (outs) {
+    case 0: launch_fwd_t<MODE, INIT, 0>(lt, blocks, wpr, s, nullptr); break;
+    case 1: launch_fwd_t<MODE, INIT, 1>(lt, blocks, wpr, s, nullptr); break;
+    case 2: launch_fwd_t<MODE, INIT, 2>(lt, blocks, wpr, s, nullptr); break;
+    case 3: launch_fwd_t<MODE, INIT, 3>(lt, blocks, wpr, s, nullptr); break;
+    case 4: launch_fwd_t<MODE, INIT, 4>(lt, blocks, wpr, s, nullptr); break;
+    case 5: launch_fwd_t<MODE, INIT, 5>(lt, blocks, wpr, s, nullptr); break;
+    case 6: launch_fwd_t<MODE, INIT, 6>(lt, blocks, wpr, s, nullptr); break;
+    default: launch_fwd_t<MODE, INIT, 7>(lt, blocks, wpr, s, nullptr); break;
+    }
+}
+
+template <int MODE>
+void launch_fwd_mode(bool init, unsigned outs, const LaunchTable &lt, int blocks, int wpr, hipStream_t s)
+{
+    if (init) launch_fwd_outs<MODE, true>(outs, lt, blocks, wpr, s);
+    else launch_fwd_outs<MODE, false>(outs, lt, blocks, wpr, s);
+}
+
+void launch_fwd(int mode, bool init, unsigned outs, const LaunchTable &lt, int blocks, int wpr, hipStream_t s)
+{
+    switch (mode) {
+    case PQ_W1_BINARY: launch_fwd_mode<PQ_W1_BINARY>(init, outs, lt, blocks, wpr, s); break;
+    case PQ_W158_SEQ_TERNARY: launch_fwd_mode<PQ_W158_SEQ_TERNARY>(init, outs, lt, blocks, wpr, s); break;
+    case PQ_W2_SEQ: launch_fwd_mode<PQ_W2_SEQ>(init, outs, lt, blocks, wpr, s); break;
+    case PQ_W3_LSQ: launch_fwd_mode<PQ_W3_LSQ>(init, outs, lt, blocks, wpr, s); break;
+    default: launch_fwd_mode<PQ_W4_LSQ>(init, outs, lt, blocks, wpr, s); break;
+    }
+}
+
+template <int MODE, int WPR, bool GBF16>
+void launch_bwd_t(bool wdw, bool wmask, const LaunchTable &lt, int blocks, hipStream_t s)
+{
+    if (wdw && wmask)
+        hipLaunchKernelGGL((k_quant_bwd<MODE, WPR, GBF16, true, true>), dim3(blocks), dim3(256), 0, s, lt);
+    else if (wdw)
+        hipLaunchKernelGGL((k_quant_bwd<MODE, WPR, GBF16, true, false>), dim3(blocks), dim3(256), 0, s, lt);
+    else if (wmask)
+        hipLaunchKernelGGL((k_quant_bwd<MODE, WPR, GBF16, false, true>), dim3(blocks), dim3(256), 0, s, lt);
+    else
+        hipLaunchKernelGGL((k_quant_bwd<MODE, WPR, GBF16, false, false>), dim3(blocks), dim3(256), 0, s, lt);
+}
+
+template <int MODE>
+void launch_bwd_mode(int wpr, bool gbf, bool wdw, bool wmask, const LaunchTable &lt, int blocks, hipStream_t s)
+{
+    if (wpr == 1) {
+        if (gbf) launch_bwd_t<MODE, 1, true>(wdw, wmask, lt, blocks, s);
+        else launch_bwd_t<MODE, 1, false>(wdw, wmask, lt, blocks, s);
+    } else {
+        if (gbf) launch_bwd_t<MODE, 4, true>(wdw, wmask, lt, blocks, s);
+        else launch_bwd_t<MODE, 4, false>(wdw, wmask, lt, blocks, s);
+    }
+}
+
+void launch_bwd(int mode, int wpr, bool gbf, bool wdw, bool wmask, const LaunchTable &lt, int blocks, hipStream_t s)
+{
+    switch (mode) {
+    case PQ_W1_BINARY: launch_bwd_mode<PQ_W1_BINARY>(wpr, gbf, wdw, wmask, lt, blocks, s); break;
+    case PQ_W158_SEQ_TERNARY: launch_bwd_mode<PQ_W158_SEQ_TERNARY>(wpr, gbf, wdw, wmask, lt, blocks, s); break;
+    case PQ_W2_SEQ: launch_bwd_mode<PQ_W2_SEQ>(wpr, gbf, wdw, wmask, lt, blocks, s); break;
+    case PQ_W3_LSQ: launch_bwd_mode<PQ_W3_LSQ>(wpr, gbf, wdw, wmask, lt, blocks, s); break;
+    default: launch_bwd_mode<PQ_W4_LSQ>(wpr, gbf, wdw, wmask, lt, blocks, s); break;
+    }
+}
+
+unsigned fwd_outs(const pq_mat &m)
+{
+    return (m.wq_bf16 ? OUT_BF16 : 0u) | (m.wq_f32 ? OUT_F32 : 0u) | (m.codes ? OUT_CODES : 0u);
+}
+
+pq_status check_fwd_descs(int mode, int count, const pq_mat *host, unsigned flags, unsigned *outs)
+{
+    if (!valid_mode(mode)) return PQ_ERR_MODE;
+    if ((flags & ~PQ_INIT_ALPHA) != 0) return PQ_ERR_MODE;
+    if (count < 0) return PQ_ERR_ARG;
+    if (count > 0 && !host) return PQ_ERR_NULL;
+    bool have_first = false;
+    for (int i = 0; i < count; ++i) {
+        const pq_mat &m = host[i];
+        if (m.rows < 0 || !valid_cols(m.cols)) return PQ_ERR_SHAPE;
+        if (m.rows == 0) continue;  // enqueues nothing; its pointers are not used
+        const unsigned o = fwd_outs(m);
+        if (!have_first) {
+            *outs = o;
+            have_first = true;
+        } else if (o != *outs) {
+            return PQ_ERR_ARG;  // one output set per launch
+        }
+        if (!m.W || !m.alpha) return PQ_ERR_NULL;
+        if (!aligned16(m.W) || !ptr_ok(m.wq_bf16) || !ptr_ok(m.wq_f32) || !ptr_ok(m.codes) ||
+            !ptr_ok(m.alpha))
+            return PQ_ERR_ALIGN;
+    }
+    return PQ_OK;
+}
+
+pq_status check_bwd_descs(int mode, int count, const pq_mat *host, int g_dtype, bool *wdw, bool *wmask)
+{
+    if (!valid_mode(mode)) return PQ_ERR_MODE;
+    if (g_dtype != PQ_G_F32 && g_dtype != PQ_G_BF16) return PQ_ERR_MODE;
+    if (count < 0) return PQ_ERR_ARG;
+    if (count > 0 && !host) return PQ_ERR_NULL;
+    bool have_first = false;
+    for (int i = 0; i < count; ++i) {
+        const pq_mat &m = host[i];
+        if (m.rows < 0 || !valid_cols(m.cols)) return PQ_ERR_SHAPE;
+        if (m.rows == 0) continue;  // enqueues nothing; its pointers are not used
+        if (!m.W || !m.alpha || !m.G || !m.dalpha) return PQ_ERR_NULL;
+        if (!aligned16(m.W) || !aligned16(m.G) || !ptr_ok(m.dW) || !ptr_ok(m.mask_bits) ||
+            !ptr_ok(m.alpha) || !ptr_ok(m.dalpha))
+            return PQ_ERR_ALIGN;
+        if (!(m.grad_scale == m.grad_scale) || m.grad_scale > 1e300 || m.grad_scale < -1e300)
+            return PQ_ERR_ARG;
+        if (g_dtype == PQ_G_BF16 && m.dW && static_cast<const void *>(m.dW) == m.G) return PQ_ERR_ARG;
+        const bool d = m.dW != nullptr, k = m.mask_bits != nullptr;
+        if (!have_first) {
+            *wdw = d;
+            *wmask = k;
+            have_first = true;
+        } else if (d != *wdw || k != *wmask) {
+            return PQ_ERR_ARG;
+        }
+    }
+    return PQ_OK;
+}
+
+}  // namespace
+}  // namespace pq
+
+using namespace pq;
+
+extern "C" {
+
+int64_t pq_code_row_bytes(int mode, int64_t cols)
+{
+    if (!valid_mode(mode) || cols <= 0) return -1;
+    return (cols * code_bits(mode) + 7) / 8;
+}
+
+double pq_default_grad_scale(int mode, int64_t rows, int64_t cols)
+{
+    if (!valid_mode(mode) || rows <= 0 || cols <= 0) return 0.0;
+    const double qp = mode == PQ_W3_LSQ ? 3.0 : (mode == PQ_W4_LSQ ? 7.0 : 1.0);
+    return 1.0 / sqrt(static_cast<double>(rows) * static_cast<double>(cols) * qp);
+}
+
+const char *pq_status_str(pq_status s)
+{
+    switch (s) {
+    case PQ_OK: return "PQ_OK";
+    case PQ_ERR_NULL: return "PQ_ERR_NULL: a required pointer is NULL";
+    case PQ_ERR_SHAPE: return "PQ_ERR_SHAPE: bad rows/cols/M/N/K (cols and K must be positive multiples of 8)";
+    case PQ_ERR_MODE: return "PQ_ERR_MODE: unknown mode, flag or dtype";
+    case PQ_ERR_ALIGN: return "PQ_ERR_ALIGN: array pointer not 16-byte aligned";
+    case PQ_ERR_UNSUPPORTED: return "PQ_ERR_UNSUPPORTED";
+    case PQ_ERR_HIP: return "PQ_ERR_HIP: kernel launch failed";
+    case PQ_ERR_ARG: return "PQ_ERR_ARG: bad argument (descriptor table, grad_scale or aliasing)";
+    }
+    return "unknown pq_status";
+}
+
+const char *pq_version(void) { return "libpq 0.1 (gfx950)"; }
+
+pq_status pq_quantize_fwd_grouped(int mode, int count, const pq_mat *descs_host,
+                                  const pq_mat *descs_dev, unsigned flags, void *stream)
+{
+    unsigned outs = 0;
+    pq_status st = check_fwd_descs(mode, count, descs_host, flags, &outs);
+    if (st != PQ_OK) return st;
+    if (count > 0 && !descs_dev) return PQ_ERR_NULL;
+    const bool init = (flags & PQ_INIT_ALPHA) != 0;
+    return launch_grouped(count, descs_host, descs_dev, static_cast<hipStream_t>(stream),
+                          [&](const LaunchTable &lt, int blocks, int wpr, hipStream_t s) {
+                              launch_fwd(mode, init, outs, lt, blocks, wpr, s);
+                          });
+}
+
+pq_status pq_quantize_fwd(int mode, int64_t rows, int64_t cols, const float *W, float *alpha,
+                          unsigned flags, void *Wq_bf16, float *Wq_f32, uint8_t *codes,
+                          void *stream)
+{
+    pq_mat m = {};
+    m.W = W;
+    m.alpha = alpha;
+    m.wq_bf16 = Wq_bf16;
+    m.wq_f32 = Wq_f32;
+    m.codes = codes;
+    m.rows = rows;
+    m.cols = cols;
+    unsigned outs = 0;
+    pq_status st = check_fwd_descs(mode, 1, &m, flags, &outs);
+    if (st != PQ_OK) return st;
+    const bool init = (flags & PQ_INIT_ALPHA) != 0;
+    return launch_grouped(1, &m, nullptr, static_cast<hipStream_t>(stream),
+                          [&](const LaunchTable &lt, int blocks, int wpr, hipStream_t s) {
+                              launch_fwd(mode, init, outs, lt, blocks, wpr, s);
+                          });
+}
+
+pq_status pq_quantize_bwd_grouped(int mode, int count, const pq_mat *descs_host,
+                                  const pq_mat *descs_dev, int g_dtype, void *stream)
+{
+    bool wdw = false, wmask = false;
+    pq_status st = check_bwd_descs(mode, count, descs_host, g_dtype, &wdw, &wmask);
+    if (st != PQ_OK) return st;
+    if (count > 0 && !descs_dev) return PQ_ERR_NULL;
+    return launch_grouped(count, descs_host, descs_dev, static_cast<hipStream_t>(stream),
+                          [&](const LaunchTable &lt, int blocks, int wpr, hipStream_t s) {
+                              launch_bwd(mode, wpr, g_dtype == PQ_G_BF16, wdw, wmask, lt, blocks, s);
+                          });
+}
+
+pq_status pq_quantize_bwd(int mode, int64_t rows, int64_t cols, const float *W, const float *alpha,
+                          const void *G, int g_dtype, double grad_scale, float *dW, float *dalpha,
+                          uint8_t *mask_bits, void *stream)
+{
+    pq_mat m = {};
+    m.W = W;
+    m.alpha = const_cast<float *>(alpha);
+    m.G = G;
+    m.dW = dW;
+    m.dalpha = dalpha;
+    m.mask_bits = mask_bits;
+    m.grad_scale = grad_scale;
+    m.rows = rows;
+    m.cols = cols;
+    bool wdw = false, wmask = false;
+    pq_status st = check_bwd_descs(mode, 1, &m, g_dtype, &wdw, &wmask);
+    if (st != PQ_OK) return st;
+    return launch_grouped(1, &m, nullptr, static_cast<hipStream_t>(stream),
+                          [&](const LaunchTable &lt, int blocks, int wpr, hipStream_t s) {
+                              launch_bwd(mode, wpr, g_dtype == PQ_G_BF16, wdw, wmask, lt, blocks, s);
+                          });
+}
+
+static pq_status pack_common(int mode, int64_t rows, int64_t cols, const float *W,
+                             const float *alpha, uint8_t *packed, void *alpha_bf16, void *stream)
+{
+    if (!W || !alpha || !packed || !alpha_bf16) return PQ_ERR_NULL;
+    if (rows < 0 || !valid_cols(cols)) return PQ_ERR_SHAPE;
+    if (!aligned16(W) || !aligned16(alpha) || !aligned16(packed) || !aligned16(alpha_bf16))
+        return PQ_ERR_ALIGN;
+    pq_mat m = {};
+    m.W = W;
+    m.alpha = const_cast<float *>(alpha);
+    m.codes = packed;
+    m.rows = rows;
+    m.cols = cols;
+    return launch_grouped(1, &m, nullptr, static_cast<hipStream_t>(stream),
+                          [&](const LaunchTable &lt, int blocks, int wpr, hipStream_t s) {
+                              constexpr unsigned O = OUT_CODES | OUT_ALPHA_BF16;
+                              if (mode == PQ_W2_SEQ)
+                                  launch_fwd_t<PQ_W2_SEQ, false, O>(lt, blocks, wpr, s, alpha_bf16);
+                              else
+                                  launch_fwd_t<PQ_W4_LSQ, false, O>(lt, blocks, wpr, s, alpha_bf16);
+                          });
+}
+
+pq_status pq_pack_w2(int64_t rows, int64_t cols, const float *W, const float *alpha,
+                     uint8_t *packed, void *alpha_bf16, void *stream)
+{
+    return pack_common(PQ_W2_SEQ, rows, cols, W, alpha, packed, alpha_bf16, stream);
+}
+
+pq_status pq_pack_w4(int64_t rows, int64_t cols, const float *W, const float *alpha,
+                     uint8_t *packed, void *alpha_bf16, void *stream)
+{
+    return pack_common(PQ_W4_LSQ, rows, cols, W, alpha, packed, alpha_bf16, stream);
+}
+
+}  // extern "C"

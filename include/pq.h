@@ -1,0 +1,252 @@
+/*
+ * pq.h -- C ABI of libpq, the gfx950 (MI355X) implementation of the ParetoQ
+ * quantized linear layer: per-row fake-quantization of fp32 shadow weights at
+ * 1 / 1.58 / 2 / 3 / 4 bits, its straight-through backward with the learned
+ * per-row scale's gradient, 2-bit (and 4-bit) export packing, and the
+ * packed-weight x bf16-activation GEMM used at deployment.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [Note]     "ParetoQ, the strongest low-bit QAT I could find" -- sections
+ *              "QAT versus PTQ", "Finding 3", "The 2-bit recipe, in full",
+ *              "Paper vs. code".
+ *   [Rebuttal] "ParetoQ: Improving Scaling Laws in Extremely Low-bit LLM
+ *              Quantization" -- authors' replies, part on why SEQ beats LSQ.
+ *   [News]     "Meta's ParetoQ compares five bit widths and puts the accuracy
+ *              cliff at 1 bit" -- speed and storage paragraphs.
+ *   [Abstract] "ParetoQ: Scaling Laws in Extremely Low-bit LLM Quantization".
+ *
+ * Conventions shared by every entry point
+ *   Memory     Every array argument is a DEVICE pointer owned by the caller;
+ *              the library never allocates, frees or keeps a pointer after
+ *              the call returns.  Arrays are row-major and contiguous
+ *              (leading dimension = cols).  Weight matrices are [out, in]:
+ *              a "row" is one output channel, the unit the scale alpha
+ *              belongs to ([Note] "Paper vs. code": one learned scale per
+ *              row, shape (rows, 1)).
+ *   Streams    `stream` is a hipStream_t (NULL = the null stream).  Calls only
+ *              enqueue work on it and return; results are ready when the
+ *              stream is.  The library has no global mutable state, so calls
+ *              from several host threads are safe.
+ *   bf16       bf16 arrays are passed as void* and hold IEEE bfloat16 bit
+ *              patterns; every cast to bf16 rounds to nearest-even.
+ *   Errors     Arguments are checked on the host before anything is enqueued:
+ *              a NULL required pointer -> PQ_ERR_NULL; rows, cols, M, N or K
+ *              negative, cols not a positive multiple of 8, or K not a
+ *              positive multiple of 64 -> PQ_ERR_SHAPE; an unknown mode, flag or dtype -> PQ_ERR_MODE;
+ *              an array pointer not 16-byte aligned -> PQ_ERR_ALIGN; a bad
+ *              descriptor table or grad_scale -> PQ_ERR_ARG.  A failed launch
+ *              -> PQ_ERR_HIP.  On any error nothing is enqueued.  Zero rows
+ *              (or M = 0 / N = 0) is valid and enqueues nothing; the array
+ *              pointers of such an empty matrix are not checked or used.
+ *   Inputs     Weights, scales and gradients must be finite (not checked;
+ *              outputs are unspecified otherwise).  A scale alpha <= 1e-5 is
+ *              used as 1e-5 in the arithmetic (and stored unchanged), so an
+ *              all-zero row gives finite outputs.
+ */
+#ifndef PQ_H_
+#define PQ_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pq_status {
+    PQ_OK = 0,
+    PQ_ERR_NULL = 1,
+    PQ_ERR_SHAPE = 2,
+    PQ_ERR_MODE = 3,
+    PQ_ERR_ALIGN = 4,
+    PQ_ERR_UNSUPPORTED = 5,
+    PQ_ERR_HIP = 6,
+    PQ_ERR_ARG = 7
+} pq_status;
+
+/* Bit widths of the unified framework ([Abstract]: 1, 1.58, 2, 3, 4 bits).
+ * SEQ at 1.58 and 2 bits, LSQ at 3 and 4 bits ([Note] "Paper vs. code",
+ * dispatch row).  Level sets, in units of alpha:
+ *   PQ_W1_BINARY         {-1, +1}            sign(w), sign(0) = +1
+ *   PQ_W158_SEQ_TERNARY  {-2/3, 0, +2/3}     ([Note] "Finding 3"; bins of
+ *                                             [Rebuttal], 1.58-bit bullet)
+ *   PQ_W2_SEQ            {-3/4,-1/4,1/4,3/4} ([Note] "Finding 3" and the SEQ
+ *                                             formula row of "Paper vs. code")
+ *   PQ_W3_LSQ            {-4 .. 3}           ([Note] "Finding 3": integer grid)
+ *   PQ_W4_LSQ            {-8 .. 7}
+ * Stored codes: 1 bit for binary (0 -> -1, 1 -> +1); 2 bits for ternary and
+ * 2-bit SEQ (code = step + 1 resp. step + 2, so ternary never stores 3; the
+ * [News] storage paragraph notes ternary is commonly held in 2-bit integers);
+ * a 4-bit nibble for LSQ (code = step + 2^(b-1)).  Codes are a bit stream
+ * per row, first element in the lowest bits of the first byte. */
+typedef enum pq_mode {
+    PQ_W1_BINARY = 0,
+    PQ_W158_SEQ_TERNARY = 1,
+    PQ_W2_SEQ = 2,
+    PQ_W3_LSQ = 3,
+    PQ_W4_LSQ = 4
+} pq_mode;
+
+/* pq_quantize_fwd flag: compute alpha from the row first and store it
+ * ([Note] "The 2-bit recipe" table and the scale-init row of "Paper vs.
+ * code": alpha = max|w| for SEQ and ternary, max|w| / (2^(b-1)-1) for LSQ;
+ * mean|w| for 1 bit, summed in binary64). */
+#define PQ_INIT_ALPHA 1u
+
+/* Upstream-gradient dtypes for pq_quantize_bwd. */
+#define PQ_G_F32 0
+#define PQ_G_BF16 1
+
+/* Bytes per row of the code array of `mode` for `cols` weights
+ * (cols * code_bits / 8), or -1 for a bad mode / cols. */
+int64_t pq_code_row_bytes(int mode, int64_t cols);
+
+/* Default alpha-gradient scale 1/sqrt(n * Qp) with n = rows * cols and
+ * Qp = 1, 1, 1, 3, 7 for 1, 1.58, 2, 3, 4 bits ([Note] "Paper vs. code",
+ * LSQ-gradient row: LSQ's 1/sqrt(n * Qp)).  Returns 0 for a bad argument. */
+double pq_default_grad_scale(int mode, int64_t rows, int64_t cols);
+
+/* Human-readable name of a status code (static string). */
+const char *pq_status_str(pq_status s);
+
+/* Library version string (static). */
+const char *pq_version(void);
+
+/*
+ * pq_quantize_fwd -- forward fake-quantization of one weight matrix.
+ * Every training step re-quantizes the fp32 shadow weights ([Note] "QAT
+ * versus PTQ"); per weight w of row i, with a = max(alpha[i], 1e-5):
+ *   x = w / a (IEEE division), clipped to [-0.99, 0.99] for SEQ / ternary
+ *   ([Note] "Paper vs. code", first bullet) or to [Qn, Qp] for LSQ, rounded
+ *   half-to-even onto the mode's grid; q = a * level; Wq = bf16(q), the cast
+ *   to the activation dtype ([Note] "Paper vs. code", last bullet).
+ *
+ *   mode      pq_mode
+ *   rows,cols W is [rows, cols] fp32; cols a positive multiple of 8
+ *   W         in   [rows, cols] fp32 shadow weights
+ *   alpha     in   [rows] fp32 per-row scale; with PQ_INIT_ALPHA it is OUT:
+ *                  written with the row statistic, then used
+ *   flags     0 or PQ_INIT_ALPHA
+ *   Wq_bf16   out  [rows, cols] bf16 fake-quantized weights, or NULL
+ *   Wq_f32    out  [rows, cols] the same values before the bf16 cast, or NULL
+ *   codes     out  [rows, pq_code_row_bytes(mode, cols)] packed codes, or NULL
+ *   stream    hipStream_t
+ */
+pq_status pq_quantize_fwd(int mode, int64_t rows, int64_t cols, const float *W,
+                          float *alpha, unsigned flags, void *Wq_bf16, float *Wq_f32,
+                          uint8_t *codes, void *stream);
+
+/*
+ * pq_quantize_bwd -- straight-through backward of pq_quantize_fwd.
+ * Per weight (same a and x as the forward, bit for bit):
+ *   inside = x within the clip range, bounds included ([-0.99, 0.99] SEQ and
+ *            ternary, [Qn, Qp] LSQ, [-1, 1] binary);
+ *   dW     = G inside, exactly +0 outside -- the rounding is treated as the
+ *            identity inside the range and the clamp is flat outside ([Note]
+ *            "QAT versus PTQ" and the gradient paragraph of "The 2-bit
+ *            recipe, in full");
+ *   dalpha = grad_scale * sum_j s_j * G_j per row, with s = level - x inside
+ *            and s = the boundary level outside (clipped weights still feed
+ *            the scale), accumulated in binary64 and rounded once ([Note]
+ *            "Paper vs. code", LSQ-gradient row).
+ *
+ *   W, alpha   in   as in the forward (alpha is the value the forward used)
+ *   G          in   [rows, cols] dL/dWq, fp32 (PQ_G_F32) or bf16 (PQ_G_BF16)
+ *   g_dtype    PQ_G_F32 or PQ_G_BF16
+ *   grad_scale the alpha-gradient scale; pass pq_default_grad_scale(...)
+ *              for LSQ's 1/sqrt(n*Qp); must be finite
+ *   dW         out  [rows, cols] fp32, or NULL; may alias G when g_dtype is
+ *                   PQ_G_F32 (each element is read before it is written)
+ *   dalpha     out  [rows] fp32
+ *   mask_bits  out  [rows, cols/8] the `inside` bit per weight, first weight
+ *                   in the lowest bit, or NULL
+ */
+pq_status pq_quantize_bwd(int mode, int64_t rows, int64_t cols, const float *W,
+                          const float *alpha, const void *G, int g_dtype,
+                          double grad_scale, float *dW, float *dalpha,
+                          uint8_t *mask_bits, void *stream);
+
+/*
+ * pq_pack_w2 -- export a 2-bit SEQ layer for deployment: the forward's codes
+ * (bit-identical to pq_quantize_fwd(PQ_W2_SEQ, ...) codes) and the scale
+ * rounded to bf16.  Memory savings exist only after export ([Note] "Paper
+ * vs. code", last bullet); the deployed GEMM consumes this format ([News]
+ * speed paragraph).
+ *   W          in   [rows, cols] fp32, cols a positive multiple of 8
+ *   alpha      in   [rows] fp32
+ *   packed     out  [rows, cols/4] u8, 4 codes per byte, first in bits 0-1
+ *   alpha_bf16 out  [rows] bf16
+ */
+pq_status pq_pack_w2(int64_t rows, int64_t cols, const float *W, const float *alpha,
+                     uint8_t *packed, void *alpha_bf16, void *stream);
+
+/* pq_pack_w4 -- the 4-bit LSQ counterpart of pq_pack_w2 (packed [rows,
+ * cols/2] u8, low nibble first), feeding pq_w4a16_gemm, the 4-bit comparison
+ * point of the [News] speed paragraph. */
+pq_status pq_pack_w4(int64_t rows, int64_t cols, const float *W, const float *alpha,
+                     uint8_t *packed, void *alpha_bf16, void *stream);
+
+/*
+ * pq_w2a16_gemm -- deployment GEMM with packed 2-bit SEQ weights and bf16
+ * activations ([News] speed paragraph: 2-bit-weight kernel against FP16 and
+ * 4-bit weights at a 16384 x 16384 weight; the layer has no bias, [Note]
+ * "Paper vs. code"):
+ *   Y[m, n] = bf16( alpha_bf16[n] * sum_k X[m, k] * level(code[n, k]) )
+ * with level(c) = (c - 1.5) / 2, fp32 accumulation.
+ *   M, N, K    X is [M, K]; K a positive multiple of 64 (so every packed
+ *              row is a whole number of 16-byte words); M, N >= 0
+ *   X          in   [M, K] bf16 activations
+ *   packed     in   [N, K/4] u8 from pq_pack_w2
+ *   alpha_bf16 in   [N] bf16
+ *   Y          out  [M, N] bf16
+ */
+pq_status pq_w2a16_gemm(int64_t M, int64_t N, int64_t K, const void *X,
+                        const uint8_t *packed, const void *alpha_bf16, void *Y,
+                        void *stream);
+
+/* pq_w4a16_gemm -- the same GEMM on pq_pack_w4 weights: packed [N, K/2],
+ * level(c) = c - 8. */
+pq_status pq_w4a16_gemm(int64_t M, int64_t N, int64_t K, const void *X,
+                        const uint8_t *packed, const void *alpha_bf16, void *Y,
+                        void *stream);
+
+/*
+ * Grouped launches: one kernel launch over a whole stack of matrices (for
+ * example every projection of every layer of a model), since a training step
+ * re-quantizes all of them with the same mode.
+ *
+ * pq_mat describes one matrix.  The caller fills an array of them twice --
+ * in host memory (checked and used for launch sizing) and an identical copy
+ * in device memory (read by the kernels); the two must hold the same values.
+ * Unused fields may be NULL.  Any count >= 0 is accepted (large stacks are
+ * split over several launches internally).
+ */
+typedef struct pq_mat {
+    const float *W;       /* [rows, cols] fp32                             */
+    float *alpha;         /* [rows] fp32 (in; out with PQ_INIT_ALPHA)      */
+    void *wq_bf16;        /* fwd out [rows, cols] bf16, or NULL            */
+    float *wq_f32;        /* fwd out [rows, cols] fp32, or NULL            */
+    uint8_t *codes;       /* fwd out codes, or NULL                        */
+    const void *G;        /* bwd in [rows, cols] (dtype per call)          */
+    float *dW;            /* bwd out [rows, cols] fp32, or NULL            */
+    float *dalpha;        /* bwd out [rows] fp32                           */
+    uint8_t *mask_bits;   /* bwd out [rows, cols/8], or NULL               */
+    double grad_scale;    /* bwd alpha-gradient scale for this matrix      */
+    int64_t rows;
+    int64_t cols;         /* positive multiple of 8                        */
+} pq_mat;
+
+/* Forward over `count` matrices; per matrix exactly pq_quantize_fwd.
+ * descs_host / descs_dev: identical pq_mat[count] in host / device memory. */
+pq_status pq_quantize_fwd_grouped(int mode, int count, const pq_mat *descs_host,
+                                  const pq_mat *descs_dev, unsigned flags, void *stream);
+
+/* Backward over `count` matrices; per matrix exactly pq_quantize_bwd with
+ * that entry's grad_scale. */
+pq_status pq_quantize_bwd_grouped(int mode, int count, const pq_mat *descs_host,
+                                  const pq_mat *descs_dev, int g_dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PQ_H_ */

@@ -1,0 +1,124 @@
+"""The C ABI without a GPU: the library loads, exports every symbol that
+include/pq.h declares, and rejects bad arguments on the host (nothing is
+enqueued, so no device is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def pq():
+    from bit_quantization_aware_amd import pq as _pq
+    return _pq
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "pq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(pq):
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(pq.lib, n), n
+    assert set(names) == set(pq.EXPORTS)
+
+
+def test_struct_layout(pq):
+    assert ctypes.sizeof(pq.pq_mat) == 96
+
+
+def test_helpers(pq):
+    assert pq.pq_code_row_bytes(pq.PQ_W2_SEQ, 64) == 16
+    assert pq.pq_code_row_bytes(pq.PQ_W1_BINARY, 64) == 8
+    assert pq.pq_code_row_bytes(pq.PQ_W4_LSQ, 64) == 32
+    assert pq.pq_code_row_bytes(9, 64) == -1
+    assert pq.pq_default_grad_scale(pq.PQ_W4_LSQ, 4, 16) == pytest.approx((4 * 16 * 7) ** -0.5)
+    assert pq.pq_default_grad_scale(pq.PQ_W2_SEQ, 0, 16) == 0.0
+    assert "NULL" in pq.pq_status_str(1)
+    assert "gfx950" in pq.pq_version()
+
+
+A = 0x100000          # fake, 16-byte aligned device addresses: never dereferenced,
+B = 0x200000          # because every call below fails validation first
+MIS = 0x100004        # not 16-byte aligned
+
+
+def rc(fn, *args):
+    return fn(*args)
+
+
+def test_fwd_argument_checks(pq):
+    L = pq.lib
+    assert L.pq_quantize_fwd(2, 4, 64, None, A, 0, B, None, None, None) == 1      # W NULL
+    assert L.pq_quantize_fwd(2, 4, 64, A, None, 0, B, None, None, None) == 1      # alpha NULL
+    assert L.pq_quantize_fwd(2, 4, 60, A, B, 0, B, None, None, None) == 2         # cols % 8
+    assert L.pq_quantize_fwd(2, 4, 0, A, B, 0, B, None, None, None) == 2          # cols 0
+    assert L.pq_quantize_fwd(2, -1, 64, A, B, 0, B, None, None, None) == 2        # rows < 0
+    assert L.pq_quantize_fwd(7, 4, 64, A, B, 0, B, None, None, None) == 3         # mode
+    assert L.pq_quantize_fwd(2, 4, 64, A, B, 4, B, None, None, None) == 3         # flag
+    assert L.pq_quantize_fwd(2, 4, 64, MIS, B, 0, B, None, None, None) == 4       # align
+    assert L.pq_quantize_fwd(2, 4, 64, A, B, 0, MIS, None, None, None) == 4
+    assert L.pq_quantize_fwd(2, 0, 64, A, B, 0, B, None, None, None) == 0         # empty: no-op
+
+
+def test_bwd_argument_checks(pq):
+    L = pq.lib
+    ok = (2, 4, 64, A, B, A, 0, 1.0, B, B, None, None)
+    args = list(ok)
+    args[5] = None
+    assert L.pq_quantize_bwd(*args) == 1                                         # G NULL
+    args = list(ok)
+    args[9] = None
+    assert L.pq_quantize_bwd(*args) == 1                                         # dalpha NULL
+    args = list(ok)
+    args[6] = 5
+    assert L.pq_quantize_bwd(*args) == 3                                         # g dtype
+    args = list(ok)
+    args[7] = float("nan")
+    assert L.pq_quantize_bwd(*args) == 7                                         # grad_scale
+    args = list(ok)
+    args[6], args[8] = 1, A
+    assert L.pq_quantize_bwd(*args) == 7                                         # bf16 G aliased
+    args = list(ok)
+    args[5] = MIS
+    assert L.pq_quantize_bwd(*args) == 4
+    args = list(ok)
+    args[1] = 0
+    assert L.pq_quantize_bwd(*args) == 0                                         # empty
+
+
+def test_pack_and_gemm_argument_checks(pq):
+    L = pq.lib
+    assert L.pq_pack_w2(4, 64, None, A, B, A, None) == 1
+    assert L.pq_pack_w2(4, 12, A, A, B, A, None) == 2
+    assert L.pq_pack_w4(4, 64, A, A, MIS, A, None) == 4
+    assert L.pq_w2a16_gemm(4, 8, 64, None, A, B, A, None) == 1
+    assert L.pq_w2a16_gemm(4, 8, 60, A, A, B, A, None) == 2
+    assert L.pq_w2a16_gemm(4, 8, 72, A, A, B, A, None) == 2                       # K % 64
+    assert L.pq_w2a16_gemm(-1, 8, 64, A, A, B, A, None) == 2
+    assert L.pq_w4a16_gemm(4, 8, 64, A, MIS, B, A, None) == 4
+    assert L.pq_w2a16_gemm(0, 8, 64, A, A, B, A, None) == 0                       # empty
+
+
+def test_grouped_argument_checks(pq):
+    L = pq.lib
+    mats = (pq.pq_mat * 2)()
+    mats[0].W, mats[0].alpha, mats[0].rows, mats[0].cols = A, B, 4, 64
+    mats[1].W, mats[1].alpha, mats[1].rows, mats[1].cols = A, B, 4, 60
+    h = ctypes.addressof(mats)
+    assert L.pq_quantize_fwd_grouped(2, 2, h, A, 0, None) == 2                    # cols % 8
+    mats[1].cols = 64
+    mats[1].wq_bf16 = B
+    assert L.pq_quantize_fwd_grouped(2, 2, h, A, 0, None) == 7                    # mixed outputs
+    assert L.pq_quantize_fwd_grouped(2, 2, h, None, 0, None) == 7 or \
+        L.pq_quantize_fwd_grouped(2, 2, h, None, 0, None) == 1
+    assert L.pq_quantize_fwd_grouped(2, -1, h, A, 0, None) == 7
+    assert L.pq_quantize_fwd_grouped(2, 0, None, None, 0, None) == 0              # empty stack
+    assert L.pq_quantize_bwd_grouped(2, 2, h, A, 0, None) == 1                    # G NULL
