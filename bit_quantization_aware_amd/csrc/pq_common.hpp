@@ -9,6 +9,13 @@
 
 namespace pq {
 
+// Global-memory (address space 1) pointers: descriptors are loaded from
+// memory, so without this the compiler could only emit flat accesses.
+#define PQ_GLOBAL __attribute__((address_space(1)))
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 inline bool valid_mode(int mode) { return mode >= PQ_W1_BINARY && mode <= PQ_W4_LSQ; }

@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "pq_common.hpp"
 
 namespace pq {
@@ -62,11 +64,26 @@ template <> struct Mode<PQ_W4_LSQ> {
     static constexpr float lo = -8.0f, hi = 7.0f;
 };
 
+// x = w / a rounded to binary32, computed as RN32(RN64(w * y)) with
+// y = RN64(1 / a) taken once per row.  This equals the correctly rounded
+// binary32 quotient whenever |w / a| >= 2^-125: the exact quotient of two
+// binary32 numbers is never a binary32 rounding midpoint and lies at a
+// relative distance of at least 2^-50 from every midpoint, while the binary64
+// product is within 2^-52 (relative) of it, so both round the same way.
+// Quotients in or near the subnormal range take the IEEE division.
+__device__ __forceinline__ float div_rn(float w, float a, double y)
+{
+    const double q = static_cast<double>(w) * y;
+    float x = static_cast<float>(q);
+    if (__builtin_expect(fabs(q) < 0x1p-125 && q != 0.0, 0)) x = w / a;
+    return x;
+}
+
 // One weight: returns its code; writes the level (binary32, exact) and x = w/a.
 template <int MODE>
-__device__ __forceinline__ uint32_t quant1(float w, float a, float &lvl, float &x)
+__device__ __forceinline__ uint32_t quant1(float w, float a, double y, float &lvl, float &x)
 {
-    x = w / a;
+    x = div_rn(w, a, y);
     if constexpr (MODE == PQ_W2_SEQ) {
         // [Note] "Paper vs. code", SEQ row: round(Clip(x) * k/2 - 0.5) + 0.5, k = 4;
         // the level (r + 0.5) * 2/k is exact, so alpha * level equals the
@@ -173,7 +190,7 @@ __global__ __launch_bounds__(256) void k_quant_fwd(LaunchTable lt, void *alpha_b
 
     const int64_t cols = m.cols;
     const int nq = static_cast<int>(cols >> 2);
-    const float4 *wr = reinterpret_cast<const float4 *>(m.W + row * cols);
+    const PQ_GLOBAL f32x4 *wr = (const PQ_GLOBAL f32x4 *)(m.W + row * cols);
 
     float alpha_raw;
     if constexpr (INIT) {
@@ -181,7 +198,7 @@ __global__ __launch_bounds__(256) void k_quant_fwd(LaunchTable lt, void *alpha_b
         if constexpr (MODE == PQ_W1_BINARY) {
             double s = 0.0;
             for (int q = tl; q < nq; q += TEAM) {
-                float4 v = wr[q];
+                const f32x4 v = wr[q];
                 s += static_cast<double>(fabsf(v.x));
                 s += static_cast<double>(fabsf(v.y));
                 s += static_cast<double>(fabsf(v.z));
@@ -192,7 +209,7 @@ __global__ __launch_bounds__(256) void k_quant_fwd(LaunchTable lt, void *alpha_b
         } else {
             float mx = 0.0f;
             for (int q = tl; q < nq; q += TEAM) {
-                float4 v = wr[q];
+                const f32x4 v = wr[q];
                 mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
             }
             mx = team_max<WPR>(mx, lds_f);
@@ -204,6 +221,7 @@ __global__ __launch_bounds__(256) void k_quant_fwd(LaunchTable lt, void *alpha_b
         alpha_raw = m.alpha[row];
     }
     const float a = alpha_raw > kAlphaFloor ? alpha_raw : kAlphaFloor;
+    const double y = 1.0 / static_cast<double>(a);
 
     if constexpr ((OUTS & OUT_ALPHA_BF16) != 0) {
         if (tl == 0) {
@@ -212,39 +230,42 @@ __global__ __launch_bounds__(256) void k_quant_fwd(LaunchTable lt, void *alpha_b
         }
     }
 
-    uint2 *wq16 = (OUTS & OUT_BF16) ? reinterpret_cast<uint2 *>(static_cast<uint16_t *>(m.wq_bf16) + row * cols) : nullptr;
-    float4 *wq32 = (OUTS & OUT_F32) ? reinterpret_cast<float4 *>(m.wq_f32 + row * cols) : nullptr;
-    uint8_t *crow = (OUTS & OUT_CODES) ? m.codes + row * (cols * CW / 8) : nullptr;
+    PQ_GLOBAL u32x2 *wq16 = (OUTS & OUT_BF16) ? (PQ_GLOBAL u32x2 *)(static_cast<uint16_t *>(m.wq_bf16) + row * cols) : nullptr;
+    PQ_GLOBAL f32x4 *wq32 = (OUTS & OUT_F32) ? (PQ_GLOBAL f32x4 *)(m.wq_f32 + row * cols) : nullptr;
+    PQ_GLOBAL uint8_t *crow = (OUTS & OUT_CODES) ? (PQ_GLOBAL uint8_t *)(m.codes + row * (cols * CW / 8)) : nullptr;
 
-    for (int base = 0; base < nq; base += TEAM * kUnroll) {
-        float4 v[kUnroll] = {};
+    // One pass: kUnroll quads per lane, loads first.  GUARD only on the last.
+    auto pass = [&](int base, auto guard_c) {
+        constexpr bool GUARD = decltype(guard_c)::value;
+        f32x4 v[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int q = base + u * TEAM + tl;
-            if (q < nq) v[u] = wr[q];
+            if (!GUARD || q < nq) v[u] = wr[q];
+            else v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int q = base + u * TEAM + tl;
-            const bool act = q < nq;
+            const bool act = !GUARD || q < nq;
             float l0, l1, l2, l3, x;
-            const uint32_t c0 = quant1<MODE>(v[u].x, a, l0, x);
-            const uint32_t c1 = quant1<MODE>(v[u].y, a, l1, x);
-            const uint32_t c2 = quant1<MODE>(v[u].z, a, l2, x);
-            const uint32_t c3 = quant1<MODE>(v[u].w, a, l3, x);
+            const uint32_t c0 = quant1<MODE>(v[u].x, a, y, l0, x);
+            const uint32_t c1 = quant1<MODE>(v[u].y, a, y, l1, x);
+            const uint32_t c2 = quant1<MODE>(v[u].z, a, y, l2, x);
+            const uint32_t c3 = quant1<MODE>(v[u].w, a, y, l3, x);
             const float q0 = a * l0, q1 = a * l1, q2 = a * l2, q3 = a * l3;
             if constexpr ((OUTS & OUT_BF16) != 0) {
-                if (act) wq16[q] = make_uint2(pack_bf16x2(q0, q1), pack_bf16x2(q2, q3));
+                if (act) wq16[q] = u32x2{pack_bf16x2(q0, q1), pack_bf16x2(q2, q3)};
             }
             if constexpr ((OUTS & OUT_F32) != 0) {
-                if (act) wq32[q] = make_float4(q0, q1, q2, q3);
+                if (act) wq32[q] = f32x4{q0, q1, q2, q3};
             }
             if constexpr ((OUTS & OUT_CODES) != 0) {
                 if constexpr (CW == 2) {
                     if (act) crow[q] = static_cast<uint8_t>(c0 | (c1 << 2) | (c2 << 4) | (c3 << 6));
                 } else if constexpr (CW == 4) {
                     if (act)
-                        reinterpret_cast<uint16_t *>(crow)[q] =
+                        ((PQ_GLOBAL uint16_t *)crow)[q] =
                             static_cast<uint16_t>(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
                 } else {
                     // 1 bit: a nibble per quad; even lane takes its odd neighbour's.
@@ -254,7 +275,11 @@ __global__ __launch_bounds__(256) void k_quant_fwd(LaunchTable lt, void *alpha_b
                 }
             }
         }
-    }
+    };
+    constexpr int STEP = TEAM * kUnroll;
+    const int nfull = nq / STEP * STEP;
+    for (int base = 0; base < nfull; base += STEP) pass(base, std::false_type{});
+    if (nfull < nq) pass(nfull, std::true_type{});
 }
 
 // Backward: per weight the forward's x and level (bit-identical), the clip
@@ -277,37 +302,44 @@ __global__ __launch_bounds__(256) void k_quant_bwd(LaunchTable lt)
 
     const int64_t cols = m.cols;
     const int nq = static_cast<int>(cols >> 2);
-    const float4 *wr = reinterpret_cast<const float4 *>(m.W + row * cols);
-    const float4 *gr32 = GBF16 ? nullptr : reinterpret_cast<const float4 *>(static_cast<const float *>(m.G) + row * cols);
-    const uint2 *gr16 = GBF16 ? reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(m.G) + row * cols) : nullptr;
-    float4 *dwr = WDW ? reinterpret_cast<float4 *>(m.dW + row * cols) : nullptr;
-    uint8_t *mrow = WMASK ? m.mask_bits + row * (cols >> 3) : nullptr;
+    const PQ_GLOBAL f32x4 *wr = (const PQ_GLOBAL f32x4 *)(m.W + row * cols);
+    const PQ_GLOBAL f32x4 *gr32 = (const PQ_GLOBAL f32x4 *)(static_cast<const float *>(m.G) + row * cols);
+    const PQ_GLOBAL u32x2 *gr16 = (const PQ_GLOBAL u32x2 *)(static_cast<const uint16_t *>(m.G) + row * cols);
+    PQ_GLOBAL f32x4 *dwr = WDW ? (PQ_GLOBAL f32x4 *)(m.dW + row * cols) : nullptr;
+    PQ_GLOBAL uint8_t *mrow = WMASK ? (PQ_GLOBAL uint8_t *)(m.mask_bits + row * (cols >> 3)) : nullptr;
 
     const float alpha_raw = m.alpha[row];
     const float a = alpha_raw > kAlphaFloor ? alpha_raw : kAlphaFloor;
+    const double y = 1.0 / static_cast<double>(a);
     constexpr float lo = Mode<MODE>::lo, hi = Mode<MODE>::hi;
     double acc = 0.0;
 
-    for (int base = 0; base < nq; base += TEAM * kUnroll) {
-        float4 wv[kUnroll] = {}, gv[kUnroll] = {};
+    // One pass: kUnroll quads per lane; all W and G loads are issued before
+    // any store, so dW may overwrite G in place.
+    auto pass = [&](int base, auto guard_c) {
+        constexpr bool GUARD = decltype(guard_c)::value;
+        f32x4 wv[kUnroll], gv[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int q = base + u * TEAM + tl;
-            if (q < nq) {
+            if (!GUARD || q < nq) {
                 wv[u] = wr[q];
                 if constexpr (GBF16) {
-                    const uint2 h = gr16[q];
-                    gv[u] = make_float4(bf16_to_f32(h.x & 0xFFFFu), bf16_to_f32(h.x >> 16),
-                                        bf16_to_f32(h.y & 0xFFFFu), bf16_to_f32(h.y >> 16));
+                    const u32x2 h = gr16[q];
+                    gv[u] = f32x4{bf16_to_f32(h.x & 0xFFFFu), bf16_to_f32(h.x >> 16),
+                                  bf16_to_f32(h.y & 0xFFFFu), bf16_to_f32(h.y >> 16)};
                 } else {
                     gv[u] = gr32[q];
                 }
+            } else {
+                wv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                gv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int q = base + u * TEAM + tl;
-            const bool act = q < nq;
+            const bool act = !GUARD || q < nq;
             const float w4[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
             const float g4[4] = {gv[u].x, gv[u].y, gv[u].z, gv[u].w};
             float d4[4];
@@ -315,22 +347,28 @@ __global__ __launch_bounds__(256) void k_quant_bwd(LaunchTable lt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 float lvl, x;
-                quant1<MODE>(w4[e], a, lvl, x);
+                quant1<MODE>(w4[e], a, y, lvl, x);
                 const bool inside = (x >= lo) && (x <= hi);
                 d4[e] = inside ? g4[e] : 0.0f;
                 nib |= static_cast<uint32_t>(inside) << e;
                 const double s = static_cast<double>(lvl) - (inside ? static_cast<double>(x) : 0.0);
-                if (act) acc += s * static_cast<double>(g4[e]);
+                // inactive lanes loaded zeros, so their products are +0
+                acc += s * static_cast<double>(g4[e]);
             }
             if constexpr (WDW) {
-                if (act) dwr[q] = make_float4(d4[0], d4[1], d4[2], d4[3]);
+                if (act) dwr[q] = f32x4{d4[0], d4[1], d4[2], d4[3]};
             }
             if constexpr (WMASK) {
                 const uint32_t hi4 = __shfl_down(nib, 1);
                 if (act && (tl & 1) == 0) mrow[q >> 1] = static_cast<uint8_t>(nib | (hi4 << 4));
             }
         }
-    }
+    };
+    constexpr int STEP = TEAM * kUnroll;
+    const int nfull = nq / STEP * STEP;
+    for (int base = 0; base < nfull; base += STEP) pass(base, std::false_type{});
+    if (nfull < nq) pass(nfull, std::true_type{});
+
     acc = team_sum<WPR>(acc, lds_d);
     if (tl == 0) m.dalpha[row] = static_cast<float>(m.grad_scale * acc);
 }

@@ -281,3 +281,37 @@ def test_mobilellm_125m_full_stack(mode):
     print(f"[125M stack mode={mode}: {n} matrices]", flush=True)
     outs = run_grouped(mode, mats, init=True)
     check_grouped(mode, mats, outs, f"125M m{mode}")
+
+
+BOUNDARIES = {
+    O.SEQ2: [0.0, 0.5, -0.5, 0.99, -0.99, 0.25, -0.75],
+    O.TERNARY: [1.0 / 3.0, -1.0 / 3.0, 0.99, -0.99, 0.0],
+    O.LSQ3: [-4.0, 3.0, -3.5, 2.5, 0.5, -0.5, 1.5],
+    O.LSQ4: [-8.0, 7.0, -7.5, 6.5, 0.5, -0.5, 3.5],
+    O.BINARY: [1.0, -1.0, 0.0],
+}
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_division_at_decision_boundaries(mode):
+    """w / alpha is computed on the GPU as a binary64 product with 1/alpha;
+    it must round exactly like the IEEE binary32 division wherever the result
+    decides a code or a mask bit: weights at fl32(b * alpha) and +-3 ulps for
+    every decision boundary b, over 300 log-spread scales."""
+    rng = np.random.default_rng(300 + mode)
+    alphas = np.exp(rng.uniform(np.log(1e-4), np.log(30.0), 300)).astype(np.float32)
+    cols_raw = []
+    for b in BOUNDARIES[mode]:
+        w0 = (np.float32(b) * alphas).astype(np.float32)
+        for k in range(-3, 4):
+            w = w0.copy()
+            step = np.float32(np.inf) if k > 0 else np.float32(-np.inf)
+            for _ in range(abs(k)):
+                w = np.nextafter(w, step).astype(np.float32)
+            cols_raw.append(w)
+    W = np.stack(cols_raw, axis=1).astype(np.float32)
+    pad = (-W.shape[1]) % 8
+    W = np.concatenate([W, np.zeros((W.shape[0], pad), np.float32)], axis=1)
+    G = rng.standard_normal(W.shape).astype(np.float32)
+    check_fwd(mode, W, alphas, False, f"div-boundary fwd m{mode}")
+    check_bwd(mode, W, alphas, G, f"div-boundary bwd m{mode}")
