@@ -35,17 +35,21 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <map>
+#include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "pq_common.hpp"
 
-// Streaming-kernel shape: waves per block and groups in flight per wave.
-// Tiled kernel shapes <TM, TN, WM, WN, BK> for 16 < M <= 64 and M > 64.
-#ifndef PQ_TILE_MID
-#define PQ_TILE_MID 2, 1, 2, 2, 256
+// Tiled-kernel LDS ring depth (2- and 4-bit); streaming-kernel shape: waves
+// per block, groups in flight per wave and column tiles per block.
+#ifndef PQ_TILE_P2
+#define PQ_TILE_P2 6
 #endif
-#ifndef PQ_TILE_BIG
-#define PQ_TILE_BIG 4, 4, 2, 2, 128
+#ifndef PQ_TILE_P4
+#define PQ_TILE_P4 4
 #endif
 #ifndef PQ_STREAM_NW
 #define PQ_STREAM_NW 4
@@ -81,240 +85,361 @@ struct GemmArgs {
     int M, N, K;
 };
 
-// Decode of one 4-bit output bf16x2 from a dword of codes: nibbles I and
-// I+4 -> mantissa bits 3-6 of each half of bf16 2.0, i.e. 2 + c/8.
-template <int I>
-__device__ __forceinline__ uint32_t decode_pair4(uint32_t d)
+// ---------------------------------------------------------------------------
+// Tiled kernel for M > 16.
+//
+// A block owns a 64 x 256 output tile; its four waves each own 64 columns
+// (4 x 4 MFMA tiles of 16 x 16), so every wave reads the whole 64-row
+// activation tile and every decoded weight fragment feeds four MFMAs.  K runs
+// in stages of 64.  Each stage's activation tile (64 rows x 128 B) and code
+// tile (256 columns x 16 B, or 32 B at 4 bits) are copied global -> LDS by
+// the gfx950 LDS-DMA loads (global_load_lds_dwordx4), with no register or
+// VALU traffic, into a ring of P stage buffers kept P - 1 stages ahead.  One
+// s_waitcnt plus one barrier per stage orders the ring.
+//
+// LDS activation layout: row r holds its eight 16-byte k-chunks with chunk c
+// stored in slot c ^ xswz(r).  The DMA writes 1 KB contiguous per wave
+// instruction (eight rows), so the swizzle is applied on the global side:
+// the lane that fills slot s of row r fetches chunk s ^ xswz(r).
+//
+// Lane (i16, grp) takes k = 16 * grp + 8 * t + [0, 8) of the stage at k-step
+// t, so its codes for a stage are one dword (2-bit) or two (4-bit), and the
+// decode yields the eight codes in natural k order:
+//   2-bit: w0 = (d & 0x03030303) | ((d << 2) & 0x30303030) holds codes
+//          (4q, 4q+1) as fp4 nibbles in byte q, w1 the same of d >> 4 holds
+//          (4q+2, 4q+3); the fp4 -> bf16 pair convert of bytes (w0.0, w1.0,
+//          w0.1, w1.1) gives codes 0..7 as c/2, bytes 2 and 3 give 8..15.
+//   4-bit: byte p of d & 0x0F0F0F0F and of (d >> 4) & 0x0F0F0F0F hold codes
+//          2p and 2p+1; a byte permute places them in the two bf16 halves and
+//          (q << 3) | 0x40004000 makes 2 + c/8.
+// Row sums of X for the level offset come from v_dot2_f32_bf16 on the A
+// fragments already in registers (wave w sums row tile w).
+//
+// When the tile grid is too small to fill the chip, K is split over blocks;
+// each split writes fp32 partials (with its own offset term) to a
+// workspace and a second kernel sums the splits, scales by alpha and rounds
+// to bf16.  Block order is XCD-aware: the eight XCDs take workgroups round
+// robin, so consecutive tile indices are given to the blocks of one XCD and
+// the m-tiles that share a weight tile share that XCD's L2.
+// ---------------------------------------------------------------------------
+constexpr int kTileM = 64;
+constexpr int kTileN = 256;
+constexpr int kStageK = 64;
+
+struct TileArgs {
+    const uint16_t *X;       // [M, K] bf16
+    const uint8_t *packed;   // [N, K * BITS / 8]
+    const uint16_t *alpha;   // [N] bf16
+    uint16_t *Y;             // [M, N] bf16 (single split)
+    float *ws;               // [splits, M, N] fp32 partials (several splits)
+    int M, N, K;
+    int mtiles, ntiles, splits;
+    int kps;                 // k per split, a multiple of kStageK
+};
+
+// Activation LDS swizzle: chunk c of tile row r sits in slot c ^ xswz(r).
+// Rows 0-7 (and 8-15) get distinct slots and rows r, r + 8 differ in the
+// slot's low bit, so the 16 rows one A-operand read touches are spread over
+// all banks whether the LDS serves 8 or 16 lanes of a 16-byte read per clock.
+__device__ __forceinline__ int xswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <int BITS>
+struct TileCfg {
+    static constexpr int CB = 8 * BITS;                  // code bytes per column per stage
+    static constexpr int XBYTES = kTileM * kStageK * 2;  // 8 KB
+    static constexpr int CBYTES = kTileN * CB;           // 4 or 8 KB
+    static constexpr int SBYTES = XBYTES + CBYTES;
+    static constexpr int P = BITS == 2 ? PQ_TILE_P2 : PQ_TILE_P4;  // ring depth (72 / 64 KB)
+    static constexpr int LOADS = 2 + CBYTES / 4096;      // DMA instructions per wave per stage
+};
+
+// One LDS-DMA load: every lane fetches 16 bytes at `base + off` (`base`
+// wave-uniform, in SGPRs) and the wave's 64 results land contiguously at LDS
+// byte address `lds_addr` (via M0).  Issued from asm so that the compiler,
+// which cannot tell the ring slots apart, does not wait for every DMA before
+// each LDS read; the kernel orders the ring itself with s_waitcnt vmcnt and
+// s_barrier.  The instruction writes no VGPRs.
+__device__ __forceinline__ void dma16(const void *base, uint32_t off, uint32_t lds_addr)
 {
-    constexpr int sh = 4 * I - 3;
-    uint32_t t;
-    if constexpr (sh >= 0) t = d >> sh;
-    else t = d << (-sh);
-    return (t & 0x00780078u) | 0x40004000u;
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds_addr)
+                 : "memory", "m0");
 }
 
-// B operand (8 bf16) for MFMA k-step T of a stage from the lane's code dwords.
-// 2-bit: dword T/2; its even codes (T even) or odd codes (T odd) as exact
-// bf16 c/2 through the fp4 convert (pairs (4b, 4b+2) resp. (4b+1, 4b+3)).
-// 4-bit: dword T, pairs (i, i+4).
-template <int BITS, int T>
-__device__ __forceinline__ bf16x8 decode_b(const uint32_t *cw)
+__device__ __forceinline__ void block_barrier()
 {
-    uint4 r;
-    if constexpr (BITS == 2) {
-        const uint32_t d = cw[T >> 1];
-        const uint32_t m = ((T & 1) ? (d >> 2) : d) & 0x33333333u;
-        r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(m, 1.0f, 0));
-        r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(m, 1.0f, 1));
-        r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(m, 1.0f, 2));
-        r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(m, 1.0f, 3));
-    } else {
-        const uint32_t d = cw[T];
-        r.x = decode_pair4<0>(d);
-        r.y = decode_pair4<1>(d);
-        r.z = decode_pair4<2>(d);
-        r.w = decode_pair4<3>(d);
-    }
-    return __builtin_bit_cast(bf16x8, r);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
-template <int BITS, int TM, int TN, int WM, int WN, int BK>
-__global__ __launch_bounds__(256) void k_gemm(GemmArgs g)
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
 {
-    static_assert(WM * WN == 4, "four waves per block");
-    static_assert(BK == 128 || BK == 256, "code loads are 8- or 16-byte (2-bit) / 16- or 32-byte (4-bit) per lane");
-    constexpr int BM = 16 * TM * WM;
-    constexpr int BN = 16 * TN * WN;
-    constexpr int KSTEPS = BK / 32;               // MFMA k-steps per stage
-    constexpr int CW = BK * BITS / 128;           // code dwords per lane per tile per stage
-    constexpr int CH = BITS == 2 ? 16 : 8;        // X staging chunk (elements), one permutation block
-    constexpr int CPR = BK / CH;                  // chunks per X row per stage
-    constexpr int NCHUNK = BM * CPR;
-    constexpr int NCT = (NCHUNK + 255) / 256;     // chunks per thread
-    constexpr int LDS_ROW = BK + 8;               // bf16 per LDS row (+16 bytes of padding)
-    static_assert(CPR <= 64 && (64 % CPR) == 0, "a row's chunks stay inside one wave");
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
-    __shared__ __attribute__((aligned(16))) uint16_t xs[BM * LDS_ROW];
-    __shared__ float ssum[BM];
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL));
+}
+
+template <int BITS, int P>
+__global__ __launch_bounds__(256, 2) void k_gemm_tile(TileArgs g)
+{
+    using C = TileCfg<BITS>;
+    static_assert(P >= 3, "ring depth");
+    // Ring: P activation stages, then P code stages.
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[P * C::SBYTES];
+    __shared__ float ssum[kTileM];
+    constexpr int XR = 0;                 // activation region
+    constexpr int CR = P * C::XBYTES;     // code region
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int i16 = lane & 15, grp = lane >> 4;
 
+    // Block -> (m-tile, n-tile, split), consecutive indices on one XCD.
+    int t = blockIdx.x;
+    const int nb = gridDim.x;
+    if ((nb & 7) == 0) t = (t & 7) * (nb >> 3) + (t >> 3);
+    const int mt = t % g.mtiles;
+    t /= g.mtiles;
+    const int nt = t % g.ntiles;
+    const int split = t / g.ntiles;
+
     const int M = g.M, N = g.N, K = g.K;
-    const int m0 = blockIdx.y * BM;
-    const int n0 = blockIdx.x * BN;
+    const int m0 = mt * kTileM, n0 = nt * kTileN;
+    const int kbeg = split * g.kps;
+    const int kend = min(K, kbeg + g.kps);
+    const int ns = (kend - kbeg) / kStageK;
     const int64_t row_bytes = static_cast<int64_t>(K) * BITS / 8;
 
-    // This lane's weight rows (one per N tile) and their validity.
-    const uint8_t *crow[TN];
-    bool cval[TN];
+    // DMA sources: a wave-uniform base (advanced per stage) plus a fixed
+    // per-lane byte offset.  Rows >= M and columns >= N read row M-1 / N-1.
+    const uint8_t *xbase = reinterpret_cast<const uint8_t *>(g.X + static_cast<int64_t>(m0) * K + kbeg);
+    const uint8_t *cbase = g.packed + static_cast<int64_t>(n0) * row_bytes + static_cast<int64_t>(kbeg) * BITS / 8;
+    uint32_t xoff[2];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * 16 * TN + j * 16 + i16;
-        cval[j] = n < N;
-        crow[j] = g.packed + static_cast<int64_t>(cval[j] ? n : 0) * row_bytes;
+    for (int q = 0; q < 2; ++q) {
+        const int r = 8 * (2 * w + q) + (lane >> 3);
+        const int c = (lane & 7) ^ xswz(r);
+        xoff[q] = static_cast<uint32_t>((min(m0 + r, M - 1) - m0) * K * 2 + 16 * c);
     }
+    constexpr int NCL = C::CBYTES / 4096;   // code DMA instructions per wave
+    uint32_t coff[NCL];
+#pragma unroll
+    for (int q = 0; q < NCL; ++q) {
+        const int cl = BITS == 2 ? 64 * w + lane : 64 * w + 32 * q + (lane >> 1);
+        const int part = BITS == 2 ? 0 : 16 * (lane & 1);
+        coff[q] = static_cast<uint32_t>((min(n0 + cl, N - 1) - n0) * row_bytes + part);
+    }
+    const uint32_t lds_base = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)lds));
 
-    floatx4 acc[TM][TN];
+    // DMA of stage s (clamped to the last stage, so that every iteration
+    // issues the same number of loads) into ring slot `slot`.
+    auto issue = [&](int s, int slot) {
+        const int sc = min(s, ns - 1);
+        const uint8_t *xs = xbase + sc * (kStageK * 2);
+        const uint8_t *cs = cbase + sc * (kStageK * BITS / 8);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+        for (int q = 0; q < 2; ++q)
+            dma16(xs, xoff[q], lds_base + XR + slot * C::XBYTES + (2 * w + q) * 1024);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < NCL; ++q)
+            dma16(cs, coff[q], lds_base + CR + slot * C::CBYTES + (NCL * w + q) * 1024);
+    };
 
-    float xsum[NCT];
+    floatx4 acc[4][4];
 #pragma unroll
-    for (int r = 0; r < NCT; ++r) xsum[r] = 0.f;
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float rs = 0.f;
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t ones2 = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
 
-    // Register stages: X chunks and code dwords for the next stage.
-    uint4 xr[NCT][CH / 8];
-    uint32_t cnext[TN][CW];
-    uint32_t ccur[TN][CW];
+    // Loop-invariant per-lane LDS addresses; a[i] is row tile (i + w) & 3 so
+    // that a[0] is the tile whose row sums this wave keeps.
+    const int swz = xswz(i16);
+    const uint8_t *xa[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int T = 0; T < 2; ++T)
+            xa[i][T] = lds + XR + (16 * ((i + w) & 3) + i16) * 128 + (((2 * grp + T) ^ swz) << 4);
+    const uint8_t *ca = lds + CR + (64 * w + i16) * C::CB + grp * (BITS == 2 ? 4 : 8);
 
-    auto load_stage = [&](int kb) {
+    auto compute = [&](auto slot_c) {
+        constexpr int SLOT = decltype(slot_c)::value;
+        uint32_t d[4][BITS / 2];
 #pragma unroll
-        for (int r = 0; r < NCT; ++r) {
-            const int c = tid + 256 * r;
-            const int row = c / CPR, kc = c % CPR;
-            const int m = m0 + row;
-            const int k = kb + kc * CH;
-            const bool v = (c < NCHUNK) && (m < M) && (k < K);
-            const uint4 *src = reinterpret_cast<const uint4 *>(g.X + static_cast<int64_t>(v ? m : 0) * K + (v ? k : 0));
-#pragma unroll
-            for (int h = 0; h < CH / 8; ++h) xr[r][h] = v ? src[h] : make_uint4(0, 0, 0, 0);
-        }
-        // codes: lane group grp covers k in [kb + grp*BK/4, kb + (grp+1)*BK/4)
-        const int kq = kb + grp * (BK / 4);
-        const bool kv = kq < K;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const bool v = kv && cval[j];
-            const uint8_t *p = crow[j] + (v ? static_cast<int64_t>(kq) * BITS / 8 : 0);
-            if constexpr (CW == 2) {
-                const uint2 t = v ? *reinterpret_cast<const uint2 *>(p) : make_uint2(0, 0);
-                cnext[j][0] = t.x;
-                cnext[j][1] = t.y;
+        for (int j = 0; j < 4; ++j) {
+            const uint8_t *p = ca + SLOT * C::CBYTES + 16 * j * C::CB;
+            if constexpr (BITS == 2) {
+                d[j][0] = *reinterpret_cast<const uint32_t *>(p);
             } else {
-#pragma unroll
-                for (int q = 0; q < CW / 4; ++q) {
-                    const uint4 t = v ? reinterpret_cast<const uint4 *>(p)[q] : make_uint4(0, 0, 0, 0);
-                    cnext[j][4 * q + 0] = t.x;
-                    cnext[j][4 * q + 1] = t.y;
-                    cnext[j][4 * q + 2] = t.z;
-                    cnext[j][4 * q + 3] = t.w;
-                }
+                const uint2 v = *reinterpret_cast<const uint2 *>(p);
+                d[j][0] = v.x;
+                d[j][1] = v.y;
             }
         }
-    };
-
-    auto store_stage = [&]() {
+        uint32_t w0[4], w1[4];
+        if constexpr (BITS == 2) {
 #pragma unroll
-        for (int r = 0; r < NCT; ++r) {
-            const int c = tid + 256 * r;
-            if (c < NCHUNK) {
-                const int row = c / CPR, kc = c % CPR;
-                uint4 o[CH / 8];
-                float s = 0.f;
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t x = d[j][0];
+                const uint32_t y = x >> 4;
+                w0[j] = (x & 0x03030303u) | ((x << 2) & 0x30303030u);
+                w1[j] = (y & 0x03030303u) | ((y << 2) & 0x30303030u);
+            }
+        }
+        static_for<0, 2>([&](auto tc) {
+            constexpr int T = decltype(tc)::value;
+            bf16x8 a[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(xa[i][T] + SLOT * C::XBYTES));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint4 b;
                 if constexpr (BITS == 2) {
-                    // evens then odds of the 16-wide block: [0,2,...,14, 1,3,...,15]
-                    const uint32_t r8[8] = {xr[r][0].x, xr[r][0].y, xr[r][0].z, xr[r][0].w,
-                                            xr[r][1].x, xr[r][1].y, xr[r][1].z, xr[r][1].w};
-                    uint32_t w[8];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        w[j] = (r8[2 * j] & 0xFFFFu) | (r8[2 * j + 1] << 16);
-                        w[4 + j] = (r8[2 * j] >> 16) | (r8[2 * j + 1] & 0xFFFF0000u);
-                    }
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) s += bf16_to_f32(r8[j] & 0xFFFFu) + bf16_to_f32(r8[j] >> 16);
-                    o[0] = make_uint4(w[0], w[1], w[2], w[3]);
-                    o[1] = make_uint4(w[4], w[5], w[6], w[7]);
+                    b.x = fp4x2_to_bf16x2<2 * T>(w0[j]);
+                    b.y = fp4x2_to_bf16x2<2 * T>(w1[j]);
+                    b.z = fp4x2_to_bf16x2<2 * T + 1>(w0[j]);
+                    b.w = fp4x2_to_bf16x2<2 * T + 1>(w1[j]);
                 } else {
-                    // [0,4,1,5,2,6,3,7]
-                    const uint32_t d[4] = {xr[r][0].x, xr[r][0].y, xr[r][0].z, xr[r][0].w};
-                    o[0] = make_uint4((d[0] & 0xFFFFu) | (d[2] << 16), (d[0] >> 16) | (d[2] & 0xFFFF0000u),
-                                      (d[1] & 0xFFFFu) | (d[3] << 16), (d[1] >> 16) | (d[3] & 0xFFFF0000u));
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) s += bf16_to_f32(d[j] & 0xFFFFu) + bf16_to_f32(d[j] >> 16);
+                    const uint32_t x = d[j][T];
+                    const uint32_t lo = x & 0x0F0F0F0Fu;
+                    const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;
+                    b.x = (__builtin_amdgcn_perm(hi, lo, 0x0C040C00u) << 3) | 0x40004000u;
+                    b.y = (__builtin_amdgcn_perm(hi, lo, 0x0C050C01u) << 3) | 0x40004000u;
+                    b.z = (__builtin_amdgcn_perm(hi, lo, 0x0C060C02u) << 3) | 0x40004000u;
+                    b.w = (__builtin_amdgcn_perm(hi, lo, 0x0C070C03u) << 3) | 0x40004000u;
                 }
-                xsum[r] += s;
-                uint4 *dst = reinterpret_cast<uint4 *>(xs + row * LDS_ROW + kc * CH);
+                const bf16x8 bv = __builtin_bit_cast(bf16x8, b);
+                // Weights as the MFMA A operand: the lane's outputs are four
+                // consecutive columns n of one row m.
 #pragma unroll
-                for (int h = 0; h < CH / 8; ++h) dst[h] = o[h];
+                for (int i = 0; i < 4; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv, a[i], acc[i][j], 0, 0, 0);
             }
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int q = 0; q < CW; ++q) ccur[j][q] = cnext[j][q];
-    };
-
-    auto compute_stage = [&]() {
-        static_for<0, KSTEPS>([&](auto tc) {
-            constexpr int t = decltype(tc)::value;
-            bf16x8 a[TM];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int row = wm * 16 * TM + i * 16 + i16;
-                const uint4 v = *reinterpret_cast<const uint4 *>(xs + row * LDS_ROW + grp * (BK / 4) + 8 * t);
-                a[i] = __builtin_bit_cast(bf16x8, v);
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const bf16x8 b = decode_b<BITS, t>(ccur[j]);
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc[i][j], 0, 0, 0);
-            }
+            const uint4 aw = __builtin_bit_cast(uint4, a[0]);
+            rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, aw.x), ones2, rs, false);
+            rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, aw.y), ones2, rs, false);
+            rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, aw.z), ones2, rs, false);
+            rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, aw.w), ones2, rs, false);
         });
     };
 
-    const int nstages = (K + BK - 1) / BK;
-    load_stage(0);
-    for (int s = 0; s < nstages; ++s) {
-        __syncthreads();  // previous stage's LDS reads are done
-        store_stage();
-        __syncthreads();
-        if (s + 1 < nstages) load_stage((s + 1) * BK);
-        compute_stage();
+    // Prologue: P - 1 stages in flight.
+#pragma unroll
+    for (int s = 0; s < P - 1; ++s) issue(s, s);
+    int s = 0;
+    for (; s + P <= ns; s += P) {
+        static_for<0, P>([&](auto pc) {
+            constexpr int p = decltype(pc)::value;
+            wait_vmcnt<(P - 2) * C::LOADS>();  // this wave's part of stage s + p has landed
+            block_barrier();                   // all parts landed; the previous slot is free
+            issue(s + p + P - 1, (p + P - 1) % P);
+            compute(std::integral_constant<int, p>{});
+        });
     }
+    // Tail (fewer than P stages left): slot = stage index mod P, which is
+    // s + p mod P = p here since s is a multiple of P.
+    static_for<0, P - 1>([&](auto pc) {
+        constexpr int p = decltype(pc)::value;
+        if (s + p < ns) {
+            wait_vmcnt<(P - 2) * C::LOADS>();
+            block_barrier();
+            issue(s + p + P - 1, (p + P - 1) % P);
+            compute(std::integral_constant<int, p>{});
+        }
+    });
+    wait_vmcnt<0>();
 
-    // X row sums: reduce over the CPR lanes that staged each row.
-#pragma unroll
-    for (int r = 0; r < NCT; ++r) {
-        float v = xsum[r];
-#pragma unroll
-        for (int o = 1; o < CPR; o <<= 1) v += __shfl_xor(v, o);
-        const int c = tid + 256 * r;
-        if (c < NCHUNK && (c % CPR) == 0) ssum[c / CPR] = v;
-    }
+    // Row sums: combine the four k-groups, publish row 16w + i16.
+    rs += __shfl_xor(rs, 16);
+    rs += __shfl_xor(rs, 32);
+    if (grp == 0) ssum[16 * w + i16] = rs;
     __syncthreads();
 
-    // Epilogue: lane holds rows 4*grp + e of each 16x16 tile, column i16.
+    // Epilogue: acc[i][j][e] is row m0 + 16 * ((i + w) & 3) + i16, column
+    // n0 + 64w + 16j + 4grp + e.
+    constexpr float kOff = BITS == 2 ? 0.75f : 3.0f;
+    constexpr float kMul = BITS == 2 ? 1.0f : 8.0f;
+    const bool vec = (N & 3) == 0;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * 16 * TN + j * 16 + i16;
+    for (int j = 0; j < 4; ++j) {
+        const int n = n0 + 64 * w + 16 * j + 4 * grp;
         if (n >= N) continue;
-        const float al = bf16_to_f32(g.alpha[n]);
+        float al[4] = {1.f, 1.f, 1.f, 1.f};
+        if (g.splits == 1) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
+            for (int e = 0; e < 4; ++e) al[e] = n + e < N ? bf16_to_f32(g.alpha[n + e]) : 0.f;
+        }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int rl = wm * 16 * TM + i * 16 + 4 * grp + e;
-                const int m = m0 + rl;
-                if (m >= M) continue;
-                float v;
-                if constexpr (BITS == 2) {
-                    v = acc[i][j][e] - 0.75f * ssum[rl];
+        for (int i = 0; i < 4; ++i) {
+            const int rl = 16 * ((i + w) & 3) + i16;
+            const int m = m0 + rl;
+            if (m >= M) continue;
+            const float sr = kOff * ssum[rl];
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = kMul * (acc[i][j][e] - sr);
+            const int64_t o = static_cast<int64_t>(m) * N + n;
+            if (g.splits == 1) {
+                if (vec) {
+                    *reinterpret_cast<u32x2 *>(g.Y + o) =
+                        u32x2{pack_bf16x2(al[0] * v[0], al[1] * v[1]), pack_bf16x2(al[2] * v[2], al[3] * v[3])};
                 } else {
-                    v = 8.0f * (acc[i][j][e] - 3.0f * ssum[rl]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) g.Y[o + e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(al[e] * v[e]));
                 }
-                const float y = al * v;
-                const __bf16 h = static_cast<__bf16>(y);
-                g.Y[static_cast<int64_t>(m) * N + n] = __builtin_bit_cast(uint16_t, h);
+            } else {
+                float *dst = g.ws + static_cast<int64_t>(split) * M * N + o;
+                if (vec) {
+                    *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) dst[e] = v[e];
+                }
             }
+        }
+    }
+}
+
+// Sum of the split-K partials, scaled by alpha and rounded to bf16.  Four
+// consecutive elements of the flattened [M, N] output per thread.
+__global__ __launch_bounds__(256) void k_splitk_finalize(const float *ws, const uint16_t *alpha,
+                                                         uint16_t *Y, int64_t total, int N, int splits)
+{
+    const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+    if (i0 >= total) return;
+    if (i0 + 4 <= total) {
+        f32x4 s = *reinterpret_cast<const f32x4 *>(ws + i0);
+        for (int k = 1; k < splits; ++k) s += *reinterpret_cast<const f32x4 *>(ws + k * total + i0);
+        uint32_t o[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t e = i0 + 2 * h;
+            const float a0 = bf16_to_f32(alpha[e % N]);
+            const float a1 = bf16_to_f32(alpha[(e + 1) % N]);
+            o[h] = pack_bf16x2(a0 * s[2 * h], a1 * s[2 * h + 1]);
+        }
+        *reinterpret_cast<u32x2 *>(Y + i0) = u32x2{o[0], o[1]};
+    } else {
+        for (int64_t e = i0; e < total; ++e) {
+            float s = 0.f;
+            for (int k = 0; k < splits; ++k) s += ws[k * total + e];
+            const __bf16 h = static_cast<__bf16>(bf16_to_f32(alpha[e % N]) * s);
+            Y[e] = __builtin_bit_cast(uint16_t, h);
         }
     }
 }
@@ -553,12 +678,70 @@ void launch_stream(const GemmArgs &a, hipStream_t s)
                        dim3(64 * PQ_STREAM_NW), 0, s, a);
 }
 
-template <int BITS, int TM, int TN, int WM, int WN, int BK>
-void launch(const GemmArgs &a, hipStream_t s)
+// Split-K workspace: one fp32 buffer per (device, stream), grown on demand.
+// Growing waits for the stream, so a buffer in use is never freed early.
+struct Workspace {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+
+pq_status workspace(hipStream_t stream, size_t bytes, float **out)
 {
-    constexpr int BM = 16 * TM * WM, BN = 16 * TN * WN;
-    dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM);
-    hipLaunchKernelGGL((k_gemm<BITS, TM, TN, WM, WN, BK>), grid, dim3(256), 0, s, a);
+    static std::mutex mu;
+    static std::map<std::pair<int, hipStream_t>, Workspace> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PQ_ERR_HIP;
+    std::lock_guard<std::mutex> lock(mu);
+    Workspace &w = cache[{dev, stream}];
+    if (w.bytes < bytes) {
+        if (w.ptr) {
+            if (hipStreamSynchronize(stream) != hipSuccess || hipFree(w.ptr) != hipSuccess) return PQ_ERR_HIP;
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        if (hipMalloc(&w.ptr, bytes) != hipSuccess) {
+            w.ptr = nullptr;
+            return PQ_ERR_HIP;
+        }
+        w.bytes = bytes;
+    }
+    *out = static_cast<float *>(w.ptr);
+    return PQ_OK;
+}
+
+// Tiled path: choose the K split so that about two blocks per CU are live,
+// each split keeping at least four stages.
+template <int BITS>
+pq_status launch_tile(const GemmArgs &a, hipStream_t s)
+{
+    constexpr int kTargetBlocks = 512;
+    constexpr int kMinStages = 4;
+    const int mtiles = (a.M + kTileM - 1) / kTileM;
+    const int ntiles = (a.N + kTileN - 1) / kTileN;
+    const int64_t tiles = static_cast<int64_t>(mtiles) * ntiles;
+    const int stages = a.K / kStageK;
+    int splits = 1;
+    if (tiles < kTargetBlocks * 3 / 4) {
+        const int want = static_cast<int>((kTargetBlocks + tiles - 1) / tiles);
+        splits = std::max(1, std::min(want, stages / kMinStages));
+    }
+    const int sps = (stages + splits - 1) / splits;  // stages per split
+    splits = (stages + sps - 1) / sps;
+    TileArgs t{a.X, a.packed, a.alpha, a.Y, nullptr, a.M, a.N, a.K, mtiles, ntiles, splits, sps * kStageK};
+    const int64_t total = static_cast<int64_t>(a.M) * a.N;
+    if (splits > 1) {
+        pq_status st = workspace(s, static_cast<size_t>(splits) * total * sizeof(float), &t.ws);
+        if (st != PQ_OK) return st;
+    }
+    const int64_t blocks = tiles * splits;
+    if (blocks > INT32_MAX) return PQ_ERR_SHAPE;
+    hipLaunchKernelGGL((k_gemm_tile<BITS, TileCfg<BITS>::P>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, t);
+    if (splits > 1) {
+        const int64_t threads = (total + 3) / 4;
+        hipLaunchKernelGGL(k_splitk_finalize, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s,
+                           t.ws, a.alpha, a.Y, total, a.N, splits);
+    }
+    return PQ_OK;
 }
 
 template <int BITS>
@@ -582,9 +765,10 @@ pq_status gemm(int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *pa
         else if (M <= 2 * RPL) launch_stream<BITS, 2>(a, s);
         else if (M <= 4 * RPL) launch_stream<BITS, 4>(a, s);
         else launch_stream<BITS, 16 / RPL>(a, s);
-    } else if (M <= 16) launch<BITS, 1, 1, 1, 4, 256>(a, s);
-    else if (M <= 64) launch<BITS, PQ_TILE_MID>(a, s);
-    else launch<BITS, PQ_TILE_BIG>(a, s);
+    } else {
+        const pq_status st = launch_tile<BITS>(a, s);
+        if (st != PQ_OK) return st;
+    }
     return hipGetLastError() == hipSuccess ? PQ_OK : PQ_ERR_HIP;
 }
 
