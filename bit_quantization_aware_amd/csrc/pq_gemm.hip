@@ -45,6 +45,12 @@
 
 // Tiled-kernel LDS ring depth (2- and 4-bit); streaming-kernel shape: waves
 // per block, groups in flight per wave and column tiles per block.
+#ifndef PQ_TILE_WN
+#define PQ_TILE_WN 4
+#endif
+#ifndef PQ_TILE_DMA_MID
+#define PQ_TILE_DMA_MID 1
+#endif
 #ifndef PQ_TILE_P2
 #define PQ_TILE_P2 6
 #endif
@@ -123,7 +129,6 @@ struct GemmArgs {
 // the m-tiles that share a weight tile share that XCD's L2.
 // ---------------------------------------------------------------------------
 constexpr int kTileM = 64;
-constexpr int kTileN = 256;
 constexpr int kStageK = 64;
 
 struct TileArgs {
@@ -143,14 +148,20 @@ struct TileArgs {
 // all banks whether the LDS serves 8 or 16 lanes of a 16-byte read per clock.
 __device__ __forceinline__ int xswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-template <int BITS>
+// Tile of WN waves along N (64 columns each): 64 x 64*WN outputs per block.
+template <int BITS, int WN>
 struct TileCfg {
+    static constexpr int TN = 64 * WN;                   // columns per block
     static constexpr int CB = 8 * BITS;                  // code bytes per column per stage
     static constexpr int XBYTES = kTileM * kStageK * 2;  // 8 KB
-    static constexpr int CBYTES = kTileN * CB;           // 4 or 8 KB
+    static constexpr int CBYTES = TN * CB;
     static constexpr int SBYTES = XBYTES + CBYTES;
-    static constexpr int P = BITS == 2 ? PQ_TILE_P2 : PQ_TILE_P4;  // ring depth (72 / 64 KB)
-    static constexpr int LOADS = 2 + CBYTES / 4096;      // DMA instructions per wave per stage
+    static constexpr int P = BITS == 2 ? PQ_TILE_P2 : PQ_TILE_P4;  // ring depth
+    static constexpr int XI = 8 / WN;                    // activation DMAs per wave per stage
+    static constexpr int NCL = CB / 16;                  // code DMAs per wave per stage
+    static constexpr int LOADS = XI + NCL;
+    static_assert(WN == 4 || WN == 8, "block width");
+    static_assert(P * SBYTES <= 120 * 1024, "ring fits in LDS");
 };
 
 // One LDS-DMA load: every lane fetches 16 bytes at `base + off` (`base`
@@ -186,10 +197,10 @@ __device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w)
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL));
 }
 
-template <int BITS, int P>
-__global__ __launch_bounds__(256, 2) void k_gemm_tile(TileArgs g)
+template <int BITS, int P, int WN>
+__global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
 {
-    using C = TileCfg<BITS>;
+    using C = TileCfg<BITS, WN>;
     static_assert(P >= 3, "ring depth");
     // Ring: P activation stages, then P code stages.
     __shared__ __attribute__((aligned(1024))) uint8_t lds[P * C::SBYTES];
@@ -212,7 +223,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(TileArgs g)
     const int split = t / g.ntiles;
 
     const int M = g.M, N = g.N, K = g.K;
-    const int m0 = mt * kTileM, n0 = nt * kTileN;
+    const int m0 = mt * kTileM, n0 = nt * C::TN;
     const int kbeg = split * g.kps;
     const int kend = min(K, kbeg + g.kps);
     const int ns = (kend - kbeg) / kStageK;
@@ -222,14 +233,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(TileArgs g)
     // per-lane byte offset.  Rows >= M and columns >= N read row M-1 / N-1.
     const uint8_t *xbase = reinterpret_cast<const uint8_t *>(g.X + static_cast<int64_t>(m0) * K + kbeg);
     const uint8_t *cbase = g.packed + static_cast<int64_t>(n0) * row_bytes + static_cast<int64_t>(kbeg) * BITS / 8;
-    uint32_t xoff[2];
+    uint32_t xoff[C::XI];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int r = 8 * (2 * w + q) + (lane >> 3);
+    for (int q = 0; q < C::XI; ++q) {
+        const int r = 8 * (C::XI * w + q) + (lane >> 3);
         const int c = (lane & 7) ^ xswz(r);
         xoff[q] = static_cast<uint32_t>((min(m0 + r, M - 1) - m0) * K * 2 + 16 * c);
     }
-    constexpr int NCL = C::CBYTES / 4096;   // code DMA instructions per wave
+    constexpr int NCL = C::NCL;
     uint32_t coff[NCL];
 #pragma unroll
     for (int q = 0; q < NCL; ++q) {
@@ -247,8 +258,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(TileArgs g)
         const uint8_t *xs = xbase + sc * (kStageK * 2);
         const uint8_t *cs = cbase + sc * (kStageK * BITS / 8);
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-            dma16(xs, xoff[q], lds_base + XR + slot * C::XBYTES + (2 * w + q) * 1024);
+        for (int q = 0; q < C::XI; ++q)
+            dma16(xs, xoff[q], lds_base + XR + slot * C::XBYTES + (C::XI * w + q) * 1024);
 #pragma unroll
         for (int q = 0; q < NCL; ++q)
             dma16(cs, coff[q], lds_base + CR + slot * C::CBYTES + (NCL * w + q) * 1024);
@@ -274,25 +285,36 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(TileArgs g)
             xa[i][T] = lds + XR + (16 * ((i + w) & 3) + i16) * 128 + (((2 * grp + T) ^ swz) << 4);
     const uint8_t *ca = lds + CR + (64 * w + i16) * C::CB + grp * (BITS == 2 ? 4 : 8);
 
-    auto compute = [&](auto slot_c) {
-        constexpr int SLOT = decltype(slot_c)::value;
+    // Fragments of one stage: A for both k-steps and the code words.
+    struct Frag {
+        uint4 a[2][4];
         uint32_t d[4][BITS / 2];
+    };
+    auto read_frags = [&](auto slot_c, Frag &f) {
+        constexpr int SLOT = decltype(slot_c)::value;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const uint8_t *p = ca + SLOT * C::CBYTES + 16 * j * C::CB;
             if constexpr (BITS == 2) {
-                d[j][0] = *reinterpret_cast<const uint32_t *>(p);
+                f.d[j][0] = *reinterpret_cast<const uint32_t *>(p);
             } else {
                 const uint2 v = *reinterpret_cast<const uint2 *>(p);
-                d[j][0] = v.x;
-                d[j][1] = v.y;
+                f.d[j][0] = v.x;
+                f.d[j][1] = v.y;
             }
         }
+#pragma unroll
+        for (int T = 0; T < 2; ++T)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                f.a[T][i] = *reinterpret_cast<const uint4 *>(xa[i][T] + SLOT * C::XBYTES);
+    };
+    auto mma = [&](const Frag &f, auto &&between) {
         uint32_t w0[4], w1[4];
         if constexpr (BITS == 2) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const uint32_t x = d[j][0];
+                const uint32_t x = f.d[j][0];
                 const uint32_t y = x >> 4;
                 w0[j] = (x & 0x03030303u) | ((x << 2) & 0x30303030u);
                 w1[j] = (y & 0x03030303u) | ((y << 2) & 0x30303030u);
@@ -300,10 +322,6 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(TileArgs g)
         }
         static_for<0, 2>([&](auto tc) {
             constexpr int T = decltype(tc)::value;
-            bf16x8 a[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(xa[i][T] + SLOT * C::XBYTES));
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 uint4 b;
@@ -313,7 +331,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(TileArgs g)
                     b.z = fp4x2_to_bf16x2<2 * T + 1>(w0[j]);
                     b.w = fp4x2_to_bf16x2<2 * T + 1>(w1[j]);
                 } else {
-                    const uint32_t x = d[j][T];
+                    const uint32_t x = f.d[j][T];
                     const uint32_t lo = x & 0x0F0F0F0Fu;
                     const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;
                     b.x = (__builtin_amdgcn_perm(hi, lo, 0x0C040C00u) << 3) | 0x40004000u;
@@ -326,46 +344,66 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(TileArgs g)
                 // consecutive columns n of one row m.
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv, a[i], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv, __builtin_bit_cast(bf16x8, f.a[T][i]),
+                                                                         acc[i][j], 0, 0, 0);
             }
-            const uint4 aw = __builtin_bit_cast(uint4, a[0]);
+            const uint4 aw = f.a[T][0];
             rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, aw.x), ones2, rs, false);
             rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, aw.y), ones2, rs, false);
             rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, aw.z), ones2, rs, false);
             rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, aw.w), ones2, rs, false);
+            if constexpr (T == 0) {
+                __builtin_amdgcn_sched_barrier(0);
+                between();
+                __builtin_amdgcn_sched_barrier(0);
+            }
         });
     };
 
-    // Prologue: P - 1 stages in flight.
+    // Pipeline: the DMA runs P - 1 stages ahead; the LDS -> register reads
+    // of stage s + 1 are issued before the MFMAs of stage s.  Iteration s
+    // waits for stage s + 1, passes the barrier (after which the slot of
+    // stage s - 1, read two iterations back, is free), refills that slot
+    // with stage s + P - 1, reads stage s + 1 and multiplies stage s.
+    static_assert(P % 2 == 0, "the ring is unrolled with a two-deep fragment buffer");
+    Frag fr[2];
 #pragma unroll
     for (int s = 0; s < P - 1; ++s) issue(s, s);
+    wait_vmcnt<(P - 2) * C::LOADS>();
+    block_barrier();
+    read_frags(std::integral_constant<int, 0>{}, fr[0]);
+    auto step = [&](int s, auto pc) {
+        constexpr int p = decltype(pc)::value;  // s % P
+        wait_vmcnt<(P - 3) * C::LOADS>();       // this wave's part of stage s + 1 has landed
+        block_barrier();
+        if (PQ_TILE_DMA_MID == 0) issue(s + P - 1, (p + P - 1) % P);
+        read_frags(std::integral_constant<int, (p + 1) % P>{}, fr[(p + 1) & 1]);
+        // Keep the scheduler from hoisting work on the fragments just
+        // requested (which would wait on them) into this step's MFMAs.
+        __builtin_amdgcn_sched_barrier(0);
+        // The DMA refill goes between the two k-steps' MFMAs, so that the
+        // waves leaving the barrier together do not all queue on the vector
+        // memory unit before their first MFMA.
+        mma(fr[p & 1], [&]() {
+            if (PQ_TILE_DMA_MID != 0) issue(s + P - 1, (p + P - 1) % P);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+    };
     int s = 0;
     for (; s + P <= ns; s += P) {
-        static_for<0, P>([&](auto pc) {
-            constexpr int p = decltype(pc)::value;
-            wait_vmcnt<(P - 2) * C::LOADS>();  // this wave's part of stage s + p has landed
-            block_barrier();                   // all parts landed; the previous slot is free
-            issue(s + p + P - 1, (p + P - 1) % P);
-            compute(std::integral_constant<int, p>{});
-        });
+        static_for<0, P>([&](auto pc) { step(s + decltype(pc)::value, pc); });
     }
-    // Tail (fewer than P stages left): slot = stage index mod P, which is
-    // s + p mod P = p here since s is a multiple of P.
+    // Tail (fewer than P stages left); s is a multiple of P, so stage s + p
+    // sits in slot p.
     static_for<0, P - 1>([&](auto pc) {
-        constexpr int p = decltype(pc)::value;
-        if (s + p < ns) {
-            wait_vmcnt<(P - 2) * C::LOADS>();
-            block_barrier();
-            issue(s + p + P - 1, (p + P - 1) % P);
-            compute(std::integral_constant<int, p>{});
-        }
+        if (s + decltype(pc)::value < ns) step(s + decltype(pc)::value, pc);
     });
     wait_vmcnt<0>();
 
     // Row sums: combine the four k-groups, publish row 16w + i16.
     rs += __shfl_xor(rs, 16);
     rs += __shfl_xor(rs, 32);
-    if (grp == 0) ssum[16 * w + i16] = rs;
+    if (grp == 0 && w < 4) ssum[16 * w + i16] = rs;
     __syncthreads();
 
     // Epilogue: acc[i][j][e] is row m0 + 16 * ((i + w) & 3) + i16, column
@@ -465,7 +503,7 @@ __global__ __launch_bounds__(256) void k_splitk_finalize(const float *ws, const 
 // spread into bytes and completed to bf16 128 + c (exact); level = v - 136.
 // The activations are put in the matching k order (evens, then odds, of each
 // 16- or 8-wide block) by byte permutes.  The row sums of X needed by the
-// offsets come from one extra MFMA per k-step against an all-ones operand.
+// offsets are taken with v_dot2 on the activation chunks as they arrive.
 // The NW partial sums are combined in LDS in a fixed order.
 // ---------------------------------------------------------------------------
 template <int BITS, int NW, int P, int TN, int XI>
@@ -475,10 +513,11 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
     constexpr int GK = BITS == 2 ? 256 : 128;     // k per group (16 B of codes per lane per tile)
     constexpr int RPL = 512 / GK;                 // activation rows per 1 KB load (2 or 4)
     constexpr int XROW = GK + 8;                  // LDS row stride, bf16 (+16 bytes)
-    constexpr int NACC = TN * 4 + 4;
+    constexpr int NACC = TN * 4;
     static_assert(NW * NACC * 64 * 4 <= NW * 16 * XROW * 2, "reduction fits in the X slots");
 
     __shared__ __attribute__((aligned(16))) uint16_t xs[NW * 16 * XROW];
+    __shared__ float rsum[NW][16];
     float *red = reinterpret_cast<float *>(xs);
 
     const int lane = threadIdx.x & 63;
@@ -512,11 +551,15 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
     const int mrow = i16 < M ? i16 : M - 1;
 
     floatx4 acc[TN];
-    floatx4 accs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const uint4 ones_u = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
-    const bf16x8 ones = __builtin_bit_cast(bf16x8, ones_u);
+    // Row sums of X (for the level offset): each lane sums the activation
+    // chunks it loads with v_dot2 against (1, 1).
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t ones2 = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+    float rsx[XI];
+#pragma unroll
+    for (int q = 0; q < XI; ++q) rsx[q] = 0.f;
 
     uint4 cb[P][TN];
     uint4 xb[P][XI];
@@ -542,8 +585,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
     auto compute = [&](const uint4 (&c)[TN], const uint4 (&x)[XI]) {
         // activations of this group -> the wave's LDS slot (row-major)
 #pragma unroll
-        for (int q = 0; q < XI; ++q)
+        for (int q = 0; q < XI; ++q) {
             *reinterpret_cast<uint4 *>(xw + xrow_of[q] * XROW + xr_chunk * 8) = x[q];
+            rsx[q] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x[q].x), ones2, rsx[q], false);
+            rsx[q] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x[q].y), ones2, rsx[q], false);
+            rsx[q] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x[q].z), ones2, rsx[q], false);
+            rsx[q] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x[q].w), ones2, rsx[q], false);
+        }
         // Rows >= M read row M-1: with one address per lane group the LDS
         // serves the read as a broadcast.
         const uint16_t *xa = xw + mrow * XROW + grp * (GK / 4);
@@ -556,15 +604,16 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
                 const uint4 u0 = ua[2 * d];
                 const uint4 u1 = ua[2 * d + 1];
                 const uint32_t r[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+                // even / odd bf16 halves of each dword pair, one byte permute each
                 uint4 ae, ao;
-                ae.x = (r[0] & 0xFFFFu) | (r[1] << 16);
-                ae.y = (r[2] & 0xFFFFu) | (r[3] << 16);
-                ae.z = (r[4] & 0xFFFFu) | (r[5] << 16);
-                ae.w = (r[6] & 0xFFFFu) | (r[7] << 16);
-                ao.x = (r[0] >> 16) | (r[1] & 0xFFFF0000u);
-                ao.y = (r[2] >> 16) | (r[3] & 0xFFFF0000u);
-                ao.z = (r[4] >> 16) | (r[5] & 0xFFFF0000u);
-                ao.w = (r[6] >> 16) | (r[7] & 0xFFFF0000u);
+                ae.x = __builtin_amdgcn_perm(r[1], r[0], 0x05040100u);
+                ae.y = __builtin_amdgcn_perm(r[3], r[2], 0x05040100u);
+                ae.z = __builtin_amdgcn_perm(r[5], r[4], 0x05040100u);
+                ae.w = __builtin_amdgcn_perm(r[7], r[6], 0x05040100u);
+                ao.x = __builtin_amdgcn_perm(r[1], r[0], 0x07060302u);
+                ao.y = __builtin_amdgcn_perm(r[3], r[2], 0x07060302u);
+                ao.z = __builtin_amdgcn_perm(r[5], r[4], 0x07060302u);
+                ao.w = __builtin_amdgcn_perm(r[7], r[6], 0x07060302u);
                 const bf16x8 a_e = __builtin_bit_cast(bf16x8, ae);
                 const bf16x8 a_o = __builtin_bit_cast(bf16x8, ao);
 #pragma unroll
@@ -584,8 +633,6 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
                     acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_e, __builtin_bit_cast(bf16x8, be), acc[j], 0, 0, 0);
                     acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_o, __builtin_bit_cast(bf16x8, bo), acc[j], 0, 0, 0);
                 }
-                accs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_e, ones, accs, 0, 0, 0);
-                accs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_o, ones, accs, 0, 0, 0);
             }
         } else {
             uint4 ua[4];
@@ -595,10 +642,10 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
             for (int d = 0; d < 4; ++d) {
                 const uint4 xv = ua[d];
                 uint4 a;
-                a.x = (xv.x & 0xFFFFu) | (xv.y << 16);          // x0, x2
-                a.y = (xv.z & 0xFFFFu) | (xv.w << 16);          // x4, x6
-                a.z = (xv.x >> 16) | (xv.y & 0xFFFF0000u);      // x1, x3
-                a.w = (xv.z >> 16) | (xv.w & 0xFFFF0000u);      // x5, x7
+                a.x = __builtin_amdgcn_perm(xv.y, xv.x, 0x05040100u);  // x0, x2
+                a.y = __builtin_amdgcn_perm(xv.w, xv.z, 0x05040100u);  // x4, x6
+                a.z = __builtin_amdgcn_perm(xv.y, xv.x, 0x07060302u);  // x1, x3
+                a.w = __builtin_amdgcn_perm(xv.w, xv.z, 0x07060302u);  // x5, x7
                 const bf16x8 av = __builtin_bit_cast(bf16x8, a);
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
@@ -612,7 +659,6 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
                     b.w = ((hi >> 16) & 0xFFu) | ((hi >> 8) & 0x00FF0000u) | 0x43004300u;
                     acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, b), acc[j], 0, 0, 0);
                 }
-                accs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, ones, accs, 0, 0, 0);
             }
         }
     };
@@ -644,8 +690,14 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
     for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) red[(w * NACC + 4 * j + e) * 64 + lane] = acc[j][e];
+    // Row sums: reduce over the lanes that loaded chunks of the same row.
 #pragma unroll
-    for (int e = 0; e < 4; ++e) red[(w * NACC + 4 * TN + e) * 64 + lane] = accs[e];
+    for (int q = 0; q < XI; ++q) {
+        float v = rsx[q];
+#pragma unroll
+        for (int o = 1; o < 64 / RPL; o <<= 1) v += __shfl_xor(v, o);
+        if (xr_chunk == 0 && xrow_of[q] < 16) rsum[w][xrow_of[q]] = v;
+    }
     __syncthreads();
     if (w < TN) {
         const int j = w;
@@ -659,7 +711,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
                     float a = 0.f, sm = 0.f;
                     for (int v = 0; v < NW; ++v) {
                         a += red[(v * NACC + 4 * j + e) * 64 + lane];
-                        sm += red[(v * NACC + 4 * TN + e) * 64 + lane];
+                        sm += rsum[v][m];
                     }
                     const float y = BITS == 2 ? al * (a - 0.75f * sm) : al * (a - 136.0f * sm);
                     const __bf16 h = static_cast<__bf16>(y);
@@ -714,10 +766,11 @@ pq_status workspace(hipStream_t stream, size_t bytes, float **out)
 template <int BITS>
 pq_status launch_tile(const GemmArgs &a, hipStream_t s)
 {
-    constexpr int kTargetBlocks = 512;
+    constexpr int kTargetBlocks = 2048 / PQ_TILE_WN;  // two waves per SIMD
     constexpr int kMinStages = 4;
     const int mtiles = (a.M + kTileM - 1) / kTileM;
-    const int ntiles = (a.N + kTileN - 1) / kTileN;
+    using C = TileCfg<BITS, PQ_TILE_WN>;
+    const int ntiles = (a.N + C::TN - 1) / C::TN;
     const int64_t tiles = static_cast<int64_t>(mtiles) * ntiles;
     const int stages = a.K / kStageK;
     int splits = 1;
@@ -735,7 +788,8 @@ pq_status launch_tile(const GemmArgs &a, hipStream_t s)
     }
     const int64_t blocks = tiles * splits;
     if (blocks > INT32_MAX) return PQ_ERR_SHAPE;
-    hipLaunchKernelGGL((k_gemm_tile<BITS, TileCfg<BITS>::P>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, t);
+    hipLaunchKernelGGL((k_gemm_tile<BITS, C::P, PQ_TILE_WN>), dim3(static_cast<unsigned>(blocks)), dim3(64 * PQ_TILE_WN),
+                       0, s, t);
     if (splits > 1) {
         const int64_t threads = (total + 3) / 4;
         hipLaunchKernelGGL(k_splitk_finalize, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s,
