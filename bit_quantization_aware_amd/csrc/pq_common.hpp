@@ -37,13 +37,12 @@ constexpr int64_t kMaxCols = int64_t(1) << 30;
 
 inline bool valid_cols(int64_t cols) { return cols > 0 && cols % 8 == 0 && cols <= kMaxCols; }
 
-// Two fp32 -> packed bf16x2 (round to nearest-even; v_cvt_pk_bf16_f32 on gfx950).
+// Two fp32 -> packed bf16x2, round to nearest-even: one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    __bf16 a = static_cast<__bf16>(lo);
-    __bf16 b = static_cast<__bf16>(hi);
-    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
-           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16)

@@ -172,8 +172,19 @@ struct TileCfg {
 // s_barrier.  The instruction writes no VGPRs.
 __device__ __forceinline__ void dma16(const void *base, uint32_t off, uint32_t lds_addr)
 {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds_addr)
-                 : "memory", "m0");
+    // M0 is saved and restored around the load, so the compiler's own use
+    // of it (if any) is undisturbed; one wait state separates the M0 write
+    // from the LDS-DMA that reads it.
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off), "s"(base), "s"(lds_addr)
+        : "memory");
 }
 
 __device__ __forceinline__ void block_barrier()

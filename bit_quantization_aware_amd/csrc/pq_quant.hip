@@ -20,10 +20,11 @@
 // Row reductions: a butterfly over the wave (ds_bpermute), then LDS across
 // the team's waves, in a fixed order, so results are run-to-run identical.
 //
-// Arithmetic.  Every float step is one IEEE binary32 operation (built with
-// -ffp-contract=off): x = w / a with the correctly rounded division, clamp,
-// the SEQ shift, rint (v_rndne_f32, half-to-even), q = a * level with the
-// level exact in binary32, bf16 by v_cvt_pk_bf16_f32 (nearest-even).
+// Arithmetic.  Every float step gives the IEEE binary32 result of the
+// definition (built with -ffp-contract=off; explicit fmas only where the
+// product they absorb is exact): x = w / a correctly rounded, clamp, the SEQ
+// shift, rint (v_rndne_f32, half-to-even), q = a * level with the level
+// exact in binary32, bf16 by v_cvt_pk_bf16_f32 (nearest-even).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -31,6 +32,14 @@
 #include <type_traits>
 
 #include "pq_common.hpp"
+
+// Blocks per CU the register allocation must allow (occupancy floor).
+#ifndef PQ_QUANT_FWD_MINB
+#define PQ_QUANT_FWD_MINB 8
+#endif
+#ifndef PQ_QUANT_BWD_MINB
+#define PQ_QUANT_BWD_MINB 4
+#endif
 
 namespace pq {
 namespace {
@@ -70,46 +79,53 @@ template <> struct Mode<PQ_W4_LSQ> {
 // binary32 numbers is never a binary32 rounding midpoint and lies at a
 // relative distance of at least 2^-50 from every midpoint, while the binary64
 // product is within 2^-52 (relative) of it, so both round the same way.
-// Quotients in or near the subnormal range take the IEEE division.
-__device__ __forceinline__ float div_rn(float w, float a, double y)
+// Below 2^-125 the two may differ in the last subnormal place.  The forward
+// outputs cannot see that: for |x| <= 2^-125 every mode's rounding input is
+// exactly -0.5 (SEQ 2-bit) or +-0 (ternary, LSQ), whatever x is.  The
+// backward, whose alpha gradient uses x itself, re-divides such weights
+// (see tiny_key).
+__device__ __forceinline__ float div_fast(float w, double y)
 {
-    const double q = static_cast<double>(w) * y;
-    float x = static_cast<float>(q);
-    if (__builtin_expect(fabs(q) < 0x1p-125 && q != 0.0, 0)) x = w / a;
-    return x;
+    return static_cast<float>(static_cast<double>(w) * y);
 }
 
-// One weight: returns its code; writes the level (binary32, exact) and x = w/a.
-template <int MODE>
-__device__ __forceinline__ uint32_t quant1(float w, float a, double y, float &lvl, float &x)
+// Key for "0 < |w| < t" with one unsigned min per weight: (bits << 1) drops
+// the sign, and the -2 sends +-0 to the top of the range.
+__device__ __forceinline__ uint32_t tiny_key(float w)
 {
-    x = div_rn(w, a, y);
+    return (__builtin_bit_cast(uint32_t, w) << 1) - 2u;
+}
+
+// One weight from its quotient x: returns the code; writes the level
+// (binary32, exact).  Every step is the binary32 operation of the
+// definition; an fma is used only where its single rounding equals the
+// definition's (the product it absorbs is exact).
+template <int MODE>
+__device__ __forceinline__ uint32_t quant_x(float w, float x, float &lvl)
+{
     if constexpr (MODE == PQ_W2_SEQ) {
-        // [Note] "Paper vs. code", SEQ row: round(Clip(x) * k/2 - 0.5) + 0.5, k = 4;
-        // the level (r + 0.5) * 2/k is exact, so alpha * level equals the
-        // page's alpha * (r + 0.5) / k * 2 bit for bit.
-        float xc = fminf(fmaxf(x, -kClip), kClip);
-        float z = xc * 2.0f;
-        z = z - 0.5f;
-        float rf = __builtin_rintf(z);
-        lvl = (rf + 0.5f) * 0.5f;
+        // [Note] "Paper vs. code", SEQ row: round(Clip(x) * k/2 - 0.5) + 0.5, k = 4.
+        // xc * 2 is exact, so fma(xc, 2, -0.5) rounds xc * 2 - 0.5 once, as the
+        // two-step form does; the level (r + 0.5) * 2/k = r/2 + 1/4 is exact.
+        const float xc = __builtin_amdgcn_fmed3f(x, -kClip, kClip);
+        const float rf = __builtin_rintf(__builtin_fmaf(xc, 2.0f, -0.5f));
+        lvl = __builtin_fmaf(rf, 0.5f, 0.25f);
         return static_cast<uint32_t>(static_cast<int>(rf) + 2);
     } else if constexpr (MODE == PQ_W158_SEQ_TERNARY) {
         // [Rebuttal] 1.58-bit bullet: stretch to [-1.5, 1.5], three equal bins.
-        float xc = fminf(fmaxf(x, -kClip), kClip);
-        float v = xc * 1.5f;
-        int r = static_cast<int>(__builtin_rintf(v));
+        const float xc = __builtin_amdgcn_fmed3f(x, -kClip, kClip);
+        const int r = static_cast<int>(__builtin_rintf(xc * 1.5f));
         lvl = static_cast<float>(r) * kTwoThirds;
         return static_cast<uint32_t>(r + 1);
     } else if constexpr (MODE == PQ_W3_LSQ || MODE == PQ_W4_LSQ) {
         // LSQ integer grid: round(clamp(x, Qn, Qp)).
-        float xc = fminf(fmaxf(x, Mode<MODE>::lo), Mode<MODE>::hi);
-        int r = static_cast<int>(__builtin_rintf(xc));
+        const float xc = __builtin_amdgcn_fmed3f(x, Mode<MODE>::lo, Mode<MODE>::hi);
+        const int r = static_cast<int>(__builtin_rintf(xc));
         lvl = static_cast<float>(r);
         return static_cast<uint32_t>(r - static_cast<int>(Mode<MODE>::lo));
     } else {
         // 1 bit: sign(w) with sign(0) = +1.
-        bool pos = w >= 0.0f;
+        const bool pos = w >= 0.0f;
         lvl = pos ? 1.0f : -1.0f;
         return pos ? 1u : 0u;
     }
@@ -172,7 +188,7 @@ enum : unsigned { OUT_BF16 = 1, OUT_F32 = 2, OUT_CODES = 4, OUT_ALPHA_BF16 = 8 }
 // Forward: optional alpha init, then per quad: quantize, emit bf16 / fp32 /
 // codes.  OUT_ALPHA_BF16 (export) also writes bf16(alpha) per row.
 template <int MODE, bool INIT, int WPR, unsigned OUTS>
-__global__ __launch_bounds__(256) void k_quant_fwd(LaunchTable lt, void *alpha_bf16_single)
+__global__ __launch_bounds__(256, PQ_QUANT_FWD_MINB) void k_quant_fwd(LaunchTable lt, void *alpha_bf16_single)
 {
     constexpr int RPB = 4 / WPR;
     constexpr int TEAM = 64 * WPR;
@@ -248,11 +264,11 @@ __global__ __launch_bounds__(256) void k_quant_fwd(LaunchTable lt, void *alpha_b
         for (int u = 0; u < kUnroll; ++u) {
             const int q = base + u * TEAM + tl;
             const bool act = !GUARD || q < nq;
-            float l0, l1, l2, l3, x;
-            const uint32_t c0 = quant1<MODE>(v[u].x, a, y, l0, x);
-            const uint32_t c1 = quant1<MODE>(v[u].y, a, y, l1, x);
-            const uint32_t c2 = quant1<MODE>(v[u].z, a, y, l2, x);
-            const uint32_t c3 = quant1<MODE>(v[u].w, a, y, l3, x);
+            float l0, l1, l2, l3;
+            const uint32_t c0 = quant_x<MODE>(v[u].x, div_fast(v[u].x, y), l0);
+            const uint32_t c1 = quant_x<MODE>(v[u].y, div_fast(v[u].y, y), l1);
+            const uint32_t c2 = quant_x<MODE>(v[u].z, div_fast(v[u].z, y), l2);
+            const uint32_t c3 = quant_x<MODE>(v[u].w, div_fast(v[u].w, y), l3);
             const float q0 = a * l0, q1 = a * l1, q2 = a * l2, q3 = a * l3;
             if constexpr ((OUTS & OUT_BF16) != 0) {
                 if (act) wq16[q] = u32x2{pack_bf16x2(q0, q1), pack_bf16x2(q2, q3)};
@@ -286,7 +302,7 @@ __global__ __launch_bounds__(256) void k_quant_fwd(LaunchTable lt, void *alpha_b
 // gate, dW = inside ? G : +0, and the binary64 alpha-gradient partial
 // (level - x inside, the boundary level outside).
 template <int MODE, int WPR, bool GBF16, bool WDW, bool WMASK>
-__global__ __launch_bounds__(256) void k_quant_bwd(LaunchTable lt)
+__global__ __launch_bounds__(256, PQ_QUANT_BWD_MINB) void k_quant_bwd(LaunchTable lt)
 {
     constexpr int RPB = 4 / WPR;
     constexpr int TEAM = 64 * WPR;
@@ -311,11 +327,44 @@ __global__ __launch_bounds__(256) void k_quant_bwd(LaunchTable lt)
     const float alpha_raw = m.alpha[row];
     const float a = alpha_raw > kAlphaFloor ? alpha_raw : kAlphaFloor;
     const double y = 1.0 / static_cast<double>(a);
+    // |w| < a * 2^-123 covers every quotient below 2^-125 (the product is
+    // rounded at most once, in the subnormal range, far from a factor of 4).
+    const uint32_t tkey = tiny_key(a * 0x1p-123f);
     constexpr float lo = Mode<MODE>::lo, hi = Mode<MODE>::hi;
     double acc = 0.0;
 
+    // The arithmetic of one quad, on W and G already in registers.  EXACT:
+    // quotients by the IEEE division, else by the binary64 product.  Returns
+    // the quad's mask nibble.
+    auto quad = [&](const f32x4 &wq, const f32x4 &gq, int q, bool act, auto exact_c) -> uint32_t {
+        constexpr bool EXACT = decltype(exact_c)::value;
+        const float w4[4] = {wq.x, wq.y, wq.z, wq.w};
+        const float g4[4] = {gq.x, gq.y, gq.z, gq.w};
+        float d4[4];
+        uint32_t nib = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float lvl;
+            const float x = EXACT ? w4[e] / a : div_fast(w4[e], y);
+            quant_x<MODE>(w4[e], x, lvl);
+            const bool inside = (x >= lo) && (x <= hi);
+            d4[e] = inside ? g4[e] : 0.0f;
+            nib |= static_cast<uint32_t>(inside) << e;
+            const double s = static_cast<double>(lvl) - (inside ? static_cast<double>(x) : 0.0);
+            // inactive lanes loaded zeros, so their products are +0
+            acc += s * static_cast<double>(g4[e]);
+        }
+        if constexpr (WDW) {
+            if (act) dwr[q] = f32x4{d4[0], d4[1], d4[2], d4[3]};
+        }
+        return nib;
+    };
+
     // One pass: kUnroll quads per lane; all W and G loads are issued before
-    // any store, so dW may overwrite G in place.
+    // any store, so dW may overwrite G in place.  A quad holding a weight
+    // with a quotient below 2^-125 (0 < |w| < a * 2^-123) takes the exact
+    // body (rare); the test is one unsigned min per weight.  The mask
+    // nibbles are paired across lanes after the (divergent) quad bodies.
     auto pass = [&](int base, auto guard_c) {
         constexpr bool GUARD = decltype(guard_c)::value;
         f32x4 wv[kUnroll], gv[kUnroll];
@@ -336,31 +385,28 @@ __global__ __launch_bounds__(256) void k_quant_bwd(LaunchTable lt)
                 gv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
+        uint32_t nibs = 0;
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int q = base + u * TEAM + tl;
             const bool act = !GUARD || q < nq;
-            const float w4[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
-            const float g4[4] = {gv[u].x, gv[u].y, gv[u].z, gv[u].w};
-            float d4[4];
-            uint32_t nib = 0;
+            const uint32_t kmin = min(min(tiny_key(wv[u].x), tiny_key(wv[u].y)),
+                                      min(tiny_key(wv[u].z), tiny_key(wv[u].w)));
+            uint32_t nib;
+            if (__builtin_expect(kmin < tkey, 0)) nib = quad(wv[u], gv[u], q, act, std::true_type{});
+            else nib = quad(wv[u], gv[u], q, act, std::false_type{});
+            nibs |= nib << (4 * u);
+        }
+        if constexpr (WMASK) {
+            // a nibble per quad; the even lane takes its odd neighbour's
+            // into the high half of the byte
+            const uint32_t hi = __shfl_down(nibs, 1);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float lvl, x;
-                quant1<MODE>(w4[e], a, y, lvl, x);
-                const bool inside = (x >= lo) && (x <= hi);
-                d4[e] = inside ? g4[e] : 0.0f;
-                nib |= static_cast<uint32_t>(inside) << e;
-                const double s = static_cast<double>(lvl) - (inside ? static_cast<double>(x) : 0.0);
-                // inactive lanes loaded zeros, so their products are +0
-                acc += s * static_cast<double>(g4[e]);
-            }
-            if constexpr (WDW) {
-                if (act) dwr[q] = f32x4{d4[0], d4[1], d4[2], d4[3]};
-            }
-            if constexpr (WMASK) {
-                const uint32_t hi4 = __shfl_down(nib, 1);
-                if (act && (tl & 1) == 0) mrow[q >> 1] = static_cast<uint8_t>(nib | (hi4 << 4));
+            for (int u = 0; u < kUnroll; ++u) {
+                const int q = base + u * TEAM + tl;
+                const bool act = !GUARD || q < nq;
+                if (act && (tl & 1) == 0)
+                    mrow[q >> 1] = static_cast<uint8_t>(((nibs >> (4 * u)) & 0xFu) | (((hi >> (4 * u)) & 0xFu) << 4));
             }
         }
     };
