@@ -44,6 +44,19 @@
 namespace pq {
 namespace {
 
+// Streaming access: every weight, gradient and output is touched once, so
+// loads and stores are nontemporal (they do not displace other data in L2).
+template <typename P>
+__device__ __forceinline__ auto ld_stream(const P *p)
+{
+    return __builtin_nontemporal_load(p);
+}
+template <typename P, typename V>
+__device__ __forceinline__ void st_stream(P *p, V v)
+{
+    __builtin_nontemporal_store(v, p);
+}
+
 // [Note] "Paper vs. code", first bullet: clip w/alpha to +-(1 - 1e-2).
 constexpr float kClip = 0.99f;
 // alpha <= 1e-5 is used as 1e-5 (the pages are silent; keeps 0/0 away).
@@ -257,11 +270,13 @@ __global__ __launch_bounds__(256, PQ_QUANT_FWD_MINB) void k_quant_fwd(LaunchTabl
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int q = base + u * TEAM + tl;
-            if (!GUARD || q < nq) v[u] = wr[q];
+            if (!GUARD || q < nq) v[u] = ld_stream(&wr[q]);
             else v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
+            // in the tail pass, quad slots no lane of the team owns are skipped
+            if (GUARD && base + u * TEAM >= nq) break;
             const int q = base + u * TEAM + tl;
             const bool act = !GUARD || q < nq;
             float l0, l1, l2, l3;
@@ -355,7 +370,7 @@ __global__ __launch_bounds__(256, PQ_QUANT_BWD_MINB) void k_quant_bwd(LaunchTabl
             acc += s * static_cast<double>(g4[e]);
         }
         if constexpr (WDW) {
-            if (act) dwr[q] = f32x4{d4[0], d4[1], d4[2], d4[3]};
+            if (act) st_stream(&dwr[q], f32x4{d4[0], d4[1], d4[2], d4[3]});
         }
         return nib;
     };
@@ -372,13 +387,13 @@ __global__ __launch_bounds__(256, PQ_QUANT_BWD_MINB) void k_quant_bwd(LaunchTabl
         for (int u = 0; u < kUnroll; ++u) {
             const int q = base + u * TEAM + tl;
             if (!GUARD || q < nq) {
-                wv[u] = wr[q];
+                wv[u] = ld_stream(&wr[q]);
                 if constexpr (GBF16) {
-                    const u32x2 h = gr16[q];
+                    const u32x2 h = ld_stream(&gr16[q]);
                     gv[u] = f32x4{bf16_to_f32(h.x & 0xFFFFu), bf16_to_f32(h.x >> 16),
                                   bf16_to_f32(h.y & 0xFFFFu), bf16_to_f32(h.y >> 16)};
                 } else {
-                    gv[u] = gr32[q];
+                    gv[u] = ld_stream(&gr32[q]);
                 }
             } else {
                 wv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -388,6 +403,7 @@ __global__ __launch_bounds__(256, PQ_QUANT_BWD_MINB) void k_quant_bwd(LaunchTabl
         uint32_t nibs = 0;
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
+            if (GUARD && base + u * TEAM >= nq) break;  // slot empty for the whole team
             const int q = base + u * TEAM + tl;
             const bool act = !GUARD || q < nq;
             const uint32_t kmin = min(min(tiny_key(wv[u].x), tiny_key(wv[u].y)),
