@@ -46,7 +46,53 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="skip sweep / comparison GEMMs")
+    p.add_argument("--pmc-workload", action="store_true",
+                   help="no timing: a 1 GiB copy (counter calibration), then every step kernel "
+                        "three times in step order, for rocprofv3 --pmc passes")
+    p.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="turn the two --pmc-workload counter runs into the traffic table")
+    p.add_argument("--pmc-out", default=os.path.join(ROOT, "profiles", "hbm_traffic_bench_kernels.md"))
+    p.add_argument("--pmc-command", default="", help="command lines recorded in the traffic table")
     return p.parse_args()
+
+
+# Sources whose kernels each bench kernel runs: the traffic recorded for a
+# kernel is reported only while these files are unchanged.
+KERNEL_SOURCES = {
+    "fwd": ("pq_quant.hip", "pq_common.hpp"),
+    "bwd": ("pq_quant.hip", "pq_common.hpp"),
+    "pack": ("pq_quant.hip", "pq_common.hpp"),
+}
+for _m in (1, 4, 16, 64, 512):
+    KERNEL_SOURCES[f"gemm_m{_m}"] = ("pq_gemm.hip", "pq_common.hpp")
+CALIB_BYTES = 1 << 30   # the calibration copy reads and writes 1 GiB
+
+
+def source_sha(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "bit_quantization_aware_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(path):
+    """kernel -> HBM bytes per launch, from the traffic table, for kernels
+    whose sources still match the hash recorded with the counters."""
+    out = {}
+    try:
+        lines = open(path).read().splitlines()
+    except OSError:
+        return out
+    for ln in lines:
+        cells = [c.strip() for c in ln.strip().strip("|").split("|")]
+        if len(cells) >= 6 and cells[0] in KERNEL_SOURCES:
+            try:
+                if cells[1] == source_sha(cells[0]):
+                    out[cells[0]] = int(float(cells[5]))
+            except (ValueError, OSError):
+                pass
+    return out
 
 
 def fwd_bytes(rows, cols, cw):
@@ -65,8 +111,90 @@ def gemm_bytes(M, N, K, bits):
     return N * K * bits / 8 + 2 * N + 2 * M * K + 2 * M * N
 
 
+def pmc_summarize(args):
+    """Per-kernel HBM bytes from the FETCH_SIZE and WRITE_SIZE passes of
+    --pmc-workload, scaled by what each counter reads for the 1 GiB copy."""
+    import csv
+    import glob
+
+    def load(d, counter):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not f:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        rows = [r for r in csv.DictReader(open(f[0])) if r["Counter_Name"] == counter]
+        per = {}
+        for r in rows:
+            key = int(r["Dispatch_Id"])
+            e = per.setdefault(key, [r["Kernel_Name"], 0.0])
+            e[1] += float(r["Counter_Value"])
+        return [per[k] for k in sorted(per)]
+
+    fetch = load(args.pmc_summarize[0], "FETCH_SIZE")
+    write = load(args.pmc_summarize[1], "WRITE_SIZE")
+
+    def last(seq, pred, n):
+        hits = [v for name, v in seq if pred(name)]
+        return hits[-n:] if len(hits) >= n else None
+
+    copy_pred = lambda n: "copy" in n.lower() and "pq::" not in n
+    groups = {
+        "fwd": lambda n: "k_quant_fwd<2, false, 1, 5u>" in n,
+        "bwd": lambda n: "k_quant_bwd<2, 1, false, true, false>" in n,
+        "pack": lambda n: "k_quant_fwd<2, false, 1, 12u>" in n,
+        "gemm_m1": lambda n: "k_gemm_stream<2, 4, 3, 2, 1>" in n,
+        "gemm_m4": lambda n: "k_gemm_stream<2, 4, 3, 2, 2>" in n,
+        "gemm_m16": lambda n: "k_gemm_stream<2, 4, 3, 2, 8>" in n,
+    }
+    cf, cw_ = last(fetch, copy_pred, 3), last(write, copy_pred, 3)
+    if not cf or not cw_:
+        raise SystemExit("calibration copy dispatches not found")
+    fscale = CALIB_BYTES / (np.mean(cf) * 1024.0)
+    wscale = CALIB_BYTES / (np.mean(cw_) * 1024.0)
+    res = {}
+    for k, pred in groups.items():
+        f, w = last(fetch, pred, 3), last(write, pred, 3)
+        if f and w:
+            res[k] = (np.mean(f), np.mean(w))
+    tile = lambda n: "k_gemm_tile<2," in n
+    fin = lambda n: "k_splitk_finalize" in n
+    f6, w6 = last(fetch, tile, 6), last(write, tile, 6)
+    ff, wf = last(fetch, fin, 3), last(write, fin, 3)
+    if f6 and w6 and ff and wf:
+        res["gemm_m64"] = (np.mean(f6[:3]) + np.mean(ff), np.mean(w6[:3]) + np.mean(wf))
+        res["gemm_m512"] = (np.mean(f6[3:]), np.mean(w6[3:]))
+    lines = [
+        "# HBM traffic per launch of the bench.py step kernels (rocprofv3 PMC)",
+        "",
+        "Counters: `FETCH_SIZE` and `WRITE_SIZE` (KiB per dispatch), each collected in its own",
+        "rocprofv3 pass over `bench.py --pmc-workload` (one MI355X). Each counter is scaled by what",
+        "it reads for a plain 1 GiB device copy in the same run (1 GiB read, 1 GiB written):",
+        f"FETCH scale = {fscale:.4f}, WRITE scale = {wscale:.4f}. Means over the last three launches",
+        "of each kernel; gemm_m64 adds its split-K finalize launch. `sha` is the hash of the kernel",
+        "sources the counters were taken on (bench.py reports `traffic` only while it matches).",
+        "",
+        "Commands:",
+        "```",
+    ] + [c for c in args.pmc_command.split(";;") if c] + [
+        "```",
+        "",
+        "| kernel | sha | FETCH KiB | WRITE KiB | scaled bytes (read) | scaled bytes (total) |",
+        "|---|---|---|---|---|---|",
+    ]
+    for k, (f, w) in res.items():
+        rb = f * 1024.0 * fscale
+        tb = rb + w * 1024.0 * wscale
+        lines.append(f"| {k} | {source_sha(k)} | {f:.0f} | {w:.0f} | {rb:.0f} | {tb:.0f} |")
+    os.makedirs(os.path.dirname(args.pmc_out), exist_ok=True)
+    with open(args.pmc_out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     args = parse()
+    if args.pmc_summarize:
+        pmc_summarize(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the quantizer shards "
               "by rows and the GEMM by output columns with no exchange, but this build measures "
@@ -130,6 +258,28 @@ def main():
     init_ms = e0.elapsed_time(e1)
 
     kernels = ["fwd", "bwd", "pack"] + [f"gemm_m{M}" for M in GEMM_MS]
+
+    if args.pmc_workload:
+        src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).uniform_()
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        launches = {
+            "fwd": lambda: pq.pq_quantize_fwd_grouped(mode, ftab, 0),
+            "bwd": lambda: pq.pq_quantize_bwd_grouped(mode, btab, pq.PQ_G_F32),
+            "pack": lambda: pq.pq_pack_w2(GEMM_NK, GEMM_NK, W16, a16, packed[0], ab16[0]),
+        }
+        for j, M in enumerate(GEMM_MS):
+            launches[f"gemm_m{M}"] = (lambda M=M, j=j: pq.pq_w2a16_gemm(
+                M, GEMM_NK, GEMM_NK, Xs[M], packed[1 + j % (ROTATE - 1)], ab16[1 + j % (ROTATE - 1)], Ys[M]))
+        for k in kernels:
+            for _ in range(3):
+                launches[k]()
+            torch.cuda.synchronize()
+            print(f"pmc workload: {k} x3", flush=True)
+        return
 
     def step(it, evs):
         evs[0].record(stream)
@@ -203,7 +353,10 @@ def main():
     roofline = dict(rl[dominant])
     roofline.pop("ms", None)
     roofline["kernel"] = dominant
-    roofline["traffic"] = None
+    traffic = recorded_traffic(args.pmc_out)
+    roofline["traffic"] = traffic.get(dominant)
+    for k in rl:
+        rl[k]["traffic"] = traffic.get(k)
     roofline["units_per_launch"] = per_launch_units.get(dominant, "one GEMM call")
 
     qt_ms = avg["fwd"] + avg["bwd"]
@@ -309,35 +462,40 @@ def gemm_compare(torch, pq, W16, a16, Xs, stream):
     return res
 
 
-def cpu_baseline(shapes, alg_bytes):
-    """The oracle (plain C, OpenMP over rows) on the same 2-bit stack:
-    one forward + backward pass over all 210 matrices."""
+def cpu_baseline(shapes, alg_bytes, min_seconds=10.0, max_passes=50):
+    """The oracle (plain C, OpenMP over rows) on the same 2-bit stack: whole
+    forward + backward passes over all 210 matrices, repeated until about
+    ten seconds of CPU work have been timed."""
     import oracle as O
     from bit_quantization_aware_amd import synth
 
     cores = len(os.sched_getaffinity(0))
     O.set_threads(cores)
-    t = 0.0
+    data = []
     for k in range(len(shapes)):
         W = synth.weight("mobilellm_125m", k)
         G = synth.upstream_grad("mobilellm_125m", k)
-        alpha = O.alpha_init(O.SEQ2, W)
-        t0 = time.perf_counter()
-        O.quantize_fwd(O.SEQ2, W, alpha)
-        O.quantize_bwd(O.SEQ2, W, alpha, G)
-        t += time.perf_counter() - t0
+        data.append((W, G, O.alpha_init(O.SEQ2, W)))
+    t, passes = 0.0, 0
+    while t < min_seconds and passes < max_passes:
+        for W, G, alpha in data:
+            t0 = time.perf_counter()
+            O.quantize_fwd(O.SEQ2, W, alpha)
+            O.quantize_bwd(O.SEQ2, W, alpha, G)
+            t += time.perf_counter() - t0
+        passes += 1
     cpu = ""
     try:
         with open("/proc/cpuinfo") as f:
             cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
     except OSError:
         pass
-    return {"value": round(alg_bytes / t / 1e9, 3), "unit": "GB/s", "cores": O.max_threads(),
-            "kind": "oracle", "seconds": round(t, 3), "cpu": cpu,
-            "sample": "one 2-bit SEQ forward + backward pass over all 210 matrices of the "
-                      "MobileLLM-125M stack (the full GPU workload of steps 1-2), same "
-                      "algorithmic byte count; the oracle also writes fp32 values and mask "
-                      "bits the GPU step does not"}
+    return {"value": round(passes * alg_bytes / t / 1e9, 3), "unit": "GB/s", "cores": O.max_threads(),
+            "kind": "oracle", "seconds": round(t, 3), "passes": passes, "cpu": cpu,
+            "sample": f"{passes} whole 2-bit SEQ forward + backward passes over the 210 matrices of "
+                      "the MobileLLM-125M stack (the GPU workload of steps 1-2, same algorithmic "
+                      "bytes per pass); the oracle also writes fp32 values and mask bits the GPU "
+                      "step does not"}
 
 
 if __name__ == "__main__":

@@ -17,27 +17,30 @@
  *
  * Conventions shared by every entry point
  *   Memory     Every array argument is a DEVICE pointer owned by the caller;
- *              the library never allocates, frees or keeps a pointer after
- *              the call returns.  Arrays are row-major and contiguous
+ *              the library keeps no pointer after the call returns.  The only
+ *              memory the library allocates itself is the GEMM's split-K
+ *              workspace (see pq_w2a16_gemm).  Arrays are row-major and contiguous
  *              (leading dimension = cols).  Weight matrices are [out, in]:
  *              a "row" is one output channel, the unit the scale alpha
  *              belongs to ([Note] "Paper vs. code": one learned scale per
  *              row, shape (rows, 1)).
  *   Streams    `stream` is a hipStream_t (NULL = the null stream).  Calls only
  *              enqueue work on it and return; results are ready when the
- *              stream is.  The library has no global mutable state, so calls
- *              from several host threads are safe.
+ *              stream is.  The only global state is the workspace cache,
+ *              guarded by a mutex, so calls from several host threads are
+ *              safe.
  *   bf16       bf16 arrays are passed as void* and hold IEEE bfloat16 bit
  *              patterns; every cast to bf16 rounds to nearest-even.
  *   Errors     Arguments are checked on the host before anything is enqueued:
  *              a NULL required pointer -> PQ_ERR_NULL; rows, cols, M, N or K
  *              negative, cols not a positive multiple of 8, or K not a
- *              positive multiple of 64 -> PQ_ERR_SHAPE; an unknown mode, flag or dtype -> PQ_ERR_MODE;
- *              an array pointer not 16-byte aligned -> PQ_ERR_ALIGN; a bad
- *              descriptor table or grad_scale -> PQ_ERR_ARG.  A failed launch
- *              -> PQ_ERR_HIP.  On any error nothing is enqueued.  Zero rows
- *              (or M = 0 / N = 0) is valid and enqueues nothing; the array
- *              pointers of such an empty matrix are not checked or used.
+ *              positive multiple of 64 -> PQ_ERR_SHAPE; an unknown mode,
+ *              flag or dtype -> PQ_ERR_MODE; an array pointer not 16-byte
+ *              aligned -> PQ_ERR_ALIGN; a bad descriptor table or grad_scale
+ *              -> PQ_ERR_ARG.  A failed launch -> PQ_ERR_HIP.  On any error
+ *              nothing is enqueued.  Zero rows (or M = 0 / N = 0) is valid
+ *              and enqueues nothing; the array pointers of such an empty
+ *              matrix are not checked or used.
  *   Inputs     Weights, scales and gradients must be finite (not checked;
  *              outputs are unspecified otherwise).  A scale alpha <= 1e-5 is
  *              used as 1e-5 in the arithmetic (and stored unchanged), so an
@@ -198,6 +201,15 @@ pq_status pq_pack_w4(int64_t rows, int64_t cols, const float *W, const float *al
  *   packed     in   [N, K/4] u8 from pq_pack_w2
  *   alpha_bf16 in   [N] bf16
  *   Y          out  [M, N] bf16
+ * Workspace.  For M > 16 the output is cut into 64 x 256 tiles; when there
+ * are too few tiles to fill the chip, K is split over blocks, each split
+ * writes fp32 partial sums to a workspace of splits * M * N * 4 bytes, and a
+ * second kernel on the same stream adds them in split order and writes Y.
+ * The workspace is device memory owned by the library: one buffer per
+ * (device, stream), allocated on first need and, when a larger one is
+ * needed, replaced after the stream has been synchronized.  It lives until
+ * the process ends.  Allocation failure returns PQ_ERR_HIP with nothing
+ * enqueued.
  */
 pq_status pq_w2a16_gemm(int64_t M, int64_t N, int64_t K, const void *X,
                         const uint8_t *packed, const void *alpha_bf16, void *Y,
