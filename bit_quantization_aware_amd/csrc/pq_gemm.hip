@@ -49,10 +49,10 @@
 #define PQ_TILE_WN 4
 #endif
 #ifndef PQ_TILE_DMA_MID
-#define PQ_TILE_DMA_MID 1
+#define PQ_TILE_DMA_MID 0
 #endif
 #ifndef PQ_TILE_P2
-#define PQ_TILE_P2 6
+#define PQ_TILE_P2 4
 #endif
 #ifndef PQ_TILE_P4
 #define PQ_TILE_P4 4
@@ -97,11 +97,14 @@ struct GemmArgs {
 // A block owns a 64 x 256 output tile; its four waves each own 64 columns
 // (4 x 4 MFMA tiles of 16 x 16), so every wave reads the whole 64-row
 // activation tile and every decoded weight fragment feeds four MFMAs.  K runs
-// in stages of 64.  Each stage's activation tile (64 rows x 128 B) and code
-// tile (256 columns x 16 B, or 32 B at 4 bits) are copied global -> LDS by
-// the gfx950 LDS-DMA loads (global_load_lds_dwordx4), with no register or
-// VALU traffic, into a ring of P stage buffers kept P - 1 stages ahead.  One
-// s_waitcnt plus one barrier per stage orders the ring.
+// in stages of 64.  Each stage's activation tile (64 rows x 128 B) is copied
+// global -> LDS by the gfx950 LDS-DMA load (global_load_lds_dwordx4), with no
+// register or VALU traffic, into a ring of four stage buffers kept three
+// stages ahead.  Codes are fetched the same way but 64 bytes per column at a
+// time (four stages at 2 bits, two at 4), so every DMA instruction reads 16
+// runs of 64 contiguous bytes instead of 64 scattered 16-byte pieces; the
+// fetches are double-buffered.  One s_waitcnt plus one barrier per stage
+// orders both rings.
 //
 // LDS activation layout: row r holds its eight 16-byte k-chunks with chunk c
 // stored in slot c ^ xswz(r).  The DMA writes 1 KB contiguous per wave
@@ -154,14 +157,16 @@ struct TileCfg {
     static constexpr int TN = 64 * WN;                   // columns per block
     static constexpr int CB = 8 * BITS;                  // code bytes per column per stage
     static constexpr int XBYTES = kTileM * kStageK * 2;  // 8 KB
-    static constexpr int CBYTES = TN * CB;
-    static constexpr int SBYTES = XBYTES + CBYTES;
-    static constexpr int P = BITS == 2 ? PQ_TILE_P2 : PQ_TILE_P4;  // ring depth
+    static constexpr int CBYTES = TN * CB;               // codes of one stage
+    static constexpr int SS = 64 / CB;                   // stages per code fetch (64 B per column)
+    static constexpr int CSS = SS * CBYTES;              // codes of one fetch
+    static constexpr int P = BITS == 2 ? PQ_TILE_P2 : PQ_TILE_P4;  // activation ring depth
     static constexpr int XI = 8 / WN;                    // activation DMAs per wave per stage
-    static constexpr int NCL = CB / 16;                  // code DMAs per wave per stage
-    static constexpr int LOADS = XI + NCL;
+    static constexpr int NC = 4;                         // code DMAs per wave per fetch
+    static constexpr int LDS = P * XBYTES + 2 * CSS;
     static_assert(WN == 4 || WN == 8, "block width");
-    static_assert(P * SBYTES <= 120 * 1024, "ring fits in LDS");
+    static_assert(NC * WN * 1024 == CSS, "one fetch is NC 1-KB DMAs per wave");
+    static_assert(P == 4, "the unrolled ring assumes four activation slots");
 };
 
 // One LDS-DMA load: every lane fetches 16 bytes at `base + off` (`base`
@@ -213,8 +218,8 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
 {
     using C = TileCfg<BITS, WN>;
     static_assert(P >= 3, "ring depth");
-    // Ring: P activation stages, then P code stages.
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[P * C::SBYTES];
+    // LDS: P activation stages, then two code fetches (double buffer).
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
     __shared__ float ssum[kTileM];
     constexpr int XR = 0;                 // activation region
     constexpr int CR = P * C::XBYTES;     // code region
@@ -251,29 +256,38 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
         const int c = (lane & 7) ^ xswz(r);
         xoff[q] = static_cast<uint32_t>((min(m0 + r, M - 1) - m0) * K * 2 + 16 * c);
     }
-    constexpr int NCL = C::NCL;
-    uint32_t coff[NCL];
+    // Code DMAs: one fetch covers SS stages of the block's columns, 64
+    // contiguous bytes per column.  DMA i of wave w brings columns
+    // 16 (NC w + i) .. +15; lane l reads the 16-byte piece l >> 4 of column
+    // l & 15, so each instruction reads 16 runs of 64 bytes and lands as
+    // [piece][16 columns][16 B] in LDS.
+    constexpr int NC = C::NC;
+    uint32_t coff[NC];
+    const int cpiece = lane >> 4;
+    const int cstage = (16 * cpiece) / C::CB, cwithin = (16 * cpiece) % C::CB;
 #pragma unroll
-    for (int q = 0; q < NCL; ++q) {
-        const int cl = BITS == 2 ? 64 * w + lane : 64 * w + 32 * q + (lane >> 1);
-        const int part = BITS == 2 ? 0 : 16 * (lane & 1);
-        coff[q] = static_cast<uint32_t>((min(n0 + cl, N - 1) - n0) * row_bytes + part);
+    for (int i = 0; i < NC; ++i) {
+        const int cl = 16 * (NC * w + i) + (lane & 15);
+        coff[i] = static_cast<uint32_t>((min(n0 + cl, N - 1) - n0) * row_bytes + cwithin);
     }
     const uint32_t lds_base = static_cast<uint32_t>(
         reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)lds));
 
-    // DMA of stage s (clamped to the last stage, so that every iteration
-    // issues the same number of loads) into ring slot `slot`.
-    auto issue = [&](int s, int slot) {
-        const int sc = min(s, ns - 1);
-        const uint8_t *xs = xbase + sc * (kStageK * 2);
-        const uint8_t *cs = cbase + sc * (kStageK * BITS / 8);
+    // Activation DMA of stage st (clamped to the last stage, so that every
+    // iteration issues the same loads) into ring slot `slot`.
+    auto issue_x = [&](int st, int slot) {
+        const uint8_t *xs = xbase + min(st, ns - 1) * (kStageK * 2);
 #pragma unroll
         for (int q = 0; q < C::XI; ++q)
             dma16(xs, xoff[q], lds_base + XR + slot * C::XBYTES + (C::XI * w + q) * 1024);
+    };
+    // Code DMA of fetch G into buffer G & 1; a lane whose stage lies past
+    // the split's end re-reads the last stage (in bounds, never used).
+    auto issue_c = [&](int G) {
+        const uint32_t so = static_cast<uint32_t>(min(G * C::SS + cstage, ns - 1) * C::CB);
 #pragma unroll
-        for (int q = 0; q < NCL; ++q)
-            dma16(cs, coff[q], lds_base + CR + slot * C::CBYTES + (NCL * w + q) * 1024);
+        for (int i = 0; i < NC; ++i)
+            dma16(cbase, coff[i] + so, lds_base + CR + (G & 1) * C::CSS + (NC * w + i) * 1024);
     };
 
     floatx4 acc[4][4];
@@ -294,18 +308,27 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
 #pragma unroll
         for (int T = 0; T < 2; ++T)
             xa[i][T] = lds + XR + (16 * ((i + w) & 3) + i16) * 128 + (((2 * grp + T) ^ swz) << 4);
-    const uint8_t *ca = lds + CR + (64 * w + i16) * C::CB + grp * (BITS == 2 ? 4 : 8);
+    // Code reads: column 64w + 16j + i16 is in DMA block 4w + j; 2-bit lanes
+    // take dword grp of the stage's 16-byte piece, 4-bit lanes bytes
+    // 8 (grp & 1) of piece 2 (stage) + (grp >> 1).
+    const uint8_t *ca = lds + CR + (4 * w) * 1024 + i16 * 16 +
+                        (BITS == 2 ? 4 * grp : 8 * (grp & 1) + 256 * (grp >> 1));
 
     // Fragments of one stage: A for both k-steps and the code words.
     struct Frag {
         uint4 a[2][4];
         uint32_t d[4][BITS / 2];
     };
-    auto read_frags = [&](auto slot_c, Frag &f) {
-        constexpr int SLOT = decltype(slot_c)::value;
+    // Fragments of stage st, with PH = st mod 2*SS known at compile time
+    // (activation slot PH mod P, code buffer (PH / SS) & 1, stage PH mod SS).
+    auto read_frags = [&](auto ph_c, Frag &f) {
+        constexpr int PH = decltype(ph_c)::value;
+        constexpr int SLOT = PH % P;
+        constexpr int CBUF = (PH / C::SS) & 1;
+        constexpr int CST = PH % C::SS;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint8_t *p = ca + SLOT * C::CBYTES + 16 * j * C::CB;
+            const uint8_t *p = ca + CBUF * C::CSS + j * 1024 + CST * (C::CB == 16 ? 256 : 512);
             if constexpr (BITS == 2) {
                 f.d[j][0] = *reinterpret_cast<const uint32_t *>(p);
             } else {
@@ -371,42 +394,57 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
         });
     };
 
-    // Pipeline: the DMA runs P - 1 stages ahead; the LDS -> register reads
-    // of stage s + 1 are issued before the MFMAs of stage s.  Iteration s
-    // waits for stage s + 1, passes the barrier (after which the slot of
-    // stage s - 1, read two iterations back, is free), refills that slot
-    // with stage s + P - 1, reads stage s + 1 and multiplies stage s.
-    static_assert(P % 2 == 0, "the ring is unrolled with a two-deep fragment buffer");
+    // Pipeline.  Activation DMAs run P - 1 stages ahead; code fetch G + 2 is
+    // issued in the last iteration that reads fetch G's buffer (after its
+    // barrier), SS stages before it is needed.  Iteration s waits for
+    // stage s + 1 (and its codes), passes the barrier, refills, reads stage
+    // s + 1's fragments and multiplies stage s.  Loads retire in order, so
+    // the wait leaves in flight exactly the DMAs issued after stage s + 1's
+    // activation DMA that iteration s does not need: stage s + 2's
+    // activations and the code fetches of iterations s - 1 and (when SS > 2)
+    // s - 2.
+    constexpr int U = 2 * C::SS > P ? 2 * C::SS : P;   // unroll: phases of slots and buffers
+    static_assert(U % P == 0 && U % (2 * C::SS) == 0, "unroll covers both rings");
     Frag fr[2];
+    issue_c(0);
 #pragma unroll
-    for (int s = 0; s < P - 1; ++s) issue(s, s);
-    wait_vmcnt<(P - 2) * C::LOADS>();
+    for (int st = 0; st < P - 1; ++st) issue_x(st, st);
+    issue_c(1);
+    wait_vmcnt<2 * C::XI + NC>();
     block_barrier();
     read_frags(std::integral_constant<int, 0>{}, fr[0]);
     auto step = [&](int s, auto pc) {
-        constexpr int p = decltype(pc)::value;  // s % P
-        wait_vmcnt<(P - 3) * C::LOADS>();       // this wave's part of stage s + 1 has landed
+        constexpr int p = decltype(pc)::value;  // s mod U
+        // A fetch issued at iteration i is first read at iteration i + SS, so
+        // the one from s - 2 may stay in flight only when SS > 2.
+        constexpr bool code_prev2 = ((p - 1 + U) % C::SS) == 0 && C::SS > 2;
+        constexpr bool code_prev1 = (p % C::SS) == 0;
+        constexpr bool code_now = ((p + 1) % C::SS) == 0;
+        wait_vmcnt<C::XI + NC * (int(code_prev2) + int(code_prev1))>();
         block_barrier();
-        if (PQ_TILE_DMA_MID == 0) issue(s + P - 1, (p + P - 1) % P);
-        read_frags(std::integral_constant<int, (p + 1) % P>{}, fr[(p + 1) & 1]);
+        auto refill = [&]() {
+            issue_x(s + P - 1, (p + P - 1) % P);
+            if constexpr (code_now) issue_c((s + 1) / C::SS + 1);
+        };
+        if (PQ_TILE_DMA_MID == 0) refill();
+        read_frags(std::integral_constant<int, (p + 1) % U>{}, fr[(p + 1) & 1]);
         // Keep the scheduler from hoisting work on the fragments just
         // requested (which would wait on them) into this step's MFMAs.
         __builtin_amdgcn_sched_barrier(0);
-        // The DMA refill goes between the two k-steps' MFMAs, so that the
-        // waves leaving the barrier together do not all queue on the vector
-        // memory unit before their first MFMA.
+        // The refill goes between the two k-steps' MFMAs, so that the waves
+        // leaving the barrier together do not all queue on the vector memory
+        // unit before their first MFMA.
         mma(fr[p & 1], [&]() {
-            if (PQ_TILE_DMA_MID != 0) issue(s + P - 1, (p + P - 1) % P);
+            if (PQ_TILE_DMA_MID != 0) refill();
         });
         __builtin_amdgcn_sched_barrier(0);
     };
     int s = 0;
-    for (; s + P <= ns; s += P) {
-        static_for<0, P>([&](auto pc) { step(s + decltype(pc)::value, pc); });
+    for (; s + U <= ns; s += U) {
+        static_for<0, U>([&](auto pc) { step(s + decltype(pc)::value, pc); });
     }
-    // Tail (fewer than P stages left); s is a multiple of P, so stage s + p
-    // sits in slot p.
-    static_for<0, P - 1>([&](auto pc) {
+    // Tail (fewer than U stages left); s is a multiple of U.
+    static_for<0, U - 1>([&](auto pc) {
         if (s + decltype(pc)::value < ns) step(s + decltype(pc)::value, pc);
     });
     wait_vmcnt<0>();
