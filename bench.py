@@ -462,7 +462,7 @@ def gemm_compare(torch, pq, W16, a16, Xs, stream):
     return res
 
 
-def cpu_baseline(shapes, alg_bytes, min_seconds=10.0, max_passes=50):
+def cpu_baseline(shapes, alg_bytes, min_seconds=10.0, max_passes=400):
     """The oracle (plain C, OpenMP over rows) on the same 2-bit stack: whole
     forward + backward passes over all 210 matrices, repeated until about
     ten seconds of CPU work have been timed."""

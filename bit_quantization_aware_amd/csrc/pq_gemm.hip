@@ -48,6 +48,9 @@
 #ifndef PQ_TILE_WN
 #define PQ_TILE_WN 4
 #endif
+#ifndef PQ_TILE_TARGET_WAVES
+#define PQ_TILE_TARGET_WAVES 2048
+#endif
 #ifndef PQ_TILE_DMA_MID
 #define PQ_TILE_DMA_MID 0
 #endif
@@ -815,7 +818,7 @@ pq_status workspace(hipStream_t stream, size_t bytes, float **out)
 template <int BITS>
 pq_status launch_tile(const GemmArgs &a, hipStream_t s)
 {
-    constexpr int kTargetBlocks = 2048 / PQ_TILE_WN;  // two waves per SIMD
+    constexpr int kTargetBlocks = PQ_TILE_TARGET_WAVES / PQ_TILE_WN;
     constexpr int kMinStages = 4;
     const int mtiles = (a.M + kTileM - 1) / kTileM;
     using C = TileCfg<BITS, PQ_TILE_WN>;

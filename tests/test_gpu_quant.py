@@ -283,6 +283,41 @@ def test_mobilellm_125m_full_stack(mode):
     check_grouped(mode, mats, outs, f"125M m{mode}")
 
 
+def test_mobilellm_1p5b_layers_with_outliers():
+    """MobileLLM-1.5B-shaped layers (hidden 1600, FFN 4352, GQA kv width 400;
+    weights ~N(0, 0.02^2) with 0.1 % of them scaled by 10): the 7 matrices of
+    layers 0, 27 and 53 in one grouped 2-bit fwd + bwd launch, every output
+    checked, then the packed export of each matrix."""
+    shapes = synth.mobilellm_1p5b_shapes()
+    ks = [k for k, (l, _, _, _) in enumerate(shapes) if l in (0, 27, 53)]
+    mats = [(synth.weight("mobilellm_1p5b", k), synth.upstream_grad("mobilellm_1p5b", k)) for k in ks]
+    assert any(np.abs(W).max() > 0.15 for W, _ in mats), "outliers present"
+    print(f"[1.5B layers 0/27/53: {len(mats)} matrices]", flush=True)
+    outs = run_grouped(O.SEQ2, mats, init=True)
+    check_grouped(O.SEQ2, mats, outs, "1.5B")
+    for i, ((W, _), o) in enumerate(zip(mats, outs)):
+        rows, cols = W.shape
+        packed = torch.empty(rows, cols // 4, dtype=torch.uint8, device="cuda")
+        ab = empty_bf16(rows)
+        pq.pq_pack_w2(rows, cols, dev(W), dev(o["alpha"]), packed, ab)
+        torch.cuda.synchronize()
+        p_o, ab_o = O.pack(O.SEQ2, W, o["alpha"])
+        assert_bits_equal(host(packed), p_o, f"1.5B[{i}] packed")
+        assert_bits_equal(host(ab), ab_o, f"1.5B[{i}] alpha bf16")
+
+
+@pytest.mark.parametrize("mode", [O.SEQ2, O.TERNARY])
+def test_llama3_8b_projections(mode):
+    """The four Llama-3-8B projection shapes (4096x4096, 1024x4096,
+    14336x4096, 4096x14336; weights ~N(0, 0.015^2)) in one grouped fwd + bwd
+    launch, 2-bit SEQ and ternary, every output checked."""
+    n = len(synth.llama3_8b_shapes())
+    mats = [(synth.weight("llama3_8b", k), synth.upstream_grad("llama3_8b", k)) for k in range(n)]
+    print(f"[Llama-3-8B projections mode={mode}]", flush=True)
+    outs = run_grouped(mode, mats, init=True)
+    check_grouped(mode, mats, outs, f"llama m{mode}")
+
+
 BOUNDARIES = {
     O.SEQ2: [0.0, 0.5, -0.5, 0.99, -0.99, 0.25, -0.75],
     O.TERNARY: [1.0 / 3.0, -1.0 / 3.0, 0.99, -0.99, 0.0],
