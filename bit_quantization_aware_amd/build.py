@@ -4,7 +4,9 @@ hipcc compiles each HIP source to an object (in parallel), then links the
 shared library next to this file.  Flags:
   -ffp-contract=off      every float step stays one IEEE operation (the
                          quantizer is bit-exact by construction);
-  -packed-fp32-ops off   no v_pk_*_f32 instructions are generated.
+  -packed-fp32-ops off   no v_pk_*_f32 instructions are generated;
+  -amdgpu-mfma-vgpr-form MFMA accumulators live in ordinary VGPRs (no copies
+                         between AGPRs and VGPRs around the MFMA chains).
 """
 import concurrent.futures as cf
 import os
@@ -21,6 +23,7 @@ SOURCES = ["pq_quant.hip", "pq_gemm.hip"]
 ARCH = "gfx950"
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-command-line-argument"]
 
 

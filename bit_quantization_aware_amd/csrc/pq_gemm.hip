@@ -63,11 +63,38 @@
 #ifndef PQ_STREAM_NW
 #define PQ_STREAM_NW 4
 #endif
-#ifndef PQ_STREAM_P
-#define PQ_STREAM_P 3
-#endif
 #ifndef PQ_STREAM_TN
-#define PQ_STREAM_TN 2
+#define PQ_STREAM_TN 4
+#endif
+// 4-bit streaming kernel: column tiles per block (with one activation DMA
+// per group, and with more), stages for 1, 2, 4 DMAs
+#ifndef PQ_STREAM4_TN1
+#define PQ_STREAM4_TN1 2
+#endif
+#ifndef PQ_STREAM4_TN
+#define PQ_STREAM4_TN 4
+#endif
+#ifndef PQ_STREAM4_D1
+#define PQ_STREAM4_D1 6
+#endif
+#ifndef PQ_STREAM4_D2
+#define PQ_STREAM4_D2 5
+#endif
+#ifndef PQ_STREAM4_D4
+#define PQ_STREAM4_D4 4
+#endif
+// streaming-kernel stages in flight for 1, 2, 4 and 8 activation DMAs per group
+#ifndef PQ_STREAM_D1
+#define PQ_STREAM_D1 6
+#endif
+#ifndef PQ_STREAM_D2
+#define PQ_STREAM_D2 5
+#endif
+#ifndef PQ_STREAM_D4
+#define PQ_STREAM_D4 4
+#endif
+#ifndef PQ_STREAM_D8
+#define PQ_STREAM_D8 3
 #endif
 
 namespace pq {
@@ -135,6 +162,9 @@ struct GemmArgs {
 // the m-tiles that share a weight tile share that XCD's L2.
 // ---------------------------------------------------------------------------
 constexpr int kTileM = 64;
+// Largest K: the DMA loads address a block's rows with 32-bit offsets from a
+// wave-uniform base (at most 256 weight rows or 64 activation rows apart).
+constexpr int64_t kMaxGemmK = int64_t(1) << 24;
 constexpr int kStageK = 64;
 
 struct TileArgs {
@@ -203,11 +233,22 @@ __device__ __forceinline__ void block_barrier()
 }
 
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+// The empty asm with a memory clobber keeps the compiler from moving LDS
+// reads of DMA-filled buffers above the wait (LDS loads cannot fault, so it
+// would otherwise be free to hoist them).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
 {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+    asm volatile("" ::: "memory");
+}
+
+// s_waitcnt lgkmcnt(0): every LDS access of the wave has completed.
+__device__ __forceinline__ void wait_lgkmcnt0()
+{
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+    asm volatile("" ::: "memory");
 }
 
 template <int SEL>
@@ -257,7 +298,7 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
     for (int q = 0; q < C::XI; ++q) {
         const int r = 8 * (C::XI * w + q) + (lane >> 3);
         const int c = (lane & 7) ^ xswz(r);
-        xoff[q] = static_cast<uint32_t>((min(m0 + r, M - 1) - m0) * K * 2 + 16 * c);
+        xoff[q] = static_cast<uint32_t>(static_cast<int64_t>(min(m0 + r, M - 1) - m0) * K * 2 + 16 * c);
     }
     // Code DMAs: one fetch covers SS stages of the block's columns, 64
     // contiguous bytes per column.  DMA i of wave w brings columns
@@ -537,16 +578,28 @@ __global__ __launch_bounds__(256) void k_splitk_finalize(const float *ws, const 
 // ---------------------------------------------------------------------------
 // Weight-streaming kernel for M <= 16 (decode and small batches).
 //
-// The weight (N*K*BITS/8 bytes) is the whole cost.  A block owns 16*TN output
-// columns and its NW waves split K between them (wave w takes groups w,
-// w+NW, ...), so no barrier is needed until the final reduction.  Per group
-// a wave needs 16 bytes of codes per lane per tile and the group's k-slice of
-// the M activation rows; both are fetched P groups ahead into registers
-// (vector loads retire in order, so activations must be requested as early
-// as the codes they meet).  Activations move row-contiguously, only the M
-// real rows (XI = ceil(M / rows-per-load) loads), and are turned into MFMA A
-// fragments through a wave-private LDS slot.  Output rows >= M come from
-// stale A rows and are never stored; columns >= N read a clamped row.
+// The weight (N*K*BITS/8 bytes, read once) is the whole cost, and HBM gives
+// its rate only with many bytes in flight per CU.  A block owns TN column
+// tiles of 16 and its NW waves share K out by groups (256 k at 2 bits, 128
+// at 4: 64 bytes of each weight row), wave w taking groups w, w + NW, ..., so
+// that at any moment the block reads neighbouring pieces of the same rows.
+// Every wave streams its groups through a private LDS ring of D stages with
+// the LDS-DMA load (global_load_lds_dwordx4, no registers used): per group
+// one 1-KB DMA per column tile (lane (i16, grp) fetches bytes 16*grp ..
+// 16*grp+15 of the group's 64 in row i16) and ceil(M / RPL) 1-KB DMAs of
+// activations, so up to D * (TN + XI) KB per wave are in flight.  The ring
+// is private to the wave: a stage waits on the wave's own s_waitcnt only,
+// and the block meets at a barrier once, to add the NW partial sums.  Each
+// block starts its walk at its own offset, so blocks do not read the same
+// activation lines in lockstep.
+//
+// LDS.  A code block is read back by the lane that fetched each 16 bytes,
+// which is that lane's MFMA B fragment for the decode below.  An activation
+// DMA holds RPL rows interleaved in 16-byte chunks (lane l fetches chunk
+// l / RPL of row RPL*q + l % RPL) and consecutive DMAs sit 16*RPL bytes
+// further apart than their size, so the 16 rows one A-operand read touches
+// fall on distinct banks.  Rows >= M are fetched as row M - 1; their outputs
+// are never stored.  Columns >= N read a clamped row.
 //
 // Decode.  2-bit: with D & 0x33333333 every nibble holds one code in its low
 // two bits, the e2m1 value c/2; v_cvt_scalef32_pk_bf16_fp4 turns each byte
@@ -555,102 +608,105 @@ __global__ __launch_bounds__(256) void k_splitk_finalize(const float *ws, const 
 // spread into bytes and completed to bf16 128 + c (exact); level = v - 136.
 // The activations are put in the matching k order (evens, then odds, of each
 // 16- or 8-wide block) by byte permutes.  The row sums of X needed by the
-// offsets are taken with v_dot2 on the activation chunks as they arrive.
-// The NW partial sums are combined in LDS in a fixed order.
+// offsets are taken with v_dot2 on the chunk each lane fetched.  The NW
+// partial sums are combined in LDS in a fixed order.
 // ---------------------------------------------------------------------------
-template <int BITS, int NW, int P, int TN, int XI>
+template <int BITS>
+struct StreamGeom {
+    static constexpr int GK = BITS == 2 ? 256 : 128;  // k per group (64 bytes of a row)
+    static constexpr int RPL = 512 / GK;              // activation rows per 1-KB DMA
+    static constexpr int XQS = 1024 + 16 * RPL;       // LDS stride of the activation DMAs
+};
+
+template <int BITS, int TN, int NW, int D, int XI>
 __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
 {
-    static_assert(TN <= NW, "one wave finishes each tile");
-    constexpr int GK = BITS == 2 ? 256 : 128;     // k per group (16 B of codes per lane per tile)
-    constexpr int RPL = 512 / GK;                 // activation rows per 1 KB load (2 or 4)
-    constexpr int XROW = GK + 8;                  // LDS row stride, bf16 (+16 bytes)
+    using SG = StreamGeom<BITS>;
+    constexpr int GK = SG::GK, RPL = SG::RPL, XQS = SG::XQS;
+    constexpr int SLOT = TN * 1024 + XI * XQS;  // one stage: codes, then activations
+    constexpr int WLDS = D * SLOT;              // one wave's ring
     constexpr int NACC = TN * 4;
-    static_assert(NW * NACC * 64 * 4 <= NW * 16 * XROW * 2, "reduction fits in the X slots");
+    constexpr int PER_STAGE = TN + XI;          // DMAs per stage
+    static_assert(D >= 1 && D * PER_STAGE < 64, "DMAs in flight fit the vmcnt counter");
+    static_assert(NW * WLDS + NW * 16 * 4 <= 160 * 1024, "LDS");
+    static_assert(NACC * 64 * 4 <= WLDS, "partial sums fit in the wave's ring");
+    static_assert(TN <= NW, "one wave finishes each tile");
+    static_assert(RPL * XI <= 16 + RPL - 1, "at most 16 activation rows");
 
-    __shared__ __attribute__((aligned(16))) uint16_t xs[NW * 16 * XROW];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[NW * WLDS];
     __shared__ float rsum[NW][16];
-    float *red = reinterpret_cast<float *>(xs);
 
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int i16 = lane & 15, grp = lane >> 4;
     const int M = g.M, N = g.N, K = g.K;
     const int n0 = blockIdx.x * 16 * TN;
     const int G = K / GK;
+    // This wave's groups are w, w + NW, w + 2 NW, ...: at any moment the
+    // block's waves read neighbouring 64-byte pieces of the same rows.
+    const int nit = G > w ? (G - w + NW - 1) / NW : 0;
     const int64_t row_bytes = static_cast<int64_t>(K) * BITS / 8;
 
-    typedef __attribute__((address_space(1))) const u32x4 guint4;
-    guint4 *cp[TN];
+    // DMA sources: a wave-uniform base plus a 32-bit per-lane offset (the
+    // host bounds K so that every offset fits).
+    const uint8_t *cbase = g.packed + static_cast<int64_t>(n0) * row_bytes;
+    uint32_t coff[TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        int n = n0 + 16 * j + i16;
-        n = n < N ? n : N - 1;
-        cp[j] = (guint4 *)(g.packed + n * row_bytes + grp * 16);
-    }
-    // activation loads: lane -> (row within the load, 8-element chunk)
-    const int xr_sub = lane / (64 / RPL), xr_chunk = lane % (64 / RPL);
-    guint4 *xp[XI];
-    int xrow_of[XI];
+    for (int j = 0; j < TN; ++j)
+        coff[j] = static_cast<uint32_t>((min(n0 + 16 * j + i16, N - 1) - n0) * row_bytes + 16 * grp);
+    uint32_t xoff[XI];
 #pragma unroll
     for (int q = 0; q < XI; ++q) {
-        int r = RPL * q + xr_sub;
-        xrow_of[q] = r;
-        r = r < M ? r : M - 1;
-        xp[q] = (guint4 *)(g.X + static_cast<int64_t>(r) * K + xr_chunk * 8);
+        const int r = min(RPL * q + lane % RPL, M - 1);
+        xoff[q] = static_cast<uint32_t>((static_cast<int64_t>(r) * K + (lane / RPL) * 8) * 2);
     }
-    uint16_t *xw = xs + w * 16 * XROW;            // this wave's slot
-    const int mrow = i16 < M ? i16 : M - 1;
+    const uint32_t ring = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)lds)) + w * WLDS;
+    const uint8_t *wring = lds + w * WLDS;
+    const int rot = nit > 0 ? static_cast<int>(blockIdx.x % static_cast<unsigned>(nit)) : 0;
+
+    auto issue = [&](int it, int slot) {
+        int i = it + rot;
+        i = i >= nit ? i - nit : i;
+        const uint32_t gi = static_cast<uint32_t>(w + NW * i);
+        const uint32_t sb = ring + slot * SLOT;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) dma16(cbase, coff[j] + gi * 64, sb + j * 1024);
+#pragma unroll
+        for (int q = 0; q < XI; ++q) dma16(g.X, xoff[q] + gi * (GK * 2), sb + TN * 1024 + q * XQS);
+    };
 
     floatx4 acc[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
-    // Row sums of X (for the level offset): each lane sums the activation
-    // chunks it loads with v_dot2 against (1, 1).
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     const bf16x2_t ones2 = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
     float rsx[XI];
 #pragma unroll
     for (int q = 0; q < XI; ++q) rsx[q] = 0.f;
+    // A-operand row of this lane; rows >= M repeat row M - 1 (an LDS broadcast).
+    const int mrow = i16 < M ? i16 : M - 1;
+    const int aoff = TN * 1024 + (mrow / RPL) * XQS + (mrow % RPL) * 16;
 
-    uint4 cb[P][TN];
-    uint4 xb[P][XI];
-
-    // This wave's groups are w + NW*i, i < nit; each block walks them from
-    // its own starting point, so at any moment the blocks read different
-    // activation lines (all blocks read the same X, and in lockstep they
-    // would queue on the same L2 channel).  Loads past the end read an
-    // in-bounds group and their results are never used.
-    const int nit = G > w ? (G - w + NW - 1) / NW : 0;
-    const int rot = nit > 0 ? static_cast<int>(blockIdx.x % static_cast<unsigned>(nit)) : 0;
-    auto load = [&](int it, uint4 (&c)[TN], uint4 (&x)[XI]) {
-        int i = it + rot;
-        i = i >= nit ? i - nit : i;
-        int gi = w + NW * i;
-        gi = gi < G ? gi : G - 1;
+    auto compute = [&](int slot) {
+        const uint8_t *sp = wring + slot * SLOT;
+        uint4 c[TN];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) c[j] = __builtin_bit_cast(uint4, cp[j][gi * 4]);
-#pragma unroll
-        for (int q = 0; q < XI; ++q) x[q] = __builtin_bit_cast(uint4, xp[q][gi * (GK / 8)]);
-    };
-
-    auto compute = [&](const uint4 (&c)[TN], const uint4 (&x)[XI]) {
-        // activations of this group -> the wave's LDS slot (row-major)
+        for (int j = 0; j < TN; ++j) c[j] = *reinterpret_cast<const uint4 *>(sp + j * 1024 + lane * 16);
 #pragma unroll
         for (int q = 0; q < XI; ++q) {
-            *reinterpret_cast<uint4 *>(xw + xrow_of[q] * XROW + xr_chunk * 8) = x[q];
-            rsx[q] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x[q].x), ones2, rsx[q], false);
-            rsx[q] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x[q].y), ones2, rsx[q], false);
-            rsx[q] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x[q].z), ones2, rsx[q], false);
-            rsx[q] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x[q].w), ones2, rsx[q], false);
+            const uint4 v = *reinterpret_cast<const uint4 *>(sp + TN * 1024 + q * XQS + lane * 16);
+            rsx[q] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.x), ones2, rsx[q], false);
+            rsx[q] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.y), ones2, rsx[q], false);
+            rsx[q] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.z), ones2, rsx[q], false);
+            rsx[q] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.w), ones2, rsx[q], false);
         }
-        // Rows >= M read row M-1: with one address per lane group the LDS
-        // serves the read as a broadcast.
-        const uint16_t *xa = xw + mrow * XROW + grp * (GK / 4);
+        // chunk ch of the lane's row sits at aoff + ch * 16 * RPL
+        const uint8_t *xa = sp + aoff;
         if constexpr (BITS == 2) {
-            uint4 ua[8];  // issue every A read of the group before the decode work
+            uint4 ua[8];  // k = 64 * grp + [0, 64): chunks 8 * grp .. 8 * grp + 7
 #pragma unroll
-            for (int q = 0; q < 8; ++q) ua[q] = *reinterpret_cast<const uint4 *>(xa + 8 * q);
+            for (int q = 0; q < 8; ++q) ua[q] = *reinterpret_cast<const uint4 *>(xa + (8 * grp + q) * 32);
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 const uint4 u0 = ua[2 * d];
@@ -670,9 +726,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
                 const bf16x8 a_o = __builtin_bit_cast(bf16x8, ao);
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
-                    const uint32_t D = d == 0 ? c[j].x : d == 1 ? c[j].y : d == 2 ? c[j].z : c[j].w;
-                    const uint32_t m0 = D & 0x33333333u;
-                    const uint32_t m1 = (D >> 2) & 0x33333333u;
+                    const uint32_t Dw = d == 0 ? c[j].x : d == 1 ? c[j].y : d == 2 ? c[j].z : c[j].w;
+                    const uint32_t m0 = Dw & 0x33333333u;
+                    const uint32_t m1 = (Dw >> 2) & 0x33333333u;
                     uint4 be, bo;
                     be.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(m0, 1.0f, 0));
                     be.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(m0, 1.0f, 1));
@@ -687,9 +743,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
                 }
             }
         } else {
-            uint4 ua[4];
+            uint4 ua[4];  // k = 32 * grp + [0, 32): chunks 4 * grp .. 4 * grp + 3
 #pragma unroll
-            for (int q = 0; q < 4; ++q) ua[q] = *reinterpret_cast<const uint4 *>(xa + 8 * q);
+            for (int q = 0; q < 4; ++q) ua[q] = *reinterpret_cast<const uint4 *>(xa + (4 * grp + q) * 64);
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 const uint4 xv = ua[d];
@@ -701,9 +757,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
                 const bf16x8 av = __builtin_bit_cast(bf16x8, a);
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
-                    const uint32_t D = d == 0 ? c[j].x : d == 1 ? c[j].y : d == 2 ? c[j].z : c[j].w;
-                    const uint32_t lo = D & 0x0F0F0F0Fu;          // nibbles 0,2,4,6 in bytes
-                    const uint32_t hi = (D >> 4) & 0x0F0F0F0Fu;   // nibbles 1,3,5,7
+                    const uint32_t Dw = d == 0 ? c[j].x : d == 1 ? c[j].y : d == 2 ? c[j].z : c[j].w;
+                    const uint32_t lo = Dw & 0x0F0F0F0Fu;          // nibbles 0,2,4,6 in bytes
+                    const uint32_t hi = (Dw >> 4) & 0x0F0F0F0Fu;   // nibbles 1,3,5,7
                     uint4 b;
                     b.x = (lo & 0xFFu) | ((lo << 8) & 0x00FF0000u) | 0x43004300u;
                     b.y = ((lo >> 16) & 0xFFu) | ((lo >> 8) & 0x00FF0000u) | 0x43004300u;
@@ -715,40 +771,45 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
         }
     };
 
-#pragma unroll
-    for (int s = 0; s < P; ++s) load(s, cb[s], xb[s]);
-    // Steady state: no conditionals, so the compiler can count the loads in
-    // flight and wait only for the slot being consumed.
-    int base = 0;
-    for (; base + P <= nit; base += P) {
-        static_for<0, P>([&](auto sc) {
-            constexpr int s = decltype(sc)::value;
-            compute(cb[s], xb[s]);
-            load(base + s + P, cb[s], xb[s]);
-            // keep the scheduler from hoisting later slots' work above this
-            // slot's wait (which would wait for every load in flight)
-            __builtin_amdgcn_sched_barrier(0);
-        });
+    // Prologue: the first min(D, nit) stages.  Steady state: stage s is
+    // consumed when at most D - 1 later stages are still in flight, and its
+    // slot is refilled with stage s + D once its LDS reads have returned.
+    // The last stages drain with exact counts.
+    const int npro = min(D, nit);
+    for (int s = 0; s < npro; ++s) issue(s, s);
+    int s = 0, slot = 0;
+    for (; s + D < nit; ++s) {
+        wait_vmcnt<(D - 1) * PER_STAGE>();
+        compute(slot);
+        wait_lgkmcnt0();
+        issue(s + D, slot);
+        slot = slot + 1 == D ? 0 : slot + 1;
     }
-    static_for<0, P>([&](auto sc) {
-        constexpr int s = decltype(sc)::value;
-        if (base + s < nit) compute(cb[s], xb[s]);
+    static_for<0, D>([&](auto tc) {
+        constexpr int r = D - 1 - decltype(tc)::value;  // stages issued after this one
+        const int st = nit - 1 - r;
+        if (st >= s) {
+            wait_vmcnt<r * PER_STAGE>();
+            compute(st % D);
+        }
     });
 
     // Combine the NW partial sums in LDS (fixed order); wave j < TN finishes
     // tile j for all rows.
     __syncthreads();
+    float *red = reinterpret_cast<float *>(lds);
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) red[(w * NACC + 4 * j + e) * 64 + lane] = acc[j][e];
-    // Row sums: reduce over the lanes that loaded chunks of the same row.
+    // Row sums: reduce over the lanes that fetched chunks of the same row.
 #pragma unroll
     for (int q = 0; q < XI; ++q) {
         float v = rsx[q];
 #pragma unroll
-        for (int o = 1; o < 64 / RPL; o <<= 1) v += __shfl_xor(v, o);
-        if (xr_chunk == 0 && xrow_of[q] < 16) rsum[w][xrow_of[q]] = v;
+        for (int o = RPL; o < 64; o <<= 1) v += __shfl_xor(v, o);
+        const int r = RPL * q + lane % RPL;
+        if (lane < RPL && r < 16) rsum[w][r] = v;
     }
     __syncthreads();
     if (w < TN) {
@@ -774,12 +835,24 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
     }
 }
 
+// Streaming-kernel shapes by activation DMAs per group (XI): column tiles
+// per block, waves per block, stages in flight.  The 4-bit decode costs
+// about twice the VALU work per weight byte, so with few activation rows
+// 4-bit blocks take fewer column tiles and the chip runs two per CU.
+template <int BITS, int XI>
+struct StreamCfg {
+    static constexpr int TN = BITS == 2 ? PQ_STREAM_TN : (XI == 1 ? PQ_STREAM4_TN1 : PQ_STREAM4_TN);
+    static constexpr int NW = PQ_STREAM_NW;
+    static constexpr int D = BITS == 2 ? (XI == 1 ? PQ_STREAM_D1 : XI == 2 ? PQ_STREAM_D2 : XI <= 4 ? PQ_STREAM_D4 : PQ_STREAM_D8)
+                                       : (XI == 1 ? PQ_STREAM4_D1 : XI == 2 ? PQ_STREAM4_D2 : PQ_STREAM4_D4);
+};
+
 template <int BITS, int XI>
 void launch_stream(const GemmArgs &a, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_gemm_stream<BITS, PQ_STREAM_NW, PQ_STREAM_P, PQ_STREAM_TN, XI>),
-                       dim3((a.N + 16 * PQ_STREAM_TN - 1) / (16 * PQ_STREAM_TN)),
-                       dim3(64 * PQ_STREAM_NW), 0, s, a);
+    using C = StreamCfg<BITS, XI>;
+    hipLaunchKernelGGL((k_gemm_stream<BITS, C::TN, C::NW, C::D, XI>), dim3((a.N + 16 * C::TN - 1) / (16 * C::TN)),
+                       dim3(64 * C::NW), 0, s, a);
 }
 
 // Split-K workspace: one fp32 buffer per (device, stream), grown on demand.
@@ -855,7 +928,7 @@ pq_status gemm(int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *pa
                const void *alpha_bf16, void *Y, void *stream)
 {
     if (!X || !packed || !alpha_bf16 || !Y) return PQ_ERR_NULL;
-    if (M < 0 || N < 0 || K <= 0 || K % 64 != 0 || K > kMaxCols || M > INT32_MAX / 2 ||
+    if (M < 0 || N < 0 || K <= 0 || K % 64 != 0 || K > kMaxGemmK || M > INT32_MAX / 2 ||
         N > INT32_MAX / 2)
         return PQ_ERR_SHAPE;
     if (!aligned16(X) || !aligned16(packed) || !aligned16(Y) || !aligned16(alpha_bf16))

@@ -34,7 +34,8 @@
  *   Errors     Arguments are checked on the host before anything is enqueued:
  *              a NULL required pointer -> PQ_ERR_NULL; rows, cols, M, N or K
  *              negative, cols not a positive multiple of 8, or K not a
- *              positive multiple of 64 -> PQ_ERR_SHAPE; an unknown mode,
+ *              positive multiple of 64 or above 2^24 -> PQ_ERR_SHAPE; an
+ *              unknown mode,
  *              flag or dtype -> PQ_ERR_MODE; an array pointer not 16-byte
  *              aligned -> PQ_ERR_ALIGN; a bad descriptor table or grad_scale
  *              -> PQ_ERR_ARG.  A failed launch -> PQ_ERR_HIP.  On any error
@@ -196,7 +197,9 @@ pq_status pq_pack_w4(int64_t rows, int64_t cols, const float *W, const float *al
  *   Y[m, n] = bf16( alpha_bf16[n] * sum_k X[m, k] * level(code[n, k]) )
  * with level(c) = (c - 1.5) / 2, fp32 accumulation.
  *   M, N, K    X is [M, K]; K a positive multiple of 64 (so every packed
- *              row is a whole number of 16-byte words); M, N >= 0
+ *              row is a whole number of 16-byte words) and at most 2^24
+ *              (the kernels address a block's rows with 32-bit offsets);
+ *              M, N >= 0
  *   X          in   [M, K] bf16 activations
  *   packed     in   [N, K/4] u8 from pq_pack_w2
  *   alpha_bf16 in   [N] bf16

@@ -99,6 +99,34 @@ def test_gemm_zero_and_edge_values():
     assert np.allclose(Y[:, 0], -0.75 * 0.5 * K) and np.allclose(Y[:, 1], 0.75 * 0.5 * K)
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 64, 7680), (2, 100, 8192), (2, 1000, 16384), (1, 257, 5888),
+                                   (1, 8, 16384), (2, 16, 6144)])
+def test_gemm_small_m_long_k_full_compare(M, N, K):
+    """One or two activation rows against long rows of weights (the decode
+    shape), ragged and narrow N; every output."""
+    print(f"[gemm small-M M={M} N={N} K={K}]", flush=True)
+    X, packed, ab = make_case(O.SEQ2, 11 * M + N + K, M, N, K)
+    Y = gpu_gemm(O.SEQ2, X, packed, ab, N)
+    check(Y, O.gemm_ref(O.SEQ2, X, packed, ab, N), f"small-M {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M", [1, 2, 4])
+def test_gemm_wide_range_activations(M):
+    """Activations spanning ten decades inside every 128-k chunk, exact zeros
+    and whole zero chunks, against the binary64 reference."""
+    N, K = 96, 8192
+    rng = np.random.default_rng(100 + M)
+    W = synth.normal_f32(rng, (N, K), 0.02)
+    alpha = O.alpha_init(O.SEQ2, W)
+    packed, ab = O.pack(O.SEQ2, W, alpha)
+    x = rng.standard_normal((M, K)) * 10.0 ** rng.uniform(-6, 4, (M, K))
+    x[:, ::7] = 0.0
+    x[:, 256:512] = 0.0
+    X = synth.to_bf16_bits(x.astype(np.float32))
+    Y = gpu_gemm(O.SEQ2, X, packed, ab, N)
+    check(Y, O.gemm_ref(O.SEQ2, X, packed, ab, N), f"wide range M={M}")
+
+
 def sample_points(rng, M, N, count):
     ms = np.concatenate([[0, M - 1, 0, M - 1], rng.integers(0, M, count)])
     ns = np.concatenate([[0, 0, N - 1, N - 1], rng.integers(0, N, count)])
