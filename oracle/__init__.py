@@ -50,6 +50,9 @@ def lib():
         L.pqo_gemm_ref.argtypes = [ctypes.c_int, _i64, _i64, _i64, _u16p, _u8p, _u16p, _f64p]
         L.pqo_gemm_ref_at.argtypes = [ctypes.c_int, _i64, _i64, _i64, _u16p, _u8p, _u16p,
                                       _i64p, _i64p, _i64, _f64p]
+        L.pqo_tiled_bytes.argtypes = [_i64, _i64]
+        L.pqo_tiled_bytes.restype = _i64
+        L.pqo_tile_codes.argtypes = [_i64, _i64, _u8p, _u8p]
         L.pqo_set_threads.argtypes = [ctypes.c_int]
         _lib = L
     return _lib
@@ -167,6 +170,25 @@ def pack(mode: int, W: np.ndarray, alpha: np.ndarray):
     _check(lib().pqo_pack(mode, rows, cols, _p(W, _f32p), _p(alpha, _f32p),
                           _p(packed, _u8p), _p(ab, _u16p)))
     return packed, ab
+
+
+def tiled_bytes(rows: int, row_bytes: int) -> int:
+    return int(lib().pqo_tiled_bytes(rows, row_bytes))
+
+
+def tile_codes(packed: np.ndarray) -> np.ndarray:
+    """Deployment byte order (flat uint8) of row-major code rows [rows, rb]."""
+    packed = _c(packed, np.uint8)
+    rows, rb = packed.shape
+    out = np.empty(tiled_bytes(rows, rb), np.uint8)
+    _check(lib().pqo_tile_codes(rows, rb, _p(packed, _u8p), _p(out, _u8p)))
+    return out
+
+
+def pack_tiled(mode: int, W: np.ndarray, alpha: np.ndarray):
+    """Export in the deployment byte order: (tiled codes uint8 flat, alpha bf16 bits)."""
+    packed, ab = pack(mode, W, alpha)
+    return tile_codes(packed), ab
 
 
 def gemm_ref(mode: int, X_bf16: np.ndarray, packed: np.ndarray, alpha_bf16: np.ndarray, N: int):

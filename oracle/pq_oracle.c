@@ -2,7 +2,8 @@
  * pq_oracle.c -- plain, slow, CPU reference ("the oracle") for the ParetoQ
  * quantized linear layer: alpha init, forward fake-quantization at
  * 1 / 1.58 / 2 / 3 / 4 bits, the straight-through backward with the per-row
- * scale gradient, 2-bit / 4-bit export packing and the packed-weight GEMM.
+ * scale gradient, 2-bit / 4-bit export packing (and the deployment byte
+ * order of the exported codes) and the packed-weight GEMM.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg may load this library.  It shares no code,
@@ -415,6 +416,44 @@ int pqo_pack(int mode, int64_t rows, int64_t cols, const float *W, const float *
     if (pqo_quantize_fwd(mode, rows, cols, W, alpha, NULL, NULL, packed) != 0) return -1;
     if (alpha_bf16)
         for (int64_t i = 0; i < rows; ++i) alpha_bf16[i] = pqo_bf16_rne(alpha[i]);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Deployment layout of the exported codes.  The pages fix only what a packed
+ * 2-bit weight holds (four codes per byte and a bf16 scale per row, [News]
+ * storage and speed paragraphs); the byte order the deployed GEMM reads is
+ * this library's own, defined here from the row-major code rows that the
+ * forward emits (rb bytes per row):
+ *   groups   g = 0 .. G-1,  G  = ceil(rb / 64)   (64 bytes of every row)
+ *   tiles    t = 0 .. Np/16-1, Np = rows rounded up to a multiple of 16
+ *   pieces   p = 0 .. 3  (16 bytes each), row r = 0 .. 15 of the tile,
+ *            byte e = 0 .. 15 of the piece
+ *   tiled[(((g * (Np/16) + t) * 4 + p) * 16 + r) * 16 + e]
+ *       = rowmajor[(16 t + r) * rb + 64 g + 16 p + e]
+ *   when the row 16 t + r < rows and the byte 64 g + 16 p + e < rb, else 0.
+ * So every 64-byte group of all rows is one contiguous run (group-major), and
+ * inside it each tile of 16 rows is 1 KB.  Size: G * Np * 64 bytes.
+ * ------------------------------------------------------------------------- */
+int64_t pqo_tiled_bytes(int64_t rows, int64_t rb)
+{
+    if (rows < 0 || rb < 0) return -1;
+    return ((rb + 63) / 64) * ((rows + 15) / 16 * 16) * 64;
+}
+
+int pqo_tile_codes(int64_t rows, int64_t rb, const uint8_t *rowmajor, uint8_t *tiled)
+{
+    if (rows < 0 || rb < 0) return -1;
+    const int64_t G = (rb + 63) / 64, T = (rows + 15) / 16;
+    for (int64_t g = 0; g < G; ++g)
+        for (int64_t t = 0; t < T; ++t)
+            for (int p = 0; p < 4; ++p)
+                for (int r = 0; r < 16; ++r)
+                    for (int e = 0; e < 16; ++e) {
+                        const int64_t dst = (((g * T + t) * 4 + p) * 16 + r) * 16 + e;
+                        const int64_t n = 16 * t + r, c = 64 * g + 16 * p + e;
+                        tiled[dst] = (n < rows && c < rb) ? rowmajor[n * rb + c] : 0;
+                    }
     return 0;
 }
 

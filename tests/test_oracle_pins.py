@@ -9,7 +9,10 @@ What each pin stands on:
     "round acts as the identity inside the clip range" -- the chain rule
     derives the gradient independently of the oracle's hand-derived formula;
   * finite differences where every weight is clipped (q is linear in alpha);
-  * alpha init, GEMM and bf16 rounding: numpy / torch library routines.
+  * alpha init, GEMM and bf16 rounding: numpy / torch library routines;
+  * the deployment byte order of exported codes: a numpy axis shuffle of the
+    padded code rows and hand-worked positions (the layout is the library's
+    own definition; the pages fix only four codes per byte).
 Parity unpinned (documented readings): the 1-bit quantizer, the ternary
 alpha-gradient of clipped weights, and n / Qp of the default gradient scale.
 """
@@ -436,3 +439,42 @@ def test_gemm_ref_is_matmul_of_dequantized_weight(mode):
     ms = rng.integers(0, M, 17)
     ns = rng.integers(0, N, 17)
     assert np.array_equal(O.gemm_ref_at(mode, X, packed, ab, N, ms, ns), Y[ms, ns])
+
+
+def _tile_by_reshape(P):
+    """The deployment byte order as a numpy index shuffle: pad to whole tiles
+    and groups, then order the axes (group, tile, piece, row, byte)."""
+    rows, rb = P.shape
+    Np, G = -(-rows // 16) * 16, -(-rb // 64)
+    pad = np.zeros((Np, G * 64), np.uint8)
+    pad[:rows, :rb] = P
+    return pad.reshape(Np // 16, 16, G, 4, 16).transpose(2, 0, 3, 1, 4).reshape(-1)
+
+
+@pytest.mark.parametrize("rows,rb", [(16, 64), (20, 144), (1, 2), (33, 16), (48, 256), (7, 200),
+                                     (0, 64), (5, 0)])
+def test_tile_codes_matches_axis_shuffle(rows, rb):
+    rng = np.random.default_rng(rows * 1000 + rb)
+    P = rng.integers(0, 256, (rows, rb), dtype=np.uint8)
+    T = O.tile_codes(P)
+    assert T.size == O.tiled_bytes(rows, rb) == -(-rb // 64) * (-(-rows // 16) * 16) * 64
+    assert np.array_equal(T, _tile_by_reshape(P))
+
+
+def test_tile_codes_hand_positions():
+    # 20 rows of 144 bytes (2-bit codes of 576 weights): 32 padded rows, 3 groups.
+    P = (np.arange(20 * 144) % 251 + 1).astype(np.uint8).reshape(20, 144)
+    T = O.tile_codes(P)
+    assert T.size == 3 * 32 * 64
+    # row 17, byte 70: group 1, tile 1, piece 0, tile row 1, byte 6
+    assert T[((1 * 2 + 1) * 4 + 0) * 256 + 1 * 16 + 6] == P[17, 70]
+    # row 0, byte 143: group 2, piece 0, byte 15
+    assert T[(2 * 2 * 4) * 256 + 15] == P[0, 143]
+    # row 19, byte 0: tile 1, tile row 3
+    assert T[1024 + 3 * 16] == P[19, 0]
+    # padding: bytes past the row (group 2, piece 1) and rows past 20 are zero
+    assert not T[(2 * 2 * 4 + 1) * 256:(2 * 2 * 4 + 4) * 256].any()
+    assert not T[1024 + 4 * 16:1024 + 16 * 16].any()
+    # every stored byte appears exactly once: nonzero bytes are a permutation
+    assert np.count_nonzero(T) == P.size
+    assert np.array_equal(np.sort(T[T != 0]), np.sort(P.reshape(-1)))
