@@ -146,7 +146,7 @@ def pmc_summarize(args):
     groups = {
         "fwd": lambda n: "k_quant_fwd<2, false, 1, 5u>" in n,
         "bwd": lambda n: "k_quant_bwd<2, 1, false, true, false>" in n,
-        "pack": lambda n: "k_quant_fwd<2, false, 1, 12u>" in n,
+        "pack": lambda n: "k_quant_fwd<2, false, 1, 28u>" in n,
         # k_gemm_stream<BITS, TN, NW, D, XI>: M = 1, 4, 16 use XI = 1, 2, 8
         "gemm_m1": lambda n: re.search(r"k_gemm_stream<2, \d+, \d+, \d+, 1>", n) is not None,
         "gemm_m4": lambda n: re.search(r"k_gemm_stream<2, \d+, \d+, \d+, 2>", n) is not None,
@@ -246,7 +246,8 @@ def main():
     W16 = torch.from_numpy(synth.weight("square16k", 0)).to(dev)
     a16 = torch.zeros(GEMM_NK, dtype=torch.float32, device=dev)
     pq.pq_quantize_fwd(mode, GEMM_NK, GEMM_NK, W16, a16, pq.PQ_INIT_ALPHA, None, None, None)
-    packed = [torch.empty(GEMM_NK, GEMM_NK // 4, dtype=torch.uint8, device=dev) for _ in range(ROTATE)]
+    pbytes = pq.pq_packed_bytes(pq.PQ_W2_SEQ, GEMM_NK, GEMM_NK)
+    packed = [torch.empty(pbytes, dtype=torch.uint8, device=dev) for _ in range(ROTATE)]
     ab16 = [torch.empty(GEMM_NK, dtype=torch.bfloat16, device=dev) for _ in range(ROTATE)]
     for i in range(ROTATE):
         pq.pq_pack_w2(GEMM_NK, GEMM_NK, W16, a16, packed[i], ab16[i])
@@ -442,7 +443,8 @@ def gemm_compare(torch, pq, W16, a16, Xs, stream):
     dequantized weight, at the same shapes (8 rotating weight copies each)."""
     N = K = GEMM_NK
     res = {}
-    p4 = [torch.empty(N, K // 2, dtype=torch.uint8, device="cuda") for _ in range(ROTATE)]
+    p4 = [torch.empty(pq.pq_packed_bytes(pq.PQ_W4_LSQ, N, K), dtype=torch.uint8, device="cuda")
+          for _ in range(ROTATE)]
     a4 = torch.zeros(N, dtype=torch.float32, device="cuda")
     pq.pq_quantize_fwd(pq.PQ_W4_LSQ, N, K, W16, a4, pq.PQ_INIT_ALPHA, None, None, None)
     ab4 = [torch.empty(N, dtype=torch.bfloat16, device="cuda") for _ in range(ROTATE)]

@@ -115,10 +115,11 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 struct GemmArgs {
     const uint16_t *X;       // [M, K] bf16
-    const uint8_t *packed;   // [N, K * BITS / 8]
+    const uint8_t *packed;   // export byte order: [groups][N / 16 tiles][1 KB]
     const uint16_t *alpha;   // [N] bf16
     uint16_t *Y;             // [M, N] bf16
     int M, N, K;
+    int64_t gstride;         // bytes per 64-byte group of all rows (Np * 64)
 };
 
 // ---------------------------------------------------------------------------
@@ -130,11 +131,11 @@ struct GemmArgs {
 // in stages of 64.  Each stage's activation tile (64 rows x 128 B) is copied
 // global -> LDS by the gfx950 LDS-DMA load (global_load_lds_dwordx4), with no
 // register or VALU traffic, into a ring of four stage buffers kept three
-// stages ahead.  Codes are fetched the same way but 64 bytes per column at a
-// time (four stages at 2 bits, two at 4), so every DMA instruction reads 16
-// runs of 64 contiguous bytes instead of 64 scattered 16-byte pieces; the
-// fetches are double-buffered.  One s_waitcnt plus one barrier per stage
-// orders both rings.
+// stages ahead.  Codes are fetched the same way but one 64-byte group per
+// column at a time (four stages at 2 bits, two at 4): in the export byte
+// order a group of 16 columns is one contiguous 1-KB tile, so every DMA
+// instruction reads 1 KB in one piece; the fetches are double-buffered.  One
+// s_waitcnt plus one barrier per stage orders both rings.
 //
 // LDS activation layout: row r holds its eight 16-byte k-chunks with chunk c
 // stored in slot c ^ xswz(r).  The DMA writes 1 KB contiguous per wave
@@ -162,20 +163,23 @@ struct GemmArgs {
 // the m-tiles that share a weight tile share that XCD's L2.
 // ---------------------------------------------------------------------------
 constexpr int kTileM = 64;
-// Largest K: the DMA loads address a block's rows with 32-bit offsets from a
-// wave-uniform base (at most 256 weight rows or 64 activation rows apart).
+// Largest K and N: the DMA loads address with 32-bit offsets from a
+// wave-uniform base -- up to 64 activation rows, or one 64-byte group of all
+// weight rows (N * 64 bytes).
 constexpr int64_t kMaxGemmK = int64_t(1) << 24;
+constexpr int64_t kMaxGemmN = int64_t(1) << 24;
 constexpr int kStageK = 64;
 
 struct TileArgs {
     const uint16_t *X;       // [M, K] bf16
-    const uint8_t *packed;   // [N, K * BITS / 8]
+    const uint8_t *packed;   // export byte order (see GemmArgs)
     const uint16_t *alpha;   // [N] bf16
     uint16_t *Y;             // [M, N] bf16 (single split)
     float *ws;               // [splits, M, N] fp32 partials (several splits)
     int M, N, K;
     int mtiles, ntiles, splits;
-    int kps;                 // k per split, a multiple of kStageK
+    int kps;                 // k per split, a multiple of the 64-byte group
+    int64_t gstride;         // bytes per 64-byte group of all rows
 };
 
 // Activation LDS swizzle: chunk c of tile row r sits in slot c ^ xswz(r).
@@ -287,12 +291,10 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
     const int kbeg = split * g.kps;
     const int kend = min(K, kbeg + g.kps);
     const int ns = (kend - kbeg) / kStageK;
-    const int64_t row_bytes = static_cast<int64_t>(K) * BITS / 8;
 
     // DMA sources: a wave-uniform base (advanced per stage) plus a fixed
     // per-lane byte offset.  Rows >= M and columns >= N read row M-1 / N-1.
     const uint8_t *xbase = reinterpret_cast<const uint8_t *>(g.X + static_cast<int64_t>(m0) * K + kbeg);
-    const uint8_t *cbase = g.packed + static_cast<int64_t>(n0) * row_bytes + static_cast<int64_t>(kbeg) * BITS / 8;
     uint32_t xoff[C::XI];
 #pragma unroll
     for (int q = 0; q < C::XI; ++q) {
@@ -300,20 +302,22 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
         const int c = (lane & 7) ^ xswz(r);
         xoff[q] = static_cast<uint32_t>(static_cast<int64_t>(min(m0 + r, M - 1) - m0) * K * 2 + 16 * c);
     }
-    // Code DMAs: one fetch covers SS stages of the block's columns, 64
-    // contiguous bytes per column.  DMA i of wave w brings columns
-    // 16 (NC w + i) .. +15; lane l reads the 16-byte piece l >> 4 of column
-    // l & 15, so each instruction reads 16 runs of 64 bytes and lands as
-    // [piece][16 columns][16 B] in LDS.
+    // Code DMAs: one fetch covers SS stages of the block's columns, one
+    // 64-byte group of each.  DMA i of wave w brings columns 16 (NC w + i) ..
+    // +15, which is one 1-KB tile of the export order: lane l reads the
+    // 16-byte piece l >> 4 of column l & 15 and it lands as [piece][16
+    // columns][16 B] in LDS.
     constexpr int NC = C::NC;
-    uint32_t coff[NC];
+    constexpr int SS = C::SS;
+    uint32_t ccol[NC];
     const int cpiece = lane >> 4;
     const int cstage = (16 * cpiece) / C::CB, cwithin = (16 * cpiece) % C::CB;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-        const int cl = 16 * (NC * w + i) + (lane & 15);
-        coff[i] = static_cast<uint32_t>((min(n0 + cl, N - 1) - n0) * row_bytes + cwithin);
+        const int cl = min(n0 + 16 * (NC * w + i) + (lane & 15), N - 1);
+        ccol[i] = static_cast<uint32_t>((cl >> 4) * 1024 + (cl & 15) * 16);
     }
+    const int64_t g_first = kbeg / (SS * kStageK);  // the split starts a group
     const uint32_t lds_base = static_cast<uint32_t>(
         reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)lds));
 
@@ -325,13 +329,17 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
         for (int q = 0; q < C::XI; ++q)
             dma16(xs, xoff[q], lds_base + XR + slot * C::XBYTES + (C::XI * w + q) * 1024);
     };
-    // Code DMA of fetch G into buffer G & 1; a lane whose stage lies past
-    // the split's end re-reads the last stage (in bounds, never used).
+    // Code DMA of fetch G (group g_first + G) into buffer G & 1; a lane
+    // whose stage lies past the split's end re-reads the last stage (in
+    // bounds, never used), which lies in the same group or, for a fetch
+    // wholly past the end, in the split's last group.
     auto issue_c = [&](int G) {
-        const uint32_t so = static_cast<uint32_t>(min(G * C::SS + cstage, ns - 1) * C::CB);
+        const int st = min(G * SS + cstage, ns - 1);
+        const uint8_t *cb = g.packed + (g_first + min(G, (ns - 1) / SS)) * g.gstride;
+        const uint32_t po = static_cast<uint32_t>((((st % SS) * C::CB + cwithin) >> 4) * 256);
 #pragma unroll
         for (int i = 0; i < NC; ++i)
-            dma16(cbase, coff[i] + so, lds_base + CR + (G & 1) * C::CSS + (NC * w + i) * 1024);
+            dma16(cb, ccol[i] + po, lds_base + CR + (G & 1) * C::CSS + (NC * w + i) * 1024);
     };
 
     floatx4 acc[4][4];
@@ -581,17 +589,18 @@ __global__ __launch_bounds__(256) void k_splitk_finalize(const float *ws, const 
 // The weight (N*K*BITS/8 bytes, read once) is the whole cost, and HBM gives
 // its rate only with many bytes in flight per CU.  A block owns TN column
 // tiles of 16 and its NW waves share K out by groups (256 k at 2 bits, 128
-// at 4: 64 bytes of each weight row), wave w taking groups w, w + NW, ..., so
-// that at any moment the block reads neighbouring pieces of the same rows.
-// Every wave streams its groups through a private LDS ring of D stages with
-// the LDS-DMA load (global_load_lds_dwordx4, no registers used): per group
-// one 1-KB DMA per column tile (lane (i16, grp) fetches bytes 16*grp ..
-// 16*grp+15 of the group's 64 in row i16) and ceil(M / RPL) 1-KB DMAs of
-// activations, so up to D * (TN + XI) KB per wave are in flight.  The ring
-// is private to the wave: a stage waits on the wave's own s_waitcnt only,
-// and the block meets at a barrier once, to add the NW partial sums.  Each
-// block starts its walk at its own offset, so blocks do not read the same
-// activation lines in lockstep.
+// at 4: 64 bytes of each weight row), wave w taking groups w, w + NW, ....
+// In the export byte order a group of all rows is one contiguous run, so at
+// any moment the blocks of the whole grid, which walk the groups in the same
+// order, read one window of consecutive addresses: each DMA 1 KB, each block
+// TN KB, the grid one run per group.  Every wave streams its groups through a
+// private LDS ring of D stages with the LDS-DMA load
+// (global_load_lds_dwordx4, no registers used): per group one 1-KB DMA per
+// column tile (lane (i16, grp) fetches bytes 16*grp .. 16*grp+15 of the
+// group's 64 in row i16) and ceil(M / RPL) 1-KB DMAs of activations, so up to
+// D * (TN + XI) KB per wave are in flight.  The ring is private to the wave:
+// a stage waits on the wave's own s_waitcnt only, and the block meets at a
+// barrier once, to add the NW partial sums.
 //
 // LDS.  A code block is read back by the lane that fetched each 16 bytes,
 // which is that lane's MFMA B fragment for the decode below.  An activation
@@ -645,15 +654,15 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
     // This wave's groups are w, w + NW, w + 2 NW, ...: at any moment the
     // block's waves read neighbouring 64-byte pieces of the same rows.
     const int nit = G > w ? (G - w + NW - 1) / NW : 0;
-    const int64_t row_bytes = static_cast<int64_t>(K) * BITS / 8;
 
     // DMA sources: a wave-uniform base plus a 32-bit per-lane offset (the
-    // host bounds K so that every offset fits).
-    const uint8_t *cbase = g.packed + static_cast<int64_t>(n0) * row_bytes;
+    // host bounds K and N so that every offset fits).  Code tile j of group
+    // gi is the 1 KB at gi * gstride + (n0 / 16 + j) * 1024; tiles past the
+    // last one re-read it (their outputs are not stored).
+    const int last_tile = (N - 1) >> 4;
     uint32_t coff[TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-        coff[j] = static_cast<uint32_t>((min(n0 + 16 * j + i16, N - 1) - n0) * row_bytes + 16 * grp);
+    for (int j = 0; j < TN; ++j) coff[j] = static_cast<uint32_t>(min((n0 >> 4) + j, last_tile) * 1024 + lane * 16);
     uint32_t xoff[XI];
 #pragma unroll
     for (int q = 0; q < XI; ++q) {
@@ -663,15 +672,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
     const uint32_t ring = static_cast<uint32_t>(
         reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)lds)) + w * WLDS;
     const uint8_t *wring = lds + w * WLDS;
-    const int rot = nit > 0 ? static_cast<int>(blockIdx.x % static_cast<unsigned>(nit)) : 0;
 
     auto issue = [&](int it, int slot) {
-        int i = it + rot;
-        i = i >= nit ? i - nit : i;
-        const uint32_t gi = static_cast<uint32_t>(w + NW * i);
+        const uint32_t gi = static_cast<uint32_t>(w + NW * it);
         const uint32_t sb = ring + slot * SLOT;
+        const uint8_t *cb = g.packed + static_cast<int64_t>(gi) * g.gstride;
 #pragma unroll
-        for (int j = 0; j < TN; ++j) dma16(cbase, coff[j] + gi * 64, sb + j * 1024);
+        for (int j = 0; j < TN; ++j) dma16(cb, coff[j], sb + j * 1024);
 #pragma unroll
         for (int q = 0; q < XI; ++q) dma16(g.X, xoff[q] + gi * (GK * 2), sb + TN * 1024 + q * XQS);
     };
@@ -903,9 +910,11 @@ pq_status launch_tile(const GemmArgs &a, hipStream_t s)
         const int want = static_cast<int>((kTargetBlocks + tiles - 1) / tiles);
         splits = std::max(1, std::min(want, stages / kMinStages));
     }
-    const int sps = (stages + splits - 1) / splits;  // stages per split
+    // stages per split: whole 64-byte groups, so every split starts a group
+    const int sps = ((stages + splits - 1) / splits + C::SS - 1) / C::SS * C::SS;
     splits = (stages + sps - 1) / sps;
-    TileArgs t{a.X, a.packed, a.alpha, a.Y, nullptr, a.M, a.N, a.K, mtiles, ntiles, splits, sps * kStageK};
+    TileArgs t{a.X, a.packed, a.alpha, a.Y, nullptr, a.M, a.N, a.K, mtiles, ntiles, splits, sps * kStageK,
+               a.gstride};
     const int64_t total = static_cast<int64_t>(a.M) * a.N;
     if (splits > 1) {
         pq_status st = workspace(s, static_cast<size_t>(splits) * total * sizeof(float), &t.ws);
@@ -928,14 +937,14 @@ pq_status gemm(int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *pa
                const void *alpha_bf16, void *Y, void *stream)
 {
     if (!X || !packed || !alpha_bf16 || !Y) return PQ_ERR_NULL;
-    if (M < 0 || N < 0 || K <= 0 || K % 64 != 0 || K > kMaxGemmK || M > INT32_MAX / 2 ||
-        N > INT32_MAX / 2)
+    if (M < 0 || N < 0 || K <= 0 || K % 64 != 0 || K > kMaxGemmK || M > INT32_MAX / 2 || N > kMaxGemmN)
         return PQ_ERR_SHAPE;
     if (!aligned16(X) || !aligned16(packed) || !aligned16(Y) || !aligned16(alpha_bf16))
         return PQ_ERR_ALIGN;
     if (M == 0 || N == 0) return PQ_OK;
     GemmArgs a{static_cast<const uint16_t *>(X), packed, static_cast<const uint16_t *>(alpha_bf16),
-               static_cast<uint16_t *>(Y), static_cast<int>(M), static_cast<int>(N), static_cast<int>(K)};
+               static_cast<uint16_t *>(Y), static_cast<int>(M), static_cast<int>(N), static_cast<int>(K),
+               (N + 15) / 16 * 16 * 64};
     hipStream_t s = static_cast<hipStream_t>(stream);
     constexpr int GK = BITS == 2 ? 256 : 128;
     constexpr int RPL = 512 / GK;

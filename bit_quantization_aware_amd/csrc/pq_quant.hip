@@ -196,8 +196,23 @@ __device__ __forceinline__ double team_sum(double v, double *lds4)
 // before any math, to keep U * 16 bytes per lane in flight).
 constexpr int kUnroll = 4;
 
-enum : unsigned { OUT_BF16 = 1, OUT_F32 = 2, OUT_CODES = 4, OUT_ALPHA_BF16 = 8 };
+enum : unsigned { OUT_BF16 = 1, OUT_F32 = 2, OUT_CODES = 4, OUT_ALPHA_BF16 = 8, OUT_TILED = 16 };
 
+// Forward rows per wave: with one wave per row (launches of many short
+// rows) each wave takes two rows in turn, which halves the number of waves
+// to launch and retire; a team of four waves takes one row.
+constexpr int fwd_rows_per_wave(int wpr) { return wpr == 1 ? 2 : 1; }
+
+// Export byte order of the codes (OUT_TILED, single matrix).  The 64-byte
+// groups of all rows are stored group after group; inside a group, each tile
+// of 16 rows is 1 KB ordered [16-byte piece][row of the tile][byte]:
+//   byte kb of row n -> (kb / 64) * Np * 64 + (n / 16) * 1024
+//                       + ((kb / 16) % 4) * 256 + (n % 16) * 16 + kb % 16,
+// Np = rows rounded up to 16.  Bytes past a row's end within its last group,
+// and the rows from `rows` to Np, are zero.  A 1-KB tile is then exactly the
+// deployment GEMM's MFMA operand for 16 columns and 64 code bytes, fetched
+// with one contiguous load.
+//
 // Forward: optional alpha init, then per quad: quantize, emit bf16 / fp32 /
 // codes.  OUT_ALPHA_BF16 (export) also writes bf16(alpha) per row.
 template <int MODE, bool INIT, int WPR, unsigned OUTS>
@@ -209,108 +224,160 @@ __global__ __launch_bounds__(256, PQ_QUANT_FWD_MINB) void k_quant_fwd(LaunchTabl
     __shared__ float lds_f[4];
     __shared__ double lds_d[4];
 
+    constexpr bool TILED = (OUTS & OUT_TILED) != 0;
+    static_assert(!TILED || ((OUTS & OUT_CODES) != 0 && (CW == 2 || CW == 4)), "tiled export of 2- or 4-bit codes");
     const int wave = threadIdx.x >> 6;
     const int tl = (wave % WPR) * 64 + (threadIdx.x & 63);
-    const int b = blockIdx.x;
+    int b = blockIdx.x;
+    if constexpr (TILED) {
+        // The eight XCDs take blocks round robin; give the blocks of one XCD
+        // consecutive rows, so that the 16 rows of a tile -- whose code
+        // pieces share cache lines -- are written through one L2.
+        const int nb = gridDim.x;
+        if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);
+    }
     const int k = find_matrix(lt, b);
     const pq_mat m = lt.table ? lt.table[k] : lt.single;
-    const int64_t row = static_cast<int64_t>(b - lt.block_start[k]) * RPB + wave / WPR;
-    if (row >= m.rows) return;  // only when WPR == 1 (RPB rows per block)
-
     const int64_t cols = m.cols;
     const int nq = static_cast<int>(cols >> 2);
-    const PQ_GLOBAL f32x4 *wr = (const PQ_GLOBAL f32x4 *)(m.W + row * cols);
+    constexpr int RPW = fwd_rows_per_wave(WPR);
+    const int64_t row0 = static_cast<int64_t>(b - lt.block_start[k]) * (RPB * RPW) + wave / WPR;
 
-    float alpha_raw;
-    if constexpr (INIT) {
-        // [Note] "The 2-bit recipe" table / scale-init row of "Paper vs. code".
-        if constexpr (MODE == PQ_W1_BINARY) {
-            double s = 0.0;
-            for (int q = tl; q < nq; q += TEAM) {
-                const f32x4 v = wr[q];
-                s += static_cast<double>(fabsf(v.x));
-                s += static_cast<double>(fabsf(v.y));
-                s += static_cast<double>(fabsf(v.z));
-                s += static_cast<double>(fabsf(v.w));
+    // One row (RPB rows per block, one after the other RPW times).
+    auto one_row = [&](const int64_t row) {
+        // Tiled export: this row's 16-byte slot in every tile, and the group stride.
+        PQ_GLOBAL uint8_t *tbase = nullptr;
+        int64_t gstride = 0, gbytes = 0;
+        if constexpr (TILED) {
+            const int64_t np = (m.rows + 15) & ~int64_t(15);
+            gstride = np * 64;
+            gbytes = (cols * CW / 8 + 63) / 64 * 64;
+            tbase = (PQ_GLOBAL uint8_t *)m.codes + (row >> 4) * 1024 + (row & 15) * 16;
+            if (row >= m.rows) {
+                // padding row of the last tile: zero pieces in every group
+                if (row < np)
+                    for (int64_t p = tl; p < gbytes / 16; p += TEAM)
+                        *(PQ_GLOBAL u32x4 *)(tbase + (p >> 2) * gstride + (p & 3) * 256) = u32x4{0u, 0u, 0u, 0u};
+                return;
             }
-            s = team_sum<WPR>(s, lds_d);
-            alpha_raw = static_cast<float>(s / static_cast<double>(cols));
+        }
+        if (row >= m.rows) return;  // only when WPR == 1 (RPB rows per block)
+        const PQ_GLOBAL f32x4 *wr = (const PQ_GLOBAL f32x4 *)(m.W + row * cols);
+
+        float alpha_raw;
+        if constexpr (INIT) {
+            // [Note] "The 2-bit recipe" table / scale-init row of "Paper vs. code".
+            if constexpr (MODE == PQ_W1_BINARY) {
+                double s = 0.0;
+                for (int q = tl; q < nq; q += TEAM) {
+                    const f32x4 v = wr[q];
+                    s += static_cast<double>(fabsf(v.x));
+                    s += static_cast<double>(fabsf(v.y));
+                    s += static_cast<double>(fabsf(v.z));
+                    s += static_cast<double>(fabsf(v.w));
+                }
+                s = team_sum<WPR>(s, lds_d);
+                alpha_raw = static_cast<float>(s / static_cast<double>(cols));
+            } else {
+                float mx = 0.0f;
+                for (int q = tl; q < nq; q += TEAM) {
+                    const f32x4 v = wr[q];
+                    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+                }
+                mx = team_max<WPR>(mx, lds_f);
+                if constexpr (MODE == PQ_W3_LSQ || MODE == PQ_W4_LSQ) mx = mx / Mode<MODE>::hi;
+                alpha_raw = mx;
+            }
+            if (tl == 0) m.alpha[row] = alpha_raw;
         } else {
-            float mx = 0.0f;
-            for (int q = tl; q < nq; q += TEAM) {
-                const f32x4 v = wr[q];
-                mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            alpha_raw = m.alpha[row];
+        }
+        const float a = alpha_raw > kAlphaFloor ? alpha_raw : kAlphaFloor;
+        const double y = 1.0 / static_cast<double>(a);
+
+        if constexpr ((OUTS & OUT_ALPHA_BF16) != 0) {
+            if (tl == 0) {
+                __bf16 h = static_cast<__bf16>(alpha_raw);
+                static_cast<uint16_t *>(alpha_bf16_single)[row] = __builtin_bit_cast(uint16_t, h);
             }
-            mx = team_max<WPR>(mx, lds_f);
-            if constexpr (MODE == PQ_W3_LSQ || MODE == PQ_W4_LSQ) mx = mx / Mode<MODE>::hi;
-            alpha_raw = mx;
         }
-        if (tl == 0) m.alpha[row] = alpha_raw;
-    } else {
-        alpha_raw = m.alpha[row];
-    }
-    const float a = alpha_raw > kAlphaFloor ? alpha_raw : kAlphaFloor;
-    const double y = 1.0 / static_cast<double>(a);
 
-    if constexpr ((OUTS & OUT_ALPHA_BF16) != 0) {
-        if (tl == 0) {
-            __bf16 h = static_cast<__bf16>(alpha_raw);
-            static_cast<uint16_t *>(alpha_bf16_single)[row] = __builtin_bit_cast(uint16_t, h);
-        }
-    }
+        PQ_GLOBAL u32x2 *wq16 =
+            (OUTS & OUT_BF16) ? (PQ_GLOBAL u32x2 *)(static_cast<uint16_t *>(m.wq_bf16) + row * cols) : nullptr;
+        PQ_GLOBAL f32x4 *wq32 = (OUTS & OUT_F32) ? (PQ_GLOBAL f32x4 *)(m.wq_f32 + row * cols) : nullptr;
+        PQ_GLOBAL uint8_t *crow = (OUTS & OUT_CODES) ? (PQ_GLOBAL uint8_t *)(m.codes + row * (cols * CW / 8)) : nullptr;
 
-    PQ_GLOBAL u32x2 *wq16 = (OUTS & OUT_BF16) ? (PQ_GLOBAL u32x2 *)(static_cast<uint16_t *>(m.wq_bf16) + row * cols) : nullptr;
-    PQ_GLOBAL f32x4 *wq32 = (OUTS & OUT_F32) ? (PQ_GLOBAL f32x4 *)(m.wq_f32 + row * cols) : nullptr;
-    PQ_GLOBAL uint8_t *crow = (OUTS & OUT_CODES) ? (PQ_GLOBAL uint8_t *)(m.codes + row * (cols * CW / 8)) : nullptr;
-
-    // One pass: kUnroll quads per lane, loads first.  GUARD only on the last.
-    auto pass = [&](int base, auto guard_c) {
-        constexpr bool GUARD = decltype(guard_c)::value;
-        f32x4 v[kUnroll];
+        // One pass: kUnroll quads per lane, loads first.  GUARD only on the last.
+        auto pass = [&](int base, auto guard_c) {
+            constexpr bool GUARD = decltype(guard_c)::value;
+            f32x4 v[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int q = base + u * TEAM + tl;
-            if (!GUARD || q < nq) v[u] = ld_stream(&wr[q]);
-            else v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+            for (int u = 0; u < kUnroll; ++u) {
+                const int q = base + u * TEAM + tl;
+                if (!GUARD || q < nq) v[u] = ld_stream(&wr[q]);
+                else v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            // in the tail pass, quad slots no lane of the team owns are skipped
-            if (GUARD && base + u * TEAM >= nq) break;
-            const int q = base + u * TEAM + tl;
-            const bool act = !GUARD || q < nq;
-            float l0, l1, l2, l3;
-            const uint32_t c0 = quant_x<MODE>(v[u].x, div_fast(v[u].x, y), l0);
-            const uint32_t c1 = quant_x<MODE>(v[u].y, div_fast(v[u].y, y), l1);
-            const uint32_t c2 = quant_x<MODE>(v[u].z, div_fast(v[u].z, y), l2);
-            const uint32_t c3 = quant_x<MODE>(v[u].w, div_fast(v[u].w, y), l3);
-            const float q0 = a * l0, q1 = a * l1, q2 = a * l2, q3 = a * l3;
-            if constexpr ((OUTS & OUT_BF16) != 0) {
-                if (act) wq16[q] = u32x2{pack_bf16x2(q0, q1), pack_bf16x2(q2, q3)};
-            }
-            if constexpr ((OUTS & OUT_F32) != 0) {
-                if (act) wq32[q] = f32x4{q0, q1, q2, q3};
-            }
-            if constexpr ((OUTS & OUT_CODES) != 0) {
-                if constexpr (CW == 2) {
-                    if (act) crow[q] = static_cast<uint8_t>(c0 | (c1 << 2) | (c2 << 4) | (c3 << 6));
-                } else if constexpr (CW == 4) {
-                    if (act)
-                        ((PQ_GLOBAL uint16_t *)crow)[q] =
-                            static_cast<uint16_t>(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
-                } else {
-                    // 1 bit: a nibble per quad; even lane takes its odd neighbour's.
-                    const uint32_t nib = c0 | (c1 << 1) | (c2 << 2) | (c3 << 3);
-                    const uint32_t hi = __shfl_down(nib, 1);
-                    if (act && (tl & 1) == 0) crow[q >> 1] = static_cast<uint8_t>(nib | (hi << 4));
+            for (int u = 0; u < kUnroll; ++u) {
+                // in the tail pass, quad slots no lane of the team owns are skipped
+                if (GUARD && base + u * TEAM >= nq) break;
+                const int q = base + u * TEAM + tl;
+                const bool act = !GUARD || q < nq;
+                float l0, l1, l2, l3;
+                const uint32_t c0 = quant_x<MODE>(v[u].x, div_fast(v[u].x, y), l0);
+                const uint32_t c1 = quant_x<MODE>(v[u].y, div_fast(v[u].y, y), l1);
+                const uint32_t c2 = quant_x<MODE>(v[u].z, div_fast(v[u].z, y), l2);
+                const uint32_t c3 = quant_x<MODE>(v[u].w, div_fast(v[u].w, y), l3);
+                const float q0 = a * l0, q1 = a * l1, q2 = a * l2, q3 = a * l3;
+                if constexpr ((OUTS & OUT_BF16) != 0) {
+                    if (act) wq16[q] = u32x2{pack_bf16x2(q0, q1), pack_bf16x2(q2, q3)};
+                }
+                if constexpr ((OUTS & OUT_F32) != 0) {
+                    if (act) wq32[q] = f32x4{q0, q1, q2, q3};
+                }
+                if constexpr (TILED) {
+                    // A quad is CW / 2 code bytes, and base + u * TEAM starts a
+                    // whole 64-byte group g0; the lane's byte offset from there
+                    // (tl or 2 tl) splits into group, piece and byte.
+                    const int64_t g0 = (static_cast<int64_t>(base + u * TEAM) * (CW / 2)) >> 6;
+                    if constexpr (CW == 2) {
+                        PQ_GLOBAL uint8_t *d = tbase + (g0 + (tl >> 6)) * gstride + ((tl >> 4) & 3) * 256 + (tl & 15);
+                        if (act) *d = static_cast<uint8_t>(c0 | (c1 << 2) | (c2 << 4) | (c3 << 6));
+                    } else {
+                        PQ_GLOBAL uint8_t *d =
+                            tbase + (g0 + (tl >> 5)) * gstride + ((tl >> 3) & 3) * 256 + ((2 * tl) & 15);
+                        if (act)
+                            *(PQ_GLOBAL uint16_t *)d = static_cast<uint16_t>(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
+                    }
+                } else if constexpr ((OUTS & OUT_CODES) != 0) {
+                    if constexpr (CW == 2) {
+                        if (act) crow[q] = static_cast<uint8_t>(c0 | (c1 << 2) | (c2 << 4) | (c3 << 6));
+                    } else if constexpr (CW == 4) {
+                        if (act)
+                            ((PQ_GLOBAL uint16_t *)crow)[q] =
+                                static_cast<uint16_t>(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
+                    } else {
+                        // 1 bit: a nibble per quad; even lane takes its odd neighbour's.
+                        const uint32_t nib = c0 | (c1 << 1) | (c2 << 2) | (c3 << 3);
+                        const uint32_t hi = __shfl_down(nib, 1);
+                        if (act && (tl & 1) == 0) crow[q >> 1] = static_cast<uint8_t>(nib | (hi << 4));
+                    }
                 }
             }
+        };
+        constexpr int STEP = TEAM * kUnroll;
+        const int nfull = nq / STEP * STEP;
+        for (int base = 0; base < nfull; base += STEP) pass(base, std::false_type{});
+        if (nfull < nq) pass(nfull, std::true_type{});
+        if constexpr (TILED) {
+            // zero the bytes of the last group past the row's end (< 64 bytes)
+            const int64_t rb = cols * CW / 8;
+            const int64_t kb = rb + tl;
+            if (kb < gbytes) tbase[(kb >> 6) * gstride + ((kb >> 4) & 3) * 256 + (kb & 15)] = 0;
         }
     };
-    constexpr int STEP = TEAM * kUnroll;
-    const int nfull = nq / STEP * STEP;
-    for (int base = 0; base < nfull; base += STEP) pass(base, std::false_type{});
-    if (nfull < nq) pass(nfull, std::true_type{});
+#pragma unroll 1
+    for (int rr = 0; rr < RPW; ++rr) one_row(row0 + rr * RPB);
 }
 
 // Backward: per weight the forward's x and level (bit-identical), the clip
@@ -442,25 +509,33 @@ __global__ __launch_bounds__(256, PQ_QUANT_BWD_MINB) void k_quant_bwd(LaunchTabl
 // Rows a launch needs before one wave per row fills the chip
 // (256 CUs x 4 SIMDs x 4 waves).
 constexpr int64_t kWaveRowsThreshold = 4096;
+// Mean row length from which a team of four waves per row is faster even
+// with many rows (measured: from 4096 columns on, for fwd, bwd and export).
+constexpr int64_t kTeamColsThreshold = 4096;
 
-pq_status check_mat(const pq_mat &m, bool need_w)
+int choose_wpr(int64_t total_rows, int64_t total_elems)
 {
-    if (m.rows < 0) return PQ_ERR_SHAPE;
-    if (!valid_cols(m.cols)) return PQ_ERR_SHAPE;
-    if (need_w && (!m.W || !m.alpha)) return PQ_ERR_NULL;
-    return PQ_OK;
+    const bool many_rows = total_rows >= kWaveRowsThreshold;
+    const bool short_rows = total_elems < kTeamColsThreshold * total_rows;
+    return many_rows && short_rows ? 1 : 4;
 }
 
 bool ptr_ok(const void *p) { return p == nullptr || aligned16(p); }
 
+// One or more launches over a stack (kMaxGroup matrices each), with one
+// team size for the whole stack; `fwd` launches take fwd_rows_per_wave rows
+// per wave.
 template <typename F>
-pq_status launch_grouped(int count, const pq_mat *host, const pq_mat *dev, hipStream_t stream,
+pq_status launch_grouped(int count, const pq_mat *host, const pq_mat *dev, hipStream_t stream, bool fwd,
                          F &&launch_one)
 {
-    int64_t total_rows = 0;
-    for (int i = 0; i < count; ++i) total_rows += host[i].rows;
-    const int wpr = total_rows >= kWaveRowsThreshold ? 1 : 4;
-    const int rpb = 4 / wpr;
+    int64_t total_rows = 0, total_elems = 0;
+    for (int i = 0; i < count; ++i) {
+        total_rows += host[i].rows;
+        total_elems += host[i].rows * host[i].cols;
+    }
+    const int wpr = choose_wpr(total_rows, total_elems);
+    const int rpb = (4 / wpr) * (fwd ? fwd_rows_per_wave(wpr) : 1);  // rows per block
     for (int start = 0; start < count; start += kMaxGroup) {
         const int n = count - start < kMaxGroup ? count - start : kMaxGroup;
         LaunchTable lt;
@@ -478,7 +553,6 @@ pq_status launch_grouped(int count, const pq_mat *host, const pq_mat *dev, hipSt
         launch_one(lt, static_cast<int>(blocks), wpr, stream);
         if (hipGetLastError() != hipSuccess) return PQ_ERR_HIP;
     }
-    (void)total_rows;
     return PQ_OK;
 }
 
@@ -634,6 +708,13 @@ int64_t pq_code_row_bytes(int mode, int64_t cols)
     return (cols * code_bits(mode) + 7) / 8;
 }
 
+int64_t pq_packed_bytes(int mode, int64_t rows, int64_t cols)
+{
+    if ((mode != PQ_W2_SEQ && mode != PQ_W4_LSQ) || rows < 0 || !valid_cols(cols)) return -1;
+    const int64_t rb = cols * code_bits(mode) / 8;
+    return (rb + 63) / 64 * ((rows + 15) / 16 * 16) * 64;
+}
+
 double pq_default_grad_scale(int mode, int64_t rows, int64_t cols)
 {
     if (!valid_mode(mode) || rows <= 0 || cols <= 0) return 0.0;
@@ -666,7 +747,7 @@ pq_status pq_quantize_fwd_grouped(int mode, int count, const pq_mat *descs_host,
     if (st != PQ_OK) return st;
     if (count > 0 && !descs_dev) return PQ_ERR_NULL;
     const bool init = (flags & PQ_INIT_ALPHA) != 0;
-    return launch_grouped(count, descs_host, descs_dev, static_cast<hipStream_t>(stream),
+    return launch_grouped(count, descs_host, descs_dev, static_cast<hipStream_t>(stream), true,
                           [&](const LaunchTable &lt, int blocks, int wpr, hipStream_t s) {
                               launch_fwd(mode, init, outs, lt, blocks, wpr, s);
                           });
@@ -688,7 +769,7 @@ pq_status pq_quantize_fwd(int mode, int64_t rows, int64_t cols, const float *W, 
     pq_status st = check_fwd_descs(mode, 1, &m, flags, &outs);
     if (st != PQ_OK) return st;
     const bool init = (flags & PQ_INIT_ALPHA) != 0;
-    return launch_grouped(1, &m, nullptr, static_cast<hipStream_t>(stream),
+    return launch_grouped(1, &m, nullptr, static_cast<hipStream_t>(stream), true,
                           [&](const LaunchTable &lt, int blocks, int wpr, hipStream_t s) {
                               launch_fwd(mode, init, outs, lt, blocks, wpr, s);
                           });
@@ -701,7 +782,7 @@ pq_status pq_quantize_bwd_grouped(int mode, int count, const pq_mat *descs_host,
     pq_status st = check_bwd_descs(mode, count, descs_host, g_dtype, &wdw, &wmask);
     if (st != PQ_OK) return st;
     if (count > 0 && !descs_dev) return PQ_ERR_NULL;
-    return launch_grouped(count, descs_host, descs_dev, static_cast<hipStream_t>(stream),
+    return launch_grouped(count, descs_host, descs_dev, static_cast<hipStream_t>(stream), false,
                           [&](const LaunchTable &lt, int blocks, int wpr, hipStream_t s) {
                               launch_bwd(mode, wpr, g_dtype == PQ_G_BF16, wdw, wmask, lt, blocks, s);
                           });
@@ -724,12 +805,14 @@ pq_status pq_quantize_bwd(int mode, int64_t rows, int64_t cols, const float *W, 
     bool wdw = false, wmask = false;
     pq_status st = check_bwd_descs(mode, 1, &m, g_dtype, &wdw, &wmask);
     if (st != PQ_OK) return st;
-    return launch_grouped(1, &m, nullptr, static_cast<hipStream_t>(stream),
+    return launch_grouped(1, &m, nullptr, static_cast<hipStream_t>(stream), false,
                           [&](const LaunchTable &lt, int blocks, int wpr, hipStream_t s) {
                               launch_bwd(mode, wpr, g_dtype == PQ_G_BF16, wdw, wmask, lt, blocks, s);
                           });
 }
 
+// Export: one launch over the rows rounded up to 16 (the padding rows of the
+// last tile are written as zeros).
 static pq_status pack_common(int mode, int64_t rows, int64_t cols, const float *W,
                              const float *alpha, uint8_t *packed, void *alpha_bf16, void *stream)
 {
@@ -737,20 +820,31 @@ static pq_status pack_common(int mode, int64_t rows, int64_t cols, const float *
     if (rows < 0 || !valid_cols(cols)) return PQ_ERR_SHAPE;
     if (!aligned16(W) || !aligned16(alpha) || !aligned16(packed) || !aligned16(alpha_bf16))
         return PQ_ERR_ALIGN;
+    if (rows == 0) return PQ_OK;
     pq_mat m = {};
     m.W = W;
     m.alpha = const_cast<float *>(alpha);
     m.codes = packed;
     m.rows = rows;
     m.cols = cols;
-    return launch_grouped(1, &m, nullptr, static_cast<hipStream_t>(stream),
-                          [&](const LaunchTable &lt, int blocks, int wpr, hipStream_t s) {
-                              constexpr unsigned O = OUT_CODES | OUT_ALPHA_BF16;
-                              if (mode == PQ_W2_SEQ)
-                                  launch_fwd_t<PQ_W2_SEQ, false, O>(lt, blocks, wpr, s, alpha_bf16);
-                              else
-                                  launch_fwd_t<PQ_W4_LSQ, false, O>(lt, blocks, wpr, s, alpha_bf16);
-                          });
+    const int64_t np = (rows + 15) / 16 * 16;
+    const int wpr = choose_wpr(np, np * cols);
+    const int rpb = (4 / wpr) * fwd_rows_per_wave(wpr);
+    const int64_t blocks = (np + rpb - 1) / rpb;
+    if (blocks > INT32_MAX) return PQ_ERR_SHAPE;
+    LaunchTable lt;
+    lt.table = nullptr;
+    lt.single = m;
+    lt.count = 1;
+    lt.block_start[0] = 0;
+    lt.block_start[1] = static_cast<int32_t>(blocks);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    constexpr unsigned O = OUT_CODES | OUT_TILED | OUT_ALPHA_BF16;
+    if (mode == PQ_W2_SEQ)
+        launch_fwd_t<PQ_W2_SEQ, false, O>(lt, static_cast<int>(blocks), wpr, s, alpha_bf16);
+    else
+        launch_fwd_t<PQ_W4_LSQ, false, O>(lt, static_cast<int>(blocks), wpr, s, alpha_bf16);
+    return hipGetLastError() == hipSuccess ? PQ_OK : PQ_ERR_HIP;
 }
 
 pq_status pq_pack_w2(int64_t rows, int64_t cols, const float *W, const float *alpha,

@@ -27,7 +27,7 @@ STATUS = {0: "PQ_OK", 1: "PQ_ERR_NULL", 2: "PQ_ERR_SHAPE", 3: "PQ_ERR_MODE", 4: 
           5: "PQ_ERR_UNSUPPORTED", 6: "PQ_ERR_HIP", 7: "PQ_ERR_ARG"}
 
 # Every symbol include/pq.h declares.
-EXPORTS = ("pq_code_row_bytes", "pq_default_grad_scale", "pq_status_str", "pq_version",
+EXPORTS = ("pq_code_row_bytes", "pq_packed_bytes", "pq_default_grad_scale", "pq_status_str", "pq_version",
            "pq_quantize_fwd", "pq_quantize_bwd", "pq_pack_w2", "pq_pack_w4", "pq_w2a16_gemm",
            "pq_w4a16_gemm", "pq_quantize_fwd_grouped", "pq_quantize_bwd_grouped")
 
@@ -54,6 +54,8 @@ def _load():
     i32 = ctypes.c_int
     L.pq_code_row_bytes.argtypes = [i32, i64]
     L.pq_code_row_bytes.restype = i64
+    L.pq_packed_bytes.argtypes = [i32, i64, i64]
+    L.pq_packed_bytes.restype = i64
     L.pq_default_grad_scale.argtypes = [i32, i64, i64]
     L.pq_default_grad_scale.restype = dbl
     L.pq_status_str.argtypes = [i32]
@@ -68,7 +70,8 @@ def _load():
     L.pq_quantize_fwd_grouped.argtypes = [i32, i32, vp, vp, u32, vp]
     L.pq_quantize_bwd_grouped.argtypes = [i32, i32, vp, vp, i32, vp]
     for name in EXPORTS:
-        if name not in ("pq_code_row_bytes", "pq_default_grad_scale", "pq_status_str", "pq_version"):
+        if name not in ("pq_code_row_bytes", "pq_packed_bytes", "pq_default_grad_scale", "pq_status_str",
+                        "pq_version"):
             getattr(L, name).restype = i32
     return L
 
@@ -99,6 +102,10 @@ def _check(rc: int, fn: str) -> None:
 
 def pq_code_row_bytes(mode: int, cols: int) -> int:
     return int(lib.pq_code_row_bytes(mode, cols))
+
+
+def pq_packed_bytes(mode: int, rows: int, cols: int) -> int:
+    return int(lib.pq_packed_bytes(mode, rows, cols))
 
 
 def pq_default_grad_scale(mode: int, rows: int, cols: int) -> float:

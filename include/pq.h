@@ -20,7 +20,8 @@
  *              the library keeps no pointer after the call returns.  The only
  *              memory the library allocates itself is the GEMM's split-K
  *              workspace (see pq_w2a16_gemm).  Arrays are row-major and contiguous
- *              (leading dimension = cols).  Weight matrices are [out, in]:
+ *              (leading dimension = cols), except the exported codes of
+ *              pq_pack_w2 / pq_pack_w4 (the export byte order below).  Weight matrices are [out, in]:
  *              a "row" is one output channel, the unit the scale alpha
  *              belongs to ([Note] "Paper vs. code": one learned scale per
  *              row, shape (rows, 1)).
@@ -33,8 +34,9 @@
  *              patterns; every cast to bf16 rounds to nearest-even.
  *   Errors     Arguments are checked on the host before anything is enqueued:
  *              a NULL required pointer -> PQ_ERR_NULL; rows, cols, M, N or K
- *              negative, cols not a positive multiple of 8, or K not a
- *              positive multiple of 64 or above 2^24 -> PQ_ERR_SHAPE; an
+ *              negative, cols not a positive multiple of 8, K not a
+ *              positive multiple of 64 or above 2^24, or N above 2^24 ->
+ *              PQ_ERR_SHAPE; an
  *              unknown mode,
  *              flag or dtype -> PQ_ERR_MODE; an array pointer not 16-byte
  *              aligned -> PQ_ERR_ALIGN; a bad descriptor table or grad_scale
@@ -170,22 +172,42 @@ pq_status pq_quantize_bwd(int mode, int64_t rows, int64_t cols, const float *W,
                           uint8_t *mask_bits, void *stream);
 
 /*
+ * Export byte order.  The exported codes hold the same bytes as the
+ * forward's code rows (pq_quantize_fwd `codes`: rb = cols * b / 8 bytes per
+ * row, four 2-bit or two 4-bit codes per byte, first code lowest), reordered
+ * for the deployment GEMM, which reads 16 rows x 64 bytes as one MFMA operand
+ * ([News] speed paragraph: the 2-bit kernel consumes packed weights; the
+ * pages fix four codes per byte and a bf16 scale per row, not a byte order).
+ * With Np = rows rounded up to a multiple of 16 and G = ceil(rb / 64):
+ *   byte c of row n (c < rb, n < rows) is stored at
+ *     (c / 64) * Np * 64 + (n / 16) * 1024 + ((c / 16) % 4) * 256
+ *       + (n % 16) * 16 + c % 16,
+ * i.e. group-major runs of 64 bytes of every row, each 16-row tile 1 KB
+ * ordered [16-byte piece][row][byte].  Every other byte (rows rows .. Np - 1,
+ * bytes rb .. 64 G - 1 of a row) is written as 0.  Total size
+ * G * Np * 64 bytes = pq_packed_bytes(mode, rows, cols).
+ */
+int64_t pq_packed_bytes(int mode, int64_t rows, int64_t cols);
+
+/*
  * pq_pack_w2 -- export a 2-bit SEQ layer for deployment: the forward's codes
- * (bit-identical to pq_quantize_fwd(PQ_W2_SEQ, ...) codes) and the scale
- * rounded to bf16.  Memory savings exist only after export ([Note] "Paper
- * vs. code", last bullet); the deployed GEMM consumes this format ([News]
- * speed paragraph).
+ * (the bytes of pq_quantize_fwd(PQ_W2_SEQ, ...) codes, bit for bit) in the
+ * export byte order, and the scale rounded to bf16.  Memory savings exist
+ * only after export ([Note] "Paper vs. code", last bullet); the deployed
+ * GEMM consumes this format ([News] speed paragraph).
  *   W          in   [rows, cols] fp32, cols a positive multiple of 8
  *   alpha      in   [rows] fp32
- *   packed     out  [rows, cols/4] u8, 4 codes per byte, first in bits 0-1
+ *   packed     out  pq_packed_bytes(PQ_W2_SEQ, rows, cols) bytes, export
+ *                   byte order (above); every byte is written
  *   alpha_bf16 out  [rows] bf16
  */
 pq_status pq_pack_w2(int64_t rows, int64_t cols, const float *W, const float *alpha,
                      uint8_t *packed, void *alpha_bf16, void *stream);
 
-/* pq_pack_w4 -- the 4-bit LSQ counterpart of pq_pack_w2 (packed [rows,
- * cols/2] u8, low nibble first), feeding pq_w4a16_gemm, the 4-bit comparison
- * point of the [News] speed paragraph. */
+/* pq_pack_w4 -- the 4-bit LSQ counterpart of pq_pack_w2 (two codes per byte,
+ * low nibble first; pq_packed_bytes(PQ_W4_LSQ, rows, cols) bytes in the
+ * export byte order), feeding pq_w4a16_gemm, the 4-bit comparison point of
+ * the [News] speed paragraph. */
 pq_status pq_pack_w4(int64_t rows, int64_t cols, const float *W, const float *alpha,
                      uint8_t *packed, void *alpha_bf16, void *stream);
 
@@ -197,11 +219,13 @@ pq_status pq_pack_w4(int64_t rows, int64_t cols, const float *W, const float *al
  *   Y[m, n] = bf16( alpha_bf16[n] * sum_k X[m, k] * level(code[n, k]) )
  * with level(c) = (c - 1.5) / 2, fp32 accumulation.
  *   M, N, K    X is [M, K]; K a positive multiple of 64 (so every packed
- *              row is a whole number of 16-byte words) and at most 2^24
- *              (the kernels address a block's rows with 32-bit offsets);
- *              M, N >= 0
+ *              row is a whole number of 16-byte pieces) and at most 2^24,
+ *              0 <= N <= 2^24 (the kernels address up to 64 activation rows
+ *              or one 64-byte group of all weight rows with 32-bit offsets);
+ *              M >= 0
  *   X          in   [M, K] bf16 activations
- *   packed     in   [N, K/4] u8 from pq_pack_w2
+ *   packed     in   pq_packed_bytes(PQ_W2_SEQ, N, K) bytes from pq_pack_w2
+ *                   (export byte order; the padding bytes are never used)
  *   alpha_bf16 in   [N] bf16
  *   Y          out  [M, N] bf16
  * Workspace.  For M > 16 the output is cut into 64 x 256 tiles; when there
@@ -218,8 +242,8 @@ pq_status pq_w2a16_gemm(int64_t M, int64_t N, int64_t K, const void *X,
                         const uint8_t *packed, const void *alpha_bf16, void *Y,
                         void *stream);
 
-/* pq_w4a16_gemm -- the same GEMM on pq_pack_w4 weights: packed [N, K/2],
- * level(c) = c - 8. */
+/* pq_w4a16_gemm -- the same GEMM on pq_pack_w4 weights
+ * (pq_packed_bytes(PQ_W4_LSQ, N, K) bytes), level(c) = c - 8. */
 pq_status pq_w4a16_gemm(int64_t M, int64_t N, int64_t K, const void *X,
                         const uint8_t *packed, const void *alpha_bf16, void *Y,
                         void *stream);

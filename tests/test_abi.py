@@ -39,6 +39,13 @@ def test_helpers(pq):
     assert pq.pq_code_row_bytes(pq.PQ_W1_BINARY, 64) == 8
     assert pq.pq_code_row_bytes(pq.PQ_W4_LSQ, 64) == 32
     assert pq.pq_code_row_bytes(9, 64) == -1
+    # export size: 64-byte groups of every row, rows rounded up to 16
+    assert pq.pq_packed_bytes(pq.PQ_W2_SEQ, 16384, 16384) == 16384 * 4096
+    assert pq.pq_packed_bytes(pq.PQ_W2_SEQ, 20, 576) == 3 * 32 * 64
+    assert pq.pq_packed_bytes(pq.PQ_W4_LSQ, 1, 8) == 16 * 64
+    assert pq.pq_packed_bytes(pq.PQ_W2_SEQ, 0, 64) == 0
+    assert pq.pq_packed_bytes(pq.PQ_W1_BINARY, 16, 64) == -1
+    assert pq.pq_packed_bytes(pq.PQ_W2_SEQ, 16, 12) == -1
     assert pq.pq_default_grad_scale(pq.PQ_W4_LSQ, 4, 16) == pytest.approx((4 * 16 * 7) ** -0.5)
     assert pq.pq_default_grad_scale(pq.PQ_W2_SEQ, 0, 16) == 0.0
     assert "NULL" in pq.pq_status_str(1)
@@ -105,6 +112,8 @@ def test_pack_and_gemm_argument_checks(pq):
     assert L.pq_w2a16_gemm(-1, 8, 64, A, A, B, A, None) == 2
     assert L.pq_w4a16_gemm(4, 8, 64, A, MIS, B, A, None) == 4
     assert L.pq_w2a16_gemm(0, 8, 64, A, A, B, A, None) == 0                       # empty
+    assert L.pq_w2a16_gemm(1, (1 << 24) + 16, 64, A, A, B, A, None) == 2          # N bound
+    assert L.pq_pack_w2(0, 64, A, A, B, A, None) == 0                             # empty
 
 
 def test_grouped_argument_checks(pq):

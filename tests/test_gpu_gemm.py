@@ -37,10 +37,14 @@ REL = 2e-2
 
 
 def gpu_gemm(mode, X, packed, ab, N):
+    """packed: the oracle's row-major code rows [N, rb]; the GPU gets them in
+    the export byte order (the oracle's tile_codes)."""
     M, K = X.shape
     Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
     fn = pq.pq_w2a16_gemm if mode == O.SEQ2 else pq.pq_w4a16_gemm
-    fn(M, N, K, dev(X), dev(packed), dev(ab), Y)
+    tiled = O.tile_codes(packed)
+    assert tiled.size == pq.pq_packed_bytes(mode, N, K)
+    fn(M, N, K, dev(X), dev(tiled), dev(ab), Y)
     torch.cuda.synchronize()
     return synth.bf16_bits_to_f32(host(Y)).astype(np.float64)
 

@@ -201,21 +201,46 @@ def test_deterministic_dalpha():
     assert all(np.array_equal(runs[0].view(np.uint32), r.view(np.uint32)) for r in runs)
 
 
-@pytest.mark.parametrize("mode", [O.SEQ2, O.LSQ4])
-def test_pack_matches_forward_codes(mode):
-    W, _ = synth.random_case(80, 333, 1600)
-    alpha = O.alpha_init(mode, W)
+def gpu_pack(mode, W, alpha):
+    """Export on the GPU into a buffer prefilled with 0xA5, so that a byte the
+    kernel does not write (padding included) shows up."""
     rows, cols = W.shape
-    packed = torch.empty(rows, pq.pq_code_row_bytes(mode, cols), dtype=torch.uint8, device="cuda")
+    nbytes = pq.pq_packed_bytes(mode, rows, cols)
+    packed = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device="cuda")
     ab = empty_bf16(rows)
     fn = pq.pq_pack_w2 if mode == O.SEQ2 else pq.pq_pack_w4
     fn(rows, cols, dev(W), dev(alpha), packed, ab)
     torch.cuda.synchronize()
+    return host(packed), host(ab)
+
+
+@pytest.mark.parametrize("mode", [O.SEQ2, O.LSQ4])
+def test_pack_matches_forward_codes(mode):
+    # 333 rows (three padding rows in the last tile), 1600 columns (a partly
+    # filled last 64-byte group at both widths)
+    W, _ = synth.random_case(80, 333, 1600)
+    alpha = O.alpha_init(mode, W)
+    packed, ab = gpu_pack(mode, W, alpha)
     p_o, ab_o = O.pack(mode, W, alpha)
-    assert_bits_equal(host(packed), p_o, "packed")
-    assert_bits_equal(host(ab), ab_o, "alpha bf16")
+    assert_bits_equal(packed, O.tile_codes(p_o), "packed")
+    assert_bits_equal(ab, ab_o, "alpha bf16")
     _, _, _, codes_fwd = gpu_fwd(mode, W, alpha, False, want_f32=False)
-    assert_bits_equal(host(packed), codes_fwd, "pack == fwd codes")
+    assert_bits_equal(packed, O.tile_codes(codes_fwd), "pack == fwd codes in export order")
+
+
+@pytest.mark.parametrize("mode", [O.SEQ2, O.LSQ4])
+@pytest.mark.parametrize("rows,cols", [(1, 8), (17, 64), (16, 1024), (4100, 264), (4096, 520), (8192, 256)])
+def test_pack_export_order_shapes(mode, rows, cols):
+    """Export byte order across the launch shapes: one row per block (fewer
+    than 4096 rows) and one per wave, with and without the XCD row remap
+    (block count a multiple of 8 or not), padding rows and partial groups."""
+    rng = np.random.default_rng(rows * 7 + cols)
+    W = synth.normal_f32(rng, (rows, cols), 0.02)
+    alpha = O.alpha_init(mode, W)
+    packed, ab = gpu_pack(mode, W, alpha)
+    p_o, ab_o = O.pack(mode, W, alpha)
+    assert_bits_equal(packed, O.tile_codes(p_o), f"packed {rows}x{cols}")
+    assert_bits_equal(ab, ab_o, "alpha bf16")
 
 
 # ----------------------------------------------------------------------------
@@ -297,13 +322,10 @@ def test_mobilellm_1p5b_layers_with_outliers():
     check_grouped(O.SEQ2, mats, outs, "1.5B")
     for i, ((W, _), o) in enumerate(zip(mats, outs)):
         rows, cols = W.shape
-        packed = torch.empty(rows, cols // 4, dtype=torch.uint8, device="cuda")
-        ab = empty_bf16(rows)
-        pq.pq_pack_w2(rows, cols, dev(W), dev(o["alpha"]), packed, ab)
-        torch.cuda.synchronize()
+        packed, ab = gpu_pack(O.SEQ2, W, o["alpha"])
         p_o, ab_o = O.pack(O.SEQ2, W, o["alpha"])
-        assert_bits_equal(host(packed), p_o, f"1.5B[{i}] packed")
-        assert_bits_equal(host(ab), ab_o, f"1.5B[{i}] alpha bf16")
+        assert_bits_equal(packed, O.tile_codes(p_o), f"1.5B[{i}] packed")
+        assert_bits_equal(ab, ab_o, f"1.5B[{i}] alpha bf16")
 
 
 @pytest.mark.parametrize("mode", [O.SEQ2, O.TERNARY])
