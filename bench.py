@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="skip sweep / comparison GEMMs")
+    p.add_argument("--gemm-b2b-only", action="store_true",
+                   help="only the back-to-back GEMM launches (for a kernel trace of them alone)")
     p.add_argument("--pmc-workload", action="store_true",
                    help="no timing: a 1 GiB copy (counter calibration), then every step kernel "
                         "three times in step order, for rocprofv3 --pmc passes")
@@ -146,7 +148,7 @@ def pmc_summarize(args):
     groups = {
         "fwd": lambda n: "k_quant_fwd<2, false, 1, 5u>" in n,
         "bwd": lambda n: "k_quant_bwd<2, 1, false, true, false>" in n,
-        "pack": lambda n: "k_quant_fwd<2, false, 1, 28u>" in n,
+        "pack": lambda n: re.search(r"k_quant_fwd<2, false, \d, 28u>", n) is not None,
         # k_gemm_stream<BITS, TN, NW, D, XI>: M = 1, 4, 16 use XI = 1, 2, 8
         "gemm_m1": lambda n: re.search(r"k_gemm_stream<2, \d+, \d+, \d+, 1>", n) is not None,
         "gemm_m4": lambda n: re.search(r"k_gemm_stream<2, \d+, \d+, \d+, 2>", n) is not None,
@@ -162,13 +164,19 @@ def pmc_summarize(args):
         f, w = last(fetch, pred, 3), last(write, pred, 3)
         if f and w:
             res[k] = (np.mean(f), np.mean(w))
+    # the tiled kernel serves M = 64 and 512 (same grid size): the workload
+    # launches them three times each in GEMM_STEP_ORDER
     tile = lambda n: "k_gemm_tile<2," in n
     fin = lambda n: "k_splitk_finalize" in n
-    f6, w6 = last(fetch, tile, 6), last(write, tile, 6)
+    tile_ms = [M for M in GEMM_STEP_ORDER if M > 16]
+    ft, wt = last(fetch, tile, 3 * len(tile_ms)), last(write, tile, 3 * len(tile_ms))
     ff, wf = last(fetch, fin, 3), last(write, fin, 3)
-    if f6 and w6 and ff and wf:
-        res["gemm_m64"] = (np.mean(f6[:3]) + np.mean(ff), np.mean(w6[:3]) + np.mean(wf))
-        res["gemm_m512"] = (np.mean(f6[3:]), np.mean(w6[3:]))
+    if ft and wt and ff and wf:
+        for i, M in enumerate(tile_ms):
+            f, w = np.mean(ft[3 * i:3 * i + 3]), np.mean(wt[3 * i:3 * i + 3])
+            if M == 64:  # split-K: add the finalize launch
+                f, w = f + np.mean(ff), w + np.mean(wf)
+            res[f"gemm_m{M}"] = (f, w)
     lines = [
         "# HBM traffic per launch of the bench.py step kernels (rocprofv3 PMC)",
         "",
@@ -266,6 +274,12 @@ def main():
     init_ms = e0.elapsed_time(e1)
 
     kernels = ["fwd", "bwd", "pack"] + [f"gemm_m{M}" for M in GEMM_STEP_ORDER]
+
+    if args.gemm_b2b_only:
+        ridge = MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3
+        print(json.dumps({"gemm_back_to_back": gemm_back_to_back(torch, pq, Xs, packed, ab16, Ys, stream, ridge)}),
+              flush=True)
+        return
 
     if args.pmc_workload:
         src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).uniform_()
@@ -398,6 +412,7 @@ def main():
     }
 
     if not args.no_extras:
+        out["gemm_back_to_back"] = gemm_back_to_back(torch, pq, Xs, packed, ab16, Ys, stream, ridge)
         out["sweep_bits"] = sweep_bits(torch, pq, stack, make_tables, stream)
         out["gemm_compare"] = gemm_compare(torch, pq, W16, a16, Xs, stream)
 
@@ -417,6 +432,42 @@ def time_it(torch, stream, fn, reps):
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
     return float(np.mean([evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]))
+
+
+def gemm_back_to_back(torch, pq, Xs, packed, ab16, Ys, stream, ridge, reps=40):
+    """Each GEMM of the step launched `reps` times in a row on the rotating
+    weight copies, with one event pair around the run: the kernel's rate
+    without the event packets and the other kernels of the step in between
+    (the in-step times above include both)."""
+    res = {}
+    sid = stream.cuda_stream
+    pk = [p.data_ptr() for p in packed]
+    ab = [a.data_ptr() for a in ab16]
+    for M in GEMM_MS:
+        xp, yp = Xs[M].data_ptr(), Ys[M].data_ptr()
+
+        def run(i, M=M, xp=xp, yp=yp):
+            # plain integers: the host side of a launch stays well below the
+            # kernel time, so the GPU never waits for the next launch
+            b = i % ROTATE
+            pq.pq_w2a16_gemm(M, GEMM_NK, GEMM_NK, xp, pk[b], ab[b], yp, sid)
+        for i in range(8):
+            run(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            run(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        by = gemm_bytes(M, GEMM_NK, GEMM_NK, 2)
+        fl = 2.0 * M * GEMM_NK * GEMM_NK
+        gbs, tf = by / ms / 1e6, fl / ms / 1e9
+        frac = gbs / HBM_PEAK_GBS if fl / by < ridge else tf / MFMA_BF16_PEAK_TFLOPS
+        res[f"m{M}"] = dict(ms=round(ms, 5), weight_stream_GBs=round(gbs, 1), tflops=round(tf, 2),
+                            frac=round(frac, 4))
+    return res
 
 
 def sweep_bits(torch, pq, stack, make_tables, stream):

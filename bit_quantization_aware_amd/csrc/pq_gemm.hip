@@ -75,26 +75,28 @@
 #define PQ_STREAM4_TN 4
 #endif
 #ifndef PQ_STREAM4_D1
-#define PQ_STREAM4_D1 6
+#define PQ_STREAM4_D1 3
 #endif
 #ifndef PQ_STREAM4_D2
-#define PQ_STREAM4_D2 5
+#define PQ_STREAM4_D2 3
 #endif
 #ifndef PQ_STREAM4_D4
-#define PQ_STREAM4_D4 4
+#define PQ_STREAM4_D4 3
 #endif
-// streaming-kernel stages in flight for 1, 2, 4 and 8 activation DMAs per group
+// streaming-kernel stages in flight for 1, 2, 4 and 8 activation DMAs per
+// group.  Measured on the export byte order: three stages (12-15 KB per
+// wave) stream faster than five or six.
 #ifndef PQ_STREAM_D1
-#define PQ_STREAM_D1 6
+#define PQ_STREAM_D1 3
 #endif
 #ifndef PQ_STREAM_D2
-#define PQ_STREAM_D2 5
+#define PQ_STREAM_D2 3
 #endif
 #ifndef PQ_STREAM_D4
-#define PQ_STREAM_D4 4
+#define PQ_STREAM_D4 3
 #endif
 #ifndef PQ_STREAM_D8
-#define PQ_STREAM_D8 3
+#define PQ_STREAM_D8 2
 #endif
 
 namespace pq {
@@ -587,7 +589,8 @@ __global__ __launch_bounds__(256) void k_splitk_finalize(const float *ws, const 
 // Weight-streaming kernel for M <= 16 (decode and small batches).
 //
 // The weight (N*K*BITS/8 bytes, read once) is the whole cost, and HBM gives
-// its rate only with many bytes in flight per CU.  A block owns TN column
+// its rate only with tens of KB in flight per CU (about 50-60 KB measured
+// best; more slows the stream down).  A block owns TN column
 // tiles of 16 and its NW waves share K out by groups (256 k at 2 bits, 128
 // at 4: 64 bytes of each weight row), wave w taking groups w, w + NW, ....
 // In the export byte order a group of all rows is one contiguous run, so at
