@@ -53,6 +53,10 @@ def lib():
         L.pqo_tiled_bytes.argtypes = [_i64, _i64]
         L.pqo_tiled_bytes.restype = _i64
         L.pqo_tile_codes.argtypes = [_i64, _i64, _u8p, _u8p]
+        L.pqo_adamw.argtypes = [_i64, _f32p, _f32p, _f32p, _f32p] + [ctypes.c_double] * 5 + [_i64]
+        L.pqo_qat_step.argtypes = ([ctypes.c_int, _i64, _i64, _f32p, _f32p, ctypes.c_void_p, ctypes.c_int,
+                                    ctypes.c_double, _f32p, _f32p, _f32p, _f32p] + [ctypes.c_double] * 5 +
+                                   [_i64, _u16p, _u8p, _f32p])
         L.pqo_set_threads.argtypes = [ctypes.c_int]
         _lib = L
     return _lib
@@ -170,6 +174,40 @@ def pack(mode: int, W: np.ndarray, alpha: np.ndarray):
     _check(lib().pqo_pack(mode, rows, cols, _p(W, _f32p), _p(alpha, _f32p),
                           _p(packed, _u8p), _p(ab, _u16p)))
     return packed, ab
+
+
+ADAMW_DEFAULTS = dict(lr=2e-5, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+
+
+def adamw(p, g, m, v, step, lr, beta1, beta2, eps, weight_decay):
+    """AdamW on float32 arrays; returns updated copies (p, m, v)."""
+    p, m, v = (np.array(a, dtype=np.float32, copy=True) for a in (p, m, v))
+    g = _c(g, np.float32)
+    _check(lib().pqo_adamw(p.size, _p(p, _f32p), _p(g, _f32p), _p(m, _f32p), _p(v, _f32p),
+                           lr, beta1, beta2, eps, weight_decay, step))
+    return p, m, v
+
+
+def qat_step(mode: int, W, alpha, G, mW, vW, m_alpha, v_alpha, step, grad_scale=None,
+             lr=2e-5, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0):
+    """Backward + AdamW + next forward.  Returns a dict of new arrays: W, alpha,
+    mW, vW, m_alpha, v_alpha, wq_bf16, codes, dalpha."""
+    W, alpha, mW, vW, m_alpha, v_alpha = (np.array(a, dtype=np.float32, copy=True)
+                                          for a in (W, alpha, mW, vW, m_alpha, v_alpha))
+    rows, cols = W.shape
+    if grad_scale is None:
+        grad_scale = default_grad_scale(mode, rows, cols)
+    G = np.ascontiguousarray(G)
+    wq = np.empty((rows, cols), np.uint16)
+    codes = np.empty((rows, code_row_bytes(mode, cols)), np.uint8)
+    da = np.empty(rows, np.float32)
+    _check(lib().pqo_qat_step(mode, rows, cols, _p(W, _f32p), _p(alpha, _f32p),
+                              G.ctypes.data_as(ctypes.c_void_p), int(G.dtype == np.uint16),
+                              float(grad_scale), _p(mW, _f32p), _p(vW, _f32p), _p(m_alpha, _f32p),
+                              _p(v_alpha, _f32p), lr, beta1, beta2, eps, weight_decay, step,
+                              _p(wq, _u16p), _p(codes, _u8p), _p(da, _f32p)))
+    return dict(W=W, alpha=alpha, mW=mW, vW=vW, m_alpha=m_alpha, v_alpha=v_alpha, wq_bf16=wq,
+                codes=codes, dalpha=da)
 
 
 def tiled_bytes(rows: int, row_bytes: int) -> int:

@@ -420,6 +420,98 @@ int pqo_pack(int mode, int64_t rows, int64_t cols, const float *W, const float *
 }
 
 /* ---------------------------------------------------------------------------
+ * Optimizer step.  The recipe trains W and the per-row scale alpha with AdamW
+ * at weight decay 0 ([Note] "The 2-bit recipe, in full", optimizer row); the
+ * pages give no formula, so this is AdamW as published (Adam moments with
+ * bias correction, weight decay decoupled from the gradient), in this
+ * binary32 order, one rounding per operation:
+ *   m'  = b1 * m + (1 - b1) * g
+ *   v'  = b2 * v + ((1 - b2) * g) * g
+ *   den = sqrt(v') / sqrt(1 - b2^t) + eps
+ *   p'  = p * (1 - lr * wd) - (lr / (1 - b1^t)) * m' / den
+ * The scalars b1, 1 - b1, b2, 1 - b2, sqrt(1 - b2^t), eps, 1 - lr * wd and
+ * lr / (1 - b1^t) are computed in binary64 from the hyper-parameters and
+ * rounded once to binary32.  t >= 1 is the step number.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    float b1, w1, b2, w2, s2, eps, decay, step_size;
+} adam_k;
+
+static adam_k adam_scalars(double lr, double b1, double b2, double eps, double wd, int64_t t)
+{
+    adam_k k;
+    k.b1 = (float)b1;
+    k.w1 = (float)(1.0 - b1);
+    k.b2 = (float)b2;
+    k.w2 = (float)(1.0 - b2);
+    k.s2 = (float)sqrt(1.0 - pow(b2, (double)t));
+    k.eps = (float)eps;
+    k.decay = (float)(1.0 - lr * wd);
+    k.step_size = (float)(lr / (1.0 - pow(b1, (double)t)));
+    return k;
+}
+
+static float adam_one(const adam_k *k, float p, float g, float *m, float *v)
+{
+    const float mn = k->b1 * *m + k->w1 * g;
+    const float vn = k->b2 * *v + (k->w2 * g) * g;
+    const float den = sqrtf(vn) / k->s2 + k->eps;
+    const float pd = p * k->decay;
+    *m = mn;
+    *v = vn;
+    return pd - (k->step_size * mn) / den;
+}
+
+static int adam_args_ok(double lr, double b1, double b2, double eps, double wd, int64_t t)
+{
+    return t >= 1 && lr >= 0.0 && lr < 1e30 && b1 >= 0.0 && b1 < 1.0 && b2 >= 0.0 && b2 < 1.0 &&
+           eps > 0.0 && eps < 1e30 && wd >= 0.0 && wd < 1e30;
+}
+
+/* AdamW on n parameters p with gradients g and moments m, v (all updated in
+ * place except g). */
+int pqo_adamw(int64_t n, float *p, const float *g, float *m, float *v, double lr, double b1,
+              double b2, double eps, double wd, int64_t t)
+{
+    if (n < 0 || !adam_args_ok(lr, b1, b2, eps, wd, t)) return -1;
+    const adam_k k = adam_scalars(lr, b1, b2, eps, wd, t);
+    for (int64_t i = 0; i < n; ++i) p[i] = adam_one(&k, p[i], g[i], &m[i], &v[i]);
+    return 0;
+}
+
+/* One QAT step of a quantized linear layer, as three steps of its definition
+ * in order: the straight-through backward of the current forward
+ * (pqo_quantize_bwd: dW and dalpha from W, alpha and G), AdamW on W (with
+ * dW) and on alpha (with dalpha, its own moments), then the next forward's
+ * fake-quantization of the updated W with the updated alpha
+ * (pqo_quantize_fwd).  W, alpha and the four moment arrays are updated in
+ * place; wq_bf16, codes and dalpha_out are optional outputs. */
+int pqo_qat_step(int mode, int64_t rows, int64_t cols, float *W, float *alpha, const void *G,
+                 int g_is_bf16, double grad_scale, float *mW, float *vW, float *m_alpha,
+                 float *v_alpha, double lr, double b1, double b2, double eps, double wd,
+                 int64_t t, uint16_t *wq_bf16, uint8_t *codes, float *dalpha_out)
+{
+    if (!valid_mode(mode) || rows < 0 || cols <= 0 || !W || !alpha || !G || !mW || !vW ||
+        !m_alpha || !v_alpha || !adam_args_ok(lr, b1, b2, eps, wd, t))
+        return -1;
+    float *dW = (float *)malloc((size_t)(rows * cols) * sizeof(float) + 1);
+    float *da = (float *)malloc((size_t)rows * sizeof(float) + 1);
+    if (!dW || !da) {
+        free(dW);
+        free(da);
+        return -1;
+    }
+    int rc = pqo_quantize_bwd(mode, rows, cols, W, alpha, G, g_is_bf16, grad_scale, dW, da, NULL);
+    if (rc == 0) rc = pqo_adamw(rows * cols, W, dW, mW, vW, lr, b1, b2, eps, wd, t);
+    if (rc == 0) rc = pqo_adamw(rows, alpha, da, m_alpha, v_alpha, lr, b1, b2, eps, wd, t);
+    if (rc == 0) rc = pqo_quantize_fwd(mode, rows, cols, W, alpha, wq_bf16, NULL, codes);
+    if (rc == 0 && dalpha_out) memcpy(dalpha_out, da, (size_t)rows * sizeof(float));
+    free(dW);
+    free(da);
+    return rc;
+}
+
+/* ---------------------------------------------------------------------------
  * Deployment layout of the exported codes.  The pages fix only what a packed
  * 2-bit weight holds (four codes per byte and a bf16 scale per row, [News]
  * storage and speed paragraphs); the byte order the deployed GEMM reads is

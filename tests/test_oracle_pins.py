@@ -12,7 +12,10 @@ What each pin stands on:
   * alpha init, GEMM and bf16 rounding: numpy / torch library routines;
   * the deployment byte order of exported codes: a numpy axis shuffle of the
     padded code rows and hand-worked positions (the layout is the library's
-    own definition; the pages fix only four codes per byte).
+    own definition; the pages fix only four codes per byte);
+  * AdamW: torch.optim.AdamW in float64 over five steps, and the first-step
+    closed form (bias corrections cancel); the fused QAT step against the
+    pinned backward, AdamW and forward called in turn.
 Parity unpinned (documented readings): the 1-bit quantizer, the ternary
 alpha-gradient of clipped weights, and n / Qp of the default gradient scale.
 """
@@ -478,3 +481,83 @@ def test_tile_codes_hand_positions():
     # every stored byte appears exactly once: nonzero bytes are a permutation
     assert np.count_nonzero(T) == P.size
     assert np.array_equal(np.sort(T[T != 0]), np.sort(P.reshape(-1)))
+
+
+# ----------------------------------------------------------------------------
+# Optimizer step (AdamW, decoupled weight decay) and the fused QAT step
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("wd", [0.0, 0.1])
+def test_adamw_matches_torch_float64(wd):
+    """Five AdamW steps in binary32 against torch.optim.AdamW in float64 (its
+    own implementation of the published algorithm): a dropped bias
+    correction, eps under the square root or weight decay folded into the
+    gradient would move p by far more than the few ulps allowed."""
+    rng = np.random.default_rng(77)
+    n = 4096
+    hp = dict(lr=1e-2, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=wd)
+    p = (rng.standard_normal(n) * 0.05).astype(np.float32)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    tp = torch.nn.Parameter(torch.from_numpy(p.astype(np.float64)))
+    opt = torch.optim.AdamW([tp], lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                            weight_decay=wd, foreach=False)
+    for t in range(1, 6):
+        g = (rng.standard_normal(n) * 10.0 ** rng.uniform(-6, 0, n)).astype(np.float32)
+        p_prev = p
+        p, m, v = O.adamw(p, g, m, v, t, **hp)
+        tp.grad = torch.from_numpy(g.astype(np.float64))
+        opt.step()
+        ref = tp.detach().numpy()
+        st = opt.state[tp]
+        # binary32 roundings of p accumulate over the steps (at most ~t ulps
+        # of the larger of p before and after); the update itself is exact to
+        # ~1e-7 relative.  Every plausible formula slip moves p by ~lr.
+        mag = np.maximum(np.abs(p_prev), np.abs(ref)).astype(np.float32)
+        tol = 2 * t * np.spacing(mag) + 1e-6 * hp["lr"]
+        assert np.all(np.abs(p - ref) <= tol), f"step {t}"
+        mr = st["exp_avg"].numpy()  # a signed running sum: compare on its scale
+        assert np.allclose(m, mr, rtol=1e-5, atol=1e-6 * np.abs(mr).max())
+        assert np.allclose(v, st["exp_avg_sq"].numpy(), rtol=1e-5, atol=0)
+
+
+def test_adamw_first_step_closed_form():
+    """At t = 1 from zero moments the bias corrections cancel:
+    m_hat = g, v_hat = g^2, so p' = p (1 - lr wd) - lr g / (|g| + eps)."""
+    rng = np.random.default_rng(78)
+    n = 1000
+    lr, wd, eps = 3e-3, 0.05, 1e-8
+    p = rng.standard_normal(n).astype(np.float32)
+    g = (rng.standard_normal(n) * 10.0 ** rng.uniform(-5, 1, n)).astype(np.float32)
+    p1, m1, v1 = O.adamw(p, g, np.zeros(n), np.zeros(n), 1, lr, 0.9, 0.999, eps, wd)
+    p64, g64 = p.astype(np.float64), g.astype(np.float64)
+    want = p64 * (1 - lr * wd) - lr * g64 / (np.abs(g64) + eps)
+    mag = np.maximum(np.abs(p64), np.abs(want)).astype(np.float32)
+    assert np.all(np.abs(p1 - want) <= 2 * np.spacing(mag) + 1e-6 * lr)
+    assert np.allclose(m1, 0.1 * g64, rtol=1e-6)
+    assert np.allclose(v1, 0.001 * g64 * g64, rtol=1e-5)
+
+
+@pytest.mark.parametrize("mode", [O.SEQ2, O.TERNARY, O.LSQ4, O.BINARY])
+@pytest.mark.parametrize("g_bf16", [False, True])
+def test_qat_step_is_bwd_then_adamw_then_fwd(mode, g_bf16):
+    """The fused step's definition, checked against the three pinned pieces
+    called one after the other."""
+    rng = np.random.default_rng(79 + mode)
+    rows, cols = 24, 96
+    W = synth.normal_f32(rng, (rows, cols), 0.02)
+    alpha = O.alpha_init(mode, W) * np.float32(0.8)
+    G = synth.normal_f32(rng, (rows, cols))
+    Gin = synth.to_bf16_bits(G) if g_bf16 else G
+    mW = synth.normal_f32(rng, (rows, cols), 1e-3)
+    vW = np.abs(synth.normal_f32(rng, (rows, cols), 1e-6))
+    ma = synth.normal_f32(rng, (rows,), 1e-3)
+    va = np.abs(synth.normal_f32(rng, (rows,), 1e-6))
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    out = O.qat_step(mode, W, alpha, Gin, mW, vW, ma, va, 7, **hp)
+    dW, da, _ = O.quantize_bwd(mode, W, alpha, Gin)
+    W1, mW1, vW1 = O.adamw(W, dW, mW, vW, 7, **hp)
+    a1, ma1, va1 = O.adamw(alpha, da, ma, va, 7, **hp)
+    wq1, _, codes1 = O.quantize_fwd(mode, W1, a1)
+    for k, want in (("W", W1), ("mW", mW1), ("vW", vW1), ("alpha", a1), ("m_alpha", ma1),
+                    ("v_alpha", va1), ("wq_bf16", wq1), ("codes", codes1), ("dalpha", da)):
+        assert np.array_equal(out[k].view(np.uint8), np.ascontiguousarray(want).view(np.uint8)), k
