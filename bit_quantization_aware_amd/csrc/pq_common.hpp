@@ -55,14 +55,18 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16)
 // kernel-argument segment, so the per-block lookup is a few scalar-cache hits.
 constexpr int kMaxGroup = 448;
 
-struct LaunchTable {
-    const pq_mat *table;  // device descriptors, or nullptr -> use `single`
-    pq_mat single;
+template <typename D>
+struct LaunchTableT {
+    const D *table;  // device descriptors, or nullptr -> use `single`
+    D single;
     int count;
     int32_t block_start[kMaxGroup + 1];
 };
+using LaunchTable = LaunchTableT<pq_mat>;
+using StepTable = LaunchTableT<pq_step_mat>;
 
-__device__ __forceinline__ int find_matrix(const LaunchTable &lt, int b)
+template <typename D>
+__device__ __forceinline__ int find_matrix(const LaunchTableT<D> &lt, int b)
 {
     int lo = 0, hi = lt.count - 1;
     while (lo < hi) {

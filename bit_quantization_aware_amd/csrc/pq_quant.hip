@@ -29,6 +29,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
 #include <type_traits>
 
 #include "pq_common.hpp"
@@ -203,6 +204,25 @@ enum : unsigned { OUT_BF16 = 1, OUT_F32 = 2, OUT_CODES = 4, OUT_ALPHA_BF16 = 8, 
 // to launch and retire; a team of four waves takes one row.
 constexpr int fwd_rows_per_wave(int wpr) { return wpr == 1 ? 2 : 1; }
 
+// Row-major codes of quad q (weights 4q .. 4q+3) from their four codes.  The
+// 1-bit case pairs each even lane with its odd neighbour, so every lane of
+// the wave must make this call (act only gates the store).
+template <int CW>
+__device__ __forceinline__ void store_codes(PQ_GLOBAL uint8_t *crow, int q, uint32_t c0, uint32_t c1, uint32_t c2,
+                                            uint32_t c3, bool act, int tl)
+{
+    if constexpr (CW == 2) {
+        if (act) crow[q] = static_cast<uint8_t>(c0 | (c1 << 2) | (c2 << 4) | (c3 << 6));
+    } else if constexpr (CW == 4) {
+        if (act) ((PQ_GLOBAL uint16_t *)crow)[q] = static_cast<uint16_t>(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
+    } else {
+        // 1 bit: a nibble per quad; the even lane takes its odd neighbour's.
+        const uint32_t nib = c0 | (c1 << 1) | (c2 << 2) | (c3 << 3);
+        const uint32_t hi = __shfl_down(nib, 1);
+        if (act && (tl & 1) == 0) crow[q >> 1] = static_cast<uint8_t>(nib | (hi << 4));
+    }
+}
+
 // Export byte order of the codes (OUT_TILED, single matrix).  The 64-byte
 // groups of all rows are stored group after group; inside a group, each tile
 // of 16 rows is 1 KB ordered [16-byte piece][row of the tile][byte]:
@@ -350,18 +370,7 @@ __global__ __launch_bounds__(256, PQ_QUANT_FWD_MINB) void k_quant_fwd(LaunchTabl
                             *(PQ_GLOBAL uint16_t *)d = static_cast<uint16_t>(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
                     }
                 } else if constexpr ((OUTS & OUT_CODES) != 0) {
-                    if constexpr (CW == 2) {
-                        if (act) crow[q] = static_cast<uint8_t>(c0 | (c1 << 2) | (c2 << 4) | (c3 << 6));
-                    } else if constexpr (CW == 4) {
-                        if (act)
-                            ((PQ_GLOBAL uint16_t *)crow)[q] =
-                                static_cast<uint16_t>(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
-                    } else {
-                        // 1 bit: a nibble per quad; even lane takes its odd neighbour's.
-                        const uint32_t nib = c0 | (c1 << 1) | (c2 << 2) | (c3 << 3);
-                        const uint32_t hi = __shfl_down(nib, 1);
-                        if (act && (tl & 1) == 0) crow[q >> 1] = static_cast<uint8_t>(nib | (hi << 4));
-                    }
+                    store_codes<CW>(crow, q, c0, c1, c2, c3, act, tl);
                 }
             }
         };
@@ -503,6 +512,183 @@ __global__ __launch_bounds__(256, PQ_QUANT_BWD_MINB) void k_quant_bwd(LaunchTabl
 }
 
 // ---------------------------------------------------------------------------
+// Fused QAT step: backward of the current forward, AdamW on W and alpha, and
+// the next forward, one team per row.
+//
+// Pass A streams W, G and the two moments of W once: per weight the
+// backward's x, gate and dW (bit-identical to k_quant_bwd, including the
+// exact division for tiny quotients) and the alpha-gradient partial, then
+// the AdamW update of w, m, v; the new w is stored with a plain store (it is
+// read back in pass B, from L2), the moments with streaming stores.  The
+// team's binary64 sum gives dalpha; every lane then updates alpha and its
+// moments with the same binary32 operations (identical results), and lane 0
+// stores them.  Pass B reads the new weights back and writes the next
+// forward's bf16 weights and codes, as k_quant_fwd does.
+// ---------------------------------------------------------------------------
+struct AdamK {
+    float b1, w1, b2, w2, s2, eps, decay, step_size;
+};
+
+// One AdamW update in the documented binary32 order (the kernels are built
+// with -ffp-contract=off, so no product is fused into an add).
+__device__ __forceinline__ float adam_one(const AdamK &k, float p, float g, float &m, float &v)
+{
+    const float mn = k.b1 * m + k.w1 * g;
+    const float vn = k.b2 * v + (k.w2 * g) * g;
+    const float den = __builtin_sqrtf(vn) / k.s2 + k.eps;
+    const float pd = p * k.decay;
+    m = mn;
+    v = vn;
+    return pd - (k.step_size * mn) / den;
+}
+
+// Quads per lane per pass: four streams in, so two quads keep the same bytes
+// in flight as the other kernels' four, within 128 VGPRs.
+constexpr int kStepUnroll = 2;
+
+template <int MODE, int WPR, bool GBF16>
+__global__ __launch_bounds__(256, PQ_QUANT_BWD_MINB) void k_qat_step(StepTable lt, AdamK ak)
+{
+    constexpr int RPB = 4 / WPR;
+    constexpr int TEAM = 64 * WPR;
+    constexpr int CW = Mode<MODE>::cw;
+    __shared__ double lds_d[4];
+
+    const int wave = threadIdx.x >> 6;
+    const int tl = (wave % WPR) * 64 + (threadIdx.x & 63);
+    const int b = blockIdx.x;
+    const int k = find_matrix(lt, b);
+    const pq_step_mat m = lt.table ? lt.table[k] : lt.single;
+    const int64_t row = static_cast<int64_t>(b - lt.block_start[k]) * RPB + wave / WPR;
+    if (row >= m.rows) return;
+
+    const int64_t cols = m.cols;
+    const int nq = static_cast<int>(cols >> 2);
+    PQ_GLOBAL f32x4 *wr = (PQ_GLOBAL f32x4 *)(m.W + row * cols);
+    const PQ_GLOBAL f32x4 *gr32 = (const PQ_GLOBAL f32x4 *)(static_cast<const float *>(m.G) + row * cols);
+    const PQ_GLOBAL u32x2 *gr16 = (const PQ_GLOBAL u32x2 *)(static_cast<const uint16_t *>(m.G) + row * cols);
+    PQ_GLOBAL f32x4 *mr = (PQ_GLOBAL f32x4 *)(m.mW + row * cols);
+    PQ_GLOBAL f32x4 *vr = (PQ_GLOBAL f32x4 *)(m.vW + row * cols);
+
+    const float alpha_raw = m.alpha[row];
+    const float a = alpha_raw > kAlphaFloor ? alpha_raw : kAlphaFloor;
+    const double y = 1.0 / static_cast<double>(a);
+    const uint32_t tkey = tiny_key(a * 0x1p-123f);
+    constexpr float lo = Mode<MODE>::lo, hi = Mode<MODE>::hi;
+    constexpr int STEP = TEAM * kStepUnroll;
+    const int nfull = nq / STEP * STEP;
+    double acc = 0.0;
+
+    // Pass A: backward + AdamW of one quad on values already in registers.
+    auto quad_a = [&](f32x4 &wq, const f32x4 &gq, f32x4 &mq, f32x4 &vq, auto exact_c) {
+        constexpr bool EXACT = decltype(exact_c)::value;
+        float w4[4] = {wq.x, wq.y, wq.z, wq.w};
+        const float g4[4] = {gq.x, gq.y, gq.z, gq.w};
+        float m4[4] = {mq.x, mq.y, mq.z, mq.w};
+        float v4[4] = {vq.x, vq.y, vq.z, vq.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float lvl;
+            const float x = EXACT ? w4[e] / a : div_fast(w4[e], y);
+            quant_x<MODE>(w4[e], x, lvl);
+            const bool inside = (x >= lo) && (x <= hi);
+            const float d = inside ? g4[e] : 0.0f;
+            const double s = static_cast<double>(lvl) - (inside ? static_cast<double>(x) : 0.0);
+            acc += s * static_cast<double>(g4[e]);
+            w4[e] = adam_one(ak, w4[e], d, m4[e], v4[e]);
+        }
+        wq = f32x4{w4[0], w4[1], w4[2], w4[3]};
+        mq = f32x4{m4[0], m4[1], m4[2], m4[3]};
+        vq = f32x4{v4[0], v4[1], v4[2], v4[3]};
+    };
+    auto pass_a = [&](int base, auto guard_c) {
+        constexpr bool GUARD = decltype(guard_c)::value;
+        f32x4 wv[kStepUnroll], gv[kStepUnroll], mv[kStepUnroll], vv[kStepUnroll];
+#pragma unroll
+        for (int u = 0; u < kStepUnroll; ++u) {
+            const int q = base + u * TEAM + tl;
+            if (!GUARD || q < nq) {
+                wv[u] = wr[q];
+                if constexpr (GBF16) {
+                    const u32x2 h = ld_stream(&gr16[q]);
+                    gv[u] = f32x4{bf16_to_f32(h.x & 0xFFFFu), bf16_to_f32(h.x >> 16),
+                                  bf16_to_f32(h.y & 0xFFFFu), bf16_to_f32(h.y >> 16)};
+                } else {
+                    gv[u] = ld_stream(&gr32[q]);
+                }
+                mv[u] = ld_stream(&mr[q]);
+                vv[u] = ld_stream(&vr[q]);
+            } else {
+                // inactive slots: zero weight and gradient (their products
+                // are +0); the moments are never stored
+                wv[u] = gv[u] = mv[u] = vv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kStepUnroll; ++u) {
+            if (GUARD && base + u * TEAM >= nq) break;
+            const int q = base + u * TEAM + tl;
+            const uint32_t kmin = min(min(tiny_key(wv[u].x), tiny_key(wv[u].y)),
+                                      min(tiny_key(wv[u].z), tiny_key(wv[u].w)));
+            if (__builtin_expect(kmin < tkey, 0)) quad_a(wv[u], gv[u], mv[u], vv[u], std::true_type{});
+            else quad_a(wv[u], gv[u], mv[u], vv[u], std::false_type{});
+            if (!GUARD || q < nq) {
+                wr[q] = wv[u];
+                st_stream(&mr[q], mv[u]);
+                st_stream(&vr[q], vv[u]);
+            }
+        }
+    };
+    for (int base = 0; base < nfull; base += STEP) pass_a(base, std::false_type{});
+    if (nfull < nq) pass_a(nfull, std::true_type{});
+
+    // dalpha, then AdamW on alpha (same operations in every lane).
+    acc = team_sum<WPR>(acc, lds_d);
+    const float da = static_cast<float>(m.grad_scale * acc);
+    float ma = m.m_alpha[row], va = m.v_alpha[row];
+    const float alpha_new = adam_one(ak, alpha_raw, da, ma, va);
+    if (tl == 0) {
+        m.alpha[row] = alpha_new;
+        m.m_alpha[row] = ma;
+        m.v_alpha[row] = va;
+        if (m.dalpha) m.dalpha[row] = da;
+    }
+
+    // Pass B: the next forward on the updated row.
+    if (!m.wq_bf16 && !m.codes) return;
+    const float a2 = alpha_new > kAlphaFloor ? alpha_new : kAlphaFloor;
+    const double y2 = 1.0 / static_cast<double>(a2);
+    PQ_GLOBAL u32x2 *wq16 = m.wq_bf16 ? (PQ_GLOBAL u32x2 *)(static_cast<uint16_t *>(m.wq_bf16) + row * cols) : nullptr;
+    PQ_GLOBAL uint8_t *crow = m.codes ? (PQ_GLOBAL uint8_t *)(m.codes + row * (cols * CW / 8)) : nullptr;
+    auto pass_b = [&](int base, auto guard_c) {
+        constexpr bool GUARD = decltype(guard_c)::value;
+        f32x4 v[kStepUnroll];
+#pragma unroll
+        for (int u = 0; u < kStepUnroll; ++u) {
+            const int q = base + u * TEAM + tl;
+            if (!GUARD || q < nq) v[u] = wr[q];
+            else v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < kStepUnroll; ++u) {
+            if (GUARD && base + u * TEAM >= nq) break;
+            const int q = base + u * TEAM + tl;
+            const bool act = !GUARD || q < nq;
+            float l0, l1, l2, l3;
+            const uint32_t c0 = quant_x<MODE>(v[u].x, div_fast(v[u].x, y2), l0);
+            const uint32_t c1 = quant_x<MODE>(v[u].y, div_fast(v[u].y, y2), l1);
+            const uint32_t c2 = quant_x<MODE>(v[u].z, div_fast(v[u].z, y2), l2);
+            const uint32_t c3 = quant_x<MODE>(v[u].w, div_fast(v[u].w, y2), l3);
+            if (wq16 && act)
+                st_stream(&wq16[q], u32x2{pack_bf16x2(a2 * l0, a2 * l1), pack_bf16x2(a2 * l2, a2 * l3)});
+            if (crow) store_codes<CW>(crow, q, c0, c1, c2, c3, act, tl);
+        }
+    };
+    for (int base = 0; base < nfull; base += STEP) pass_b(base, std::false_type{});
+    if (nfull < nq) pass_b(nfull, std::true_type{});
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 
@@ -525,9 +711,8 @@ bool ptr_ok(const void *p) { return p == nullptr || aligned16(p); }
 // One or more launches over a stack (kMaxGroup matrices each), with one
 // team size for the whole stack; `fwd` launches take fwd_rows_per_wave rows
 // per wave.
-template <typename F>
-pq_status launch_grouped(int count, const pq_mat *host, const pq_mat *dev, hipStream_t stream, bool fwd,
-                         F &&launch_one)
+template <typename D, typename F>
+pq_status launch_grouped(int count, const D *host, const D *dev, hipStream_t stream, bool fwd, F &&launch_one)
 {
     int64_t total_rows = 0, total_elems = 0;
     for (int i = 0; i < count; ++i) {
@@ -538,7 +723,7 @@ pq_status launch_grouped(int count, const pq_mat *host, const pq_mat *dev, hipSt
     const int rpb = (4 / wpr) * (fwd ? fwd_rows_per_wave(wpr) : 1);  // rows per block
     for (int start = 0; start < count; start += kMaxGroup) {
         const int n = count - start < kMaxGroup ? count - start : kMaxGroup;
-        LaunchTable lt;
+        LaunchTableT<D> lt;
         lt.table = dev ? dev + start : nullptr;
         lt.single = host[start];
         lt.count = n;
@@ -695,6 +880,81 @@ pq_status check_bwd_descs(int mode, int count, const pq_mat *host, int g_dtype, 
     return PQ_OK;
 }
 
+template <int MODE>
+void launch_step_mode(int wpr, bool gbf, const StepTable &lt, int blocks, const AdamK &k, hipStream_t s)
+{
+    if (wpr == 1) {
+        if (gbf) hipLaunchKernelGGL((k_qat_step<MODE, 1, true>), dim3(blocks), dim3(256), 0, s, lt, k);
+        else hipLaunchKernelGGL((k_qat_step<MODE, 1, false>), dim3(blocks), dim3(256), 0, s, lt, k);
+    } else {
+        if (gbf) hipLaunchKernelGGL((k_qat_step<MODE, 4, true>), dim3(blocks), dim3(256), 0, s, lt, k);
+        else hipLaunchKernelGGL((k_qat_step<MODE, 4, false>), dim3(blocks), dim3(256), 0, s, lt, k);
+    }
+}
+
+void launch_step(int mode, int wpr, bool gbf, const StepTable &lt, int blocks, const AdamK &k, hipStream_t s)
+{
+    switch (mode) {
+    case PQ_W1_BINARY: launch_step_mode<PQ_W1_BINARY>(wpr, gbf, lt, blocks, k, s); break;
+    case PQ_W158_SEQ_TERNARY: launch_step_mode<PQ_W158_SEQ_TERNARY>(wpr, gbf, lt, blocks, k, s); break;
+    case PQ_W2_SEQ: launch_step_mode<PQ_W2_SEQ>(wpr, gbf, lt, blocks, k, s); break;
+    case PQ_W3_LSQ: launch_step_mode<PQ_W3_LSQ>(wpr, gbf, lt, blocks, k, s); break;
+    default: launch_step_mode<PQ_W4_LSQ>(wpr, gbf, lt, blocks, k, s); break;
+    }
+}
+
+bool finite(double x) { return x == x && x < 1e300 && x > -1e300; }
+
+// AdamW scalars: binary64 from the hyper-parameters, rounded once.
+pq_status adam_scalars(const pq_adamw *hp, AdamK *k)
+{
+    if (!hp) return PQ_ERR_NULL;
+    const double lr = hp->lr, b1 = hp->beta1, b2 = hp->beta2, eps = hp->eps, wd = hp->weight_decay;
+    if (!finite(lr) || !finite(b1) || !finite(b2) || !finite(eps) || !finite(wd)) return PQ_ERR_ARG;
+    if (hp->step < 1 || lr < 0.0 || b1 < 0.0 || b1 >= 1.0 || b2 < 0.0 || b2 >= 1.0 || eps <= 0.0 || wd < 0.0)
+        return PQ_ERR_ARG;
+    const double t = static_cast<double>(hp->step);
+    k->b1 = static_cast<float>(b1);
+    k->w1 = static_cast<float>(1.0 - b1);
+    k->b2 = static_cast<float>(b2);
+    k->w2 = static_cast<float>(1.0 - b2);
+    k->s2 = static_cast<float>(sqrt(1.0 - pow(b2, t)));
+    k->eps = static_cast<float>(eps);
+    k->decay = static_cast<float>(1.0 - lr * wd);
+    k->step_size = static_cast<float>(lr / (1.0 - pow(b1, t)));
+    return PQ_OK;
+}
+
+pq_status check_step_descs(int mode, int count, const pq_step_mat *host, int g_dtype)
+{
+    if (!valid_mode(mode)) return PQ_ERR_MODE;
+    if (g_dtype != PQ_G_F32 && g_dtype != PQ_G_BF16) return PQ_ERR_MODE;
+    if (count < 0) return PQ_ERR_ARG;
+    if (count > 0 && !host) return PQ_ERR_NULL;
+    bool have_first = false, wq = false, cd = false, da = false;
+    for (int i = 0; i < count; ++i) {
+        const pq_step_mat &m = host[i];
+        if (m.rows < 0 || !valid_cols(m.cols)) return PQ_ERR_SHAPE;
+        if (m.rows == 0) continue;
+        if (!m.W || !m.alpha || !m.G || !m.mW || !m.vW || !m.m_alpha || !m.v_alpha) return PQ_ERR_NULL;
+        if (!aligned16(m.W) || !aligned16(m.G) || !aligned16(m.mW) || !aligned16(m.vW) ||
+            !ptr_ok(m.alpha) || !ptr_ok(m.m_alpha) || !ptr_ok(m.v_alpha) || !ptr_ok(m.wq_bf16) ||
+            !ptr_ok(m.codes) || !ptr_ok(m.dalpha))
+            return PQ_ERR_ALIGN;
+        if (!finite(m.grad_scale)) return PQ_ERR_ARG;
+        const bool w = m.wq_bf16 != nullptr, c = m.codes != nullptr, d = m.dalpha != nullptr;
+        if (!have_first) {
+            wq = w;
+            cd = c;
+            da = d;
+            have_first = true;
+        } else if (w != wq || c != cd || d != da) {
+            return PQ_ERR_ARG;
+        }
+    }
+    return PQ_OK;
+}
+
 }  // namespace
 }  // namespace pq
 
@@ -769,7 +1029,8 @@ pq_status pq_quantize_fwd(int mode, int64_t rows, int64_t cols, const float *W, 
     pq_status st = check_fwd_descs(mode, 1, &m, flags, &outs);
     if (st != PQ_OK) return st;
     const bool init = (flags & PQ_INIT_ALPHA) != 0;
-    return launch_grouped(1, &m, nullptr, static_cast<hipStream_t>(stream), true,
+    return launch_grouped(1, &m, static_cast<const pq_mat *>(nullptr), static_cast<hipStream_t>(stream),
+                          true,
                           [&](const LaunchTable &lt, int blocks, int wpr, hipStream_t s) {
                               launch_fwd(mode, init, outs, lt, blocks, wpr, s);
                           });
@@ -805,7 +1066,8 @@ pq_status pq_quantize_bwd(int mode, int64_t rows, int64_t cols, const float *W, 
     bool wdw = false, wmask = false;
     pq_status st = check_bwd_descs(mode, 1, &m, g_dtype, &wdw, &wmask);
     if (st != PQ_OK) return st;
-    return launch_grouped(1, &m, nullptr, static_cast<hipStream_t>(stream), false,
+    return launch_grouped(1, &m, static_cast<const pq_mat *>(nullptr), static_cast<hipStream_t>(stream),
+                          false,
                           [&](const LaunchTable &lt, int blocks, int wpr, hipStream_t s) {
                               launch_bwd(mode, wpr, g_dtype == PQ_G_BF16, wdw, wmask, lt, blocks, s);
                           });
@@ -857,6 +1119,50 @@ pq_status pq_pack_w4(int64_t rows, int64_t cols, const float *W, const float *al
                      uint8_t *packed, void *alpha_bf16, void *stream)
 {
     return pack_common(PQ_W4_LSQ, rows, cols, W, alpha, packed, alpha_bf16, stream);
+}
+
+pq_status pq_qat_step_grouped(int mode, int count, const pq_step_mat *descs_host, const pq_step_mat *descs_dev,
+                              int g_dtype, const pq_adamw *hp, void *stream)
+{
+    pq_status st = check_step_descs(mode, count, descs_host, g_dtype);
+    if (st != PQ_OK) return st;
+    AdamK k;
+    st = adam_scalars(hp, &k);
+    if (st != PQ_OK) return st;
+    if (count > 0 && !descs_dev) return PQ_ERR_NULL;
+    return launch_grouped(count, descs_host, descs_dev, static_cast<hipStream_t>(stream), false,
+                          [&](const StepTable &lt, int blocks, int wpr, hipStream_t s) {
+                              launch_step(mode, wpr, g_dtype == PQ_G_BF16, lt, blocks, k, s);
+                          });
+}
+
+pq_status pq_qat_step(int mode, int64_t rows, int64_t cols, float *W, float *alpha, const void *G, int g_dtype,
+                      double grad_scale, float *mW, float *vW, float *m_alpha, float *v_alpha,
+                      const pq_adamw *hp, void *Wq_bf16, uint8_t *codes, float *dalpha, void *stream)
+{
+    pq_step_mat m = {};
+    m.W = W;
+    m.alpha = alpha;
+    m.G = G;
+    m.mW = mW;
+    m.vW = vW;
+    m.m_alpha = m_alpha;
+    m.v_alpha = v_alpha;
+    m.wq_bf16 = Wq_bf16;
+    m.codes = codes;
+    m.dalpha = dalpha;
+    m.grad_scale = grad_scale;
+    m.rows = rows;
+    m.cols = cols;
+    pq_status st = check_step_descs(mode, 1, &m, g_dtype);
+    if (st != PQ_OK) return st;
+    AdamK k;
+    st = adam_scalars(hp, &k);
+    if (st != PQ_OK) return st;
+    return launch_grouped(1, &m, static_cast<const pq_step_mat *>(nullptr), static_cast<hipStream_t>(stream), false,
+                          [&](const StepTable &lt, int blocks, int wpr, hipStream_t s) {
+                              launch_step(mode, wpr, g_dtype == PQ_G_BF16, lt, blocks, k, s);
+                          });
 }
 
 }  // extern "C"

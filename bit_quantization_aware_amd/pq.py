@@ -29,7 +29,8 @@ STATUS = {0: "PQ_OK", 1: "PQ_ERR_NULL", 2: "PQ_ERR_SHAPE", 3: "PQ_ERR_MODE", 4: 
 # Every symbol include/pq.h declares.
 EXPORTS = ("pq_code_row_bytes", "pq_packed_bytes", "pq_default_grad_scale", "pq_status_str", "pq_version",
            "pq_quantize_fwd", "pq_quantize_bwd", "pq_pack_w2", "pq_pack_w4", "pq_w2a16_gemm",
-           "pq_w4a16_gemm", "pq_quantize_fwd_grouped", "pq_quantize_bwd_grouped")
+           "pq_w4a16_gemm", "pq_quantize_fwd_grouped", "pq_quantize_bwd_grouped", "pq_qat_step",
+           "pq_qat_step_grouped")
 
 
 class PQError(RuntimeError):
@@ -44,6 +45,21 @@ class pq_mat(ctypes.Structure):
                 ("wq_f32", ctypes.c_void_p), ("codes", ctypes.c_void_p), ("G", ctypes.c_void_p),
                 ("dW", ctypes.c_void_p), ("dalpha", ctypes.c_void_p), ("mask_bits", ctypes.c_void_p),
                 ("grad_scale", ctypes.c_double), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+class pq_adamw(ctypes.Structure):
+    """Mirror of `struct pq_adamw` in include/pq.h."""
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double), ("step", ctypes.c_int64)]
+
+
+class pq_step_mat(ctypes.Structure):
+    """Mirror of `struct pq_step_mat` in include/pq.h."""
+    _fields_ = [("W", ctypes.c_void_p), ("alpha", ctypes.c_void_p), ("G", ctypes.c_void_p),
+                ("mW", ctypes.c_void_p), ("vW", ctypes.c_void_p), ("m_alpha", ctypes.c_void_p),
+                ("v_alpha", ctypes.c_void_p), ("wq_bf16", ctypes.c_void_p), ("codes", ctypes.c_void_p),
+                ("dalpha", ctypes.c_void_p), ("grad_scale", ctypes.c_double), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64)]
 
 
 def _load():
@@ -69,6 +85,8 @@ def _load():
     L.pq_w4a16_gemm.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp]
     L.pq_quantize_fwd_grouped.argtypes = [i32, i32, vp, vp, u32, vp]
     L.pq_quantize_bwd_grouped.argtypes = [i32, i32, vp, vp, i32, vp]
+    L.pq_qat_step.argtypes = [i32, i64, i64, vp, vp, vp, i32, dbl, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.pq_qat_step_grouped.argtypes = [i32, i32, vp, vp, i32, vp, vp]
     for name in EXPORTS:
         if name not in ("pq_code_row_bytes", "pq_packed_bytes", "pq_default_grad_scale", "pq_status_str",
                         "pq_version"):
@@ -159,19 +177,21 @@ class MatTable:
     Build it once per stack of matrices and pass it to the grouped calls;
     it keeps the device copy (a torch uint8 tensor) alive."""
 
+    STRUCT = pq_mat
+    POINTERS = ("W", "alpha", "wq_bf16", "wq_f32", "codes", "G", "dW", "dalpha", "mask_bits")
+
     def __init__(self, mats: Sequence[dict], device="cuda"):
         n = len(mats)
         self.count = n
-        self.host = (pq_mat * max(n, 1))()
+        self.host = (self.STRUCT * max(n, 1))()
         for i, m in enumerate(mats):
             d = self.host[i]
-            for f in ("W", "alpha", "wq_bf16", "wq_f32", "codes", "G", "dW", "dalpha",
-                      "mask_bits"):
+            for f in self.POINTERS:
                 setattr(d, f, _ptr(m.get(f)))
             d.grad_scale = float(m.get("grad_scale", 0.0))
             d.rows = int(m["rows"])
             d.cols = int(m["cols"])
-        raw = bytes(memoryview(self.host).cast("B"))[: n * ctypes.sizeof(pq_mat)]
+        raw = bytes(memoryview(self.host).cast("B"))[: n * ctypes.sizeof(self.STRUCT)]
         self.dev = torch.frombuffer(bytearray(raw) or bytearray(1), dtype=torch.uint8).to(device)
 
     @property
@@ -191,3 +211,26 @@ def pq_quantize_fwd_grouped(mode, table: MatTable, flags=0, stream=None) -> None
 def pq_quantize_bwd_grouped(mode, table: MatTable, g_dtype=PQ_G_F32, stream=None) -> None:
     _check(lib.pq_quantize_bwd_grouped(mode, table.count, table.host_ptr, table.dev_ptr, g_dtype,
                                        _stream(stream)), "pq_quantize_bwd_grouped")
+
+
+class StepTable(MatTable):
+    """A pq_step_mat[] descriptor table (host + device copy) for the fused step."""
+
+    STRUCT = pq_step_mat
+    POINTERS = ("W", "alpha", "G", "mW", "vW", "m_alpha", "v_alpha", "wq_bf16", "codes", "dalpha")
+
+
+def adamw_params(step, lr=2e-5, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0) -> pq_adamw:
+    return pq_adamw(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), int(step))
+
+
+def pq_qat_step(mode, rows, cols, W, alpha, G, g_dtype, grad_scale, mW, vW, m_alpha, v_alpha,
+                hp: pq_adamw, Wq_bf16=None, codes=None, dalpha=None, stream=None) -> None:
+    _check(lib.pq_qat_step(mode, rows, cols, _ptr(W), _ptr(alpha), _ptr(G), g_dtype, float(grad_scale),
+                           _ptr(mW), _ptr(vW), _ptr(m_alpha), _ptr(v_alpha), ctypes.addressof(hp),
+                           _ptr(Wq_bf16), _ptr(codes), _ptr(dalpha), _stream(stream)), "pq_qat_step")
+
+
+def pq_qat_step_grouped(mode, table: StepTable, hp: pq_adamw, g_dtype=PQ_G_F32, stream=None) -> None:
+    _check(lib.pq_qat_step_grouped(mode, table.count, table.host_ptr, table.dev_ptr, g_dtype,
+                                   ctypes.addressof(hp), _stream(stream)), "pq_qat_step_grouped")

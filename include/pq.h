@@ -284,6 +284,70 @@ pq_status pq_quantize_fwd_grouped(int mode, int count, const pq_mat *descs_host,
 pq_status pq_quantize_bwd_grouped(int mode, int count, const pq_mat *descs_host,
                                   const pq_mat *descs_dev, int g_dtype, void *stream);
 
+/*
+ * Fused QAT step: the straight-through backward of the current forward,
+ * AdamW on W and alpha, and the next forward's fake-quantization, in one
+ * pass over each row.  The recipe trains the shadow weights and the per-row
+ * scale with AdamW at weight decay 0 and a cosine-decayed learning rate
+ * ([Note] "The 2-bit recipe, in full", optimizer and learning-rate rows);
+ * the pages give no update formula, so this is AdamW as published, with
+ * decoupled weight decay, computed in binary32 in this order, one rounding
+ * per operation (g = dW for W, g = dalpha for alpha):
+ *   m'  = b1 * m + (1 - b1) * g
+ *   v'  = b2 * v + ((1 - b2) * g) * g
+ *   den = sqrt(v') / sqrt(1 - b2^t) + eps
+ *   p'  = p * (1 - lr * wd) - (lr / (1 - b1^t)) * m' / den
+ * where b1, 1 - b1, b2, 1 - b2, sqrt(1 - b2^t), eps, 1 - lr * wd and
+ * lr / (1 - b1^t) are computed in binary64 on the host and rounded once to
+ * binary32.  dW and dalpha are exactly pq_quantize_bwd's (from W, alpha and
+ * G before the update); the outputs Wq / codes are exactly
+ * pq_quantize_fwd's for the updated W and alpha.
+ */
+typedef struct pq_adamw {
+    double lr;            /* this step's learning rate (the schedule is the caller's) */
+    double beta1, beta2;  /* in [0, 1) */
+    double eps;           /* > 0 */
+    double weight_decay;  /* >= 0 (the recipe uses 0) */
+    int64_t step;         /* t >= 1, for the bias corrections */
+} pq_adamw;
+
+/* One matrix of a fused step (grouped launches, as pq_mat). */
+typedef struct pq_step_mat {
+    float *W;             /* in/out [rows, cols] fp32 shadow weights        */
+    float *alpha;         /* in/out [rows] fp32 scale                       */
+    const void *G;        /* in [rows, cols] dL/dWq (dtype per call)        */
+    float *mW;            /* in/out [rows, cols] first moment of W          */
+    float *vW;            /* in/out [rows, cols] second moment of W         */
+    float *m_alpha;       /* in/out [rows] first moment of alpha            */
+    float *v_alpha;       /* in/out [rows] second moment of alpha           */
+    void *wq_bf16;        /* out [rows, cols] next forward's bf16, or NULL  */
+    uint8_t *codes;       /* out [rows, pq_code_row_bytes] codes, or NULL   */
+    float *dalpha;        /* out [rows] this step's alpha gradient, or NULL */
+    double grad_scale;    /* the alpha-gradient scale, as pq_quantize_bwd   */
+    int64_t rows;
+    int64_t cols;         /* positive multiple of 8                         */
+} pq_step_mat;
+
+/*
+ * pq_qat_step -- the fused step on one matrix.  W, alpha and the four moment
+ * arrays are updated in place; G is read only.  Wq_bf16, codes and dalpha
+ * are optional outputs (NULL skips them).  hp is a host pointer read during
+ * the call.  Errors as the other entry points; hp NULL -> PQ_ERR_NULL; a
+ * hyper-parameter out of its range (or a non-finite one), or a non-finite
+ * grad_scale -> PQ_ERR_ARG.  Weights, moments and gradients must be finite.
+ */
+pq_status pq_qat_step(int mode, int64_t rows, int64_t cols, float *W, float *alpha,
+                      const void *G, int g_dtype, double grad_scale, float *mW, float *vW,
+                      float *m_alpha, float *v_alpha, const pq_adamw *hp, void *Wq_bf16,
+                      uint8_t *codes, float *dalpha, void *stream);
+
+/* The fused step over `count` matrices in one launch; per matrix exactly
+ * pq_qat_step.  descs_host / descs_dev: identical pq_step_mat[count] in host
+ * / device memory; every entry must use the same set of optional outputs. */
+pq_status pq_qat_step_grouped(int mode, int count, const pq_step_mat *descs_host,
+                              const pq_step_mat *descs_dev, int g_dtype, const pq_adamw *hp,
+                              void *stream);
+
 #ifdef __cplusplus
 }
 #endif

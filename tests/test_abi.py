@@ -32,6 +32,8 @@ def test_every_declared_symbol_is_exported(pq):
 
 def test_struct_layout(pq):
     assert ctypes.sizeof(pq.pq_mat) == 96
+    assert ctypes.sizeof(pq.pq_step_mat) == 104
+    assert ctypes.sizeof(pq.pq_adamw) == 48
 
 
 def test_helpers(pq):
@@ -131,3 +133,45 @@ def test_grouped_argument_checks(pq):
     assert L.pq_quantize_fwd_grouped(2, -1, h, A, 0, None) == 7
     assert L.pq_quantize_fwd_grouped(2, 0, None, None, 0, None) == 0              # empty stack
     assert L.pq_quantize_bwd_grouped(2, 2, h, A, 0, None) == 1                    # G NULL
+
+
+def test_qat_step_argument_checks(pq):
+    L = pq.lib
+    hp = pq.adamw_params(1)
+    H = ctypes.addressof(hp)
+    ok = [2, 4, 64, A, B, A, 0, 1.0, A, B, A, B, H, None, None, None, None]
+    args = list(ok)
+    args[12] = None
+    assert L.pq_qat_step(*args) == 1                                              # hp NULL
+    args = list(ok)
+    args[8] = None
+    assert L.pq_qat_step(*args) == 1                                              # mW NULL
+    args = list(ok)
+    args[2] = 60
+    assert L.pq_qat_step(*args) == 2                                              # cols % 8
+    args = list(ok)
+    args[0] = 7
+    assert L.pq_qat_step(*args) == 3                                              # mode
+    args = list(ok)
+    args[9] = MIS
+    assert L.pq_qat_step(*args) == 4                                              # vW aligned
+    args = list(ok)
+    args[7] = float("nan")
+    assert L.pq_qat_step(*args) == 7                                              # grad_scale
+    for field, bad in (("step", 0), ("beta1", 1.0), ("beta2", -0.1), ("eps", 0.0), ("lr", float("inf")),
+                       ("weight_decay", -1.0)):
+        h2 = pq.adamw_params(1)
+        setattr(h2, field, bad)
+        args = list(ok)
+        args[12] = ctypes.addressof(h2)
+        assert L.pq_qat_step(*args) == 7, field
+    args = list(ok)
+    args[1] = 0
+    assert L.pq_qat_step(*args) == 0                                              # empty
+    mats = (pq.pq_step_mat * 2)()
+    for m in mats:
+        m.W, m.alpha, m.G, m.mW, m.vW, m.m_alpha, m.v_alpha = A, B, A, B, A, B, A
+        m.rows, m.cols, m.grad_scale = 4, 64, 1.0
+    mats[1].codes = B
+    assert L.pq_qat_step_grouped(2, 2, ctypes.addressof(mats), A, 0, H, None) == 7  # mixed outputs
+    assert L.pq_qat_step_grouped(2, 0, None, None, 0, H, None) == 0                # empty stack

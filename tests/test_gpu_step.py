@@ -1,0 +1,178 @@
+"""GPU parity of the fused QAT step (backward, AdamW on W and alpha, next
+forward) against the CPU oracle, through the C ABI.
+
+Bar: the updated weights and moments of W bit-exact (they depend on dW only);
+dalpha within rel 1e-5 (binary64 sums in different orders); wherever the two
+dalpha agree bit for bit (every row of these inputs, in practice) the updated
+alpha, its moments, the next forward's bf16 weights and its codes are
+bit-exact too.  A row whose dalpha differs in the last bit may differ there
+by one rounding, so for such a row alpha is held to 2 ulps and its
+downstream outputs are not compared.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from bit_quantization_aware_amd import synth
+
+from gpu_util import assert_bits_equal, assert_rel, dev, empty_bf16, host
+
+pytestmark = pytest.mark.gpu
+
+pq = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    global pq
+    from bit_quantization_aware_amd import pq as _pq
+    pq = _pq
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    O.set_threads(16)
+    yield
+
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+
+
+def make_state(seed, rows, cols, mode, zero_moments=False):
+    rng = np.random.default_rng(seed)
+    W = synth.normal_f32(rng, (rows, cols), 0.02)
+    alpha = O.alpha_init(mode, W) * np.float32(0.8)
+    G = synth.normal_f32(rng, (rows, cols))
+    if zero_moments:
+        mW, vW = np.zeros((rows, cols), np.float32), np.zeros((rows, cols), np.float32)
+        ma, va = np.zeros(rows, np.float32), np.zeros(rows, np.float32)
+    else:
+        mW = synth.normal_f32(rng, (rows, cols), 1e-3)
+        vW = np.abs(synth.normal_f32(rng, (rows, cols), 1e-6))
+        ma = synth.normal_f32(rng, (rows,), 1e-4)
+        va = np.abs(synth.normal_f32(rng, (rows,), 1e-8))
+    return dict(W=W, alpha=alpha, G=G, mW=mW, vW=vW, m_alpha=ma, v_alpha=va)
+
+
+def gpu_step(mode, st, step, g_bf16=False, outputs=True, hp=HP):
+    rows, cols = st["W"].shape
+    d = {k: dev(v) for k, v in st.items() if k != "G"}
+    G = dev(synth.to_bf16_bits(st["G"]) if g_bf16 else st["G"])
+    wq = empty_bf16(rows, cols) if outputs else None
+    codes = (torch.empty(rows, pq.pq_code_row_bytes(mode, cols), dtype=torch.uint8, device="cuda")
+             if outputs else None)
+    da = torch.empty(rows, dtype=torch.float32, device="cuda") if outputs else None
+    pq.pq_qat_step(mode, rows, cols, d["W"], d["alpha"], G, pq.PQ_G_BF16 if g_bf16 else pq.PQ_G_F32,
+                   O.default_grad_scale(mode, rows, cols), d["mW"], d["vW"], d["m_alpha"], d["v_alpha"],
+                   pq.adamw_params(step, **hp), wq, codes, da)
+    torch.cuda.synchronize()
+    out = {k: host(v) for k, v in d.items()}
+    if outputs:
+        out.update(wq_bf16=host(wq), codes=host(codes), dalpha=host(da))
+    return out
+
+
+def check_step(mode, got, want, what, outputs=True):
+    for k in ("W", "mW", "vW"):
+        assert_bits_equal(got[k], want[k], f"{what} {k}")
+    same = np.ones(got["W"].shape[0], bool)
+    if outputs:
+        assert_rel(got["dalpha"], want["dalpha"], 1e-5, np.float64(1e-35), f"{what} dalpha")
+        same = got["dalpha"].view(np.uint32) == want["dalpha"].view(np.uint32)
+        assert same.mean() > 0.99, f"{what}: dalpha differs in {np.count_nonzero(~same)} rows"
+    for k in ("alpha", "m_alpha", "v_alpha"):
+        assert_bits_equal(got[k][same], want[k][same], f"{what} {k}")
+    a_g, a_o = got["alpha"][~same], want["alpha"][~same]
+    assert np.all(np.abs(a_g - a_o) <= 2 * np.spacing(np.abs(a_o))), f"{what} alpha (dalpha 1 ulp off)"
+    if outputs:
+        assert_bits_equal(got["wq_bf16"][same], want["wq_bf16"][same], f"{what} wq_bf16")
+        assert_bits_equal(got["codes"][same], want["codes"][same], f"{what} codes")
+
+
+def oracle_step(mode, st, step, g_bf16=False, hp=HP):
+    G = synth.to_bf16_bits(st["G"]) if g_bf16 else st["G"]
+    return O.qat_step(mode, st["W"], st["alpha"], G, st["mW"], st["vW"], st["m_alpha"], st["v_alpha"],
+                      step, **hp)
+
+
+MODES = [O.BINARY, O.TERNARY, O.SEQ2, O.LSQ3, O.LSQ4]
+SHAPES = [(256, 256), (37, 72), (5, 8), (3, 1600), (1, 16384), (4100, 24), (70, 4352)]
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("shape", SHAPES)
+def test_qat_step_parity(mode, shape):
+    rows, cols = shape
+    print(f"[qat step mode={mode} shape={shape}]", flush=True)
+    st = make_state(2000 + rows + cols + mode, rows, cols, mode)
+    check_step(mode, gpu_step(mode, st, 3), oracle_step(mode, st, 3), f"m{mode} {shape}")
+
+
+@pytest.mark.parametrize("mode", [O.SEQ2, O.LSQ4])
+def test_qat_step_bf16_gradient(mode):
+    st = make_state(2100 + mode, 96, 520, mode)
+    check_step(mode, gpu_step(mode, st, 5, g_bf16=True), oracle_step(mode, st, 5, g_bf16=True), "bf16 G")
+
+
+def test_qat_step_first_step_and_chained_steps():
+    """Step 1 from zero moments, then two more steps carrying the state:
+    the GPU's own outputs feed its next step, the oracle's feed the oracle's."""
+    mode = O.SEQ2
+    st_g = make_state(2200, 64, 1536, mode, zero_moments=True)
+    st_o = {k: v.copy() for k, v in st_g.items()}
+    rng = np.random.default_rng(2201)
+    for t in (1, 2, 3):
+        got = gpu_step(mode, st_g, t)
+        want = oracle_step(mode, st_o, t)
+        check_step(mode, got, want, f"step {t}")
+        G = synth.normal_f32(rng, st_g["W"].shape)
+        for k in ("W", "alpha", "mW", "vW", "m_alpha", "v_alpha"):
+            st_g[k], st_o[k] = got[k], want[k]
+        st_g["G"], st_o["G"] = G, G
+
+
+def test_qat_step_without_outputs():
+    mode = O.TERNARY
+    st = make_state(2300, 33, 200, mode)
+    want = oracle_step(mode, st, 2)
+    check_step(mode, gpu_step(mode, st, 2, outputs=False), want, "no outputs", outputs=False)
+
+
+def test_qat_step_weight_decay_only():
+    """lr > 0 with all-zero gradients and moments: W and alpha shrink by the
+    decoupled decay factor alone (the Adam term is 0 / eps = 0)."""
+    mode = O.SEQ2
+    st = make_state(2400, 16, 64, mode, zero_moments=True)
+    st["G"] = np.zeros_like(st["G"])
+    hp = dict(lr=0.1, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.5)
+    got = gpu_step(mode, st, 1, hp=hp)
+    want = oracle_step(mode, st, 1, hp=hp)
+    check_step(mode, got, want, "decay only")
+    assert_bits_equal(got["W"], (st["W"] * np.float32(1 - 0.1 * 0.5)).astype(np.float32), "W * decay")
+
+
+def test_qat_step_grouped_mobilellm_layers():
+    """The grouped launch over the seven matrices of MobileLLM-125M layers 0
+    and 29 (576- and 1536-wide rows), step 1 from zero moments."""
+    mode = O.SEQ2
+    shapes = synth.mobilellm_125m_shapes()
+    ks = [k for k, (l, _, _, _) in enumerate(shapes) if l in (0, 29)]
+    mats, states = [], []
+    for k in ks:
+        W = synth.weight("mobilellm_125m", k)
+        rows, cols = W.shape
+        st = dict(W=W, alpha=O.alpha_init(mode, W), G=synth.upstream_grad("mobilellm_125m", k),
+                  mW=np.zeros_like(W), vW=np.zeros_like(W), m_alpha=np.zeros(rows, np.float32),
+                  v_alpha=np.zeros(rows, np.float32))
+        states.append(st)
+        d = {n: dev(v) for n, v in st.items()}
+        d.update(wq_bf16=empty_bf16(rows, cols),
+                 codes=torch.empty(rows, cols // 4, dtype=torch.uint8, device="cuda"),
+                 dalpha=torch.empty(rows, dtype=torch.float32, device="cuda"),
+                 grad_scale=O.default_grad_scale(mode, rows, cols), rows=rows, cols=cols)
+        mats.append(d)
+    table = pq.StepTable(mats)
+    pq.pq_qat_step_grouped(mode, table, pq.adamw_params(1, **HP))
+    torch.cuda.synchronize()
+    for i, (d, st) in enumerate(zip(mats, states)):
+        got = {k: host(d[k]) for k in ("W", "alpha", "mW", "vW", "m_alpha", "v_alpha", "wq_bf16", "codes",
+                                       "dalpha")}
+        check_step(mode, got, oracle_step(mode, st, 1), f"125M[{ks[i]}]")
