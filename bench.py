@@ -54,6 +54,8 @@ def parse():
     p.add_argument("--no-extras", action="store_true", help="skip sweep / comparison GEMMs")
     p.add_argument("--gemm-b2b-only", action="store_true",
                    help="only the back-to-back GEMM launches (for a kernel trace of them alone)")
+    p.add_argument("--qat-step-only", action="store_true",
+                   help="only the fused QAT step measurement (for a kernel trace of it alone)")
     p.add_argument("--pmc-workload", action="store_true",
                    help="no timing: a 1 GiB copy (counter calibration), then every step kernel "
                         "three times in step order, for rocprofv3 --pmc passes")
@@ -70,6 +72,7 @@ KERNEL_SOURCES = {
     "fwd": ("pq_quant.hip", "pq_common.hpp"),
     "bwd": ("pq_quant.hip", "pq_common.hpp"),
     "pack": ("pq_quant.hip", "pq_common.hpp"),
+    "qat_step": ("pq_quant.hip", "pq_common.hpp"),
 }
 for _m in (1, 4, 16, 64, 512):
     KERNEL_SOURCES[f"gemm_m{_m}"] = ("pq_gemm.hip", "pq_common.hpp")
@@ -109,6 +112,12 @@ def fwd_bytes(rows, cols, cw):
 
 def bwd_bytes(rows, cols):
     return cols * rows * 12 + 8 * rows
+
+
+def step_bytes(rows, cols, cw):
+    """Fused QAT step: W, G, m, v read, W, m, v written, bf16 Wq and codes
+    written; per row alpha and its two moments read and written."""
+    return cols * rows * (16 + 12 + 2 + cw / 8) + 24 * rows
 
 
 def pack_bytes(rows, cols):
@@ -153,8 +162,15 @@ def pmc_summarize(args):
         "gemm_m1": lambda n: re.search(r"k_gemm_stream<2, \d+, \d+, \d+, 1>", n) is not None,
         "gemm_m4": lambda n: re.search(r"k_gemm_stream<2, \d+, \d+, \d+, 2>", n) is not None,
         "gemm_m16": lambda n: re.search(r"k_gemm_stream<2, \d+, \d+, \d+, 8>", n) is not None,
+        "qat_step": lambda n: "k_qat_step<2, 1, false>" in n,
     }
-    cf, cw_ = last(fetch, copy_pred, 3), last(write, copy_pred, 3)
+    # the calibration copies: the three largest copy dispatches (the fused
+    # step measurement also clones tensors)
+    def calib(seq):
+        vals = sorted((v for name, v in seq if copy_pred(name)), reverse=True)
+        return vals[:3] if len(vals) >= 3 else None
+
+    cf, cw_ = calib(fetch), calib(write)
     if not cf or not cw_:
         raise SystemExit("calibration copy dispatches not found")
     fscale = CALIB_BYTES / (np.mean(cf) * 1024.0)
@@ -275,6 +291,10 @@ def main():
 
     kernels = ["fwd", "bwd", "pack"] + [f"gemm_m{M}" for M in GEMM_STEP_ORDER]
 
+    if args.qat_step_only:
+        print(json.dumps({"qat_step": qat_step_measure(torch, pq, stack, ftab, btab, stream)}), flush=True)
+        return
+
     if args.gemm_b2b_only:
         ridge = MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3
         print(json.dumps({"gemm_back_to_back": gemm_back_to_back(torch, pq, Xs, packed, ab16, Ys, stream, ridge)}),
@@ -301,6 +321,8 @@ def main():
                 launches[k]()
             torch.cuda.synchronize()
             print(f"pmc workload: {k} x3", flush=True)
+        qat_step_measure(torch, pq, stack, ftab, btab, stream, reps=3)
+        print("pmc workload: qat_step", flush=True)
         return
 
     def step(it, evs):
@@ -379,6 +401,7 @@ def main():
     roofline["traffic"] = traffic.get(dominant)
     for k in rl:
         rl[k]["traffic"] = traffic.get(k)
+    step_traffic = traffic.get("qat_step")
     roofline["units_per_launch"] = per_launch_units.get(dominant, "one GEMM call")
 
     qt_ms = avg["fwd"] + avg["bwd"]
@@ -412,6 +435,8 @@ def main():
     }
 
     if not args.no_extras:
+        out["qat_step"] = qat_step_measure(torch, pq, stack, ftab, btab, stream)
+        out["qat_step"]["traffic"] = step_traffic
         out["gemm_back_to_back"] = gemm_back_to_back(torch, pq, Xs, packed, ab16, Ys, stream, ridge)
         out["sweep_bits"] = sweep_bits(torch, pq, stack, make_tables, stream)
         out["gemm_compare"] = gemm_compare(torch, pq, W16, a16, Xs, stream)
@@ -432,6 +457,52 @@ def time_it(torch, stream, fn, reps):
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
     return float(np.mean([evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]))
+
+
+def qat_step_measure(torch, pq, stack, ftab, btab, stream, reps=10):
+    """The fused QAT step (backward, AdamW on W and alpha, next forward) over
+    the 2-bit stack in one grouped launch, against the same work unfused:
+    this library's backward and forward launches with torch's fused AdamW
+    in between (on the dW and dalpha the backward wrote)."""
+    mode = pq.PQ_W2_SEQ
+    dev = stack[0]["W"].device
+    mats = []
+    for m in stack:
+        r, c = m["rows"], m["cols"]
+        mats.append(dict(W=m["W"].clone(), alpha=m["alpha"].clone(), G=m["G"],
+                         mW=torch.zeros(r, c, device=dev), vW=torch.zeros(r, c, device=dev),
+                         m_alpha=torch.zeros(r, device=dev), v_alpha=torch.zeros(r, device=dev),
+                         wq_bf16=m["wq_bf16"], codes=m["codes"], grad_scale=m["grad_scale"], rows=r, cols=c))
+    table = pq.StepTable(mats)
+    hps = [pq.adamw_params(t + 1) for t in range(reps + 1)]
+    pq.pq_qat_step_grouped(mode, table, hps[0])
+    fused = time_it(torch, stream, lambda i: pq.pq_qat_step_grouped(mode, table, hps[i]), reps)
+    sb = sum(step_bytes(m["rows"], m["cols"], pq.CODE_BITS[mode]) for m in stack)
+    gbs = sb / fused / 1e6
+
+    # unfused: backward (dW, dalpha) -> torch AdamW -> forward
+    params = [m["W"] for m in mats] + [m["alpha"] for m in mats]
+    for m, s_ in zip(mats, stack):
+        m["W"].grad = s_["dW"]
+        m["alpha"].grad = s_["dalpha"]
+    try:
+        opt = torch.optim.AdamW(params, lr=2e-5, weight_decay=0.0, fused=True)
+        kind = "torch.optim.AdamW(fused=True)"
+    except (RuntimeError, TypeError):
+        opt = torch.optim.AdamW(params, lr=2e-5, weight_decay=0.0, foreach=True)
+        kind = "torch.optim.AdamW(foreach=True)"
+    opt.step()
+    bwd = time_it(torch, stream, lambda i: pq.pq_quantize_bwd_grouped(mode, btab, pq.PQ_G_F32), reps)
+    adam = time_it(torch, stream, lambda i: opt.step(), reps)
+    fwd = time_it(torch, stream, lambda i: pq.pq_quantize_fwd_grouped(mode, ftab, 0), reps)
+    for p_ in params:
+        p_.grad = None
+    del opt, table, mats
+    return dict(ms=round(fused, 4), bytes=int(sb), achieved_GBs=round(gbs, 1), peak_GBs=HBM_PEAK_GBS,
+                frac=round(gbs / HBM_PEAK_GBS, 4), bytes_per_weight=30.25,
+                unfused=dict(bwd_ms=round(bwd, 4), adamw_ms=round(adam, 4), fwd_ms=round(fwd, 4),
+                             total_ms=round(bwd + adam + fwd, 4), adamw=kind, bytes_per_weight=46.25),
+                speedup_vs_unfused=round((bwd + adam + fwd) / fused, 3))
 
 
 def gemm_back_to_back(torch, pq, Xs, packed, ab16, Ys, stream, ridge, reps=40):
