@@ -405,14 +405,21 @@ int pqo_quantize_bwd(int mode, int64_t rows, int64_t cols, const float *W,
 }
 
 /* ---------------------------------------------------------------------------
- * Export: the codes the forward emits for W (2-bit SEQ or 4-bit LSQ) and the
- * per-row scale rounded to bf16.  Memory savings exist only after such an
- * export ([Note] "Paper vs. code", last bullet).
+ * Export: the codes the forward emits for W and the per-row scale rounded to
+ * bf16.  Memory savings exist only after such an export ([Note] "Paper vs.
+ * code", last bullet).  Widths with a 2-bit container (ternary, 2-bit SEQ;
+ * ternary is commonly held in 2-bit integers, [News] storage paragraph) or a
+ * 4-bit one (3- and 4-bit LSQ).
  * ------------------------------------------------------------------------- */
+static int deployable(int mode)
+{
+    return mode == PQO_W158_SEQ_TERNARY || mode == PQO_W2_SEQ || mode == PQO_W3_LSQ || mode == PQO_W4_LSQ;
+}
+
 int pqo_pack(int mode, int64_t rows, int64_t cols, const float *W, const float *alpha,
              uint8_t *packed, uint16_t *alpha_bf16)
 {
-    if (mode != PQO_W2_SEQ && mode != PQO_W4_LSQ) return -1;
+    if (!deployable(mode)) return -1;
     if (pqo_quantize_fwd(mode, rows, cols, W, alpha, NULL, NULL, packed) != 0) return -1;
     if (alpha_bf16)
         for (int64_t i = 0; i < rows; ++i) alpha_bf16[i] = pqo_bf16_rne(alpha[i]);
@@ -579,7 +586,7 @@ static double gemm_one(int mode, int64_t K, const uint16_t *xrow, const uint8_t 
 int pqo_gemm_ref(int mode, int64_t M, int64_t N, int64_t K, const uint16_t *X,
                  const uint8_t *packed, const uint16_t *alpha_bf16, double *Y)
 {
-    if (mode != PQO_W2_SEQ && mode != PQO_W4_LSQ) return -1;
+    if (!deployable(mode)) return -1;
     const int64_t rb = pqo_code_row_bytes(mode, K);
 #pragma omp parallel for schedule(static) collapse(2)
     for (int64_t m = 0; m < M; ++m)
@@ -593,7 +600,7 @@ int pqo_gemm_ref_at(int mode, int64_t M, int64_t N, int64_t K, const uint16_t *X
                     const uint8_t *packed, const uint16_t *alpha_bf16,
                     const int64_t *ms, const int64_t *ns, int64_t count, double *out)
 {
-    if (mode != PQO_W2_SEQ && mode != PQO_W4_LSQ) return -1;
+    if (!deployable(mode)) return -1;
     const int64_t rb = pqo_code_row_bytes(mode, K);
     for (int64_t t = 0; t < count; ++t)
         if (ms[t] < 0 || ms[t] >= M || ns[t] < 0 || ns[t] >= N) return -1;

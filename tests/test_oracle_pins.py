@@ -425,7 +425,7 @@ def test_pack_byte_layout_lsb_first():
     assert p4.tolist() == [[0xF0, 0x98]]
 
 
-@pytest.mark.parametrize("mode", [O.SEQ2, O.LSQ4])
+@pytest.mark.parametrize("mode", [O.SEQ2, O.LSQ4, O.TERNARY, O.LSQ3])
 def test_gemm_ref_is_matmul_of_dequantized_weight(mode):
     rng = np.random.default_rng(50)
     M, N, K = 5, 24, 64
@@ -434,7 +434,8 @@ def test_gemm_ref_is_matmul_of_dequantized_weight(mode):
     packed, ab = O.pack(mode, W, alpha)
     X = synth.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
     Y = O.gemm_ref(mode, X, packed, ab, N)
-    lev = {O.SEQ2: lambda c: (c - 1.5) / 2.0, O.LSQ4: lambda c: c - 8.0}[mode]
+    lev = {O.SEQ2: lambda c: (c - 1.5) / 2.0, O.LSQ4: lambda c: c - 8.0,
+           O.TERNARY: lambda c: (c - 1.0) * np.float64(np.float32(2.0 / 3.0)), O.LSQ3: lambda c: c - 4.0}[mode]
     Wd = lev(unpack_codes(packed, mode, K).astype(np.float64)) * \
         synth.bf16_bits_to_f32(ab).astype(np.float64)[:, None]
     want = np.matmul(synth.bf16_bits_to_f32(X).astype(np.float64), Wd.T)
