@@ -12,25 +12,22 @@
 //
 // Design (gfx950, 64-wide waves, bf16 MFMA 16x16x32):
 //  * The contraction runs on MFMA in bf16 with fp32 accumulation.  Weights
-//    reach the MFMA B operand straight from packed codes, decoded in
-//    registers.  2-bit codes use gfx950's fp4 -> bf16 pair convert
-//    (v_cvt_scalef32_pk_bf16_fp4, scale 1): after masking, a nibble 0..3
-//    reads as the fp4 value c/2, so level = (c - 1.5)/2 = c/2 - 0.75; the
-//    kernel accumulates X.(c/2) on MFMA and subtracts 0.75 * rowsum(X) in
-//    the epilogue.  4-bit codes use the bf16 mantissa: 0x4000 | c << 3 is
-//    2 + c/8, so level = c - 8 = 8 * (v - 3).
-//  * A dword of codes holds 16 (2-bit) or 8 (4-bit) consecutive k.  The
-//    2-bit convert reads nibbles, so d & 0x33333333 and (d >> 2) & 0x33333333
-//    give the pairs (4b, 4b+2) and (4b+1, 4b+3) of byte b; 4-bit codes pair
-//    (i, i+4).  The MFMA sums over k in any order as long as A and B agree,
-//    so X is staged in that same order (a fixed permutation inside each 16-
-//    or 8-wide k block), and the A operand is a contiguous 16-byte LDS read.
-//  * X tiles go global -> registers -> LDS (padded rows, no bank conflicts),
-//    one stage ahead of the MFMA work; code tiles go global -> registers,
-//    one stage ahead.  The X row sums are taken while staging.
-//  * Tile shapes: see the streaming kernel below for M <= 16; the tiled
-//    kernel covers larger M (MFMA-bound), with wide column tiles so the
-//    activations are re-read from L2 as few times as possible.
+//    reach the MFMA B (or A) operand straight from packed codes, decoded in
+//    registers into an exact bf16 value v; every width's level is affine in
+//    the code, level = step * (c - zc), so the kernels accumulate X.v and the
+//    epilogue applies level = mul * (v - off) with the X row sums:
+//      2-bit container (2-bit SEQ, ternary): gfx950's fp4 -> bf16 pair
+//        convert (v_cvt_scalef32_pk_bf16_fp4, scale 1) reads a masked nibble
+//        0..3 as the fp4 value v = c/2; SEQ levels (c - 1.5)/2 give off =
+//        0.75, mul = 1; ternary levels (c - 1) * 2/3 give off = 0.5, mul =
+//        2 * 2/3.
+//      4-bit container (4- and 3-bit LSQ): v = 128 + c (streaming kernel) or
+//        v = 2 + c/8 (tiled kernel) from the bf16 mantissa; level = c - 8
+//        (c - 4 at 3 bits).
+//  * The weights are read in the export byte order (1-KB tiles of 16 rows x
+//    64 code bytes, group-major) with the LDS-DMA load; the streaming kernel
+//    (M <= 16) reads them exactly once, the tiled kernel (M > 16) once per
+//    64-row tile of activations.  See each kernel below.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -122,6 +119,7 @@ struct GemmArgs {
     uint16_t *Y;             // [M, N] bf16
     int M, N, K;
     int64_t gstride;         // bytes per 64-byte group of all rows (Np * 64)
+    float off, mul;          // level = mul * (v - off) for the decoded operand v
 };
 
 // ---------------------------------------------------------------------------
@@ -182,6 +180,7 @@ struct TileArgs {
     int mtiles, ntiles, splits;
     int kps;                 // k per split, a multiple of the 64-byte group
     int64_t gstride;         // bytes per 64-byte group of all rows
+    float off, mul;          // level = mul * (v - off) for the decoded operand v
 };
 
 // Activation LDS swizzle: chunk c of tile row r sits in slot c ^ xswz(r).
@@ -511,8 +510,6 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
 
     // Epilogue: acc[i][j][e] is row m0 + 16 * ((i + w) & 3) + i16, column
     // n0 + 64w + 16j + 4grp + e.
-    constexpr float kOff = BITS == 2 ? 0.75f : 3.0f;
-    constexpr float kMul = BITS == 2 ? 1.0f : 8.0f;
     const bool vec = (N & 3) == 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -528,10 +525,10 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
             const int rl = 16 * ((i + w) & 3) + i16;
             const int m = m0 + rl;
             if (m >= M) continue;
-            const float sr = kOff * ssum[rl];
+            const float sr = g.off * ssum[rl];
             float v[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = kMul * (acc[i][j][e] - sr);
+            for (int e = 0; e < 4; ++e) v[e] = g.mul * (acc[i][j][e] - sr);
             const int64_t o = static_cast<int64_t>(m) * N + n;
             if (g.splits == 1) {
                 if (vec) {
@@ -836,7 +833,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
                         a += red[(v * NACC + 4 * j + e) * 64 + lane];
                         sm += rsum[v][m];
                     }
-                    const float y = BITS == 2 ? al * (a - 0.75f * sm) : al * (a - 136.0f * sm);
+                    const float y = al * (g.mul * (a - g.off * sm));
                     const __bf16 h = static_cast<__bf16>(y);
                     g.Y[static_cast<int64_t>(m) * N + n] = __builtin_bit_cast(uint16_t, h);
                 }
@@ -916,8 +913,11 @@ pq_status launch_tile(const GemmArgs &a, hipStream_t s)
     // stages per split: whole 64-byte groups, so every split starts a group
     const int sps = ((stages + splits - 1) / splits + C::SS - 1) / C::SS * C::SS;
     splits = (stages + sps - 1) / sps;
+    // the tile kernel's 4-bit operand is 2 + c/8 (the stream kernel's 128 + c)
+    const float off = BITS == 2 ? a.off : 2.0f + (a.off - 128.0f) / 8.0f;
+    const float mul = BITS == 2 ? a.mul : 8.0f * a.mul;
     TileArgs t{a.X, a.packed, a.alpha, a.Y, nullptr, a.M, a.N, a.K, mtiles, ntiles, splits, sps * kStageK,
-               a.gstride};
+               a.gstride, off, mul};
     const int64_t total = static_cast<int64_t>(a.M) * a.N;
     if (splits > 1) {
         pq_status st = workspace(s, static_cast<size_t>(splits) * total * sizeof(float), &t.ws);
@@ -935,9 +935,27 @@ pq_status launch_tile(const GemmArgs &a, hipStream_t s)
     return PQ_OK;
 }
 
+// Level of a stored code as level = step * (c - zc): the code of level 0
+// and the step between levels, per width ([Note] "Finding 3" level sets).
+struct LevelMap {
+    int bits;
+    float zc, step;
+};
+
+bool level_map(int mode, LevelMap *lm)
+{
+    switch (mode) {
+    case PQ_W158_SEQ_TERNARY: *lm = {2, 1.0f, static_cast<float>(2.0 / 3.0)}; return true;
+    case PQ_W2_SEQ: *lm = {2, 1.5f, 0.5f}; return true;
+    case PQ_W3_LSQ: *lm = {4, 4.0f, 1.0f}; return true;
+    case PQ_W4_LSQ: *lm = {4, 8.0f, 1.0f}; return true;
+    default: return false;
+    }
+}
+
 template <int BITS>
 pq_status gemm(int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *packed,
-               const void *alpha_bf16, void *Y, void *stream)
+               const void *alpha_bf16, void *Y, void *stream, const LevelMap &lm)
 {
     if (!X || !packed || !alpha_bf16 || !Y) return PQ_ERR_NULL;
     if (M < 0 || N < 0 || K <= 0 || K % 64 != 0 || K > kMaxGemmK || M > INT32_MAX / 2 || N > kMaxGemmN)
@@ -947,7 +965,9 @@ pq_status gemm(int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *pa
     if (M == 0 || N == 0) return PQ_OK;
     GemmArgs a{static_cast<const uint16_t *>(X), packed, static_cast<const uint16_t *>(alpha_bf16),
                static_cast<uint16_t *>(Y), static_cast<int>(M), static_cast<int>(N), static_cast<int>(K),
-               (N + 15) / 16 * 16 * 64};
+               (N + 15) / 16 * 16 * 64,
+               // the stream kernel's operand: c / 2 (2 bits), 128 + c (4 bits); all exact
+               BITS == 2 ? lm.zc / 2.0f : 128.0f + lm.zc, BITS == 2 ? 2.0f * lm.step : lm.step};
     hipStream_t s = static_cast<hipStream_t>(stream);
     constexpr int GK = BITS == 2 ? 256 : 128;
     constexpr int RPL = 512 / GK;
@@ -968,16 +988,25 @@ pq_status gemm(int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *pa
 
 extern "C" {
 
+pq_status pq_gemm(int mode, int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *packed,
+                  const void *alpha_bf16, void *Y, void *stream)
+{
+    pq::LevelMap lm;
+    if (!pq::level_map(mode, &lm)) return PQ_ERR_MODE;
+    if (lm.bits == 2) return pq::gemm<2>(M, N, K, X, packed, alpha_bf16, Y, stream, lm);
+    return pq::gemm<4>(M, N, K, X, packed, alpha_bf16, Y, stream, lm);
+}
+
 pq_status pq_w2a16_gemm(int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *packed,
                         const void *alpha_bf16, void *Y, void *stream)
 {
-    return pq::gemm<2>(M, N, K, X, packed, alpha_bf16, Y, stream);
+    return pq_gemm(PQ_W2_SEQ, M, N, K, X, packed, alpha_bf16, Y, stream);
 }
 
 pq_status pq_w4a16_gemm(int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *packed,
                         const void *alpha_bf16, void *Y, void *stream)
 {
-    return pq::gemm<4>(M, N, K, X, packed, alpha_bf16, Y, stream);
+    return pq_gemm(PQ_W4_LSQ, M, N, K, X, packed, alpha_bf16, Y, stream);
 }
 
 }  // extern "C"

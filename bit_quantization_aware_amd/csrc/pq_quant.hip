@@ -905,6 +905,13 @@ void launch_step(int mode, int wpr, bool gbf, const StepTable &lt, int blocks, c
 
 bool finite(double x) { return x == x && x < 1e300 && x > -1e300; }
 
+// Widths with a deployment format: a 2-bit (ternary, 2-bit SEQ) or 4-bit (3-
+// and 4-bit LSQ) code container.
+bool deployable(int mode)
+{
+    return mode == PQ_W158_SEQ_TERNARY || mode == PQ_W2_SEQ || mode == PQ_W3_LSQ || mode == PQ_W4_LSQ;
+}
+
 // AdamW scalars: binary64 from the hyper-parameters, rounded once.
 pq_status adam_scalars(const pq_adamw *hp, AdamK *k)
 {
@@ -970,7 +977,7 @@ int64_t pq_code_row_bytes(int mode, int64_t cols)
 
 int64_t pq_packed_bytes(int mode, int64_t rows, int64_t cols)
 {
-    if ((mode != PQ_W2_SEQ && mode != PQ_W4_LSQ) || rows < 0 || !valid_cols(cols)) return -1;
+    if (!deployable(mode) || rows < 0 || !valid_cols(cols)) return -1;
     const int64_t rb = cols * code_bits(mode) / 8;
     return (rb + 63) / 64 * ((rows + 15) / 16 * 16) * 64;
 }
@@ -1078,6 +1085,7 @@ pq_status pq_quantize_bwd(int mode, int64_t rows, int64_t cols, const float *W, 
 static pq_status pack_common(int mode, int64_t rows, int64_t cols, const float *W,
                              const float *alpha, uint8_t *packed, void *alpha_bf16, void *stream)
 {
+    if (!deployable(mode)) return PQ_ERR_MODE;
     if (!W || !alpha || !packed || !alpha_bf16) return PQ_ERR_NULL;
     if (rows < 0 || !valid_cols(cols)) return PQ_ERR_SHAPE;
     if (!aligned16(W) || !aligned16(alpha) || !aligned16(packed) || !aligned16(alpha_bf16))
@@ -1102,11 +1110,20 @@ static pq_status pack_common(int mode, int64_t rows, int64_t cols, const float *
     lt.block_start[1] = static_cast<int32_t>(blocks);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     constexpr unsigned O = OUT_CODES | OUT_TILED | OUT_ALPHA_BF16;
-    if (mode == PQ_W2_SEQ)
-        launch_fwd_t<PQ_W2_SEQ, false, O>(lt, static_cast<int>(blocks), wpr, s, alpha_bf16);
-    else
-        launch_fwd_t<PQ_W4_LSQ, false, O>(lt, static_cast<int>(blocks), wpr, s, alpha_bf16);
+    const int nb = static_cast<int>(blocks);
+    switch (mode) {
+    case PQ_W158_SEQ_TERNARY: launch_fwd_t<PQ_W158_SEQ_TERNARY, false, O>(lt, nb, wpr, s, alpha_bf16); break;
+    case PQ_W2_SEQ: launch_fwd_t<PQ_W2_SEQ, false, O>(lt, nb, wpr, s, alpha_bf16); break;
+    case PQ_W3_LSQ: launch_fwd_t<PQ_W3_LSQ, false, O>(lt, nb, wpr, s, alpha_bf16); break;
+    default: launch_fwd_t<PQ_W4_LSQ, false, O>(lt, nb, wpr, s, alpha_bf16); break;
+    }
     return hipGetLastError() == hipSuccess ? PQ_OK : PQ_ERR_HIP;
+}
+
+pq_status pq_pack(int mode, int64_t rows, int64_t cols, const float *W, const float *alpha, uint8_t *packed,
+                  void *alpha_bf16, void *stream)
+{
+    return pack_common(mode, rows, cols, W, alpha, packed, alpha_bf16, stream);
 }
 
 pq_status pq_pack_w2(int64_t rows, int64_t cols, const float *W, const float *alpha,

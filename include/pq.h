@@ -189,6 +189,11 @@ pq_status pq_quantize_bwd(int mode, int64_t rows, int64_t cols, const float *W,
  */
 int64_t pq_packed_bytes(int mode, int64_t rows, int64_t cols);
 
+/* Widths with a deployment format ("deployable" below): PQ_W158_SEQ_TERNARY
+ * and PQ_W2_SEQ in a 2-bit container, PQ_W3_LSQ and PQ_W4_LSQ in a 4-bit one
+ * (ternary is commonly held in 2-bit integers, [News] storage paragraph).
+ * pq_packed_bytes returns -1 for any other mode. */
+
 /*
  * pq_pack_w2 -- export a 2-bit SEQ layer for deployment: the forward's codes
  * (the bytes of pq_quantize_fwd(PQ_W2_SEQ, ...) codes, bit for bit) in the
@@ -203,6 +208,13 @@ int64_t pq_packed_bytes(int mode, int64_t rows, int64_t cols);
  */
 pq_status pq_pack_w2(int64_t rows, int64_t cols, const float *W, const float *alpha,
                      uint8_t *packed, void *alpha_bf16, void *stream);
+
+/* pq_pack -- the export of any deployable width (the same contract as
+ * pq_pack_w2, with the width's code container); an other mode ->
+ * PQ_ERR_MODE.  pq_pack_w2 is pq_pack(PQ_W2_SEQ, ...), pq_pack_w4
+ * pq_pack(PQ_W4_LSQ, ...). */
+pq_status pq_pack(int mode, int64_t rows, int64_t cols, const float *W, const float *alpha,
+                  uint8_t *packed, void *alpha_bf16, void *stream);
 
 /* pq_pack_w4 -- the 4-bit LSQ counterpart of pq_pack_w2 (two codes per byte,
  * low nibble first; pq_packed_bytes(PQ_W4_LSQ, rows, cols) bytes in the
@@ -247,6 +259,14 @@ pq_status pq_w2a16_gemm(int64_t M, int64_t N, int64_t K, const void *X,
 pq_status pq_w4a16_gemm(int64_t M, int64_t N, int64_t K, const void *X,
                         const uint8_t *packed, const void *alpha_bf16, void *Y,
                         void *stream);
+
+/* pq_gemm -- the same GEMM for any deployable width, on pq_pack(mode, ...)
+ * weights, with the width's levels ([Note] "Finding 3"): ternary
+ * (c - 1) * fl32(2/3), 2-bit SEQ (c - 1.5) / 2, 3-bit LSQ c - 4, 4-bit LSQ
+ * c - 8; an other mode -> PQ_ERR_MODE.  These are the widths whose accuracy
+ * and storage the pages compare ([News] speed and storage paragraphs). */
+pq_status pq_gemm(int mode, int64_t M, int64_t N, int64_t K, const void *X,
+                  const uint8_t *packed, const void *alpha_bf16, void *Y, void *stream);
 
 /*
  * Grouped launches: one kernel launch over a whole stack of matrices (for

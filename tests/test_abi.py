@@ -47,6 +47,8 @@ def test_helpers(pq):
     assert pq.pq_packed_bytes(pq.PQ_W4_LSQ, 1, 8) == 16 * 64
     assert pq.pq_packed_bytes(pq.PQ_W2_SEQ, 0, 64) == 0
     assert pq.pq_packed_bytes(pq.PQ_W1_BINARY, 16, 64) == -1
+    assert pq.pq_packed_bytes(pq.PQ_W158_SEQ_TERNARY, 16, 1024) == 16 * 256
+    assert pq.pq_packed_bytes(pq.PQ_W3_LSQ, 16, 1024) == 16 * 512
     assert pq.pq_packed_bytes(pq.PQ_W2_SEQ, 16, 12) == -1
     assert pq.pq_default_grad_scale(pq.PQ_W4_LSQ, 4, 16) == pytest.approx((4 * 16 * 7) ** -0.5)
     assert pq.pq_default_grad_scale(pq.PQ_W2_SEQ, 0, 16) == 0.0
@@ -116,6 +118,10 @@ def test_pack_and_gemm_argument_checks(pq):
     assert L.pq_w2a16_gemm(0, 8, 64, A, A, B, A, None) == 0                       # empty
     assert L.pq_w2a16_gemm(1, (1 << 24) + 16, 64, A, A, B, A, None) == 2          # N bound
     assert L.pq_pack_w2(0, 64, A, A, B, A, None) == 0                             # empty
+    assert L.pq_pack(0, 4, 64, A, A, B, A, None) == 3                             # binary: no container
+    assert L.pq_gemm(0, 4, 8, 64, A, A, B, A, None) == 3
+    assert L.pq_gemm(1, 4, 8, 60, A, A, B, A, None) == 2                          # ternary, K % 64
+    assert L.pq_pack(3, 4, 60, A, A, B, A, None) == 2
 
 
 def test_grouped_argument_checks(pq):

@@ -1,4 +1,4 @@
-"""GPU parity of the packed-weight GEMM (2-bit SEQ and 4-bit LSQ weights,
+"""GPU parity of the packed-weight GEMM (2-bit SEQ, ternary, 3- and 4-bit LSQ weights,
 bf16 activations) against the oracle's binary64 reference, through the C ABI.
 
 Inputs (packed codes, bf16 scales, activations) come from the oracle's own
@@ -41,10 +41,14 @@ def gpu_gemm(mode, X, packed, ab, N):
     the export byte order (the oracle's tile_codes)."""
     M, K = X.shape
     Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-    fn = pq.pq_w2a16_gemm if mode == O.SEQ2 else pq.pq_w4a16_gemm
     tiled = O.tile_codes(packed)
     assert tiled.size == pq.pq_packed_bytes(mode, N, K)
-    fn(M, N, K, dev(X), dev(tiled), dev(ab), Y)
+    if mode == O.SEQ2:
+        pq.pq_w2a16_gemm(M, N, K, dev(X), dev(tiled), dev(ab), Y)
+    elif mode == O.LSQ4:
+        pq.pq_w4a16_gemm(M, N, K, dev(X), dev(tiled), dev(ab), Y)
+    else:
+        pq.pq_gemm(mode, M, N, K, dev(X), dev(tiled), dev(ab), Y)
     torch.cuda.synchronize()
     return synth.bf16_bits_to_f32(host(Y)).astype(np.float64)
 
@@ -66,7 +70,10 @@ def make_case(mode, seed, M, N, K, sigma=0.02):
     return X, packed, ab
 
 
-@pytest.mark.parametrize("mode", [O.SEQ2, O.LSQ4])
+DEPLOYABLE = [O.SEQ2, O.LSQ4, O.TERNARY, O.LSQ3]
+
+
+@pytest.mark.parametrize("mode", DEPLOYABLE)
 @pytest.mark.parametrize("M,N,K", [(8, 256, 256), (1, 64, 64), (5, 100, 320), (16, 257, 1024),
                                    (17, 64, 128), (33, 96, 192), (64, 130, 256), (65, 128, 64),
                                    (130, 300, 384), (257, 129, 512), (64, 512, 4096),
@@ -149,7 +156,7 @@ def c5_weights(mode):
     return _C5[mode]
 
 
-@pytest.mark.parametrize("mode", [O.SEQ2, O.LSQ4])
+@pytest.mark.parametrize("mode", DEPLOYABLE)
 @pytest.mark.parametrize("M", [1, 4, 16, 64, 512])
 def test_gemm_16384_sampled(mode, M):
     """Full 16384 x 16384 weight at the benchmark's M values, sampled outputs."""

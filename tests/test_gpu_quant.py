@@ -208,13 +208,17 @@ def gpu_pack(mode, W, alpha):
     nbytes = pq.pq_packed_bytes(mode, rows, cols)
     packed = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device="cuda")
     ab = empty_bf16(rows)
-    fn = pq.pq_pack_w2 if mode == O.SEQ2 else pq.pq_pack_w4
-    fn(rows, cols, dev(W), dev(alpha), packed, ab)
+    if mode == O.SEQ2:
+        pq.pq_pack_w2(rows, cols, dev(W), dev(alpha), packed, ab)
+    elif mode == O.LSQ4:
+        pq.pq_pack_w4(rows, cols, dev(W), dev(alpha), packed, ab)
+    else:
+        pq.pq_pack(mode, rows, cols, dev(W), dev(alpha), packed, ab)
     torch.cuda.synchronize()
     return host(packed), host(ab)
 
 
-@pytest.mark.parametrize("mode", [O.SEQ2, O.LSQ4])
+@pytest.mark.parametrize("mode", [O.SEQ2, O.LSQ4, O.TERNARY, O.LSQ3])
 def test_pack_matches_forward_codes(mode):
     # 333 rows (three padding rows in the last tile), 1600 columns (a partly
     # filled last 64-byte group at both widths)
@@ -228,7 +232,7 @@ def test_pack_matches_forward_codes(mode):
     assert_bits_equal(packed, O.tile_codes(codes_fwd), "pack == fwd codes in export order")
 
 
-@pytest.mark.parametrize("mode", [O.SEQ2, O.LSQ4])
+@pytest.mark.parametrize("mode", [O.SEQ2, O.LSQ4, O.TERNARY, O.LSQ3])
 @pytest.mark.parametrize("rows,cols", [(1, 8), (17, 64), (16, 1024), (4100, 264), (4096, 520), (8192, 256)])
 def test_pack_export_order_shapes(mode, rows, cols):
     """Export byte order across the launch shapes: one row per block (fewer
