@@ -560,18 +560,48 @@ def sweep_bits(torch, pq, stack, make_tables, stream):
     return res
 
 
-def gemm_compare(torch, pq, W16, a16, Xs, stream):
-    """4-bit variant of the same kernel and a hipBLASLt bf16 GEMM on the
-    dequantized weight, at the same shapes (8 rotating weight copies each)."""
+def b2b_ms(torch, stream, run, reps):
+    """Mean time per launch of `reps` launches in a row, one event pair
+    around them (after a few warm launches)."""
+    for i in range(4):
+        run(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(reps):
+        run(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def gemm_compare(torch, pq, W16, a16, Xs, stream, reps=30):
+    """The other widths through the same kernels (ternary in the 2-bit
+    container, 3- and 4-bit LSQ in nibbles) and a hipBLASLt bf16 GEMM on the
+    dequantized weight, at the same shapes: each launched back to back on 8
+    rotating weight copies (the 2-bit numbers are in gemm_back_to_back)."""
     N = K = GEMM_NK
-    res = {}
-    p4 = [torch.empty(pq.pq_packed_bytes(pq.PQ_W4_LSQ, N, K), dtype=torch.uint8, device="cuda")
-          for _ in range(ROTATE)]
-    a4 = torch.zeros(N, dtype=torch.float32, device="cuda")
-    pq.pq_quantize_fwd(pq.PQ_W4_LSQ, N, K, W16, a4, pq.PQ_INIT_ALPHA, None, None, None)
-    ab4 = [torch.empty(N, dtype=torch.bfloat16, device="cuda") for _ in range(ROTATE)]
-    for i in range(ROTATE):
-        pq.pq_pack_w4(N, K, W16, a4, p4[i], ab4[i])
+    sid = stream.cuda_stream
+    res = {f"m{M}": {} for M in GEMM_MS}
+    widths = (("ternary", pq.PQ_W158_SEQ_TERNARY, 2), ("w3", pq.PQ_W3_LSQ, 4), ("w4", pq.PQ_W4_LSQ, 4))
+    for name, md, cbits in widths:
+        a = torch.zeros(N, dtype=torch.float32, device="cuda")
+        pq.pq_quantize_fwd(md, N, K, W16, a, pq.PQ_INIT_ALPHA, None, None, None)
+        pk = [torch.empty(pq.pq_packed_bytes(md, N, K), dtype=torch.uint8, device="cuda") for _ in range(ROTATE)]
+        ab = [torch.empty(N, dtype=torch.bfloat16, device="cuda") for _ in range(ROTATE)]
+        for i in range(ROTATE):
+            pq.pq_pack(md, N, K, W16, a, pk[i], ab[i])
+        pkp, abp = [t.data_ptr() for t in pk], [t.data_ptr() for t in ab]
+        for M in GEMM_MS:
+            xp = Xs[M].data_ptr()
+            Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+            yp = Y.data_ptr()
+            ms = b2b_ms(torch, stream, lambda i: pq.pq_gemm(md, M, N, K, xp, pkp[i % ROTATE], abp[i % ROTATE], yp,
+                                                              sid), reps)
+            fl = 2.0 * M * N * K
+            res[f"m{M}"].update({f"{name}_ms": round(ms, 5), f"{name}_tflops": round(fl / ms / 1e9, 2),
+                                 f"{name}_weight_GBs": round(gemm_bytes(M, N, K, cbits) / ms / 1e6, 1)})
+        del pk, ab
     wbf = [torch.empty(N, K, dtype=torch.bfloat16, device="cuda") for _ in range(ROTATE)]
     wq = torch.empty(N, K, dtype=torch.bfloat16, device="cuda")
     pq.pq_quantize_fwd(pq.PQ_W2_SEQ, N, K, W16, torch.zeros(N, device="cuda"), pq.PQ_INIT_ALPHA,
@@ -582,14 +612,10 @@ def gemm_compare(torch, pq, W16, a16, Xs, stream):
     for M in GEMM_MS:
         X = Xs[M]
         Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-        t4 = time_it(torch, stream, lambda i: pq.pq_w4a16_gemm(M, N, K, X, p4[i % ROTATE],
-                                                                ab4[i % ROTATE], Y), 20)
-        tb = time_it(torch, stream, lambda i: torch.matmul(X, wbf[i % ROTATE].t(), out=Y), 20)
+        tb = b2b_ms(torch, stream, lambda i: torch.matmul(X, wbf[i % ROTATE].t(), out=Y), reps)
         fl = 2.0 * M * N * K
-        res[f"m{M}"] = dict(w4a16_ms=round(t4, 5), w4a16_tflops=round(fl / t4 / 1e9, 2),
-                            w4a16_weight_GBs=round(gemm_bytes(M, N, K, 4) / t4 / 1e6, 1),
-                            bf16_hipblaslt_ms=round(tb, 5),
-                            bf16_tflops=round(fl / tb / 1e9, 2))
+        res[f"m{M}"].update(bf16_hipblaslt_ms=round(tb, 5), bf16_tflops=round(fl / tb / 1e9, 2))
+    del wbf
     return res
 
 

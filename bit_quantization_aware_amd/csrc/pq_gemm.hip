@@ -204,8 +204,44 @@ struct TileCfg {
     static constexpr int LDS = P * XBYTES + 2 * CSS;
     static_assert(WN == 4 || WN == 8, "block width");
     static_assert(NC * WN * 1024 == CSS, "one fetch is NC 1-KB DMAs per wave");
-    static_assert(P == 4, "the unrolled ring assumes four activation slots");
+    static_assert(P >= 3, "activation ring depth");
 };
+
+// DMA bookkeeping of the tiled kernel's pipeline, evaluated at compile time.
+// Issue order: code fetch 0, activation stages 0 .. P-2, code fetch 1; then
+// iteration j issues activation stage j + P - 1 and, when (j + 1) % SS == 0,
+// code fetch (j + 1) / SS + 1.  Iteration s needs activation stage s + 1 and
+// code fetch (s + 1) / SS landed; loads retire in order, so the largest safe
+// vmcnt is the number of DMA instructions issued after the newer of the two.
+// Issue "times" only order the events.
+constexpr int tile_t_x(int k, int P) { return k <= P - 2 ? 1 + k : P + 1 + 2 * (k - P + 1); }
+constexpr int tile_t_c(int F, int P, int SS) { return F == 0 ? 0 : F == 1 ? P : P + 2 + 2 * ((F - 1) * SS - 1); }
+constexpr int tile_wait_at(int s, int P, int SS, int XI, int NC)
+{
+    const int a = tile_t_x(s + 1, P), b = tile_t_c((s + 1) / SS, P, SS);
+    const int newest = a > b ? a : b;
+    int n = 0;
+    for (int st = 0; st < P - 1; ++st)
+        if (1 + st > newest) n += XI;
+    if (P > newest) n += NC;
+    for (int j = 0; j < s; ++j) {
+        if (P + 1 + 2 * j > newest) n += XI;
+        if ((j + 1) % SS == 0 && P + 2 + 2 * j > newest) n += NC;
+    }
+    return n;
+}
+// The wait of unrolled phase p: the smallest safe count over the iterations
+// s = p, p + U, ... (the first ones included; steady state is reached well
+// within the range scanned).
+constexpr int tile_wait(int p, int P, int SS, int XI, int NC, int U)
+{
+    int best = 1 << 30;
+    for (int s = p; s < 4 * U + 2 * P + 2 * SS; s += U) {
+        const int w = tile_wait_at(s, P, SS, XI, NC);
+        best = w < best ? w : best;
+    }
+    return best;
+}
 
 // One LDS-DMA load: every lane fetches 16 bytes at `base + off` (`base`
 // wave-uniform, in SGPRs) and the wave's 64 results land contiguously at LDS
@@ -451,11 +487,9 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
     // issued in the last iteration that reads fetch G's buffer (after its
     // barrier), SS stages before it is needed.  Iteration s waits for
     // stage s + 1 (and its codes), passes the barrier, refills, reads stage
-    // s + 1's fragments and multiplies stage s.  Loads retire in order, so
-    // the wait leaves in flight exactly the DMAs issued after stage s + 1's
-    // activation DMA that iteration s does not need: stage s + 2's
-    // activations and the code fetches of iterations s - 1 and (when SS > 2)
-    // s - 2.
+    // s + 1's fragments and multiplies stage s.  The wait count of each
+    // unrolled phase comes from tile_wait: the DMAs issued after the newer of
+    // the two it needs may stay in flight.
     constexpr int U = 2 * C::SS > P ? 2 * C::SS : P;   // unroll: phases of slots and buffers
     static_assert(U % P == 0 && U % (2 * C::SS) == 0, "unroll covers both rings");
     Frag fr[2];
@@ -463,17 +497,14 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
 #pragma unroll
     for (int st = 0; st < P - 1; ++st) issue_x(st, st);
     issue_c(1);
-    wait_vmcnt<2 * C::XI + NC>();
+    // prologue: activation stage 0 and code fetch 0 landed
+    wait_vmcnt<(P - 2) * C::XI + NC>();
     block_barrier();
     read_frags(std::integral_constant<int, 0>{}, fr[0]);
     auto step = [&](int s, auto pc) {
         constexpr int p = decltype(pc)::value;  // s mod U
-        // A fetch issued at iteration i is first read at iteration i + SS, so
-        // the one from s - 2 may stay in flight only when SS > 2.
-        constexpr bool code_prev2 = ((p - 1 + U) % C::SS) == 0 && C::SS > 2;
-        constexpr bool code_prev1 = (p % C::SS) == 0;
         constexpr bool code_now = ((p + 1) % C::SS) == 0;
-        wait_vmcnt<C::XI + NC * (int(code_prev2) + int(code_prev1))>();
+        wait_vmcnt<tile_wait(p, P, C::SS, C::XI, NC, U)>();
         block_barrier();
         auto refill = [&]() {
             issue_x(s + P - 1, (p + P - 1) % P);
