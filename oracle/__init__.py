@@ -57,6 +57,7 @@ def lib():
         L.pqo_qat_step.argtypes = ([ctypes.c_int, _i64, _i64, _f32p, _f32p, ctypes.c_void_p, ctypes.c_int,
                                     ctypes.c_double, _f32p, _f32p, _f32p, _f32p] + [ctypes.c_double] * 5 +
                                    [_i64, _u16p, _u8p, _f32p])
+        L.pqo_gemm_ref_f32a.argtypes = [ctypes.c_int, _i64, _i64, _i64, _u16p, _u8p, _f32p, _f64p]
         L.pqo_set_threads.argtypes = [ctypes.c_int]
         _lib = L
     return _lib
@@ -238,6 +239,18 @@ def gemm_ref(mode: int, X_bf16: np.ndarray, packed: np.ndarray, alpha_bf16: np.n
     Y = np.empty((M, N), np.float64)
     _check(lib().pqo_gemm_ref(mode, M, N, K, _p(X, _u16p), _p(packed, _u8p), _p(ab, _u16p),
                               _p(Y, _f64p)))
+    return Y
+
+
+def gemm_ref_f32a(mode: int, X_bf16: np.ndarray, packed: np.ndarray, alpha: np.ndarray, N: int):
+    """Binary64 Y [M,N] with a binary32 scale per row."""
+    X = _c(X_bf16, np.uint16)
+    packed = _c(packed, np.uint8)
+    alpha = _c(alpha, np.float32)
+    M, K = X.shape
+    Y = np.empty((M, N), np.float64)
+    _check(lib().pqo_gemm_ref_f32a(mode, M, N, K, _p(X, _u16p), _p(packed, _u8p), _p(alpha, _f32p),
+                                   _p(Y, _f64p)))
     return Y
 
 

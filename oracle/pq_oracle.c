@@ -596,6 +596,21 @@ int pqo_gemm_ref(int mode, int64_t M, int64_t N, int64_t K, const uint16_t *X,
     return 0;
 }
 
+/* The same product with a binary32 scale per row (the training forward's
+ * alpha, before any export rounding): Y[m,n] = sum_k X[m,k] * alpha[n] *
+ * level(code[n,k]) in binary64. */
+int pqo_gemm_ref_f32a(int mode, int64_t M, int64_t N, int64_t K, const uint16_t *X,
+                      const uint8_t *packed, const float *alpha, double *Y)
+{
+    if (!deployable(mode)) return -1;
+    const int64_t rb = pqo_code_row_bytes(mode, K);
+#pragma omp parallel for schedule(static) collapse(2)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            Y[m * N + n] = gemm_one(mode, K, X + m * K, packed + n * rb, (double)alpha[n]);
+    return 0;
+}
+
 int pqo_gemm_ref_at(int mode, int64_t M, int64_t N, int64_t K, const uint16_t *X,
                     const uint8_t *packed, const uint16_t *alpha_bf16,
                     const int64_t *ms, const int64_t *ns, int64_t count, double *out)

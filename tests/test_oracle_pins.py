@@ -443,6 +443,10 @@ def test_gemm_ref_is_matmul_of_dequantized_weight(mode):
     ms = rng.integers(0, M, 17)
     ns = rng.integers(0, N, 17)
     assert np.array_equal(O.gemm_ref_at(mode, X, packed, ab, N, ms, ns), Y[ms, ns])
+    # binary32 scale: the same matmul with the unrounded alpha
+    Wf = lev(unpack_codes(packed, mode, K).astype(np.float64)) * alpha.astype(np.float64)[:, None]
+    want32 = np.matmul(synth.bf16_bits_to_f32(X).astype(np.float64), Wf.T)
+    assert np.allclose(O.gemm_ref_f32a(mode, X, packed, alpha, N), want32, rtol=1e-12, atol=1e-12)
 
 
 def _tile_by_reshape(P):
