@@ -102,6 +102,13 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+// Per-column scale: binary32 (the training forward's alpha) when given, else
+// the exported bf16 scale.
+__device__ __forceinline__ float col_scale(const uint16_t *a16, const float *a32, int n)
+{
+    return a32 ? a32[n] : bf16_to_f32(a16[n]);
+}
+
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F &&f)
 {
@@ -120,6 +127,7 @@ struct GemmArgs {
     int M, N, K;
     int64_t gstride;         // bytes per 64-byte group of all rows (Np * 64)
     float off, mul;          // level = mul * (v - off) for the decoded operand v
+    const float *alpha32;    // [N] binary32 scale, or nullptr (use alpha)
 };
 
 // ---------------------------------------------------------------------------
@@ -181,6 +189,7 @@ struct TileArgs {
     int kps;                 // k per split, a multiple of the 64-byte group
     int64_t gstride;         // bytes per 64-byte group of all rows
     float off, mul;          // level = mul * (v - off) for the decoded operand v
+    const float *alpha32;    // [N] binary32 scale, or nullptr (use alpha)
 };
 
 // Activation LDS swizzle: chunk c of tile row r sits in slot c ^ xswz(r).
@@ -549,7 +558,7 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
         float al[4] = {1.f, 1.f, 1.f, 1.f};
         if (g.splits == 1) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) al[e] = n + e < N ? bf16_to_f32(g.alpha[n + e]) : 0.f;
+            for (int e = 0; e < 4; ++e) al[e] = n + e < N ? col_scale(g.alpha, g.alpha32, n + e) : 0.f;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -586,7 +595,7 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
 
 // Sum of the split-K partials, scaled by alpha and rounded to bf16.  Four
 // consecutive elements of the flattened [M, N] output per thread.
-__global__ __launch_bounds__(256) void k_splitk_finalize(const float *ws, const uint16_t *alpha,
+__global__ __launch_bounds__(256) void k_splitk_finalize(const float *ws, const uint16_t *alpha, const float *alpha32,
                                                          uint16_t *Y, int64_t total, int N, int splits)
 {
     const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
@@ -598,8 +607,8 @@ __global__ __launch_bounds__(256) void k_splitk_finalize(const float *ws, const 
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int64_t e = i0 + 2 * h;
-            const float a0 = bf16_to_f32(alpha[e % N]);
-            const float a1 = bf16_to_f32(alpha[(e + 1) % N]);
+            const float a0 = col_scale(alpha, alpha32, static_cast<int>(e % N));
+            const float a1 = col_scale(alpha, alpha32, static_cast<int>((e + 1) % N));
             o[h] = pack_bf16x2(a0 * s[2 * h], a1 * s[2 * h + 1]);
         }
         *reinterpret_cast<u32x2 *>(Y + i0) = u32x2{o[0], o[1]};
@@ -607,7 +616,7 @@ __global__ __launch_bounds__(256) void k_splitk_finalize(const float *ws, const 
         for (int64_t e = i0; e < total; ++e) {
             float s = 0.f;
             for (int k = 0; k < splits; ++k) s += ws[k * total + e];
-            const __bf16 h = static_cast<__bf16>(bf16_to_f32(alpha[e % N]) * s);
+            const __bf16 h = static_cast<__bf16>(col_scale(alpha, alpha32, static_cast<int>(e % N)) * s);
             Y[e] = __builtin_bit_cast(uint16_t, h);
         }
     }
@@ -854,7 +863,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
         const int j = w;
         const int n = n0 + 16 * j + i16;
         if (n < N) {
-            const float al = bf16_to_f32(g.alpha[n]);
+            const float al = col_scale(g.alpha, g.alpha32, n);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int m = 4 * grp + e;
@@ -948,7 +957,7 @@ pq_status launch_tile(const GemmArgs &a, hipStream_t s)
     const float off = BITS == 2 ? a.off : 2.0f + (a.off - 128.0f) / 8.0f;
     const float mul = BITS == 2 ? a.mul : 8.0f * a.mul;
     TileArgs t{a.X, a.packed, a.alpha, a.Y, nullptr, a.M, a.N, a.K, mtiles, ntiles, splits, sps * kStageK,
-               a.gstride, off, mul};
+               a.gstride, off, mul, a.alpha32};
     const int64_t total = static_cast<int64_t>(a.M) * a.N;
     if (splits > 1) {
         pq_status st = workspace(s, static_cast<size_t>(splits) * total * sizeof(float), &t.ws);
@@ -961,7 +970,7 @@ pq_status launch_tile(const GemmArgs &a, hipStream_t s)
     if (splits > 1) {
         const int64_t threads = (total + 3) / 4;
         hipLaunchKernelGGL(k_splitk_finalize, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s,
-                           t.ws, a.alpha, a.Y, total, a.N, splits);
+                           t.ws, a.alpha, a.alpha32, a.Y, total, a.N, splits);
     }
     return PQ_OK;
 }
@@ -986,19 +995,20 @@ bool level_map(int mode, LevelMap *lm)
 
 template <int BITS>
 pq_status gemm(int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *packed,
-               const void *alpha_bf16, void *Y, void *stream, const LevelMap &lm)
+               const void *alpha_bf16, void *Y, void *stream, const LevelMap &lm, const float *alpha32 = nullptr)
 {
-    if (!X || !packed || !alpha_bf16 || !Y) return PQ_ERR_NULL;
+    if (!X || !packed || (!alpha_bf16 && !alpha32) || !Y) return PQ_ERR_NULL;
     if (M < 0 || N < 0 || K <= 0 || K % 64 != 0 || K > kMaxGemmK || M > INT32_MAX / 2 || N > kMaxGemmN)
         return PQ_ERR_SHAPE;
-    if (!aligned16(X) || !aligned16(packed) || !aligned16(Y) || !aligned16(alpha_bf16))
+    if (!aligned16(X) || !aligned16(packed) || !aligned16(Y) || (alpha_bf16 && !aligned16(alpha_bf16)) ||
+        (alpha32 && !aligned16(alpha32)))
         return PQ_ERR_ALIGN;
     if (M == 0 || N == 0) return PQ_OK;
     GemmArgs a{static_cast<const uint16_t *>(X), packed, static_cast<const uint16_t *>(alpha_bf16),
                static_cast<uint16_t *>(Y), static_cast<int>(M), static_cast<int>(N), static_cast<int>(K),
                (N + 15) / 16 * 16 * 64,
                // the stream kernel's operand: c / 2 (2 bits), 128 + c (4 bits); all exact
-               BITS == 2 ? lm.zc / 2.0f : 128.0f + lm.zc, BITS == 2 ? 2.0f * lm.step : lm.step};
+               BITS == 2 ? lm.zc / 2.0f : 128.0f + lm.zc, BITS == 2 ? 2.0f * lm.step : lm.step, alpha32};
     hipStream_t s = static_cast<hipStream_t>(stream);
     constexpr int GK = BITS == 2 ? 256 : 128;
     constexpr int RPL = 512 / GK;
@@ -1026,6 +1036,16 @@ pq_status pq_gemm(int mode, int64_t M, int64_t N, int64_t K, const void *X, cons
     if (!pq::level_map(mode, &lm)) return PQ_ERR_MODE;
     if (lm.bits == 2) return pq::gemm<2>(M, N, K, X, packed, alpha_bf16, Y, stream, lm);
     return pq::gemm<4>(M, N, K, X, packed, alpha_bf16, Y, stream, lm);
+}
+
+pq_status pq_gemm_f32a(int mode, int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *packed,
+                       const float *alpha, void *Y, void *stream)
+{
+    pq::LevelMap lm;
+    if (!pq::level_map(mode, &lm)) return PQ_ERR_MODE;
+    if (!alpha) return PQ_ERR_NULL;
+    if (lm.bits == 2) return pq::gemm<2>(M, N, K, X, packed, nullptr, Y, stream, lm, alpha);
+    return pq::gemm<4>(M, N, K, X, packed, nullptr, Y, stream, lm, alpha);
 }
 
 pq_status pq_w2a16_gemm(int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *packed,

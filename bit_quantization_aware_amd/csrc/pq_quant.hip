@@ -699,6 +699,15 @@ constexpr int64_t kWaveRowsThreshold = 4096;
 // with many rows (measured: from 4096 columns on, for fwd, bwd and export).
 constexpr int64_t kTeamColsThreshold = 4096;
 
+bool finite(double x) { return x == x && x < 1e300 && x > -1e300; }
+
+// Widths with a deployment format: a 2-bit (ternary, 2-bit SEQ) or 4-bit (3-
+// and 4-bit LSQ) code container.
+bool deployable(int mode)
+{
+    return mode == PQ_W158_SEQ_TERNARY || mode == PQ_W2_SEQ || mode == PQ_W3_LSQ || mode == PQ_W4_LSQ;
+}
+
 int choose_wpr(int64_t total_rows, int64_t total_elems)
 {
     const bool many_rows = total_rows >= kWaveRowsThreshold;
@@ -712,12 +721,16 @@ bool ptr_ok(const void *p) { return p == nullptr || aligned16(p); }
 // team size for the whole stack; `fwd` launches take fwd_rows_per_wave rows
 // per wave.
 template <typename D, typename F>
-pq_status launch_grouped(int count, const D *host, const D *dev, hipStream_t stream, bool fwd, F &&launch_one)
+pq_status launch_grouped(int count, const D *host, const D *dev, hipStream_t stream, bool fwd, F &&launch_one,
+                         bool pad16 = false)
 {
+    // pad16: the launch also covers the padding rows of each matrix's last
+    // 16-row tile (codes in the export byte order)
+    auto rows_of = [&](int i) { return pad16 ? (host[i].rows + 15) / 16 * 16 : host[i].rows; };
     int64_t total_rows = 0, total_elems = 0;
     for (int i = 0; i < count; ++i) {
-        total_rows += host[i].rows;
-        total_elems += host[i].rows * host[i].cols;
+        total_rows += rows_of(i);
+        total_elems += rows_of(i) * host[i].cols;
     }
     const int wpr = choose_wpr(total_rows, total_elems);
     const int rpb = (4 / wpr) * (fwd ? fwd_rows_per_wave(wpr) : 1);  // rows per block
@@ -730,7 +743,7 @@ pq_status launch_grouped(int count, const D *host, const D *dev, hipStream_t str
         int64_t blocks = 0;
         for (int i = 0; i < n; ++i) {
             lt.block_start[i] = static_cast<int32_t>(blocks);
-            blocks += (host[start + i].rows + rpb - 1) / rpb;
+            blocks += (rows_of(start + i) + rpb - 1) / rpb;
             if (blocks > INT32_MAX) return PQ_ERR_SHAPE;
         }
         lt.block_start[n] = static_cast<int32_t>(blocks);
@@ -761,7 +774,19 @@ void launch_fwd_outs(unsigned outs, const LaunchTable &lt, int blocks, int wpr, 
     case 4: launch_fwd_t<MODE, INIT, 4>(lt, blocks, wpr, s, nullptr); break;
     case 5: launch_fwd_t<MODE, INIT, 5>(lt, blocks, wpr, s, nullptr); break;
     case 6: launch_fwd_t<MODE, INIT, 6>(lt, blocks, wpr, s, nullptr); break;
-    default: launch_fwd_t<MODE, INIT, 7>(lt, blocks, wpr, s, nullptr); break;
+    case 7: launch_fwd_t<MODE, INIT, 7>(lt, blocks, wpr, s, nullptr); break;
+    default:
+        // codes in the export byte order (2- and 4-bit containers only; the
+        // host rejects other modes)
+        if constexpr (Mode<MODE>::cw != 1) {
+            switch (outs) {
+            case OUT_CODES | OUT_TILED: launch_fwd_t<MODE, INIT, 20>(lt, blocks, wpr, s, nullptr); break;
+            case OUT_BF16 | OUT_CODES | OUT_TILED: launch_fwd_t<MODE, INIT, 21>(lt, blocks, wpr, s, nullptr); break;
+            case OUT_F32 | OUT_CODES | OUT_TILED: launch_fwd_t<MODE, INIT, 22>(lt, blocks, wpr, s, nullptr); break;
+            default: launch_fwd_t<MODE, INIT, 23>(lt, blocks, wpr, s, nullptr); break;
+            }
+        }
+        break;
     }
 }
 
@@ -827,7 +852,9 @@ unsigned fwd_outs(const pq_mat &m)
 pq_status check_fwd_descs(int mode, int count, const pq_mat *host, unsigned flags, unsigned *outs)
 {
     if (!valid_mode(mode)) return PQ_ERR_MODE;
-    if ((flags & ~PQ_INIT_ALPHA) != 0) return PQ_ERR_MODE;
+    if ((flags & ~(PQ_INIT_ALPHA | PQ_CODES_EXPORT)) != 0) return PQ_ERR_MODE;
+    const bool exported = (flags & PQ_CODES_EXPORT) != 0;
+    if (exported && !deployable(mode)) return PQ_ERR_MODE;
     if (count < 0) return PQ_ERR_ARG;
     if (count > 0 && !host) return PQ_ERR_NULL;
     bool have_first = false;
@@ -835,7 +862,8 @@ pq_status check_fwd_descs(int mode, int count, const pq_mat *host, unsigned flag
         const pq_mat &m = host[i];
         if (m.rows < 0 || !valid_cols(m.cols)) return PQ_ERR_SHAPE;
         if (m.rows == 0) continue;  // enqueues nothing; its pointers are not used
-        const unsigned o = fwd_outs(m);
+        const unsigned o = fwd_outs(m) | (exported ? OUT_TILED : 0u);
+        if (exported && !m.codes) return PQ_ERR_NULL;
         if (!have_first) {
             *outs = o;
             have_first = true;
@@ -903,14 +931,6 @@ void launch_step(int mode, int wpr, bool gbf, const StepTable &lt, int blocks, c
     }
 }
 
-bool finite(double x) { return x == x && x < 1e300 && x > -1e300; }
-
-// Widths with a deployment format: a 2-bit (ternary, 2-bit SEQ) or 4-bit (3-
-// and 4-bit LSQ) code container.
-bool deployable(int mode)
-{
-    return mode == PQ_W158_SEQ_TERNARY || mode == PQ_W2_SEQ || mode == PQ_W3_LSQ || mode == PQ_W4_LSQ;
-}
 
 // AdamW scalars: binary64 from the hyper-parameters, rounded once.
 pq_status adam_scalars(const pq_adamw *hp, AdamK *k)
@@ -1014,10 +1034,10 @@ pq_status pq_quantize_fwd_grouped(int mode, int count, const pq_mat *descs_host,
     if (st != PQ_OK) return st;
     if (count > 0 && !descs_dev) return PQ_ERR_NULL;
     const bool init = (flags & PQ_INIT_ALPHA) != 0;
-    return launch_grouped(count, descs_host, descs_dev, static_cast<hipStream_t>(stream), true,
-                          [&](const LaunchTable &lt, int blocks, int wpr, hipStream_t s) {
-                              launch_fwd(mode, init, outs, lt, blocks, wpr, s);
-                          });
+    return launch_grouped(
+        count, descs_host, descs_dev, static_cast<hipStream_t>(stream), true,
+        [&](const LaunchTable &lt, int blocks, int wpr, hipStream_t s) { launch_fwd(mode, init, outs, lt, blocks, wpr, s); },
+        (flags & PQ_CODES_EXPORT) != 0);
 }
 
 pq_status pq_quantize_fwd(int mode, int64_t rows, int64_t cols, const float *W, float *alpha,
@@ -1036,11 +1056,10 @@ pq_status pq_quantize_fwd(int mode, int64_t rows, int64_t cols, const float *W, 
     pq_status st = check_fwd_descs(mode, 1, &m, flags, &outs);
     if (st != PQ_OK) return st;
     const bool init = (flags & PQ_INIT_ALPHA) != 0;
-    return launch_grouped(1, &m, static_cast<const pq_mat *>(nullptr), static_cast<hipStream_t>(stream),
-                          true,
-                          [&](const LaunchTable &lt, int blocks, int wpr, hipStream_t s) {
-                              launch_fwd(mode, init, outs, lt, blocks, wpr, s);
-                          });
+    return launch_grouped(
+        1, &m, static_cast<const pq_mat *>(nullptr), static_cast<hipStream_t>(stream), true,
+        [&](const LaunchTable &lt, int blocks, int wpr, hipStream_t s) { launch_fwd(mode, init, outs, lt, blocks, wpr, s); },
+        (flags & PQ_CODES_EXPORT) != 0);
 }
 
 pq_status pq_quantize_bwd_grouped(int mode, int count, const pq_mat *descs_host,

@@ -30,7 +30,7 @@ STATUS = {0: "PQ_OK", 1: "PQ_ERR_NULL", 2: "PQ_ERR_SHAPE", 3: "PQ_ERR_MODE", 4: 
 EXPORTS = ("pq_code_row_bytes", "pq_packed_bytes", "pq_default_grad_scale", "pq_status_str", "pq_version",
            "pq_quantize_fwd", "pq_quantize_bwd", "pq_pack_w2", "pq_pack_w4", "pq_w2a16_gemm",
            "pq_w4a16_gemm", "pq_quantize_fwd_grouped", "pq_quantize_bwd_grouped", "pq_qat_step",
-           "pq_qat_step_grouped", "pq_pack", "pq_gemm")
+           "pq_qat_step_grouped", "pq_pack", "pq_gemm", "pq_gemm_f32a")
 
 
 class PQError(RuntimeError):
@@ -85,6 +85,7 @@ def _load():
     L.pq_w4a16_gemm.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp]
     L.pq_pack.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp]
     L.pq_gemm.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp]
+    L.pq_gemm_f32a.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp]
     L.pq_quantize_fwd_grouped.argtypes = [i32, i32, vp, vp, u32, vp]
     L.pq_quantize_bwd_grouped.argtypes = [i32, i32, vp, vp, i32, vp]
     L.pq_qat_step.argtypes = [i32, i64, i64, vp, vp, vp, i32, dbl, vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -181,6 +182,14 @@ def pq_pack(mode, rows, cols, W, alpha, packed, alpha_bf16, stream=None) -> None
 def pq_gemm(mode, M, N, K, X, packed, alpha_bf16, Y, stream=None) -> None:
     _check(lib.pq_gemm(mode, M, N, K, _ptr(X), _ptr(packed), _ptr(alpha_bf16), _ptr(Y),
                        _stream(stream)), "pq_gemm")
+
+
+def pq_gemm_f32a(mode, M, N, K, X, packed, alpha, Y, stream=None) -> None:
+    _check(lib.pq_gemm_f32a(mode, M, N, K, _ptr(X), _ptr(packed), _ptr(alpha), _ptr(Y),
+                            _stream(stream)), "pq_gemm_f32a")
+
+
+PQ_CODES_EXPORT = 2
 
 
 class MatTable:

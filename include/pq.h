@@ -98,6 +98,14 @@ typedef enum pq_mode {
  * mean|w| for 1 bit, summed in binary64). */
 #define PQ_INIT_ALPHA 1u
 
+/* pq_quantize_fwd flag: write `codes` in the export byte order of
+ * pq_pack_w2 (pq_packed_bytes(mode, rows, cols) bytes, padding zeroed)
+ * instead of row-major, so that the next GEMM can read them directly (the
+ * training forward through pq_gemm_f32a, with no bf16 weights written or
+ * read).  Deployable widths only (else PQ_ERR_MODE); codes must then be
+ * non-NULL. */
+#define PQ_CODES_EXPORT 2u
+
 /* Upstream-gradient dtypes for pq_quantize_bwd. */
 #define PQ_G_F32 0
 #define PQ_G_BF16 1
@@ -131,7 +139,7 @@ const char *pq_version(void);
  *   W         in   [rows, cols] fp32 shadow weights
  *   alpha     in   [rows] fp32 per-row scale; with PQ_INIT_ALPHA it is OUT:
  *                  written with the row statistic, then used
- *   flags     0 or PQ_INIT_ALPHA
+ *   flags     0, PQ_INIT_ALPHA and/or PQ_CODES_EXPORT
  *   Wq_bf16   out  [rows, cols] bf16 fake-quantized weights, or NULL
  *   Wq_f32    out  [rows, cols] the same values before the bf16 cast, or NULL
  *   codes     out  [rows, pq_code_row_bytes(mode, cols)] packed codes, or NULL
@@ -267,6 +275,18 @@ pq_status pq_w4a16_gemm(int64_t M, int64_t N, int64_t K, const void *X,
  * and storage the pages compare ([News] speed and storage paragraphs). */
 pq_status pq_gemm(int mode, int64_t M, int64_t N, int64_t K, const void *X,
                   const uint8_t *packed, const void *alpha_bf16, void *Y, void *stream);
+
+/* pq_gemm_f32a -- pq_gemm with the binary32 scale of training (alpha [N]
+ * fp32, as pq_quantize_fwd keeps it) instead of the exported bf16 one: the
+ * QAT forward's linear layer computed from the codes, Y = bf16(alpha[n] *
+ * sum_k X[m,k] * level(code[n,k])), with the codes written by
+ * pq_quantize_fwd(..., PQ_CODES_EXPORT, ...).  It reads 1/8 or 1/4 of the
+ * bytes of the fake-quantized bf16 weights and never materialises them; the
+ * forward's own Wq = bf16(alpha * level) rounds each weight to bf16 first,
+ * so the two differ by that rounding (relative 2^-9 per weight).  Errors as
+ * pq_gemm; alpha NULL -> PQ_ERR_NULL. */
+pq_status pq_gemm_f32a(int mode, int64_t M, int64_t N, int64_t K, const void *X,
+                       const uint8_t *packed, const float *alpha, void *Y, void *stream);
 
 /*
  * Grouped launches: one kernel launch over a whole stack of matrices (for

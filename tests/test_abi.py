@@ -122,6 +122,12 @@ def test_pack_and_gemm_argument_checks(pq):
     assert L.pq_gemm(0, 4, 8, 64, A, A, B, A, None) == 3
     assert L.pq_gemm(1, 4, 8, 60, A, A, B, A, None) == 2                          # ternary, K % 64
     assert L.pq_pack(3, 4, 60, A, A, B, A, None) == 2
+    assert L.pq_gemm_f32a(2, 4, 8, 64, A, A, None, A, None) == 1                  # alpha NULL
+    assert L.pq_gemm_f32a(0, 4, 8, 64, A, A, B, A, None) == 3
+    # forward with codes in the export byte order: deployable widths, codes required
+    assert L.pq_quantize_fwd(0, 4, 64, A, B, 2, None, None, A, None) == 3
+    assert L.pq_quantize_fwd(2, 4, 64, A, B, 2, A, None, None, None) == 1
+    assert L.pq_quantize_fwd(2, 4, 64, A, B, 4, None, None, A, None) == 3         # unknown flag
 
 
 def test_grouped_argument_checks(pq):

@@ -185,3 +185,21 @@ def test_gemm_llama3_8b_sampled(M):
         rng = np.random.default_rng(k)
         ms, ns = sample_points(rng, M, N, 800)
         check(Y[ms, ns], O.gemm_ref_at(O.SEQ2, X, packed, ab, N, ms, ns), f"{name} M={M}")
+
+
+@pytest.mark.parametrize("mode", DEPLOYABLE)
+@pytest.mark.parametrize("M,N,K", [(1, 96, 1024), (16, 257, 512), (64, 576, 576), (256, 1536, 576),
+                                   (512, 576, 1536)])
+def test_gemm_f32_alpha(mode, M, N, K):
+    """The training forward's product: codes + the binary32 alpha (no bf16
+    rounding of the scale), every output against the binary64 reference."""
+    rng = np.random.default_rng(M * 3 + N + K + mode)
+    W = synth.normal_f32(rng, (N, K), 0.02)
+    alpha = O.alpha_init(mode, W)
+    packed, _ = O.pack(mode, W, alpha)
+    X = synth.to_bf16_bits(synth.normal_f32(rng, (M, K)))
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    pq.pq_gemm_f32a(mode, M, N, K, dev(X), dev(O.tile_codes(packed)), dev(alpha), Y)
+    torch.cuda.synchronize()
+    Yg = synth.bf16_bits_to_f32(host(Y)).astype(np.float64)
+    check(Yg, O.gemm_ref_f32a(mode, X, packed, alpha, N), f"f32a m{mode} {M}x{N}x{K}")

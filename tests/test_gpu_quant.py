@@ -376,3 +376,50 @@ def test_division_at_decision_boundaries(mode):
     G = rng.standard_normal(W.shape).astype(np.float32)
     check_fwd(mode, W, alphas, False, f"div-boundary fwd m{mode}")
     check_bwd(mode, W, alphas, G, f"div-boundary bwd m{mode}")
+
+
+@pytest.mark.parametrize("mode", [O.TERNARY, O.SEQ2, O.LSQ3, O.LSQ4])
+@pytest.mark.parametrize("rows,cols,init", [(333, 1600, True), (4100, 264, False), (17, 64, True),
+                                            (64, 16384, False)])
+def test_fwd_codes_in_export_order(mode, rows, cols, init):
+    """PQ_CODES_EXPORT: the forward's codes in the export byte order (padding
+    zeroed), its bf16 weights and alpha unchanged."""
+    rng = np.random.default_rng(rows + cols + mode)
+    W = synth.normal_f32(rng, (rows, cols), 0.02)
+    alpha = None if init else O.alpha_init(mode, W) * np.float32(0.9)
+    ad = dev(alpha) if alpha is not None else torch.zeros(rows, dtype=torch.float32, device="cuda")
+    wq = empty_bf16(rows, cols)
+    codes = torch.full((pq.pq_packed_bytes(mode, rows, cols),), 0xA5, dtype=torch.uint8, device="cuda")
+    flags = pq.PQ_CODES_EXPORT | (pq.PQ_INIT_ALPHA if init else 0)
+    pq.pq_quantize_fwd(mode, rows, cols, dev(W), ad, flags, wq, None, codes)
+    torch.cuda.synchronize()
+    a_o = O.alpha_init(mode, W) if init else alpha
+    wq_o, _, codes_o = O.quantize_fwd(mode, W, a_o)
+    assert_bits_equal(host(ad), a_o, "alpha")
+    assert_bits_equal(host(wq), wq_o, "wq")
+    assert_bits_equal(host(codes), O.tile_codes(codes_o), "codes (export order)")
+
+
+def test_grouped_fwd_codes_in_export_order():
+    """The grouped forward over MobileLLM-125M layer 0 (576- and 1536-wide
+    rows) writing export-order codes only, as the training forward that feeds
+    pq_gemm_f32a does."""
+    mode = O.SEQ2
+    shapes = synth.mobilellm_125m_shapes()
+    ks = [k for k, (l, _, _, _) in enumerate(shapes) if l == 0]
+    mats, Ws = [], []
+    for k in ks:
+        W = synth.weight("mobilellm_125m", k)
+        rows, cols = W.shape
+        Ws.append(W)
+        mats.append(dict(W=dev(W), alpha=torch.zeros(rows, dtype=torch.float32, device="cuda"),
+                         codes=torch.full((pq.pq_packed_bytes(mode, rows, cols),), 0xA5, dtype=torch.uint8,
+                                          device="cuda"), rows=rows, cols=cols))
+    table = pq.MatTable(mats)
+    pq.pq_quantize_fwd_grouped(mode, table, pq.PQ_INIT_ALPHA | pq.PQ_CODES_EXPORT)
+    torch.cuda.synchronize()
+    for W, m in zip(Ws, mats):
+        a_o = O.alpha_init(mode, W)
+        _, _, codes_o = O.quantize_fwd(mode, W, a_o)
+        assert_bits_equal(host(m["alpha"]), a_o, "alpha")
+        assert_bits_equal(host(m["codes"]), O.tile_codes(codes_o), f"codes {W.shape}")
