@@ -54,6 +54,8 @@ def parse():
     p.add_argument("--no-extras", action="store_true", help="skip sweep / comparison GEMMs")
     p.add_argument("--gemm-b2b-only", action="store_true",
                    help="only the back-to-back GEMM launches (for a kernel trace of them alone)")
+    p.add_argument("--train-fwd-only", action="store_true",
+                   help="only the training-forward measurement (for a kernel trace of it alone)")
     p.add_argument("--qat-step-only", action="store_true",
                    help="only the fused QAT step measurement (for a kernel trace of it alone)")
     p.add_argument("--pmc-workload", action="store_true",
@@ -291,6 +293,10 @@ def main():
 
     kernels = ["fwd", "bwd", "pack"] + [f"gemm_m{M}" for M in GEMM_STEP_ORDER]
 
+    if args.train_fwd_only:
+        print(json.dumps({"train_forward": train_forward_measure(torch, pq, stack, stream)}), flush=True)
+        return
+
     if args.qat_step_only:
         print(json.dumps({"qat_step": qat_step_measure(torch, pq, stack, ftab, btab, stream)}), flush=True)
         return
@@ -435,6 +441,7 @@ def main():
     }
 
     if not args.no_extras:
+        out["train_forward"] = train_forward_measure(torch, pq, stack, stream)
         out["qat_step"] = qat_step_measure(torch, pq, stack, ftab, btab, stream)
         out["qat_step"]["traffic"] = step_traffic
         out["gemm_back_to_back"] = gemm_back_to_back(torch, pq, Xs, packed, ab16, Ys, stream, ridge)
@@ -457,6 +464,56 @@ def time_it(torch, stream, fn, reps):
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
     return float(np.mean([evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]))
+
+
+TRAIN_TOKENS = 16384  # 8 sequences x 2048 tokens (one GPU's share of the recipe's batch)
+
+
+def train_forward_measure(torch, pq, stack, stream, reps=3):
+    """The QAT forward of every quantized linear of the 2-bit stack at
+    8 x 2048 tokens: (a) this library's forward writing only the codes in the
+    export byte order, then pq_gemm_f32a per matrix (codes + fp32 alpha);
+    (b) the forward writing bf16 weights, then hipBLASLt (torch.matmul) per
+    matrix on them."""
+    mode = pq.PQ_W2_SEQ
+    dev = stack[0]["W"].device
+    T = TRAIN_TOKENS
+    sid = stream.cuda_stream
+    xs, ys = {}, {}
+    for m in stack:
+        c, r = m["cols"], m["rows"]
+        if c not in xs:
+            xs[c] = (torch.randn(T, c, device=dev) * 0.5).to(torch.bfloat16)
+        if r not in ys:
+            ys[r] = torch.empty(T, r, dtype=torch.bfloat16, device=dev)
+    mats = [dict(W=m["W"], alpha=m["alpha"], rows=m["rows"], cols=m["cols"],
+                 codes=torch.empty(pq.pq_packed_bytes(mode, m["rows"], m["cols"]), dtype=torch.uint8, device=dev))
+            for m in stack]
+    ctab = pq.MatTable([{k: d[k] for k in ("W", "alpha", "codes", "rows", "cols")} for d in mats])
+    btab = pq.MatTable([{k: m[k] for k in ("W", "alpha", "wq_bf16", "rows", "cols")} for m in stack])
+    calls = [(m["rows"], m["cols"], xs[m["cols"]].data_ptr(), d["codes"].data_ptr(), m["alpha"].data_ptr(),
+              ys[m["rows"]].data_ptr()) for m, d in zip(stack, mats)]
+
+    def codes_path():
+        pq.pq_quantize_fwd_grouped(mode, ctab, pq.PQ_CODES_EXPORT)
+        for r, c, xp, cp, ap, yp in calls:
+            pq.pq_gemm_f32a(mode, T, r, c, xp, cp, ap, yp, sid)
+
+    def bf16_path():
+        pq.pq_quantize_fwd_grouped(mode, btab, 0)
+        for m in stack:
+            torch.matmul(xs[m["cols"]], m["wq_bf16"].t(), out=ys[m["rows"]])
+
+    a = b2b_ms(torch, stream, lambda i: codes_path(), reps)
+    b = b2b_ms(torch, stream, lambda i: bf16_path(), reps)
+    fwd_c = b2b_ms(torch, stream, lambda i: pq.pq_quantize_fwd_grouped(mode, ctab, pq.PQ_CODES_EXPORT), reps)
+    fwd_b = b2b_ms(torch, stream, lambda i: pq.pq_quantize_fwd_grouped(mode, btab, 0), reps)
+    fl = 2.0 * T * sum(m["rows"] * m["cols"] for m in stack)
+    return dict(tokens=T, codes_path_ms=round(a, 4), codes_path_tflops=round(fl / a / 1e9, 1),
+                bf16_path_ms=round(b, 4), bf16_path_tflops=round(fl / b / 1e9, 1),
+                fwd_codes_only_ms=round(fwd_c, 4), fwd_bf16_codes_ms=round(fwd_b, 4),
+                gemm="codes: pq_gemm_f32a per matrix; bf16: torch.matmul (hipBLASLt) per matrix",
+                speedup=round(b / a, 3))
 
 
 def qat_step_measure(torch, pq, stack, ftab, btab, stream, reps=10):
