@@ -58,6 +58,9 @@ def lib():
                                     ctypes.c_double, _f32p, _f32p, _f32p, _f32p] + [ctypes.c_double] * 5 +
                                    [_i64, _u16p, _u8p, _f32p])
         L.pqo_gemm_ref_f32a.argtypes = [ctypes.c_int, _i64, _i64, _i64, _u16p, _u8p, _f32p, _f64p]
+        L.pqo_num_levels.argtypes = [ctypes.c_int]
+        L.pqo_level_stats.argtypes = [ctypes.c_int, _i64, _i64, _u8p, ctypes.POINTER(ctypes.c_uint32), _f64p]
+        L.pqo_weight_movement.argtypes = [_i64, _i64, _f32p, _f32p, _f64p, _f64p]
         L.pqo_set_threads.argtypes = [ctypes.c_int]
         _lib = L
     return _lib
@@ -209,6 +212,30 @@ def qat_step(mode: int, W, alpha, G, mW, vW, m_alpha, v_alpha, step, grad_scale=
                               _p(wq, _u16p), _p(codes, _u8p), _p(da, _f32p)))
     return dict(W=W, alpha=alpha, mW=mW, vW=vW, m_alpha=m_alpha, v_alpha=v_alpha, wq_bf16=wq,
                 codes=codes, dalpha=da)
+
+
+def num_levels(mode: int) -> int:
+    return int(lib().pqo_num_levels(mode))
+
+
+def level_stats(mode: int, codes: np.ndarray, cols: int):
+    """(counts uint32 [rows, levels], entropy float64 [rows]) of row-major codes."""
+    codes = _c(codes, np.uint8)
+    rows = codes.shape[0]
+    counts = np.empty((rows, num_levels(mode)), np.uint32)
+    ent = np.empty(rows, np.float64)
+    _check(lib().pqo_level_stats(mode, rows, cols, _p(codes, _u8p),
+                                 counts.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)), _p(ent, _f64p)))
+    return counts, ent
+
+
+def weight_movement(W: np.ndarray, W0: np.ndarray):
+    """(sum (W - W0)^2, sum W0^2) per row, binary64."""
+    W, W0 = _c(W, np.float32), _c(W0, np.float32)
+    rows, cols = W.shape
+    d2, r2 = np.empty(rows, np.float64), np.empty(rows, np.float64)
+    _check(lib().pqo_weight_movement(rows, cols, _p(W, _f32p), _p(W0, _f32p), _p(d2, _f64p), _p(r2, _f64p)))
+    return d2, r2
 
 
 def tiled_bytes(rows: int, row_bytes: int) -> int:

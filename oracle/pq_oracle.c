@@ -519,6 +519,76 @@ int pqo_qat_step(int mode, int64_t rows, int64_t cols, float *W, float *alpha, c
 }
 
 /* ---------------------------------------------------------------------------
+ * Diagnostics the pages argue with: how the weights of a row spread over the
+ * levels (the level occupancy behind the SEQ-vs-LSQ argument of [Rebuttal]
+ * and [Note] "Finding 3") and how far training moved the weights from their
+ * starting point ([Note] "QAT versus PTQ": QAT compensates rather than
+ * reconstructs).
+ *   counts[i, c]  number of weights of row i stored with code c, c = 0 ..
+ *                 levels - 1 (codes are offset-binary: code c is level c);
+ *   entropy[i]    -sum_c p_c log2 p_c, p_c = counts[i, c] / cols, binary64;
+ *   sq_diff[i]    sum_j (W[i,j] - W0[i,j])^2 and sq_ref[i] = sum_j W0[i,j]^2,
+ *                 each difference and square a binary64 operation, summed
+ *                 in column order.
+ * ------------------------------------------------------------------------- */
+int pqo_num_levels(int mode)
+{
+    switch (mode) {
+    case PQO_W1_BINARY: return 2;
+    case PQO_W158_SEQ_TERNARY: return 3;
+    case PQO_W2_SEQ: return 4;
+    case PQO_W3_LSQ: return 8;
+    case PQO_W4_LSQ: return 16;
+    default: return -1;
+    }
+}
+
+int pqo_level_stats(int mode, int64_t rows, int64_t cols, const uint8_t *codes, uint32_t *counts,
+                    double *entropy)
+{
+    if (!valid_mode(mode) || rows < 0 || cols <= 0 || !codes || !counts) return -1;
+    const int L = pqo_num_levels(mode), cw = pqo_code_bits(mode);
+    const int64_t rb = pqo_code_row_bytes(mode, cols);
+    for (int64_t i = 0; i < rows; ++i) {
+        uint32_t *c = counts + i * L;
+        for (int l = 0; l < L; ++l) c[l] = 0;
+        for (int64_t j = 0; j < cols; ++j) {
+            const unsigned code = get_code(codes + i * rb, j, cw);
+            if ((int)code >= L) return -1;
+            c[code] += 1;
+        }
+        if (entropy) {
+            double h = 0.0;
+            for (int l = 0; l < L; ++l)
+                if (c[l]) {
+                    const double p = (double)c[l] / (double)cols;
+                    h -= p * log2(p);
+                }
+            entropy[i] = h;
+        }
+    }
+    return 0;
+}
+
+int pqo_weight_movement(int64_t rows, int64_t cols, const float *W, const float *W0, double *sq_diff,
+                        double *sq_ref)
+{
+    if (rows < 0 || cols <= 0 || !W || !W0 || !sq_diff || !sq_ref) return -1;
+    for (int64_t i = 0; i < rows; ++i) {
+        double d2 = 0.0, r2 = 0.0;
+        for (int64_t j = 0; j < cols; ++j) {
+            const double d = (double)W[i * cols + j] - (double)W0[i * cols + j];
+            const double r = (double)W0[i * cols + j];
+            d2 += d * d;
+            r2 += r * r;
+        }
+        sq_diff[i] = d2;
+        sq_ref[i] = r2;
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
  * Deployment layout of the exported codes.  The pages fix only what a packed
  * 2-bit weight holds (four codes per byte and a bf16 scale per row, [News]
  * storage and speed paragraphs); the byte order the deployed GEMM reads is

@@ -566,3 +566,36 @@ def test_qat_step_is_bwd_then_adamw_then_fwd(mode, g_bf16):
     for k, want in (("W", W1), ("mW", mW1), ("vW", vW1), ("alpha", a1), ("m_alpha", ma1),
                     ("v_alpha", va1), ("wq_bf16", wq1), ("codes", codes1), ("dalpha", da)):
         assert np.array_equal(out[k].view(np.uint8), np.ascontiguousarray(want).view(np.uint8)), k
+
+
+# ----------------------------------------------------------------------------
+# Diagnostics: level occupancy and weight movement
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", [O.BINARY, O.TERNARY, O.SEQ2, O.LSQ3, O.LSQ4])
+def test_level_stats_match_bincount_and_scipy(mode):
+    import scipy.stats
+    rng = np.random.default_rng(90 + mode)
+    rows, cols = 40, 264
+    W = synth.normal_f32(rng, (rows, cols), 0.02)
+    W[3] = 0.0                       # a row with one level only (entropy 0)
+    _, _, codes = O.quantize_fwd(mode, W, O.alpha_init(mode, W))
+    counts, ent = O.level_stats(mode, codes, cols)
+    c = unpack_codes(codes, mode, cols)
+    L = {O.BINARY: 2, O.TERNARY: 3, O.SEQ2: 4, O.LSQ3: 8, O.LSQ4: 16}[mode]
+    want = np.stack([np.bincount(r, minlength=L) for r in c])
+    assert np.array_equal(counts, want)
+    assert np.allclose(ent, [scipy.stats.entropy(r, base=2) for r in want], rtol=0, atol=1e-12)
+    assert ent[3] == 0.0 and counts.sum() == rows * cols
+
+
+def test_weight_movement_matches_numpy():
+    rng = np.random.default_rng(95)
+    W0 = synth.normal_f32(rng, (17, 333), 0.02)
+    W = W0 + synth.normal_f32(rng, (17, 333), 1e-4)
+    d2, r2 = O.weight_movement(W, W0)
+    want_d = ((W.astype(np.float64) - W0.astype(np.float64)) ** 2).sum(axis=1)
+    want_r = (W0.astype(np.float64) ** 2).sum(axis=1)
+    assert np.allclose(d2, want_d, rtol=1e-13, atol=0)
+    assert np.allclose(r2, want_r, rtol=1e-13, atol=0)
+    z, _ = O.weight_movement(W0, W0)
+    assert not z.any()
