@@ -30,7 +30,8 @@ STATUS = {0: "PQ_OK", 1: "PQ_ERR_NULL", 2: "PQ_ERR_SHAPE", 3: "PQ_ERR_MODE", 4: 
 EXPORTS = ("pq_code_row_bytes", "pq_packed_bytes", "pq_default_grad_scale", "pq_status_str", "pq_version",
            "pq_quantize_fwd", "pq_quantize_bwd", "pq_pack_w2", "pq_pack_w4", "pq_w2a16_gemm",
            "pq_w4a16_gemm", "pq_quantize_fwd_grouped", "pq_quantize_bwd_grouped", "pq_qat_step",
-           "pq_qat_step_grouped", "pq_pack", "pq_gemm", "pq_gemm_f32a")
+           "pq_qat_step_grouped", "pq_pack", "pq_gemm", "pq_gemm_f32a", "pq_num_levels", "pq_level_stats",
+           "pq_weight_movement")
 
 
 class PQError(RuntimeError):
@@ -86,13 +87,17 @@ def _load():
     L.pq_pack.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp]
     L.pq_gemm.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp]
     L.pq_gemm_f32a.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp]
+    L.pq_num_levels.argtypes = [i32]
+    L.pq_num_levels.restype = i32
+    L.pq_level_stats.argtypes = [i32, i64, i64, vp, vp, vp, vp]
+    L.pq_weight_movement.argtypes = [i64, i64, vp, vp, vp, vp, vp]
     L.pq_quantize_fwd_grouped.argtypes = [i32, i32, vp, vp, u32, vp]
     L.pq_quantize_bwd_grouped.argtypes = [i32, i32, vp, vp, i32, vp]
     L.pq_qat_step.argtypes = [i32, i64, i64, vp, vp, vp, i32, dbl, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.pq_qat_step_grouped.argtypes = [i32, i32, vp, vp, i32, vp, vp]
     for name in EXPORTS:
         if name not in ("pq_code_row_bytes", "pq_packed_bytes", "pq_default_grad_scale", "pq_status_str",
-                        "pq_version"):
+                        "pq_version", "pq_num_levels"):
             getattr(L, name).restype = i32
     return L
 
@@ -190,6 +195,20 @@ def pq_gemm_f32a(mode, M, N, K, X, packed, alpha, Y, stream=None) -> None:
 
 
 PQ_CODES_EXPORT = 2
+
+
+def pq_num_levels(mode: int) -> int:
+    return int(lib.pq_num_levels(mode))
+
+
+def pq_level_stats(mode, rows, cols, codes, counts, entropy=None, stream=None) -> None:
+    _check(lib.pq_level_stats(mode, rows, cols, _ptr(codes), _ptr(counts), _ptr(entropy), _stream(stream)),
+           "pq_level_stats")
+
+
+def pq_weight_movement(rows, cols, W, W0, sq_diff, sq_ref, stream=None) -> None:
+    _check(lib.pq_weight_movement(rows, cols, _ptr(W), _ptr(W0), _ptr(sq_diff), _ptr(sq_ref), _stream(stream)),
+           "pq_weight_movement")
 
 
 class MatTable:

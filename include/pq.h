@@ -388,6 +388,35 @@ pq_status pq_qat_step_grouped(int mode, int count, const pq_step_mat *descs_host
                               const pq_step_mat *descs_dev, int g_dtype, const pq_adamw *hp,
                               void *stream);
 
+/*
+ * Diagnostics.  How the weights of each row spread over the levels -- the
+ * level occupancy behind the SEQ-vs-LSQ argument ([Rebuttal], part on why
+ * SEQ beats LSQ; [Note] "Finding 3" level sets) -- and how far training
+ * moved the shadow weights from a reference ([Note] "QAT versus PTQ": QAT
+ * compensates for the quantizer rather than reconstructing the weights).
+ *
+ * pq_num_levels -- levels of a mode (2, 3, 4, 8, 16 for 1, 1.58, 2, 3, 4
+ * bits), -1 for a bad mode.
+ *
+ * pq_level_stats -- from the forward's row-major codes ([rows,
+ * pq_code_row_bytes(mode, cols)]): counts [rows, pq_num_levels(mode)] u32,
+ * counts[i, c] = weights of row i stored with code c (code c is level c,
+ * lowest first), and optionally entropy [rows] f64, -sum_c p_c log2 p_c with
+ * p_c = counts[i, c] / cols (binary64; 0 for a row on one level).  Reads
+ * 1/8 .. 1/2 byte per weight.
+ *
+ * pq_weight_movement -- sq_diff[i] = sum_j (W[i,j] - W0[i,j])^2 and
+ * sq_ref[i] = sum_j W0[i,j]^2 per row, each difference and square in
+ * binary64, summed in a fixed order (run-to-run identical); the relative
+ * movement of a matrix is sqrt(sum sq_diff / sum sq_ref).  W, W0 fp32
+ * [rows, cols] (16-byte aligned), outputs f64 [rows].
+ */
+int pq_num_levels(int mode);
+pq_status pq_level_stats(int mode, int64_t rows, int64_t cols, const uint8_t *codes,
+                         uint32_t *counts, double *entropy, void *stream);
+pq_status pq_weight_movement(int64_t rows, int64_t cols, const float *W, const float *W0,
+                             double *sq_diff, double *sq_ref, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -52,6 +52,7 @@ def test_helpers(pq):
     assert pq.pq_packed_bytes(pq.PQ_W2_SEQ, 16, 12) == -1
     assert pq.pq_default_grad_scale(pq.PQ_W4_LSQ, 4, 16) == pytest.approx((4 * 16 * 7) ** -0.5)
     assert pq.pq_default_grad_scale(pq.PQ_W2_SEQ, 0, 16) == 0.0
+    assert [pq.pq_num_levels(m) for m in range(5)] == [2, 3, 4, 8, 16] and pq.pq_num_levels(5) == -1
     assert "NULL" in pq.pq_status_str(1)
     assert "gfx950" in pq.pq_version()
 
@@ -187,3 +188,14 @@ def test_qat_step_argument_checks(pq):
     mats[1].codes = B
     assert L.pq_qat_step_grouped(2, 2, ctypes.addressof(mats), A, 0, H, None) == 7  # mixed outputs
     assert L.pq_qat_step_grouped(2, 0, None, None, 0, H, None) == 0                # empty stack
+
+
+def test_diagnostics_argument_checks(pq):
+    L = pq.lib
+    assert L.pq_level_stats(7, 4, 64, A, B, None, None) == 3
+    assert L.pq_level_stats(2, 4, 60, A, B, None, None) == 2
+    assert L.pq_level_stats(2, 4, 64, None, B, None, None) == 1
+    assert L.pq_level_stats(2, 0, 64, None, None, None, None) == 0               # empty
+    assert L.pq_weight_movement(4, 64, A, MIS, A, B, None) == 4
+    assert L.pq_weight_movement(4, 64, A, B, None, B, None) == 1
+    assert L.pq_weight_movement(-1, 64, A, B, A, B, None) == 2
