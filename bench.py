@@ -441,6 +441,7 @@ def main():
     }
 
     if not args.no_extras:
+        out["diagnostics"] = diagnostics_measure(torch, pq, W16, a16, stream)
         out["train_forward"] = train_forward_measure(torch, pq, stack, stream)
         out["qat_step"] = qat_step_measure(torch, pq, stack, ftab, btab, stream)
         out["qat_step"]["traffic"] = step_traffic
@@ -464,6 +465,31 @@ def time_it(torch, stream, fn, reps):
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
     return float(np.mean([evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]))
+
+
+def diagnostics_measure(torch, pq, W16, a16, stream, reps=10):
+    """Level occupancy of the 16384 x 16384 weight's codes and its movement
+    against a perturbed copy: one launch each."""
+    mode = pq.PQ_W2_SEQ
+    N = K = GEMM_NK
+    L = pq.pq_num_levels(mode)
+    dev = W16.device
+    codes = torch.empty(N, pq.pq_code_row_bytes(mode, K), dtype=torch.uint8, device=dev)
+    pq.pq_quantize_fwd(mode, N, K, W16, a16, 0, None, None, codes)
+    counts = torch.empty(N, L, dtype=torch.int32, device=dev)
+    ent = torch.empty(N, dtype=torch.float64, device=dev)
+    W0 = W16 + 1e-4
+    d2 = torch.empty(N, dtype=torch.float64, device=dev)
+    r2 = torch.empty(N, dtype=torch.float64, device=dev)
+    ts = b2b_ms(torch, stream, lambda i: pq.pq_level_stats(mode, N, K, codes, counts, ent), reps)
+    tm = b2b_ms(torch, stream, lambda i: pq.pq_weight_movement(N, K, W16, W0, d2, r2), reps)
+    sb, mb = N * K / 4 + N * (4 * L + 8), N * K * 8 + N * 16
+    out = dict(level_stats_ms=round(ts, 4), level_stats_GBs=round(sb / ts / 1e6, 1),
+               level_stats_frac=round(sb / ts / 1e6 / HBM_PEAK_GBS, 4),
+               movement_ms=round(tm, 4), movement_GBs=round(mb / tm / 1e6, 1),
+               movement_frac=round(mb / tm / 1e6 / HBM_PEAK_GBS, 4), shape=f"{N}x{K}")
+    del codes, W0
+    return out
 
 
 TRAIN_TOKENS = 16384  # 8 sequences x 2048 tokens (one GPU's share of the recipe's batch)

@@ -38,9 +38,28 @@ __device__ __forceinline__ double wave_sum_f64(double v)
     return v;
 }
 
+// Codes equal to l among the 32 / CW fields of a word: XOR with l in every
+// field makes the matching fields zero; OR-folding each field into its low
+// bit and counting the low bits that stay clear counts them.
+template <int CW>
+__device__ __forceinline__ uint32_t count_equal(uint32_t d, uint32_t l, uint32_t valid_fields_mask)
+{
+    if constexpr (CW == 1) {
+        const uint32_t ones = __builtin_popcount(d & valid_fields_mask);
+        return l ? ones : __builtin_popcount(valid_fields_mask) - ones;
+    } else {
+        constexpr uint32_t kLow = CW == 2 ? 0x55555555u : 0x11111111u;
+        uint32_t x = d ^ (l * kLow);
+        x |= x >> 1;
+        if constexpr (CW == 4) x |= x >> 2;
+        return __builtin_popcount(~x & kLow & valid_fields_mask);
+    }
+}
+
 // Level occupancy of one row of row-major codes (CW bits each, LSB first).
-// Each lane takes bytes lane, lane + 64, ... and counts their codes per
-// level in registers (one compare-and-add per level, no indexed registers).
+// Each lane takes 32-bit words lane, lane + 64, ... of the row (bytes when
+// the rows are not word-aligned) and counts each level with a few bit
+// operations and a popcount per word.
 template <int CW, int L>
 __global__ __launch_bounds__(256) void k_level_stats(const uint8_t *codes, int64_t rows, int64_t cols,
                                                      uint32_t *counts, double *entropy)
@@ -53,13 +72,18 @@ __global__ __launch_bounds__(256) void k_level_stats(const uint8_t *codes, int64
     uint32_t c[L];
 #pragma unroll
     for (int l = 0; l < L; ++l) c[l] = 0;
-    for (int64_t b = lane; b < rb; b += 64) {
-        const uint32_t byte = cr[b];
+    if ((rb & 3) == 0 && (reinterpret_cast<uintptr_t>(codes) & 3) == 0) {
+        const uint32_t *wr = reinterpret_cast<const uint32_t *>(cr);
+        for (int64_t i = lane; i < rb / 4; i += 64) {
+            const uint32_t d = __builtin_nontemporal_load(&wr[i]);
 #pragma unroll
-        for (int e = 0; e < 8 / CW; ++e) {
-            const uint32_t code = (byte >> (CW * e)) & ((1u << CW) - 1u);
+            for (int l = 0; l < L; ++l) c[l] += count_equal<CW>(d, static_cast<uint32_t>(l), 0xFFFFFFFFu);
+        }
+    } else {
+        for (int64_t b = lane; b < rb; b += 64) {
+            const uint32_t d = cr[b];
 #pragma unroll
-            for (int l = 0; l < L; ++l) c[l] += code == static_cast<uint32_t>(l) ? 1u : 0u;
+            for (int l = 0; l < L; ++l) c[l] += count_equal<CW>(d, static_cast<uint32_t>(l), 0xFFu);
         }
     }
 #pragma unroll
