@@ -13,9 +13,9 @@ import numpy as np
 
 from .build import LIB, build as _build
 
-BINARY, TERNARY, SEQ2, LSQ3, LSQ4 = 0, 1, 2, 3, 4
-MODES = (BINARY, TERNARY, SEQ2, LSQ3, LSQ4)
-CODE_BITS = {BINARY: 1, TERNARY: 2, SEQ2: 2, LSQ3: 4, LSQ4: 4}
+BINARY, TERNARY, SEQ2, LSQ3, LSQ4, LSQ2, LSQ158 = 0, 1, 2, 3, 4, 5, 6
+MODES = (BINARY, TERNARY, SEQ2, LSQ3, LSQ4, LSQ2, LSQ158)
+CODE_BITS = {BINARY: 1, TERNARY: 2, SEQ2: 2, LSQ3: 4, LSQ4: 4, LSQ2: 2, LSQ158: 2}
 
 _lib = None
 _f32p = ctypes.POINTER(ctypes.c_float)

@@ -46,7 +46,11 @@ enum {
     PQO_W158_SEQ_TERNARY = 1, /* 1.58 bit, SEQ                           */
     PQO_W2_SEQ = 2,           /* 2 bit, SEQ                              */
     PQO_W3_LSQ = 3,           /* 3 bit, LSQ integer grid                 */
-    PQO_W4_LSQ = 4            /* 4 bit, LSQ integer grid                 */
+    PQO_W4_LSQ = 4,           /* 4 bit, LSQ integer grid                 */
+    /* The LSQ grids the pages set against SEQ at 2 and 1.58 bits ([Rebuttal],
+     * part on why SEQ beats LSQ): the ablation, not the recipe. */
+    PQO_W2_LSQ = 5,           /* 2 bit, LSQ levels {-2, -1, 0, 1}        */
+    PQO_W158_LSQ = 6          /* 1.58 bit, LSQ levels {-1, 0, 1}         */
 };
 
 /* [Note] "Paper vs. code", first bullet: the shipped clip is 1 - 1e-2, which
@@ -57,7 +61,7 @@ static const float ALPHA_FLOOR = 1e-5f;
 /* [Note] "Finding 3": ternary SEQ levels are {-2/3, 0, +2/3} alpha. */
 static const float TWO_THIRDS = (float)(2.0 / 3.0);
 
-static int valid_mode(int mode) { return mode >= PQO_W1_BINARY && mode <= PQO_W4_LSQ; }
+static int valid_mode(int mode) { return mode >= PQO_W1_BINARY && mode <= PQO_W158_LSQ; }
 
 /* Bits per stored code: 1 for binary, 2 for ternary and 2-bit SEQ (the
  * [News] storage paragraph notes ternary is often kept as 2-bit integers),
@@ -70,14 +74,38 @@ int pqo_code_bits(int mode)
     case PQO_W2_SEQ: return 2;
     case PQO_W3_LSQ: return 4;
     case PQO_W4_LSQ: return 4;
+    case PQO_W2_LSQ: return 2;
+    case PQO_W158_LSQ: return 2;
     }
     return -1;
 }
 
-/* LSQ integer grid [Note] "Finding 3": levels -2^(b-1) .. 2^(b-1)-1. */
-static int lsq_bits(int mode) { return mode == PQO_W3_LSQ ? 3 : 4; }
-static float lsq_qn(int mode) { return -(float)(1 << (lsq_bits(mode) - 1)); }
-static float lsq_qp(int mode) { return (float)((1 << (lsq_bits(mode) - 1)) - 1); }
+/* LSQ integer grid [Note] "Finding 3": levels -2^(b-1) .. 2^(b-1)-1, so
+ * {-2, -1, 0, 1} at 2 bits ([Rebuttal], 2-bit bullet); at 1.58 bits LSQ
+ * scales the weight to [-1, 1] and rounds onto {-1, 0, 1} ([Rebuttal],
+ * 1.58-bit bullet). */
+static int is_lsq(int mode)
+{
+    return mode == PQO_W3_LSQ || mode == PQO_W4_LSQ || mode == PQO_W2_LSQ || mode == PQO_W158_LSQ;
+}
+static float lsq_qn(int mode)
+{
+    switch (mode) {
+    case PQO_W158_LSQ: return -1.0f;
+    case PQO_W2_LSQ: return -2.0f;
+    case PQO_W3_LSQ: return -4.0f;
+    default: return -8.0f;
+    }
+}
+static float lsq_qp(int mode)
+{
+    switch (mode) {
+    case PQO_W158_LSQ: return 1.0f;
+    case PQO_W2_LSQ: return 1.0f;
+    case PQO_W3_LSQ: return 3.0f;
+    default: return 7.0f;
+    }
+}
 
 /* Smallest step index r of each grid; the stored code is r - r_min. */
 static int r_min_of(int mode)
@@ -173,9 +201,9 @@ static int ternary_quantize(float w, float alpha, float *q_out, float *x_out)
     return r;
 }
 
-/* LSQ at 3/4 bits: q = alpha * round(clamp(w/alpha, Qn, Qp)) on the integer
- * grid Qn = -2^(b-1) .. Qp = 2^(b-1)-1 ([Note] "Finding 3"; the dispatch row
- * of "Paper vs. code" sends 3 and 4 bits to LSQ). */
+/* LSQ: q = alpha * round(clamp(w/alpha, Qn, Qp)) on the integer grid
+ * ([Note] "Finding 3"; the dispatch row of "Paper vs. code" sends 3 and 4
+ * bits to LSQ; the 2- and 1.58-bit grids are the [Rebuttal]'s ablation). */
 static int lsq_quantize(int mode, float w, float alpha, float *q_out, float *x_out)
 {
     float a = alpha > ALPHA_FLOOR ? alpha : ALPHA_FLOOR;
@@ -211,7 +239,9 @@ int pqo_quantize_scalar(int mode, float w, float alpha, float *q_out, float *x_o
     case PQO_W158_SEQ_TERNARY: return ternary_quantize(w, alpha, q_out, x_out);
     case PQO_W2_SEQ: return pqo_seq2_quantize(w, alpha, CLIP_SHIPPED, q_out, x_out);
     case PQO_W3_LSQ:
-    case PQO_W4_LSQ: return lsq_quantize(mode, w, alpha, q_out, x_out);
+    case PQO_W4_LSQ:
+    case PQO_W2_LSQ:
+    case PQO_W158_LSQ: return lsq_quantize(mode, w, alpha, q_out, x_out);
     }
     return 0;
 }
@@ -266,7 +296,8 @@ int pqo_max_threads(void)
  * alpha initialisation, per output row.
  *   2-bit SEQ and ternary: max|w| ([Note] "The 2-bit recipe" table and the
  *   scale-init row of "Paper vs. code").
- *   LSQ: max|w| / (2^(b-1) - 1), one binary32 division (same row).
+ *   LSQ: max|w| / Qp, Qp = 2^(b-1) - 1 (3 at 3 bits, 7 at 4, 1 for the
+ *   2-bit and the 1.58-bit LSQ grids), one binary32 division (same row).
  *   1 bit: mean|w|, summed in binary64 in column order, divided in binary64,
  *   rounded once to binary32.
  * Returns 0, or -1 on a bad argument.
@@ -287,7 +318,7 @@ int pqo_alpha_init(int mode, int64_t rows, int64_t cols, const float *W, float *
                 float v = fabsf(w[j]);
                 if (v > m) m = v;
             }
-            if (mode == PQO_W3_LSQ || mode == PQO_W4_LSQ) m = m / lsq_qp(mode);
+            if (is_lsq(mode)) m = m / lsq_qp(mode);
             alpha[i] = m;
         }
     }
@@ -331,6 +362,8 @@ static double grad_qp(int mode)
     switch (mode) {
     case PQO_W3_LSQ: return 3.0;
     case PQO_W4_LSQ: return 7.0;
+    case PQO_W2_LSQ: return 1.0;
+    case PQO_W158_LSQ: return 1.0;
     default: return 1.0;
     }
 }
@@ -383,7 +416,7 @@ int pqo_quantize_bwd(int mode, int64_t rows, int64_t cols, const float *W,
                 inside = (x >= -1.0f) && (x <= 1.0f);
                 if (inside) s = (double)r - (double)x;
                 else s = (double)r;
-            } else if (mode == PQO_W3_LSQ || mode == PQO_W4_LSQ) {
+            } else if (is_lsq(mode)) {
                 float qn = lsq_qn(mode), qp = lsq_qp(mode);
                 inside = (x >= qn) && (x <= qp);
                 if (inside) s = (double)r - (double)x;
@@ -413,7 +446,8 @@ int pqo_quantize_bwd(int mode, int64_t rows, int64_t cols, const float *W,
  * ------------------------------------------------------------------------- */
 static int deployable(int mode)
 {
-    return mode == PQO_W158_SEQ_TERNARY || mode == PQO_W2_SEQ || mode == PQO_W3_LSQ || mode == PQO_W4_LSQ;
+    return mode == PQO_W158_SEQ_TERNARY || mode == PQO_W2_SEQ || mode == PQO_W3_LSQ || mode == PQO_W4_LSQ ||
+           mode == PQO_W2_LSQ || mode == PQO_W158_LSQ;
 }
 
 int pqo_pack(int mode, int64_t rows, int64_t cols, const float *W, const float *alpha,
@@ -539,6 +573,8 @@ int pqo_num_levels(int mode)
     case PQO_W2_SEQ: return 4;
     case PQO_W3_LSQ: return 8;
     case PQO_W4_LSQ: return 16;
+    case PQO_W2_LSQ: return 4;
+    case PQO_W158_LSQ: return 3;
     default: return -1;
     }
 }

@@ -31,7 +31,7 @@ from bit_quantization_aware_amd import synth
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 MODE_NAMES = {"binary": O.BINARY, "ternary": O.TERNARY, "seq2": O.SEQ2, "lsq3": O.LSQ3,
-              "lsq4": O.LSQ4}
+              "lsq4": O.LSQ4, "lsq2": O.LSQ2, "lsq158": O.LSQ158}
 F32 = np.float32
 CLIP = F32(0.99)
 
@@ -61,11 +61,13 @@ def clip_bounds(mode):
         return F32(-4), F32(3)
     if mode == O.LSQ4:
         return F32(-8), F32(7)
-    return F32(-1), F32(1)
+    if mode == O.LSQ2:
+        return F32(-2), F32(1)
+    return F32(-1), F32(1)          # binary, 1.58-bit LSQ
 
 
 def r_min(mode):
-    return {O.BINARY: -1, O.TERNARY: -1, O.SEQ2: -2, O.LSQ3: -4, O.LSQ4: -8}[mode]
+    return {O.BINARY: -1, O.TERNARY: -1, O.SEQ2: -2, O.LSQ3: -4, O.LSQ4: -8, O.LSQ2: -2, O.LSQ158: -1}[mode]
 
 
 def unpack_codes(codes, mode, cols):
@@ -332,7 +334,7 @@ def test_alpha_grad_finite_difference_when_all_clipped(mode):
 def test_default_grad_scale_reading():
     # Documented reading (parity unpinned): 1/sqrt(n * Qp), n = rows*cols,
     # Qp = 1, 1, 1, 3, 7 for 1, 1.58, 2, 3, 4 bits.
-    for mode, qp in zip(O.MODES, (1, 1, 1, 3, 7)):
+    for mode, qp in zip(O.MODES, (1, 1, 1, 3, 7, 1, 1)):
         assert O.default_grad_scale(mode, 64, 128) == pytest.approx((64 * 128 * qp) ** -0.5)
 
 
@@ -355,7 +357,7 @@ def test_alpha_init_matches_numpy(mode):
     W[3] = 0.0
     a = O.alpha_init(mode, W)
     amax = np.abs(W).max(axis=1)
-    if mode in (O.SEQ2, O.TERNARY):
+    if mode in (O.SEQ2, O.TERNARY, O.LSQ2, O.LSQ158):   # max|w| / Qp with Qp = 1 for the LSQ ablation grids
         assert np.array_equal(a, amax)
     elif mode == O.LSQ3:
         assert np.array_equal(a, amax / F32(3))
@@ -599,3 +601,19 @@ def test_weight_movement_matches_numpy():
     assert np.allclose(r2, want_r, rtol=1e-13, atol=0)
     z, _ = O.weight_movement(W0, W0)
     assert not z.any()
+
+
+def test_seq_levels_carry_more_entropy_than_lsq():
+    """[Rebuttal], part on why SEQ beats LSQ: on the same weights with each
+    grid's own max-based init, SEQ's equal-width bins spread the weights over
+    the levels more evenly than LSQ's grid at 2 bits ({-2,-1,0,1}) and at 1.58
+    bits (LSQ's middle bin twice as wide), so the level entropy is higher."""
+    rng = np.random.default_rng(97)
+    W = synth.normal_f32(rng, (64, 1536), 0.02)
+    ent = {}
+    for mode in (O.SEQ2, O.LSQ2, O.TERNARY, O.LSQ158):
+        _, _, codes = O.quantize_fwd(mode, W, O.alpha_init(mode, W))
+        ent[mode] = O.level_stats(mode, codes, 1536)[1].mean()
+    assert ent[O.SEQ2] > ent[O.LSQ2] + 0.1
+    assert ent[O.TERNARY] > ent[O.LSQ158] + 0.1
+    assert ent[O.SEQ2] <= 2.0 and ent[O.TERNARY] <= np.log2(3)
