@@ -18,7 +18,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-inline bool valid_mode(int mode) { return mode >= PQ_W1_BINARY && mode <= PQ_W4_LSQ; }
+inline bool valid_mode(int mode) { return mode >= PQ_W1_BINARY && mode <= PQ_W158_LSQ; }
 
 inline int code_bits(int mode)
 {
@@ -28,6 +28,8 @@ inline int code_bits(int mode)
     case PQ_W2_SEQ: return 2;
     case PQ_W3_LSQ: return 4;
     case PQ_W4_LSQ: return 4;
+    case PQ_W2_LSQ: return 2;
+    case PQ_W158_LSQ: return 2;
     default: return -1;
     }
 }

@@ -989,6 +989,8 @@ bool level_map(int mode, LevelMap *lm)
     case PQ_W2_SEQ: *lm = {2, 1.5f, 0.5f}; return true;
     case PQ_W3_LSQ: *lm = {4, 4.0f, 1.0f}; return true;
     case PQ_W4_LSQ: *lm = {4, 8.0f, 1.0f}; return true;
+    case PQ_W2_LSQ: *lm = {2, 2.0f, 1.0f}; return true;    // the ablation grids ([Rebuttal])
+    case PQ_W158_LSQ: *lm = {2, 1.0f, 1.0f}; return true;
     default: return false;
     }
 }

@@ -82,6 +82,15 @@ template <> struct Mode<PQ_W3_LSQ> {
     static constexpr int cw = 4;
     static constexpr float lo = -4.0f, hi = 3.0f;  // LSQ grid -2^(b-1) .. 2^(b-1)-1
 };
+// The LSQ grids the pages set against SEQ at 2 and 1.58 bits ([Rebuttal]).
+template <> struct Mode<PQ_W2_LSQ> {
+    static constexpr int cw = 2;
+    static constexpr float lo = -2.0f, hi = 1.0f;
+};
+template <> struct Mode<PQ_W158_LSQ> {
+    static constexpr int cw = 2;
+    static constexpr float lo = -1.0f, hi = 1.0f;
+};
 template <> struct Mode<PQ_W4_LSQ> {
     static constexpr int cw = 4;
     static constexpr float lo = -8.0f, hi = 7.0f;
@@ -131,7 +140,7 @@ __device__ __forceinline__ uint32_t quant_x(float w, float x, float &lvl)
         const int r = static_cast<int>(__builtin_rintf(xc * 1.5f));
         lvl = static_cast<float>(r) * kTwoThirds;
         return static_cast<uint32_t>(r + 1);
-    } else if constexpr (MODE == PQ_W3_LSQ || MODE == PQ_W4_LSQ) {
+    } else if constexpr (MODE == PQ_W3_LSQ || MODE == PQ_W4_LSQ || MODE == PQ_W2_LSQ || MODE == PQ_W158_LSQ) {
         // LSQ integer grid: round(clamp(x, Qn, Qp)).
         const float xc = __builtin_amdgcn_fmed3f(x, Mode<MODE>::lo, Mode<MODE>::hi);
         const int r = static_cast<int>(__builtin_rintf(xc));
@@ -309,7 +318,8 @@ __global__ __launch_bounds__(256, PQ_QUANT_FWD_MINB) void k_quant_fwd(LaunchTabl
                     mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
                 }
                 mx = team_max<WPR>(mx, lds_f);
-                if constexpr (MODE == PQ_W3_LSQ || MODE == PQ_W4_LSQ) mx = mx / Mode<MODE>::hi;
+                if constexpr (MODE == PQ_W3_LSQ || MODE == PQ_W4_LSQ || MODE == PQ_W2_LSQ || MODE == PQ_W158_LSQ)
+                    mx = mx / Mode<MODE>::hi;
                 alpha_raw = mx;
             }
             if (tl == 0) m.alpha[row] = alpha_raw;
@@ -709,7 +719,8 @@ bool finite(double x) { return x == x && x < 1e300 && x > -1e300; }
 // and 4-bit LSQ) code container.
 bool deployable(int mode)
 {
-    return mode == PQ_W158_SEQ_TERNARY || mode == PQ_W2_SEQ || mode == PQ_W3_LSQ || mode == PQ_W4_LSQ;
+    return mode == PQ_W158_SEQ_TERNARY || mode == PQ_W2_SEQ || mode == PQ_W3_LSQ || mode == PQ_W4_LSQ ||
+           mode == PQ_W2_LSQ || mode == PQ_W158_LSQ;
 }
 
 int choose_wpr(int64_t total_rows, int64_t total_elems)
@@ -808,6 +819,8 @@ void launch_fwd(int mode, bool init, unsigned outs, const LaunchTable &lt, int b
     case PQ_W158_SEQ_TERNARY: launch_fwd_mode<PQ_W158_SEQ_TERNARY>(init, outs, lt, blocks, wpr, s); break;
     case PQ_W2_SEQ: launch_fwd_mode<PQ_W2_SEQ>(init, outs, lt, blocks, wpr, s); break;
     case PQ_W3_LSQ: launch_fwd_mode<PQ_W3_LSQ>(init, outs, lt, blocks, wpr, s); break;
+    case PQ_W2_LSQ: launch_fwd_mode<PQ_W2_LSQ>(init, outs, lt, blocks, wpr, s); break;
+    case PQ_W158_LSQ: launch_fwd_mode<PQ_W158_LSQ>(init, outs, lt, blocks, wpr, s); break;
     default: launch_fwd_mode<PQ_W4_LSQ>(init, outs, lt, blocks, wpr, s); break;
     }
 }
@@ -844,6 +857,8 @@ void launch_bwd(int mode, int wpr, bool gbf, bool wdw, bool wmask, const LaunchT
     case PQ_W158_SEQ_TERNARY: launch_bwd_mode<PQ_W158_SEQ_TERNARY>(wpr, gbf, wdw, wmask, lt, blocks, s); break;
     case PQ_W2_SEQ: launch_bwd_mode<PQ_W2_SEQ>(wpr, gbf, wdw, wmask, lt, blocks, s); break;
     case PQ_W3_LSQ: launch_bwd_mode<PQ_W3_LSQ>(wpr, gbf, wdw, wmask, lt, blocks, s); break;
+    case PQ_W2_LSQ: launch_bwd_mode<PQ_W2_LSQ>(wpr, gbf, wdw, wmask, lt, blocks, s); break;
+    case PQ_W158_LSQ: launch_bwd_mode<PQ_W158_LSQ>(wpr, gbf, wdw, wmask, lt, blocks, s); break;
     default: launch_bwd_mode<PQ_W4_LSQ>(wpr, gbf, wdw, wmask, lt, blocks, s); break;
     }
 }
@@ -931,6 +946,8 @@ void launch_step(int mode, int wpr, bool gbf, const StepTable &lt, int blocks, c
     case PQ_W158_SEQ_TERNARY: launch_step_mode<PQ_W158_SEQ_TERNARY>(wpr, gbf, lt, blocks, k, s); break;
     case PQ_W2_SEQ: launch_step_mode<PQ_W2_SEQ>(wpr, gbf, lt, blocks, k, s); break;
     case PQ_W3_LSQ: launch_step_mode<PQ_W3_LSQ>(wpr, gbf, lt, blocks, k, s); break;
+    case PQ_W2_LSQ: launch_step_mode<PQ_W2_LSQ>(wpr, gbf, lt, blocks, k, s); break;
+    case PQ_W158_LSQ: launch_step_mode<PQ_W158_LSQ>(wpr, gbf, lt, blocks, k, s); break;
     default: launch_step_mode<PQ_W4_LSQ>(wpr, gbf, lt, blocks, k, s); break;
     }
 }
@@ -1138,6 +1155,8 @@ static pq_status pack_common(int mode, int64_t rows, int64_t cols, const float *
     case PQ_W158_SEQ_TERNARY: launch_fwd_t<PQ_W158_SEQ_TERNARY, false, O>(lt, nb, wpr, s, alpha_bf16); break;
     case PQ_W2_SEQ: launch_fwd_t<PQ_W2_SEQ, false, O>(lt, nb, wpr, s, alpha_bf16); break;
     case PQ_W3_LSQ: launch_fwd_t<PQ_W3_LSQ, false, O>(lt, nb, wpr, s, alpha_bf16); break;
+    case PQ_W2_LSQ: launch_fwd_t<PQ_W2_LSQ, false, O>(lt, nb, wpr, s, alpha_bf16); break;
+    case PQ_W158_LSQ: launch_fwd_t<PQ_W158_LSQ, false, O>(lt, nb, wpr, s, alpha_bf16); break;
     default: launch_fwd_t<PQ_W4_LSQ, false, O>(lt, nb, wpr, s, alpha_bf16); break;
     }
     return hipGetLastError() == hipSuccess ? PQ_OK : PQ_ERR_HIP;

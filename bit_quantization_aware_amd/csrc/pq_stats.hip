@@ -142,6 +142,8 @@ int num_levels(int mode)
     case PQ_W2_SEQ: return 4;
     case PQ_W3_LSQ: return 8;
     case PQ_W4_LSQ: return 16;
+    case PQ_W2_LSQ: return 4;
+    case PQ_W158_LSQ: return 3;
     default: return -1;
     }
 }
@@ -172,6 +174,8 @@ pq_status pq_level_stats(int mode, int64_t rows, int64_t cols, const uint8_t *co
         break;
     case PQ_W2_SEQ: hipLaunchKernelGGL((k_level_stats<2, 4>), g, b, 0, s, codes, rows, cols, counts, entropy); break;
     case PQ_W3_LSQ: hipLaunchKernelGGL((k_level_stats<4, 8>), g, b, 0, s, codes, rows, cols, counts, entropy); break;
+    case PQ_W2_LSQ: hipLaunchKernelGGL((k_level_stats<2, 4>), g, b, 0, s, codes, rows, cols, counts, entropy); break;
+    case PQ_W158_LSQ: hipLaunchKernelGGL((k_level_stats<2, 3>), g, b, 0, s, codes, rows, cols, counts, entropy); break;
     default: hipLaunchKernelGGL((k_level_stats<4, 16>), g, b, 0, s, codes, rows, cols, counts, entropy); break;
     }
     return hipGetLastError() == hipSuccess ? PQ_OK : PQ_ERR_HIP;

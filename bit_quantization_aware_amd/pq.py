@@ -17,10 +17,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpq.so")
 
 PQ_W1_BINARY, PQ_W158_SEQ_TERNARY, PQ_W2_SEQ, PQ_W3_LSQ, PQ_W4_LSQ = 0, 1, 2, 3, 4
-MODES = (PQ_W1_BINARY, PQ_W158_SEQ_TERNARY, PQ_W2_SEQ, PQ_W3_LSQ, PQ_W4_LSQ)
+PQ_W2_LSQ, PQ_W158_LSQ = 5, 6  # the LSQ ablation grids at 2 and 1.58 bits
+MODES = (PQ_W1_BINARY, PQ_W158_SEQ_TERNARY, PQ_W2_SEQ, PQ_W3_LSQ, PQ_W4_LSQ, PQ_W2_LSQ, PQ_W158_LSQ)
 MODE_NAMES = {PQ_W1_BINARY: "w1_binary", PQ_W158_SEQ_TERNARY: "w1.58_ternary",
-              PQ_W2_SEQ: "w2_seq", PQ_W3_LSQ: "w3_lsq", PQ_W4_LSQ: "w4_lsq"}
-CODE_BITS = {PQ_W1_BINARY: 1, PQ_W158_SEQ_TERNARY: 2, PQ_W2_SEQ: 2, PQ_W3_LSQ: 4, PQ_W4_LSQ: 4}
+              PQ_W2_SEQ: "w2_seq", PQ_W3_LSQ: "w3_lsq", PQ_W4_LSQ: "w4_lsq", PQ_W2_LSQ: "w2_lsq",
+              PQ_W158_LSQ: "w1.58_lsq"}
+CODE_BITS = {PQ_W1_BINARY: 1, PQ_W158_SEQ_TERNARY: 2, PQ_W2_SEQ: 2, PQ_W3_LSQ: 4, PQ_W4_LSQ: 4,
+             PQ_W2_LSQ: 2, PQ_W158_LSQ: 2}
 PQ_INIT_ALPHA = 1
 PQ_G_F32, PQ_G_BF16 = 0, 1
 STATUS = {0: "PQ_OK", 1: "PQ_ERR_NULL", 2: "PQ_ERR_SHAPE", 3: "PQ_ERR_MODE", 4: "PQ_ERR_ALIGN",

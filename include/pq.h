@@ -71,7 +71,9 @@ typedef enum pq_status {
 
 /* Bit widths of the unified framework ([Abstract]: 1, 1.58, 2, 3, 4 bits).
  * SEQ at 1.58 and 2 bits, LSQ at 3 and 4 bits ([Note] "Paper vs. code",
- * dispatch row).  Level sets, in units of alpha:
+ * dispatch row); the two LSQ grids the pages set against SEQ at 2 and 1.58
+ * bits ([Rebuttal], part on why SEQ beats LSQ) are the ablation modes 5 and
+ * 6.  Level sets, in units of alpha:
  *   PQ_W1_BINARY         {-1, +1}            sign(w), sign(0) = +1
  *   PQ_W158_SEQ_TERNARY  {-2/3, 0, +2/3}     ([Note] "Finding 3"; bins of
  *                                             [Rebuttal], 1.58-bit bullet)
@@ -79,22 +81,30 @@ typedef enum pq_status {
  *                                             formula row of "Paper vs. code")
  *   PQ_W3_LSQ            {-4 .. 3}           ([Note] "Finding 3": integer grid)
  *   PQ_W4_LSQ            {-8 .. 7}
+ *   PQ_W2_LSQ            {-2, -1, 0, 1}      ([Rebuttal], 2-bit bullet)
+ *   PQ_W158_LSQ          {-1, 0, 1}          (weights scaled to [-1, 1];
+ *                                             [Rebuttal], 1.58-bit bullet)
+ * LSQ clips x to [Qn, Qp] (the set's ends) and rounds half-to-even.
  * Stored codes: 1 bit for binary (0 -> -1, 1 -> +1); 2 bits for ternary and
  * 2-bit SEQ (code = step + 1 resp. step + 2, so ternary never stores 3; the
  * [News] storage paragraph notes ternary is commonly held in 2-bit integers);
- * a 4-bit nibble for LSQ (code = step + 2^(b-1)).  Codes are a bit stream
+ * a 4-bit nibble for 3- and 4-bit LSQ (code = step + 2^(b-1)); 2 bits for
+ * the ablation grids (code = step - Qn).  Codes are a bit stream
  * per row, first element in the lowest bits of the first byte. */
 typedef enum pq_mode {
     PQ_W1_BINARY = 0,
     PQ_W158_SEQ_TERNARY = 1,
     PQ_W2_SEQ = 2,
     PQ_W3_LSQ = 3,
-    PQ_W4_LSQ = 4
+    PQ_W4_LSQ = 4,
+    PQ_W2_LSQ = 5,
+    PQ_W158_LSQ = 6
 } pq_mode;
 
 /* pq_quantize_fwd flag: compute alpha from the row first and store it
  * ([Note] "The 2-bit recipe" table and the scale-init row of "Paper vs.
- * code": alpha = max|w| for SEQ and ternary, max|w| / (2^(b-1)-1) for LSQ;
+ * code": alpha = max|w| for SEQ and ternary, max|w| / Qp for LSQ with
+ * Qp = 2^(b-1)-1, i.e. 3, 7, and 1 for both ablation grids;
  * mean|w| for 1 bit, summed in binary64). */
 #define PQ_INIT_ALPHA 1u
 
@@ -197,8 +207,9 @@ pq_status pq_quantize_bwd(int mode, int64_t rows, int64_t cols, const float *W,
  */
 int64_t pq_packed_bytes(int mode, int64_t rows, int64_t cols);
 
-/* Widths with a deployment format ("deployable" below): PQ_W158_SEQ_TERNARY
- * and PQ_W2_SEQ in a 2-bit container, PQ_W3_LSQ and PQ_W4_LSQ in a 4-bit one
+/* Widths with a deployment format ("deployable" below): PQ_W158_SEQ_TERNARY,
+ * PQ_W2_SEQ, PQ_W2_LSQ and PQ_W158_LSQ in a 2-bit container, PQ_W3_LSQ and
+ * PQ_W4_LSQ in a 4-bit one
  * (ternary is commonly held in 2-bit integers, [News] storage paragraph).
  * pq_packed_bytes returns -1 for any other mode. */
 
@@ -271,7 +282,8 @@ pq_status pq_w4a16_gemm(int64_t M, int64_t N, int64_t K, const void *X,
 /* pq_gemm -- the same GEMM for any deployable width, on pq_pack(mode, ...)
  * weights, with the width's levels ([Note] "Finding 3"): ternary
  * (c - 1) * fl32(2/3), 2-bit SEQ (c - 1.5) / 2, 3-bit LSQ c - 4, 4-bit LSQ
- * c - 8; an other mode -> PQ_ERR_MODE.  These are the widths whose accuracy
+ * c - 8, and the ablation grids c - 2 (2-bit LSQ) and c - 1 (1.58-bit LSQ);
+ * an other mode -> PQ_ERR_MODE.  These are the widths whose accuracy
  * and storage the pages compare ([News] speed and storage paragraphs). */
 pq_status pq_gemm(int mode, int64_t M, int64_t N, int64_t K, const void *X,
                   const uint8_t *packed, const void *alpha_bf16, void *Y, void *stream);
@@ -396,7 +408,7 @@ pq_status pq_qat_step_grouped(int mode, int count, const pq_step_mat *descs_host
  * compensates for the quantizer rather than reconstructing the weights).
  *
  * pq_num_levels -- levels of a mode (2, 3, 4, 8, 16 for 1, 1.58, 2, 3, 4
- * bits), -1 for a bad mode.
+ * bits; 4 and 3 for the 2- and 1.58-bit LSQ grids), -1 for a bad mode.
  *
  * pq_level_stats -- from the forward's row-major codes ([rows,
  * pq_code_row_bytes(mode, cols)]): counts [rows, pq_num_levels(mode)] u32,

@@ -52,7 +52,7 @@ def test_helpers(pq):
     assert pq.pq_packed_bytes(pq.PQ_W2_SEQ, 16, 12) == -1
     assert pq.pq_default_grad_scale(pq.PQ_W4_LSQ, 4, 16) == pytest.approx((4 * 16 * 7) ** -0.5)
     assert pq.pq_default_grad_scale(pq.PQ_W2_SEQ, 0, 16) == 0.0
-    assert [pq.pq_num_levels(m) for m in range(5)] == [2, 3, 4, 8, 16] and pq.pq_num_levels(5) == -1
+    assert [pq.pq_num_levels(m) for m in range(7)] == [2, 3, 4, 8, 16, 4, 3] and pq.pq_num_levels(7) == -1
     assert "NULL" in pq.pq_status_str(1)
     assert "gfx950" in pq.pq_version()
 

@@ -70,7 +70,7 @@ def make_case(mode, seed, M, N, K, sigma=0.02):
     return X, packed, ab
 
 
-DEPLOYABLE = [O.SEQ2, O.LSQ4, O.TERNARY, O.LSQ3]
+DEPLOYABLE = [O.SEQ2, O.LSQ4, O.TERNARY, O.LSQ3, O.LSQ2, O.LSQ158]
 
 
 @pytest.mark.parametrize("mode", DEPLOYABLE)

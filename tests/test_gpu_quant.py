@@ -30,7 +30,7 @@ def _lib():
     yield
 
 
-MODES = [O.BINARY, O.TERNARY, O.SEQ2, O.LSQ3, O.LSQ4]
+MODES = [O.BINARY, O.TERNARY, O.SEQ2, O.LSQ3, O.LSQ4, O.LSQ2, O.LSQ158]
 
 
 def gpu_fwd(mode, W, alpha=None, init=False, want_f32=True):
@@ -122,7 +122,7 @@ def adversarial_rows(mode):
     cols = 64
     a = np.float32(2.0 ** -4)
     lo, hi = {O.SEQ2: (-0.99, 0.99), O.TERNARY: (-0.99, 0.99), O.LSQ3: (-4, 3), O.LSQ4: (-8, 7),
-              O.BINARY: (-1, 1)}[mode]
+              O.BINARY: (-1, 1), O.LSQ2: (-2, 1), O.LSQ158: (-1, 1)}[mode]
     rows = []
     rows.append(np.zeros(cols, np.float32))
     ties = np.array([-0.5, 0.0, 0.5, -1.5 / 1.5, 1.0 / 3.0, -1.0 / 3.0, 2.5, -3.5, 1.5, -2.5],
@@ -232,7 +232,7 @@ def test_pack_matches_forward_codes(mode):
     assert_bits_equal(packed, O.tile_codes(codes_fwd), "pack == fwd codes in export order")
 
 
-@pytest.mark.parametrize("mode", [O.SEQ2, O.LSQ4, O.TERNARY, O.LSQ3])
+@pytest.mark.parametrize("mode", [O.SEQ2, O.LSQ4, O.TERNARY, O.LSQ3, O.LSQ2, O.LSQ158])
 @pytest.mark.parametrize("rows,cols", [(1, 8), (17, 64), (16, 1024), (4100, 264), (4096, 520), (8192, 256)])
 def test_pack_export_order_shapes(mode, rows, cols):
     """Export byte order across the launch shapes: one row per block (fewer
@@ -350,6 +350,8 @@ BOUNDARIES = {
     O.LSQ3: [-4.0, 3.0, -3.5, 2.5, 0.5, -0.5, 1.5],
     O.LSQ4: [-8.0, 7.0, -7.5, 6.5, 0.5, -0.5, 3.5],
     O.BINARY: [1.0, -1.0, 0.0],
+    O.LSQ2: [-2.0, 1.0, -1.5, -0.5, 0.5],
+    O.LSQ158: [-1.0, 1.0, -0.5, 0.5, 0.0],
 }
 
 
@@ -378,7 +380,7 @@ def test_division_at_decision_boundaries(mode):
     check_bwd(mode, W, alphas, G, f"div-boundary bwd m{mode}")
 
 
-@pytest.mark.parametrize("mode", [O.TERNARY, O.SEQ2, O.LSQ3, O.LSQ4])
+@pytest.mark.parametrize("mode", [O.TERNARY, O.SEQ2, O.LSQ3, O.LSQ4, O.LSQ2, O.LSQ158])
 @pytest.mark.parametrize("rows,cols,init", [(333, 1600, True), (4100, 264, False), (17, 64, True),
                                             (64, 16384, False)])
 def test_fwd_codes_in_export_order(mode, rows, cols, init):

@@ -24,7 +24,7 @@ def _lib():
     yield
 
 
-@pytest.mark.parametrize("mode", [O.BINARY, O.TERNARY, O.SEQ2, O.LSQ3, O.LSQ4])
+@pytest.mark.parametrize("mode", [O.BINARY, O.TERNARY, O.SEQ2, O.LSQ3, O.LSQ4, O.LSQ2, O.LSQ158])
 @pytest.mark.parametrize("rows,cols", [(37, 264), (5, 8), (2, 16384), (4100, 64)])
 def test_level_stats(mode, rows, cols):
     rng = np.random.default_rng(rows + cols + mode)

@@ -93,7 +93,7 @@ def oracle_step(mode, st, step, g_bf16=False, hp=HP):
                       step, **hp)
 
 
-MODES = [O.BINARY, O.TERNARY, O.SEQ2, O.LSQ3, O.LSQ4]
+MODES = [O.BINARY, O.TERNARY, O.SEQ2, O.LSQ3, O.LSQ4, O.LSQ2, O.LSQ158]
 SHAPES = [(256, 256), (37, 72), (5, 8), (3, 1600), (1, 16384), (4100, 24), (70, 4352)]
 
 
