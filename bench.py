@@ -488,6 +488,16 @@ def diagnostics_measure(torch, pq, W16, a16, stream, reps=10):
                level_stats_frac=round(sb / ts / 1e6 / HBM_PEAK_GBS, 4),
                movement_ms=round(tm, 4), movement_GBs=round(mb / tm / 1e6, 1),
                movement_frac=round(mb / tm / 1e6 / HBM_PEAK_GBS, 4), shape=f"{N}x{K}")
+    # the pages' SEQ-vs-LSQ argument: mean level entropy (bits) of the same
+    # weight under each grid, each with its own max-based alpha init
+    grids = {}
+    for md in (pq.PQ_W2_SEQ, pq.PQ_W2_LSQ, pq.PQ_W158_SEQ_TERNARY, pq.PQ_W158_LSQ):
+        a = torch.zeros(N, dtype=torch.float32, device=dev)
+        pq.pq_quantize_fwd(md, N, K, W16, a, pq.PQ_INIT_ALPHA, None, None, codes)
+        cnt = torch.empty(N, pq.pq_num_levels(md), dtype=torch.int32, device=dev)
+        pq.pq_level_stats(md, N, K, codes, cnt, ent)
+        grids[pq.MODE_NAMES[md]] = round(float(ent.mean()), 4)
+    out["mean_level_entropy_bits"] = grids
     del codes, W0
     return out
 
