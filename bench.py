@@ -43,6 +43,10 @@ GEMM_MS = (1, 4, 16, 64, 512)
 GEMM_STEP_ORDER = (512, 64, 16, 4, 1)
 GEMM_NK = 16384
 ROTATE = 8
+LLAMA_MS = (1, 16, 256, 4096)
+# weight copies rotated per timed GEMM: enough that one pass over them
+# exceeds the 256 MB last-level cache, so every launch streams from HBM
+ROTATE_BYTES = 320 << 20
 
 
 def parse():
@@ -56,6 +60,8 @@ def parse():
                    help="only the back-to-back GEMM launches (for a kernel trace of them alone)")
     p.add_argument("--train-fwd-only", action="store_true",
                    help="only the training-forward measurement (for a kernel trace of it alone)")
+    p.add_argument("--llama-gemm-only", action="store_true",
+                   help="print only the Llama-3-8B projection GEMM measurements")
     p.add_argument("--qat-step-only", action="store_true",
                    help="only the fused QAT step measurement (for a kernel trace of it alone)")
     p.add_argument("--pmc-workload", action="store_true",
@@ -297,6 +303,10 @@ def main():
         print(json.dumps({"train_forward": train_forward_measure(torch, pq, stack, stream)}), flush=True)
         return
 
+    if args.llama_gemm_only:
+        print(json.dumps({"llama_gemm": llama_gemm_measure(torch, pq, synth, stream)}), flush=True)
+        return
+
     if args.qat_step_only:
         print(json.dumps({"qat_step": qat_step_measure(torch, pq, stack, ftab, btab, stream)}), flush=True)
         return
@@ -448,6 +458,7 @@ def main():
         out["gemm_back_to_back"] = gemm_back_to_back(torch, pq, Xs, packed, ab16, Ys, stream, ridge)
         out["sweep_bits"] = sweep_bits(torch, pq, stack, make_tables, stream)
         out["gemm_compare"] = gemm_compare(torch, pq, W16, a16, Xs, stream)
+        out["llama_gemm"] = llama_gemm_measure(torch, pq, synth, stream)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shapes, fb + bb)
@@ -668,6 +679,38 @@ def b2b_ms(torch, stream, run, reps):
     return e0.elapsed_time(e1) / reps
 
 
+def graph_ms(torch, run, reps, check=None):
+    """Mean time per launch of `reps` launches captured in one HIP graph and
+    replayed: launches a few microseconds long are then timed without the
+    host's per-call cost between them.  run(i, sid) launches call i on the
+    stream `sid`; `check`, if given, returns the output, which must be the
+    same after the replay as after an eager call."""
+    # warm launches and capture on one stream: the library keys its
+    # workspace by stream, so nothing is allocated while capturing
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(4):
+            run(i, side.cuda_stream)
+    torch.cuda.synchronize()
+    want = check().clone() if check else None
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for i in range(reps):
+            run(i, side.cuda_stream)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    if check is not None:
+        assert torch.equal(check(), want), "graph replay changed the output"
+    del g
+    return e0.elapsed_time(e1) / reps
+
+
 def gemm_compare(torch, pq, W16, a16, Xs, stream, reps=30):
     """The other widths through the same kernels (ternary in the 2-bit
     container, 3- and 4-bit LSQ in nibbles) and a hipBLASLt bf16 GEMM on the
@@ -709,6 +752,50 @@ def gemm_compare(torch, pq, W16, a16, Xs, stream, reps=30):
         fl = 2.0 * M * N * K
         res[f"m{M}"].update(bf16_hipblaslt_ms=round(tb, 5), bf16_tflops=round(fl / tb / 1e9, 2))
     del wbf
+    return res
+
+
+def llama_gemm_measure(torch, pq, synth, stream, reps=20):
+    """The four Llama-3-8B projections (2-bit SEQ, exported) through the W2A16
+    GEMM at M in {1, 16, 256, 4096}, next to a hipBLASLt bf16 GEMM on the
+    dequantized weight.  Both rotate weight copies (ROTATE_BYTES) and run
+    back to back inside one HIP graph (so that launches of a few microseconds
+    are not bound by the host's per-call cost); frac is against the
+    weight-stream roofline below the ridge point and the bf16 MFMA peak
+    above it."""
+    res = {}
+    ridge = MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3
+    for k, (_, name, N, K) in enumerate(synth.llama3_8b_shapes()):
+        W = torch.from_numpy(synth.weight("llama3_8b", k)).to("cuda")
+        a = torch.zeros(N, dtype=torch.float32, device="cuda")
+        wq = torch.empty(N, K, dtype=torch.bfloat16, device="cuda")
+        pq.pq_quantize_fwd(pq.PQ_W2_SEQ, N, K, W, a, pq.PQ_INIT_ALPHA, wq, None, None)
+        nb = pq.pq_packed_bytes(pq.PQ_W2_SEQ, N, K)
+        R = max(2, -(-ROTATE_BYTES // nb))
+        pk = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(R)]
+        ab = [torch.empty(N, dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+        for i in range(R):
+            pq.pq_pack_w2(N, K, W, a, pk[i], ab[i])
+        del W
+        Rb = max(2, -(-ROTATE_BYTES // (N * K * 2)))
+        wb = [wq] + [wq.clone() for _ in range(Rb - 1)]
+        pkp, abp = [t.data_ptr() for t in pk], [t.data_ptr() for t in ab]
+        for M in LLAMA_MS:
+            X = torch.from_numpy(synth.activations("llama3_8b", k, M, K).view(np.int16)).to("cuda") \
+                .view(torch.bfloat16)
+            Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+            xp, yp = X.data_ptr(), Y.data_ptr()
+            ms = graph_ms(torch, lambda i, sd: pq.pq_w2a16_gemm(M, N, K, xp, pkp[i % R], abp[i % R], yp, sd),
+                          reps, check=lambda: Y)
+            tb = graph_ms(torch, lambda i, sd: torch.matmul(X, wb[i % Rb].t(), out=Y), reps)
+            fl, by = 2.0 * M * N * K, gemm_bytes(M, N, K, 2)
+            gbs, tf = by / ms / 1e6, fl / ms / 1e9
+            frac = gbs / HBM_PEAK_GBS if fl / by < ridge else tf / MFMA_BF16_PEAK_TFLOPS
+            res[f"{name}_m{M}"] = dict(ms=round(ms, 5), tflops=round(tf, 2), weight_stream_GBs=round(gbs, 1),
+                                       frac=round(frac, 4), bf16_hipblaslt_ms=round(tb, 5),
+                                       speedup_vs_bf16=round(tb / ms, 2))
+        del pk, ab, wb, wq
+        torch.cuda.empty_cache()
     return res
 
 

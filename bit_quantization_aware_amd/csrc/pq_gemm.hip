@@ -49,7 +49,7 @@
 #define PQ_TILE_TARGET_WAVES 2048
 #endif
 #ifndef PQ_TILE_DMA_MID
-#define PQ_TILE_DMA_MID 0
+#define PQ_TILE_DMA_MID 1
 #endif
 #ifndef PQ_TILE_P2
 #define PQ_TILE_P2 4
@@ -515,6 +515,12 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
         constexpr bool code_now = ((p + 1) % C::SS) == 0;
         wait_vmcnt<tile_wait(p, P, C::SS, C::XI, NC, U)>();
         block_barrier();
+        // A wave just released from the barrier issues at raised priority
+        // until its refill is out: its fragment reads, first MFMAs and DMAs
+        // then go ahead of the other block's wave on the same SIMD, which is
+        // in the middle of its own MFMAs (measured: M = 512 at 16384^2,
+        // 218 -> 206 us back to back; M = 256, 123 -> 114 us).
+        __builtin_amdgcn_s_setprio(1);
         auto refill = [&]() {
             issue_x(s + P - 1, (p + P - 1) % P);
             if constexpr (code_now) issue_c((s + 1) / C::SS + 1);
@@ -529,6 +535,7 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
         // unit before their first MFMA.
         mma(fr[p & 1], [&]() {
             if (PQ_TILE_DMA_MID != 0) refill();
+            __builtin_amdgcn_s_setprio(0);
         });
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -894,12 +901,32 @@ struct StreamCfg {
                                        : (XI == 1 ? PQ_STREAM4_D1 : XI == 2 ? PQ_STREAM4_D2 : PQ_STREAM4_D4);
 };
 
+// Column tiles per block for N: the configured width while it still gives
+// about 3/4 of a block per CU, else half of it, down to one tile.  A block
+// streams its columns' codes at the rate of its waves' DMAs in flight, so a
+// narrow N spread over more, narrower blocks reads faster (N = 4096, M = 1:
+// 5.7 us with four tiles per block, 4.1 with one); at 16384 columns four
+// tiles measured best (one tile: 19.7 us against 15.9).
+constexpr int kStreamMinBlocks = 192;
+
+template <int BITS, int XI, int TN>
+void launch_stream_tn(const GemmArgs &a, hipStream_t s)
+{
+    using C = StreamCfg<BITS, XI>;
+    if constexpr (TN > 1) {
+        if ((a.N + 16 * TN - 1) / (16 * TN) < kStreamMinBlocks) {
+            launch_stream_tn<BITS, XI, TN / 2>(a, s);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((k_gemm_stream<BITS, TN, C::NW, C::D, XI>), dim3((a.N + 16 * TN - 1) / (16 * TN)),
+                       dim3(64 * C::NW), 0, s, a);
+}
+
 template <int BITS, int XI>
 void launch_stream(const GemmArgs &a, hipStream_t s)
 {
-    using C = StreamCfg<BITS, XI>;
-    hipLaunchKernelGGL((k_gemm_stream<BITS, C::TN, C::NW, C::D, XI>), dim3((a.N + 16 * C::TN - 1) / (16 * C::TN)),
-                       dim3(64 * C::NW), 0, s, a);
+    launch_stream_tn<BITS, XI, StreamCfg<BITS, XI>::TN>(a, s);
 }
 
 // Split-K workspace: one fp32 buffer per (device, stream), grown on demand.

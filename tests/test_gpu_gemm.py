@@ -77,7 +77,8 @@ DEPLOYABLE = [O.SEQ2, O.LSQ4, O.TERNARY, O.LSQ3, O.LSQ2, O.LSQ158]
 @pytest.mark.parametrize("M,N,K", [(8, 256, 256), (1, 64, 64), (5, 100, 320), (16, 257, 1024),
                                    (17, 64, 128), (33, 96, 192), (64, 130, 256), (65, 128, 64),
                                    (130, 300, 384), (257, 129, 512), (64, 512, 4096),
-                                   (100, 1000, 2048), (200, 260, 1600), (17, 8, 64)])
+                                   (100, 1000, 2048), (200, 260, 1600), (17, 8, 64),
+                                   (16, 8192, 512), (3, 6200, 1024), (1, 12300, 256)])
 def test_gemm_small_full_compare(mode, M, N, K):
     print(f"[gemm mode={mode} M={M} N={N} K={K}]", flush=True)
     X, packed, ab = make_case(mode, 7 * M + N + K, M, N, K)
