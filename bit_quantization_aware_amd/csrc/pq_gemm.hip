@@ -45,9 +45,6 @@
 #ifndef PQ_TILE_WN
 #define PQ_TILE_WN 4
 #endif
-#ifndef PQ_TILE_TARGET_WAVES
-#define PQ_TILE_TARGET_WAVES 2048
-#endif
 #ifndef PQ_TILE_DMA_MID
 #define PQ_TILE_DMA_MID 1
 #endif
@@ -56,6 +53,10 @@
 #endif
 #ifndef PQ_TILE_P4
 #define PQ_TILE_P4 4
+#endif
+// Fewest K stages per split of the tiled kernel's K split.
+#ifndef PQ_TILE_MIN_STAGES
+#define PQ_TILE_MIN_STAGES 4
 #endif
 #ifndef PQ_STREAM_NW
 #define PQ_STREAM_NW 4
@@ -960,22 +961,44 @@ pq_status workspace(hipStream_t stream, size_t bytes, float **out)
     return PQ_OK;
 }
 
-// Tiled path: choose the K split so that about two blocks per CU are live,
-// each split keeping at least four stages.
+constexpr int kNumCU = 256;  // MI355X / MI350X compute units
+
+// Estimated time (us) of a tiled launch with `splits` K splits, from
+// measurements at 16384^2 and the Llama-3-8B shapes: blocks run in rounds of
+// up to two per CU; one stage of a block takes about 0.56 us alone on its CU
+// and 0.78 us beside a second block, plus about 3 us of pipeline fill and
+// epilogue per round; a split adds its fp32 partials, written and read back
+// at about 5 TB/s, and the finalize launch.
+double tile_cost(int64_t tiles, int stages, int splits, int64_t M, int64_t N)
+{
+    const int64_t blocks = tiles * splits;
+    const int per_cu = blocks > kNumCU ? 2 : 1;
+    const int64_t rounds = (blocks + per_cu * kNumCU - 1) / (per_cu * kNumCU);
+    const int sps = (stages + splits - 1) / splits;
+    double t = static_cast<double>(rounds) * (sps * (per_cu == 1 ? 0.56 : 0.78) + 3.0);
+    if (splits > 1) t += 2.0 + static_cast<double>(splits) * static_cast<double>(M) * static_cast<double>(N) * 8.0 / 5e6;
+    return t;
+}
+
+// Tiled path: the K split of least estimated time, each split keeping at
+// least PQ_TILE_MIN_STAGES stages.
 template <int BITS>
 pq_status launch_tile(const GemmArgs &a, hipStream_t s)
 {
-    constexpr int kTargetBlocks = PQ_TILE_TARGET_WAVES / PQ_TILE_WN;
-    constexpr int kMinStages = 4;
+    constexpr int kMinStages = PQ_TILE_MIN_STAGES;
     const int mtiles = (a.M + kTileM - 1) / kTileM;
     using C = TileCfg<BITS, PQ_TILE_WN>;
     const int ntiles = (a.N + C::TN - 1) / C::TN;
     const int64_t tiles = static_cast<int64_t>(mtiles) * ntiles;
     const int stages = a.K / kStageK;
     int splits = 1;
-    if (tiles < kTargetBlocks * 3 / 4) {
-        const int want = static_cast<int>((kTargetBlocks + tiles - 1) / tiles);
-        splits = std::max(1, std::min(want, stages / kMinStages));
+    double best = tile_cost(tiles, stages, 1, a.M, a.N);
+    for (int sp = 2; sp <= std::min(64, stages / kMinStages); ++sp) {
+        const double c = tile_cost(tiles, stages, sp, a.M, a.N);
+        if (c < best) {
+            best = c;
+            splits = sp;
+        }
     }
     // stages per split: whole 64-byte groups, so every split starts a group
     const int sps = ((stages + splits - 1) / splits + C::SS - 1) / C::SS * C::SS;
