@@ -57,9 +57,9 @@ __device__ __forceinline__ uint32_t count_equal(uint32_t d, uint32_t l, uint32_t
 }
 
 // Level occupancy of one row of row-major codes (CW bits each, LSB first).
-// Each lane takes 32-bit words lane, lane + 64, ... of the row (bytes when
-// the rows are not word-aligned) and counts each level with a few bit
-// operations and a popcount per word.
+// Each lane takes 16-byte pieces lane, lane + 64, ... of the row (32-bit
+// words, or bytes, when the rows are not 16- or 4-byte aligned) and counts
+// each level with a few bit operations and a popcount per word.
 template <int CW, int L>
 __global__ __launch_bounds__(256) void k_level_stats(const uint8_t *codes, int64_t rows, int64_t cols,
                                                      uint32_t *counts, double *entropy)
@@ -72,7 +72,18 @@ __global__ __launch_bounds__(256) void k_level_stats(const uint8_t *codes, int64
     uint32_t c[L];
 #pragma unroll
     for (int l = 0; l < L; ++l) c[l] = 0;
-    if ((rb & 3) == 0 && (reinterpret_cast<uintptr_t>(codes) & 3) == 0) {
+    if ((rb & 15) == 0 && (reinterpret_cast<uintptr_t>(codes) & 15) == 0) {
+        // 16-byte loads, several in flight per lane
+        const u32x4 *qr = reinterpret_cast<const u32x4 *>(cr);
+#pragma unroll 4
+        for (int64_t i = lane; i < rb / 16; i += 64) {
+            const u32x4 d = __builtin_nontemporal_load(&qr[i]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int l = 0; l < L; ++l) c[l] += count_equal<CW>(d[e], static_cast<uint32_t>(l), 0xFFFFFFFFu);
+        }
+    } else if ((rb & 3) == 0 && (reinterpret_cast<uintptr_t>(codes) & 3) == 0) {
         const uint32_t *wr = reinterpret_cast<const uint32_t *>(cr);
         for (int64_t i = lane; i < rb / 4; i += 64) {
             const uint32_t d = __builtin_nontemporal_load(&wr[i]);

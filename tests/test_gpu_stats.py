@@ -25,7 +25,7 @@ def _lib():
 
 
 @pytest.mark.parametrize("mode", [O.BINARY, O.TERNARY, O.SEQ2, O.LSQ3, O.LSQ4, O.LSQ2, O.LSQ158])
-@pytest.mark.parametrize("rows,cols", [(37, 264), (5, 8), (2, 16384), (4100, 64)])
+@pytest.mark.parametrize("rows,cols", [(37, 264), (5, 8), (2, 16384), (4100, 64), (9, 5120)])
 def test_level_stats(mode, rows, cols):
     rng = np.random.default_rng(rows + cols + mode)
     W = synth.normal_f32(rng, (rows, cols), 0.02)
