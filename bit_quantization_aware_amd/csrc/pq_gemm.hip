@@ -352,8 +352,8 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
     // Code DMAs: one fetch covers SS stages of the block's columns, one
     // 64-byte group of each.  DMA i of wave w brings columns 16 (NC w + i) ..
     // +15, which is one 1-KB tile of the export order: lane l reads the
-    // 16-byte piece l >> 4 of column l & 15 and it lands as [piece][16
-    // columns][16 B] in LDS.
+    // 16-byte piece l >> 4 of column l & 15 (tile offset 64 (l & 15) +
+    // 16 (l >> 4)) and it lands as [piece][16 columns][16 B] in LDS.
     constexpr int NC = C::NC;
     constexpr int SS = C::SS;
     uint32_t ccol[NC];
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
         const int cl = min(n0 + 16 * (NC * w + i) + (lane & 15), N - 1);
-        ccol[i] = static_cast<uint32_t>((cl >> 4) * 1024 + (cl & 15) * 16);
+        ccol[i] = static_cast<uint32_t>((cl >> 4) * 1024 + (cl & 15) * 64);
     }
     const int64_t g_first = kbeg / (SS * kStageK);  // the split starts a group
     const uint32_t lds_base = static_cast<uint32_t>(
@@ -383,7 +383,7 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
     auto issue_c = [&](int G) {
         const int st = min(G * SS + cstage, ns - 1);
         const uint8_t *cb = g.packed + (g_first + min(G, (ns - 1) / SS)) * g.gstride;
-        const uint32_t po = static_cast<uint32_t>((((st % SS) * C::CB + cwithin) >> 4) * 256);
+        const uint32_t po = static_cast<uint32_t>((((st % SS) * C::CB + cwithin) >> 4) * 16);
 #pragma unroll
         for (int i = 0; i < NC; ++i)
             dma16(cb, ccol[i] + po, lds_base + CR + (G & 1) * C::CSS + (NC * w + i) * 1024);
@@ -705,12 +705,15 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
 
     // DMA sources: a wave-uniform base plus a 32-bit per-lane offset (the
     // host bounds K and N so that every offset fits).  Code tile j of group
-    // gi is the 1 KB at gi * gstride + (n0 / 16 + j) * 1024; tiles past the
-    // last one re-read it (their outputs are not stored).
+    // gi is the 1 KB at gi * gstride + (n0 / 16 + j) * 1024, row r's 64 bytes
+    // at 64 r in it: lane (i16, grp) fetches bytes 16 grp .. 16 grp + 15 of
+    // row i16, which land at 16 * lane in LDS.  Tiles past the last one
+    // re-read it (their outputs are not stored).
     const int last_tile = (N - 1) >> 4;
     uint32_t coff[TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) coff[j] = static_cast<uint32_t>(min((n0 >> 4) + j, last_tile) * 1024 + lane * 16);
+    for (int j = 0; j < TN; ++j)
+        coff[j] = static_cast<uint32_t>(min((n0 >> 4) + j, last_tile) * 1024 + i16 * 64 + grp * 16);
     uint32_t xoff[XI];
 #pragma unroll
     for (int q = 0; q < XI; ++q) {

@@ -211,10 +211,11 @@ enum : unsigned { OUT_BF16 = 1, OUT_F32 = 2, OUT_CODES = 4, OUT_ALPHA_BF16 = 8, 
 // Forward rows per wave: with one wave per row (launches of many short
 // rows) each wave takes two rows in turn, which halves the number of waves
 // to launch and retire; a team of four waves takes one row.  Codes in the
-// export byte order take one row per wave: there a 128-byte line collects
-// 16-byte pieces of 8 rows, and with two rows per wave those writes spread
-// out in time enough that the lines leave L2 partly written (measured: 21x
-// the code bytes written, 2.4x the time).
+// export byte order take one row per wave, so that the rows sharing a
+// 128-byte line of the export are written close together in time (with an
+// earlier layout whose lines held 16-byte pieces of 8 rows, two rows per
+// wave let lines leave L2 partly written: 21x the code bytes written, 2.4x
+// the time).
 constexpr int fwd_rows_per_wave(int wpr, bool tiled) { return wpr == 1 && !tiled ? 2 : 1; }
 
 // Row-major codes of quad q (weights 4q .. 4q+3) from their four codes.  The
@@ -238,9 +239,9 @@ __device__ __forceinline__ void store_codes(PQ_GLOBAL uint8_t *crow, int q, uint
 
 // Export byte order of the codes (OUT_TILED, single matrix).  The 64-byte
 // groups of all rows are stored group after group; inside a group, each tile
-// of 16 rows is 1 KB ordered [16-byte piece][row of the tile][byte]:
+// of 16 rows is 1 KB ordered [row of the tile][64 bytes of the row]:
 //   byte kb of row n -> (kb / 64) * Np * 64 + (n / 16) * 1024
-//                       + ((kb / 16) % 4) * 256 + (n % 16) * 16 + kb % 16,
+//                       + (n % 16) * 64 + kb % 64,
 // Np = rows rounded up to 16.  Bytes past a row's end within its last group,
 // and the rows from `rows` to Np, are zero.  A 1-KB tile is then exactly the
 // deployment GEMM's MFMA operand for 16 columns and 64 code bytes, fetched
@@ -278,19 +279,19 @@ __global__ __launch_bounds__(256, PQ_QUANT_FWD_MINB) void k_quant_fwd(LaunchTabl
 
     // One row (RPB rows per block, one after the other RPW times).
     auto one_row = [&](const int64_t row) {
-        // Tiled export: this row's 16-byte slot in every tile, and the group stride.
+        // Tiled export: this row's 64-byte slot in every tile, and the group stride.
         PQ_GLOBAL uint8_t *tbase = nullptr;
         int64_t gstride = 0, gbytes = 0;
         if constexpr (TILED) {
             const int64_t np = (m.rows + 15) & ~int64_t(15);
             gstride = np * 64;
             gbytes = (cols * CW / 8 + 63) / 64 * 64;
-            tbase = (PQ_GLOBAL uint8_t *)m.codes + (row >> 4) * 1024 + (row & 15) * 16;
+            tbase = (PQ_GLOBAL uint8_t *)m.codes + (row >> 4) * 1024 + (row & 15) * 64;
             if (row >= m.rows) {
                 // padding row of the last tile: zero pieces in every group
                 if (row < np)
                     for (int64_t p = tl; p < gbytes / 16; p += TEAM)
-                        *(PQ_GLOBAL u32x4 *)(tbase + (p >> 2) * gstride + (p & 3) * 256) = u32x4{0u, 0u, 0u, 0u};
+                        *(PQ_GLOBAL u32x4 *)(tbase + (p >> 2) * gstride + (p & 3) * 16) = u32x4{0u, 0u, 0u, 0u};
                 return;
             }
         }
@@ -372,14 +373,14 @@ __global__ __launch_bounds__(256, PQ_QUANT_FWD_MINB) void k_quant_fwd(LaunchTabl
                 if constexpr (TILED) {
                     // A quad is CW / 2 code bytes, and base + u * TEAM starts a
                     // whole 64-byte group g0; the lane's byte offset from there
-                    // (tl or 2 tl) splits into group, piece and byte.
+                    // (tl or 2 tl) splits into group and byte.
                     const int64_t g0 = (static_cast<int64_t>(base + u * TEAM) * (CW / 2)) >> 6;
                     if constexpr (CW == 2) {
-                        PQ_GLOBAL uint8_t *d = tbase + (g0 + (tl >> 6)) * gstride + ((tl >> 4) & 3) * 256 + (tl & 15);
+                        PQ_GLOBAL uint8_t *d = tbase + (g0 + (tl >> 6)) * gstride + (tl & 63);
                         if (act) *d = static_cast<uint8_t>(c0 | (c1 << 2) | (c2 << 4) | (c3 << 6));
                     } else {
                         PQ_GLOBAL uint8_t *d =
-                            tbase + (g0 + (tl >> 5)) * gstride + ((tl >> 3) & 3) * 256 + ((2 * tl) & 15);
+                            tbase + (g0 + (tl >> 5)) * gstride + ((2 * tl) & 63);
                         if (act)
                             *(PQ_GLOBAL uint16_t *)d = static_cast<uint16_t>(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
                     }
@@ -396,7 +397,7 @@ __global__ __launch_bounds__(256, PQ_QUANT_FWD_MINB) void k_quant_fwd(LaunchTabl
             // zero the bytes of the last group past the row's end (< 64 bytes)
             const int64_t rb = cols * CW / 8;
             const int64_t kb = rb + tl;
-            if (kb < gbytes) tbase[(kb >> 6) * gstride + ((kb >> 4) & 3) * 256 + (kb & 15)] = 0;
+            if (kb < gbytes) tbase[(kb >> 6) * gstride + (kb & 63)] = 0;
         }
     };
 #pragma unroll 1

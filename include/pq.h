@@ -198,10 +198,9 @@ pq_status pq_quantize_bwd(int mode, int64_t rows, int64_t cols, const float *W,
  * pages fix four codes per byte and a bf16 scale per row, not a byte order).
  * With Np = rows rounded up to a multiple of 16 and G = ceil(rb / 64):
  *   byte c of row n (c < rb, n < rows) is stored at
- *     (c / 64) * Np * 64 + (n / 16) * 1024 + ((c / 16) % 4) * 256
- *       + (n % 16) * 16 + c % 16,
+ *     (c / 64) * Np * 64 + (n / 16) * 1024 + (n % 16) * 64 + c % 64,
  * i.e. group-major runs of 64 bytes of every row, each 16-row tile 1 KB
- * ordered [16-byte piece][row][byte].  Every other byte (rows rows .. Np - 1,
+ * ordered [row][64 bytes].  Every other byte (rows rows .. Np - 1,
  * bytes rb .. 64 G - 1 of a row) is written as 0.  Total size
  * G * Np * 64 bytes = pq_packed_bytes(mode, rows, cols).
  */

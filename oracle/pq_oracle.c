@@ -632,13 +632,13 @@ int pqo_weight_movement(int64_t rows, int64_t cols, const float *W, const float 
  * forward emits (rb bytes per row):
  *   groups   g = 0 .. G-1,  G  = ceil(rb / 64)   (64 bytes of every row)
  *   tiles    t = 0 .. Np/16-1, Np = rows rounded up to a multiple of 16
- *   pieces   p = 0 .. 3  (16 bytes each), row r = 0 .. 15 of the tile,
- *            byte e = 0 .. 15 of the piece
- *   tiled[(((g * (Np/16) + t) * 4 + p) * 16 + r) * 16 + e]
- *       = rowmajor[(16 t + r) * rb + 64 g + 16 p + e]
- *   when the row 16 t + r < rows and the byte 64 g + 16 p + e < rb, else 0.
- * So every 64-byte group of all rows is one contiguous run (group-major), and
- * inside it each tile of 16 rows is 1 KB.  Size: G * Np * 64 bytes.
+ *   row r = 0 .. 15 of the tile, byte e = 0 .. 63 of the row's group
+ *   tiled[((g * (Np/16) + t) * 16 + r) * 64 + e]
+ *       = rowmajor[(16 t + r) * rb + 64 g + e]
+ *   when the row 16 t + r < rows and the byte 64 g + e < rb, else 0.
+ * So every 64-byte group of all rows is one contiguous run (group-major),
+ * inside it each tile of 16 rows is 1 KB, and inside a tile each row's 64
+ * bytes are contiguous.  Size: G * Np * 64 bytes.
  * ------------------------------------------------------------------------- */
 int64_t pqo_tiled_bytes(int64_t rows, int64_t rb)
 {
@@ -652,13 +652,12 @@ int pqo_tile_codes(int64_t rows, int64_t rb, const uint8_t *rowmajor, uint8_t *t
     const int64_t G = (rb + 63) / 64, T = (rows + 15) / 16;
     for (int64_t g = 0; g < G; ++g)
         for (int64_t t = 0; t < T; ++t)
-            for (int p = 0; p < 4; ++p)
-                for (int r = 0; r < 16; ++r)
-                    for (int e = 0; e < 16; ++e) {
-                        const int64_t dst = (((g * T + t) * 4 + p) * 16 + r) * 16 + e;
-                        const int64_t n = 16 * t + r, c = 64 * g + 16 * p + e;
-                        tiled[dst] = (n < rows && c < rb) ? rowmajor[n * rb + c] : 0;
-                    }
+            for (int r = 0; r < 16; ++r)
+                for (int e = 0; e < 64; ++e) {
+                    const int64_t dst = ((g * T + t) * 16 + r) * 64 + e;
+                    const int64_t n = 16 * t + r, c = 64 * g + e;
+                    tiled[dst] = (n < rows && c < rb) ? rowmajor[n * rb + c] : 0;
+                }
     return 0;
 }
 

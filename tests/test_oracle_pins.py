@@ -453,12 +453,12 @@ def test_gemm_ref_is_matmul_of_dequantized_weight(mode):
 
 def _tile_by_reshape(P):
     """The deployment byte order as a numpy index shuffle: pad to whole tiles
-    and groups, then order the axes (group, tile, piece, row, byte)."""
+    and groups, then order the axes (group, tile, row, byte)."""
     rows, rb = P.shape
     Np, G = -(-rows // 16) * 16, -(-rb // 64)
     pad = np.zeros((Np, G * 64), np.uint8)
     pad[:rows, :rb] = P
-    return pad.reshape(Np // 16, 16, G, 4, 16).transpose(2, 0, 3, 1, 4).reshape(-1)
+    return pad.reshape(Np // 16, 16, G, 64).transpose(2, 0, 1, 3).reshape(-1)
 
 
 @pytest.mark.parametrize("rows,rb", [(16, 64), (20, 144), (1, 2), (33, 16), (48, 256), (7, 200),
@@ -476,15 +476,18 @@ def test_tile_codes_hand_positions():
     P = (np.arange(20 * 144) % 251 + 1).astype(np.uint8).reshape(20, 144)
     T = O.tile_codes(P)
     assert T.size == 3 * 32 * 64
-    # row 17, byte 70: group 1, tile 1, piece 0, tile row 1, byte 6
-    assert T[((1 * 2 + 1) * 4 + 0) * 256 + 1 * 16 + 6] == P[17, 70]
-    # row 0, byte 143: group 2, piece 0, byte 15
-    assert T[(2 * 2 * 4) * 256 + 15] == P[0, 143]
-    # row 19, byte 0: tile 1, tile row 3
-    assert T[1024 + 3 * 16] == P[19, 0]
-    # padding: bytes past the row (group 2, piece 1) and rows past 20 are zero
-    assert not T[(2 * 2 * 4 + 1) * 256:(2 * 2 * 4 + 4) * 256].any()
-    assert not T[1024 + 4 * 16:1024 + 16 * 16].any()
+    # row 17, byte 70: group 1, tile 1, tile row 1, byte 6 of the group
+    assert T[((1 * 2 + 1) * 16 + 1) * 64 + 6] == P[17, 70]
+    # row 0, byte 143: group 2, tile 0, tile row 0, byte 15
+    assert T[(2 * 2 * 16) * 64 + 15] == P[0, 143]
+    # row 19, byte 0: group 0, tile 1, tile row 3
+    assert T[1024 + 3 * 64] == P[19, 0]
+    # row 1, bytes 64..79 follow row 1's group-1 start: tile 0, row 1 of group 1
+    assert np.array_equal(T[(1 * 2 * 16 + 1) * 64:(1 * 2 * 16 + 1) * 64 + 16], P[1, 64:80])
+    # padding: bytes past the row in its last group (row 0, group 2, bytes 16..63)
+    # and rows past 20 (tile 1, rows 4..15, group 0) are zero
+    assert not T[(2 * 2 * 16) * 64 + 16:(2 * 2 * 16) * 64 + 64].any()
+    assert not T[1024 + 4 * 64:1024 + 16 * 64].any()
     # every stored byte appears exactly once: nonzero bytes are a permutation
     assert np.count_nonzero(T) == P.size
     assert np.array_equal(np.sort(T[T != 0]), np.sort(P.reshape(-1)))
