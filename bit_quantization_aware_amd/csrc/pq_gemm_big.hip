@@ -1,0 +1,290 @@
+// pq_gemm_big.hip -- the W2A16 GEMM for large M (gfx950): 2-bit codes in the
+// export byte order x bf16 activations, 128 x 256 output tiles.
+//
+// Sources (web pages, cited by title and section):
+//   [News] "ParetoQ ... 2-bit kernel" news item -- speed paragraph: the 2-bit
+//          weights are used packed by the deployed kernel.
+//   [Note] "ParetoQ, the strongest low-bit QAT I could find" -- "Finding 3"
+//          (the level sets) and "Paper vs. code" (no bias in the layer).
+//
+// The tiled kernel of pq_gemm.hip gives each wave a 64 x 64 output tile: per
+// 32 MFMAs a wave reads the 64 x 64 activation tile from LDS, decodes 16
+// weight columns, sums its rows and passes a barrier.  With M in the
+// thousands there are enough output tiles for wider ones: here the 4 waves
+// of a block own 64 x 128 outputs each (2 x 2 waves, 4 x 8 MFMA tiles of
+// 16 x 16), so every activation fragment read from LDS feeds 8 MFMAs instead
+// of 4 and the row sums come from a separate pass; two blocks share a CU
+// (80 KB of LDS each, 234 VGPRs per lane).  A 128 x 128 wave tile (256
+// accumulators per lane, one wave per SIMD) was slower: its accumulators
+// no longer fit beside the fragments and moved between AGPRs and VGPRs.
+//
+// Per stage of K = 64: the block's activation tile (128 rows x 128 B, 16 KB)
+// goes global -> LDS by the LDS-DMA load into a ring of four stage buffers
+// kept three stages ahead, with the same XOR swizzle of 16-byte chunks as the
+// tiled kernel; the codes come 32 bytes per column (two stages) per fetch
+// into a double buffer, two column tiles of the export order per 1-KB DMA.
+// One s_waitcnt plus one barrier per stage order both rings (the wait counts
+// from the shared pipeline model).  Within a stage the wave reads the next
+// k-step's activation fragments and the next stage's code words while its
+// MFMAs on the current ones run.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pq_common.hpp"
+#include "pq_gemm_common.hpp"
+
+// Smallest M and K, and fewest block tiles, for which the large-M kernel
+// runs; elsewhere the tiled kernel of pq_gemm.hip, whose 64 x 256 tiles or K
+// split fill the chip better and which needs no row-sum pass (16384^2 at
+// M = 512, 256 tiles here: 228 us against 205; N = 1024, K = 4096 at
+// M = 4096, 128 tiles: 78 us against 48; the MobileLLM-125M training
+// forward, K of 576 and 1536: 10.1 ms against 7.4).
+#ifndef PQ_BIG_MIN_M
+#define PQ_BIG_MIN_M 1024
+#endif
+#ifndef PQ_BIG_MIN_K
+#define PQ_BIG_MIN_K 2048
+#endif
+#ifndef PQ_BIG_MIN_TILES
+#define PQ_BIG_MIN_TILES 256
+#endif
+
+namespace pq {
+namespace {
+
+constexpr int kWaveM = 64;                          // rows per wave
+constexpr int kRT = kWaveM / 16;                    // MFMA row tiles per wave
+constexpr int kBigM = 2 * kWaveM, kBigN = 256;      // block tile
+constexpr int kBigP = 4;                            // activation ring stages
+constexpr int kBigSS = 2;                           // stages per code fetch
+constexpr int kBigXI = kBigM * kStageK * 2 / 4096;  // activation DMAs per wave per stage
+constexpr int kBigNC = 2;                           // code DMAs per wave per fetch
+constexpr int kBigXBytes = kBigM * kStageK * 2;     // 32 KB per stage
+constexpr int kBigCBytes = kBigN * 16 * kBigSS;     // 8 KB per fetch (16 B per column per stage)
+constexpr int kBigLds = kBigP * kBigXBytes + 2 * kBigCBytes;
+constexpr int kBigU = 4;                            // unrolled phases: ring slot and code buffer
+static_assert(kBigXI * 4 * 1024 == kBigXBytes, "one stage is XI 1-KB DMAs per wave");
+static_assert(kBigNC * 4 * 1024 == kBigCBytes, "one fetch is NC 1-KB DMAs per wave");
+static_assert(kBigU % kBigP == 0 && kBigU % (2 * kBigSS) == 0, "unroll covers both rings");
+// DMA byte offsets from the tile's first row stay below 2^32.
+constexpr int64_t kBigMaxK = int64_t(1) << 22;
+
+__global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, const float *rowsum, int mtiles)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kBigLds];
+    constexpr int XR = 0;
+    constexpr int CR = kBigP * kBigXBytes;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = w >> 1, wn = w & 1;  // the wave's row half and 128-column half
+    const int i16 = lane & 15, grp = lane >> 4;
+
+    // Block -> (m-tile, n-tile); consecutive indices on one XCD, m fastest,
+    // so the m-tiles sharing a weight tile share that XCD's L2.
+    int t = blockIdx.x;
+    const int nb = gridDim.x;
+    if ((nb & 7) == 0) t = (t & 7) * (nb >> 3) + (t >> 3);
+    const int mt = t % mtiles;
+    const int nt = t / mtiles;
+    const int M = g.M, N = g.N, K = g.K;
+    const int m0 = mt * kBigM, n0 = nt * kBigN;
+    const int ns = K / kStageK;
+
+    // Activation DMAs: wave w, DMA q brings tile rows 8 (8 w + q) .. + 7;
+    // lane l fills slot l & 7 of row r with chunk (l & 7) ^ xswz(r).  Rows
+    // >= M read row M - 1 (their outputs are not stored).
+    const uint8_t *xbase = reinterpret_cast<const uint8_t *>(g.X + static_cast<int64_t>(m0) * K);
+    uint32_t xoff[kBigXI];
+#pragma unroll
+    for (int q = 0; q < kBigXI; ++q) {
+        const int r = 8 * (kBigXI * w + q) + (lane >> 3);
+        const int c = (lane & 7) ^ xswz(r);
+        xoff[q] = static_cast<uint32_t>(static_cast<int64_t>(min(m0 + r, M - 1) - m0) * K * 2 + 16 * c);
+    }
+    // Code DMAs: DMA d = NC w + i of a fetch covers block column tiles 2d and
+    // 2d + 1 (16 columns each); lane l takes tile 2d + (l >> 5), the fetch's
+    // stage (l >> 4) & 1, column l & 15: 16 bytes at 64 column + 16 piece of
+    // the 1-KB export tile, landing at LDS [tile][stage][column][16 B].
+    // Column tiles past the last one re-read it.
+    const int last_tile = (N - 1) >> 4;
+    const int cst = (lane >> 4) & 1;
+    uint32_t ccol[kBigNC];
+#pragma unroll
+    for (int i = 0; i < kBigNC; ++i) {
+        const int tb = 2 * (kBigNC * w + i) + (lane >> 5);
+        ccol[i] = static_cast<uint32_t>(min((n0 >> 4) + tb, last_tile) * 1024 + (lane & 15) * 64);
+    }
+    const uint32_t lds_base = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)lds));
+
+    auto issue_x = [&](int st, int slot) __attribute__((always_inline)) {
+        const uint8_t *xs = xbase + min(st, ns - 1) * (kStageK * 2);
+#pragma unroll
+        for (int q = 0; q < kBigXI; ++q)
+            dma16(xs, xoff[q], lds_base + XR + slot * kBigXBytes + (kBigXI * w + q) * 1024);
+    };
+    // Code fetch F: stages 2F, 2F + 1 (clamped to the last stage, which is in
+    // the same 64-byte group as 2F, or for a fetch wholly past the end the
+    // last group) into buffer F & 1.
+    auto issue_c = [&](int F) __attribute__((always_inline)) {
+        const int st0 = min(kBigSS * F, ns - 1);
+        const int st = min(kBigSS * F + cst, ns - 1);
+        const uint8_t *cb = g.packed + static_cast<int64_t>(st0 >> 2) * g.gstride;
+        const uint32_t po = static_cast<uint32_t>((st & 3) * 16);
+#pragma unroll
+        for (int i = 0; i < kBigNC; ++i)
+            dma16(cb, ccol[i] + po, lds_base + CR + (F & 1) * kBigCBytes + (kBigNC * w + i) * 1024);
+    };
+
+    floatx4 acc[kRT][8];
+#pragma unroll
+    for (int i = 0; i < kRT; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // LDS read addresses.  Activation fragment of row tile i, k-step T:
+    // row wm*128 + 16 i + i16, chunk 2 grp + T (swizzled); code word of the
+    // wave's column tile j at stage-in-fetch p: dword grp of column i16.
+    const int swz = xswz(i16);
+    const uint8_t *xa0 = lds + XR + (wm * kWaveM + i16) * 128 + (((2 * grp) ^ swz) << 4);
+    const uint8_t *xa1 = lds + XR + (wm * kWaveM + i16) * 128 + (((2 * grp + 1) ^ swz) << 4);
+    const uint8_t *ca = lds + CR + (wn * 8) * 512 + i16 * 16 + grp * 4;
+
+    auto read_a = [&](auto slot_c, auto t_c, uint4 (&a)[kRT]) __attribute__((always_inline)) {
+        constexpr int SLOT = decltype(slot_c)::value;
+        constexpr int T = decltype(t_c)::value;
+        const uint8_t *base = (T == 0 ? xa0 : xa1) + SLOT * kBigXBytes;
+#pragma unroll
+        for (int i = 0; i < kRT; ++i) a[i] = *reinterpret_cast<const uint4 *>(base + i * 16 * 128);
+    };
+    auto read_c = [&](auto ph_c, uint32_t (&d)[8]) __attribute__((always_inline)) {
+        constexpr int PH = decltype(ph_c)::value;  // stage mod U
+        constexpr int BUF = (PH / kBigSS) & 1;
+        constexpr int P = PH % kBigSS;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            d[j] = *reinterpret_cast<const uint32_t *>(ca + BUF * kBigCBytes + j * 512 + P * 256);
+    };
+    // MFMAs of one k-step: weights (16 columns) as the A operand, so each
+    // lane ends with four consecutive columns of one row.
+    auto mma = [&](auto t_c, const uint4 (&a)[kRT], const uint32_t (&d)[8]) __attribute__((always_inline)) {
+        constexpr int T = decltype(t_c)::value;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t x = d[j];
+            const uint32_t y = x >> 4;
+            const uint32_t w0 = (x & 0x03030303u) | ((x << 2) & 0x30303030u);
+            const uint32_t w1 = (y & 0x03030303u) | ((y << 2) & 0x30303030u);
+            uint4 b;
+            b.x = fp4x2_to_bf16x2<2 * T>(w0);
+            b.y = fp4x2_to_bf16x2<2 * T>(w1);
+            b.z = fp4x2_to_bf16x2<2 * T + 1>(w0);
+            b.w = fp4x2_to_bf16x2<2 * T + 1>(w1);
+            const bf16x8 bv = __builtin_bit_cast(bf16x8, b);
+#pragma unroll
+            for (int i = 0; i < kRT; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv, __builtin_bit_cast(bf16x8, a[i]), acc[i][j],
+                                                                     0, 0, 0);
+        }
+    };
+
+    // Prologue: code fetch 0, activation stages 0 .. P - 2, code fetch 1
+    // (the issue order the wait model assumes); stage 0 and fetch 0 landed.
+    issue_c(0);
+#pragma unroll
+    for (int st = 0; st < kBigP - 1; ++st) issue_x(st, st);
+    issue_c(1);
+    wait_vmcnt<(kBigP - 2) * kBigXI + kBigNC>();
+    block_barrier();
+    uint4 a0[kRT], a1[kRT];
+    uint32_t dc[2][8];
+    read_a(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, a0);
+    read_c(std::integral_constant<int, 0>{}, dc[0]);
+
+    // Iteration s: wait for stage s + 1 (and its codes), barrier, refill the
+    // slot of stage s - 1 and, every second stage, the code buffer of the
+    // fetch before last; then the two k-steps of stage s, each reading the
+    // next k-step's fragments first.  Every LDS read of a ring slot or code
+    // buffer is complete before the barrier that precedes its refill.
+    auto step = [&](int s, auto pc) __attribute__((always_inline)) {
+        constexpr int p = decltype(pc)::value;  // s mod U
+        constexpr bool code_now = ((p + 1) % kBigSS) == 0;
+        wait_lgkmcnt0();
+        wait_vmcnt<tile_wait(p, kBigP, kBigSS, kBigXI, kBigNC, kBigU)>();
+        block_barrier();
+        __builtin_amdgcn_s_setprio(1);
+        issue_x(s + kBigP - 1, (p + kBigP - 1) % kBigP);
+        if constexpr (code_now) issue_c((s + 1) / kBigSS + 1);
+        // k-step 0 of stage s (a0), reading k-step 1 (a1)
+        read_a(std::integral_constant<int, p % kBigP>{}, std::integral_constant<int, 1>{}, a1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(std::integral_constant<int, 0>{}, a0, dc[p & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+        // k-step 1 of stage s (a1), reading stage s + 1's k-step 0 and codes
+        read_a(std::integral_constant<int, (p + 1) % kBigP>{}, std::integral_constant<int, 0>{}, a0);
+        read_c(std::integral_constant<int, (p + 1) % kBigU>{}, dc[(p + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(std::integral_constant<int, 1>{}, a1, dc[p & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    int s = 0;
+    for (; s + kBigU <= ns; s += kBigU) {
+        static_for<0, kBigU>([&](auto pc) __attribute__((always_inline)) { step(s + decltype(pc)::value, pc); });
+    }
+    static_for<0, kBigU - 1>([&](auto pc) __attribute__((always_inline)) {
+        if (s + decltype(pc)::value < ns) step(s + decltype(pc)::value, pc);
+    });
+    wait_vmcnt<0>();
+
+    // Epilogue: acc[i][j][e] is row m0 + wm*kWaveM + 16 i + i16, column
+    // n0 + wn*128 + 16 j + 4 grp + e.
+    const bool vec = (N & 3) == 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int n = n0 + wn * 128 + 16 * j + 4 * grp;
+        if (n >= N) continue;
+        float al[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) al[e] = n + e < N ? col_scale(g.alpha, g.alpha32, n + e) : 0.f;
+#pragma unroll
+        for (int i = 0; i < kRT; ++i) {
+            const int m = m0 + wm * kWaveM + 16 * i + i16;
+            if (m >= M) continue;
+            const float sr = g.off * rowsum[m];
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = al[e] * (g.mul * (acc[i][j][e] - sr));
+            const int64_t o = static_cast<int64_t>(m) * N + n;
+            if (vec) {
+                *reinterpret_cast<u32x2 *>(g.Y + o) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < N) g.Y[o + e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[e]));
+            }
+        }
+    }
+}
+
+}  // namespace
+
+bool gemm_big_takes(int bits, int64_t M, int64_t N, int64_t K)
+{
+    if (bits != 2 || M < PQ_BIG_MIN_M || K < PQ_BIG_MIN_K || K > kBigMaxK) return false;
+    const int64_t tiles = ((M + kBigM - 1) / kBigM) * ((N + kBigN - 1) / kBigN);
+    return tiles >= PQ_BIG_MIN_TILES && tiles <= INT32_MAX;
+}
+
+pq_status launch_gemm_big(const GemmArgs &a, const float *rowsum, hipStream_t s)
+{
+    const int mtiles = (a.M + kBigM - 1) / kBigM;
+    const int ntiles = (a.N + kBigN - 1) / kBigN;
+    hipLaunchKernelGGL(k_gemm_big2, dim3(static_cast<unsigned>(mtiles * ntiles)), dim3(256), 0, s, a, rowsum,
+                       mtiles);
+    return hipGetLastError() == hipSuccess ? PQ_OK : PQ_ERR_HIP;
+}
+
+}  // namespace pq

@@ -173,6 +173,42 @@ def test_gemm_16384_sampled(mode, M):
     assert np.all(np.isfinite(Y))
 
 
+@pytest.mark.parametrize("mode", [O.SEQ2, O.TERNARY, O.LSQ2, O.LSQ158])
+@pytest.mark.parametrize("M,N,K", [(1024, 8192, 2048), (1100, 8200, 2112), (1030, 8202, 2240)])
+def test_gemm_large_m_sampled(mode, M, N, K):
+    """The large-M path (128 x 256 tiles of 64 x 128 per wave, row sums from a
+    separate pass): ragged M and N, N not a multiple of 4, K with a partial
+    last 64-byte group and an odd number of 64-k stages; 4000 sampled outputs
+    plus every output of the first and last row and column against the
+    binary64 reference."""
+    print(f"[gemm large-M mode={mode} M={M} N={N} K={K}]", flush=True)
+    X, packed, ab = make_case(mode, 13 * M + N + K, M, N, K)
+    Y = gpu_gemm(mode, X, packed, ab, N)
+    rng = np.random.default_rng(M + N + K + mode)
+    ms, ns = sample_points(rng, M, N, 4000)
+    edge_m = np.concatenate([np.zeros(N, int), np.full(N, M - 1), np.arange(M), np.arange(M)])
+    edge_n = np.concatenate([np.arange(N), np.arange(N), np.zeros(M, int), np.full(M, N - 1)])
+    ms, ns = np.concatenate([ms, edge_m]), np.concatenate([ns, edge_n])
+    check(Y[ms, ns], O.gemm_ref_at(mode, X, packed, ab, N, ms, ns), f"large-M m{mode} {M}x{N}x{K}")
+
+
+def test_gemm_large_m_full_compare():
+    """One large-M case compared at every output, with the exported bf16 scale
+    and with the binary32 scale of the training forward."""
+    M, N, K = 1024, 8192, 2048
+    X, packed, ab = make_case(O.SEQ2, 77, M, N, K)
+    check(gpu_gemm(O.SEQ2, X, packed, ab, N), O.gemm_ref(O.SEQ2, X, packed, ab, N), "large-M full")
+    rng = np.random.default_rng(78)
+    W = synth.normal_f32(rng, (N, K), 0.02)
+    alpha = O.alpha_init(O.SEQ2, W)
+    packed, _ = O.pack(O.SEQ2, W, alpha)
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    pq.pq_gemm_f32a(O.SEQ2, M, N, K, dev(X), dev(O.tile_codes(packed)), dev(alpha), Y)
+    torch.cuda.synchronize()
+    Yg = synth.bf16_bits_to_f32(host(Y)).astype(np.float64)
+    check(Yg, O.gemm_ref_f32a(O.SEQ2, X, packed, alpha, N), "large-M f32a full")
+
+
 @pytest.mark.parametrize("M", [1, 16, 256, 4096])
 def test_gemm_llama3_8b_sampled(M):
     """The four Llama-3-8B projection shapes (2-bit SEQ), sampled outputs."""
