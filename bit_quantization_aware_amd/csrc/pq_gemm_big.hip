@@ -48,29 +48,50 @@
 #ifndef PQ_BIG_MIN_TILES
 #define PQ_BIG_MIN_TILES 256
 #endif
+// The K-split form (KH = 2): smallest M and fewest 64 x 256 tiles.
+#ifndef PQ_BIG_KH2_MIN_M
+#define PQ_BIG_KH2_MIN_M 512
+#endif
+#ifndef PQ_BIG_KH2_MIN_TILES
+#define PQ_BIG_KH2_MIN_TILES 512
+#endif
 
 namespace pq {
 namespace {
 
 constexpr int kWaveM = 64;                          // rows per wave
 constexpr int kRT = kWaveM / 16;                    // MFMA row tiles per wave
-constexpr int kBigM = 2 * kWaveM, kBigN = 256;      // block tile
-constexpr int kBigP = 4;                            // activation ring stages
-constexpr int kBigSS = 2;                           // stages per code fetch
-constexpr int kBigXI = kBigM * kStageK * 2 / 4096;  // activation DMAs per wave per stage
+constexpr int kBigN = 256;                          // block columns
+constexpr int kBigP = 4;                            // activation ring slots
+constexpr int kBigXBytes = 2 * kWaveM * kStageK * 2;  // one slot: two halves of 64 rows x 128 B
+constexpr int kBigXI = kBigXBytes / 4096;           // activation DMAs per wave per slot
 constexpr int kBigNC = 2;                           // code DMAs per wave per fetch
-constexpr int kBigXBytes = kBigM * kStageK * 2;     // 32 KB per stage
-constexpr int kBigCBytes = kBigN * 16 * kBigSS;     // 8 KB per fetch (16 B per column per stage)
+constexpr int kBigCBytes = kBigN * 16 * 2;          // one fetch: 2 stages x 16 B per column
 constexpr int kBigLds = kBigP * kBigXBytes + 2 * kBigCBytes;
 constexpr int kBigU = 4;                            // unrolled phases: ring slot and code buffer
-static_assert(kBigXI * 4 * 1024 == kBigXBytes, "one stage is XI 1-KB DMAs per wave");
+static_assert(kBigXI * 4 * 1024 == kBigXBytes, "one slot is XI 1-KB DMAs per wave");
 static_assert(kBigNC * 4 * 1024 == kBigCBytes, "one fetch is NC 1-KB DMAs per wave");
-static_assert(kBigU % kBigP == 0 && kBigU % (2 * kBigSS) == 0, "unroll covers both rings");
+
+// Two ways to use the 4 waves (2 x 2, each 64 rows x 128 columns of output):
+// KH = 1 splits the block's 128 rows in two, every iteration one K stage,
+// the two halves of a ring slot holding the two row halves; KH = 2 gives
+// the block 64 rows and splits K, every iteration two K stages (one per
+// half of the slot, each wave pair taking one), the two partial sums added
+// through LDS at the end.  KH = 2 doubles the blocks for the same M, so a
+// 16384^2 GEMM at M = 512 keeps two blocks on every CU.
+template <int KH>
+struct BigCfg {
+    static constexpr int BM = KH == 1 ? 2 * kWaveM : kWaveM;  // block rows
+    static constexpr int SS = KH == 1 ? 2 : 1;                // iterations per code fetch
+    static_assert(kBigU % kBigP == 0 && kBigU % (2 * SS) == 0, "unroll covers both rings");
+};
 // DMA byte offsets from the tile's first row stay below 2^32.
 constexpr int64_t kBigMaxK = int64_t(1) << 22;
 
+template <int KH>
 __global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, const float *rowsum, int mtiles)
 {
+    using C = BigCfg<KH>;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kBigLds];
     constexpr int XR = 0;
     constexpr int CR = kBigP * kBigXBytes;
@@ -78,7 +99,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, const float *r
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = w >> 1, wn = w & 1;  // the wave's row half and 128-column half
+    const int wm = w >> 1, wn = w & 1;  // the wave's half (rows or K) and 128-column half
     const int i16 = lane & 15, grp = lane >> 4;
 
     // Block -> (m-tile, n-tile); consecutive indices on one XCD, m fastest,
@@ -89,19 +110,25 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, const float *r
     const int mt = t % mtiles;
     const int nt = t / mtiles;
     const int M = g.M, N = g.N, K = g.K;
-    const int m0 = mt * kBigM, n0 = nt * kBigN;
+    const int m0 = mt * C::BM, n0 = nt * kBigN;
     const int ns = K / kStageK;
+    const int nit = ns / KH;  // iterations (K a multiple of 128 when KH = 2)
 
-    // Activation DMAs: wave w, DMA q brings tile rows 8 (8 w + q) .. + 7;
-    // lane l fills slot l & 7 of row r with chunk (l & 7) ^ xswz(r).  Rows
+    // Activation DMAs: wave w, DMA q fills slot rows 8 (XI w + q) .. + 7,
+    // in half h = (XI w + q) / 64 rows; lane l fills chunk slot l & 7 of slot
+    // row r with chunk (l & 7) ^ xswz(r).  The half is row half h of the
+    // stage (KH = 1) or rows 0..63 of the iteration's stage h (KH = 2).  Rows
     // >= M read row M - 1 (their outputs are not stored).
     const uint8_t *xbase = reinterpret_cast<const uint8_t *>(g.X + static_cast<int64_t>(m0) * K);
     uint32_t xoff[kBigXI];
 #pragma unroll
     for (int q = 0; q < kBigXI; ++q) {
         const int r = 8 * (kBigXI * w + q) + (lane >> 3);
+        const int h = r / kWaveM;
         const int c = (lane & 7) ^ xswz(r);
-        xoff[q] = static_cast<uint32_t>(static_cast<int64_t>(min(m0 + r, M - 1) - m0) * K * 2 + 16 * c);
+        const int rg = KH == 1 ? r : r - h * kWaveM;
+        xoff[q] = static_cast<uint32_t>(static_cast<int64_t>(min(m0 + rg, M - 1) - m0) * K * 2 +
+                                        (KH == 1 ? 0 : h * kStageK * 2) + 16 * c);
     }
     // Code DMAs: DMA d = NC w + i of a fetch covers block column tiles 2d and
     // 2d + 1 (16 columns each); lane l takes tile 2d + (l >> 5), the fetch's
@@ -119,8 +146,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, const float *r
     const uint32_t lds_base = static_cast<uint32_t>(
         reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)lds));
 
-    auto issue_x = [&](int st, int slot) __attribute__((always_inline)) {
-        const uint8_t *xs = xbase + min(st, ns - 1) * (kStageK * 2);
+    auto issue_x = [&](int it, int slot) __attribute__((always_inline)) {
+        const uint8_t *xs = xbase + min(KH * it, ns - KH) * (kStageK * 2);
 #pragma unroll
         for (int q = 0; q < kBigXI; ++q)
             dma16(xs, xoff[q], lds_base + XR + slot * kBigXBytes + (kBigXI * w + q) * 1024);
@@ -129,8 +156,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, const float *r
     // the same 64-byte group as 2F, or for a fetch wholly past the end the
     // last group) into buffer F & 1.
     auto issue_c = [&](int F) __attribute__((always_inline)) {
-        const int st0 = min(kBigSS * F, ns - 1);
-        const int st = min(kBigSS * F + cst, ns - 1);
+        const int st0 = min(2 * F, ns - 1);
+        const int st = min(2 * F + cst, ns - 1);
         const uint8_t *cb = g.packed + static_cast<int64_t>(st0 >> 2) * g.gstride;
         const uint32_t po = static_cast<uint32_t>((st & 3) * 16);
 #pragma unroll
@@ -150,7 +177,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, const float *r
     const int swz = xswz(i16);
     const uint8_t *xa0 = lds + XR + (wm * kWaveM + i16) * 128 + (((2 * grp) ^ swz) << 4);
     const uint8_t *xa1 = lds + XR + (wm * kWaveM + i16) * 128 + (((2 * grp + 1) ^ swz) << 4);
-    const uint8_t *ca = lds + CR + (wn * 8) * 512 + i16 * 16 + grp * 4;
+    const uint8_t *ca = lds + CR + (wn * 8) * 512 + i16 * 16 + grp * 4 + (KH == 2 ? wm * 256 : 0);
 
     auto read_a = [&](auto slot_c, auto t_c, uint4 (&a)[kRT]) __attribute__((always_inline)) {
         constexpr int SLOT = decltype(slot_c)::value;
@@ -160,9 +187,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, const float *r
         for (int i = 0; i < kRT; ++i) a[i] = *reinterpret_cast<const uint4 *>(base + i * 16 * 128);
     };
     auto read_c = [&](auto ph_c, uint32_t (&d)[8]) __attribute__((always_inline)) {
-        constexpr int PH = decltype(ph_c)::value;  // stage mod U
-        constexpr int BUF = (PH / kBigSS) & 1;
-        constexpr int P = PH % kBigSS;
+        constexpr int PH = decltype(ph_c)::value;  // iteration mod U
+        constexpr int BUF = (PH / C::SS) & 1;
+        constexpr int P = KH == 1 ? PH % 2 : 0;  // KH = 2: the wave's stage, in ca
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             d[j] = *reinterpret_cast<const uint32_t *>(ca + BUF * kBigCBytes + j * 512 + P * 256);
@@ -194,7 +221,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, const float *r
     // (the issue order the wait model assumes); stage 0 and fetch 0 landed.
     issue_c(0);
 #pragma unroll
-    for (int st = 0; st < kBigP - 1; ++st) issue_x(st, st);
+    for (int it = 0; it < kBigP - 1; ++it) issue_x(it, it);
     issue_c(1);
     wait_vmcnt<(kBigP - 2) * kBigXI + kBigNC>();
     block_barrier();
@@ -210,13 +237,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, const float *r
     // buffer is complete before the barrier that precedes its refill.
     auto step = [&](int s, auto pc) __attribute__((always_inline)) {
         constexpr int p = decltype(pc)::value;  // s mod U
-        constexpr bool code_now = ((p + 1) % kBigSS) == 0;
+        constexpr bool code_now = ((p + 1) % C::SS) == 0;
         wait_lgkmcnt0();
-        wait_vmcnt<tile_wait(p, kBigP, kBigSS, kBigXI, kBigNC, kBigU)>();
+        wait_vmcnt<tile_wait(p, kBigP, C::SS, kBigXI, kBigNC, kBigU)>();
         block_barrier();
         __builtin_amdgcn_s_setprio(1);
         issue_x(s + kBigP - 1, (p + kBigP - 1) % kBigP);
-        if constexpr (code_now) issue_c((s + 1) / kBigSS + 1);
+        if constexpr (code_now) issue_c((s + 1) / C::SS + 1);
         // k-step 0 of stage s (a0), reading k-step 1 (a1)
         read_a(std::integral_constant<int, p % kBigP>{}, std::integral_constant<int, 1>{}, a1);
         __builtin_amdgcn_sched_barrier(0);
@@ -231,15 +258,37 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, const float *r
         __builtin_amdgcn_sched_barrier(0);
     };
     int s = 0;
-    for (; s + kBigU <= ns; s += kBigU) {
+    for (; s + kBigU <= nit; s += kBigU) {
         static_for<0, kBigU>([&](auto pc) __attribute__((always_inline)) { step(s + decltype(pc)::value, pc); });
     }
     static_for<0, kBigU - 1>([&](auto pc) __attribute__((always_inline)) {
-        if (s + decltype(pc)::value < ns) step(s + decltype(pc)::value, pc);
+        if (s + decltype(pc)::value < nit) step(s + decltype(pc)::value, pc);
     });
     wait_vmcnt<0>();
+    if constexpr (KH == 2) {
+        // Add the second K half's sums to the first's through LDS (the ring
+        // is free: every DMA has landed and, after the barrier, every read).
+        __syncthreads();
+        float *red = reinterpret_cast<float *>(lds) + wn * (kRT * 8 * 4 * 64) + lane;
+        if (wm == 1) {
+#pragma unroll
+            for (int i = 0; i < kRT; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) red[((i * 8 + j) * 4 + e) * 64] = acc[i][j][e];
+        }
+        __syncthreads();
+        if (wm == 1) return;
+#pragma unroll
+        for (int i = 0; i < kRT; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][j][e] += red[((i * 8 + j) * 4 + e) * 64];
+    }
 
-    // Epilogue: acc[i][j][e] is row m0 + wm*kWaveM + 16 i + i16, column
+    // Epilogue: acc[i][j][e] is row m0 + wm*kWaveM (KH = 1) + 16 i + i16, column
     // n0 + wn*128 + 16 j + 4 grp + e.
     const bool vec = (N & 3) == 0;
 #pragma unroll
@@ -251,7 +300,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, const float *r
         for (int e = 0; e < 4; ++e) al[e] = n + e < N ? col_scale(g.alpha, g.alpha32, n + e) : 0.f;
 #pragma unroll
         for (int i = 0; i < kRT; ++i) {
-            const int m = m0 + wm * kWaveM + 16 * i + i16;
+            const int m = m0 + (KH == 1 ? wm * kWaveM : 0) + 16 * i + i16;
             if (m >= M) continue;
             const float sr = g.off * rowsum[m];
             float v[4];
@@ -269,21 +318,37 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, const float *r
     }
 }
 
+// Which form takes a GEMM: 0 none, 1 or 2 the KH above.
+int big_form(int bits, int64_t M, int64_t N, int64_t K)
+{
+    if (bits != 2 || K < PQ_BIG_MIN_K || K > kBigMaxK) return 0;
+    const int64_t nt = (N + kBigN - 1) / kBigN;
+    const int64_t t1 = (M + 2 * kWaveM - 1) / (2 * kWaveM) * nt;
+    const int64_t t2 = (M + kWaveM - 1) / kWaveM * nt;
+    if (M >= PQ_BIG_MIN_M && t1 >= PQ_BIG_MIN_TILES && t1 <= INT32_MAX) return 1;
+    if (M >= PQ_BIG_KH2_MIN_M && K % (2 * kStageK) == 0 && t2 >= PQ_BIG_KH2_MIN_TILES && t2 <= INT32_MAX) return 2;
+    return 0;
+}
+
 }  // namespace
 
-bool gemm_big_takes(int bits, int64_t M, int64_t N, int64_t K)
-{
-    if (bits != 2 || M < PQ_BIG_MIN_M || K < PQ_BIG_MIN_K || K > kBigMaxK) return false;
-    const int64_t tiles = ((M + kBigM - 1) / kBigM) * ((N + kBigN - 1) / kBigN);
-    return tiles >= PQ_BIG_MIN_TILES && tiles <= INT32_MAX;
-}
+bool gemm_big_takes(int bits, int64_t M, int64_t N, int64_t K) { return big_form(bits, M, N, K) != 0; }
 
 pq_status launch_gemm_big(const GemmArgs &a, const float *rowsum, hipStream_t s)
 {
-    const int mtiles = (a.M + kBigM - 1) / kBigM;
+    const int form = big_form(2, a.M, a.N, a.K);
     const int ntiles = (a.N + kBigN - 1) / kBigN;
-    hipLaunchKernelGGL(k_gemm_big2, dim3(static_cast<unsigned>(mtiles * ntiles)), dim3(256), 0, s, a, rowsum,
-                       mtiles);
+    if (form == 1) {
+        const int mtiles = (a.M + BigCfg<1>::BM - 1) / BigCfg<1>::BM;
+        hipLaunchKernelGGL(k_gemm_big2<1>, dim3(static_cast<unsigned>(mtiles * ntiles)), dim3(256), 0, s, a, rowsum,
+                           mtiles);
+    } else if (form == 2) {
+        const int mtiles = (a.M + BigCfg<2>::BM - 1) / BigCfg<2>::BM;
+        hipLaunchKernelGGL(k_gemm_big2<2>, dim3(static_cast<unsigned>(mtiles * ntiles)), dim3(256), 0, s, a, rowsum,
+                           mtiles);
+    } else {
+        return PQ_ERR_SHAPE;
+    }
     return hipGetLastError() == hipSuccess ? PQ_OK : PQ_ERR_HIP;
 }
 

@@ -174,11 +174,14 @@ def test_gemm_16384_sampled(mode, M):
 
 
 @pytest.mark.parametrize("mode", [O.SEQ2, O.TERNARY, O.LSQ2, O.LSQ158])
-@pytest.mark.parametrize("M,N,K", [(1024, 8192, 2048), (1100, 8200, 2112), (1030, 8202, 2240)])
+@pytest.mark.parametrize("M,N,K", [(1024, 8192, 2048), (1100, 8200, 2112), (1030, 8202, 2240),
+                                   (512, 16384, 2048), (600, 16200, 2176), (520, 16202, 2048)])
 def test_gemm_large_m_sampled(mode, M, N, K):
-    """The large-M path (128 x 256 tiles of 64 x 128 per wave, row sums from a
-    separate pass): ragged M and N, N not a multiple of 4, K with a partial
-    last 64-byte group and an odd number of 64-k stages; 4000 sampled outputs
+    """The large-M path (64 x 128 outputs per wave, row sums from a separate
+    pass), both forms: 128-row blocks (M >= 1024) and 64-row blocks whose
+    two wave pairs split K (the M = 512..600 cases); ragged M and N, N not a
+    multiple of 4, K with a partial last 64-byte group and, for the first
+    form, an odd number of 64-k stages; 4000 sampled outputs
     plus every output of the first and last row and column against the
     binary64 reference."""
     print(f"[gemm large-M mode={mode} M={M} N={N} K={K}]", flush=True)
