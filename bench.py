@@ -86,7 +86,7 @@ KERNEL_SOURCES = {
     "qat_step": ("pq_quant.hip", "pq_common.hpp"),
 }
 for _m in (1, 4, 16, 64, 512):
-    KERNEL_SOURCES[f"gemm_m{_m}"] = ("pq_gemm.hip", "pq_common.hpp")
+    KERNEL_SOURCES[f"gemm_m{_m}"] = ("pq_gemm.hip", "pq_gemm_big.hip", "pq_gemm_common.hpp", "pq_common.hpp")
 CALIB_BYTES = 1 << 30   # the calibration copy reads and writes 1 GiB
 
 
@@ -191,19 +191,14 @@ def pmc_summarize(args):
         f, w = last(fetch, pred, 3), last(write, pred, 3)
         if f and w:
             res[k] = (np.mean(f), np.mean(w))
-    # the tiled kernel serves M = 64 and 512 (same grid size): the workload
-    # launches them three times each in GEMM_STEP_ORDER
-    tile = lambda n: "k_gemm_tile<2," in n
-    fin = lambda n: "k_splitk_finalize" in n
-    tile_ms = [M for M in GEMM_STEP_ORDER if M > 16]
-    ft, wt = last(fetch, tile, 3 * len(tile_ms)), last(write, tile, 3 * len(tile_ms))
-    ff, wf = last(fetch, fin, 3), last(write, fin, 3)
-    if ft and wt and ff and wf:
-        for i, M in enumerate(tile_ms):
-            f, w = np.mean(ft[3 * i:3 * i + 3]), np.mean(wt[3 * i:3 * i + 3])
-            if M == 64:  # split-K: add the finalize launch
-                f, w = f + np.mean(ff), w + np.mean(wf)
-            res[f"gemm_m{M}"] = (f, w)
+    # M = 64: the tiled kernel and its split-K finalize; M = 512: the
+    # large-M kernel and its row-sum pass
+    for key, parts in (("gemm_m64", ("k_gemm_tile<2,", "k_splitk_finalize")),
+                       ("gemm_m512", ("k_gemm_big2<2>", "k_rowsum"))):
+        f = [last(fetch, lambda n, t=t: t in n, 3) for t in parts]
+        w = [last(write, lambda n, t=t: t in n, 3) for t in parts]
+        if all(f) and all(w):
+            res[key] = (sum(np.mean(x) for x in f), sum(np.mean(x) for x in w))
     lines = [
         "# HBM traffic per launch of the bench.py step kernels (rocprofv3 PMC)",
         "",
@@ -211,8 +206,9 @@ def pmc_summarize(args):
         "rocprofv3 pass over `bench.py --pmc-workload` (one MI355X). Each counter is scaled by what",
         "it reads for a plain 1 GiB device copy in the same run (1 GiB read, 1 GiB written):",
         f"FETCH scale = {fscale:.4f}, WRITE scale = {wscale:.4f}. Means over the last three launches",
-        "of each kernel; gemm_m64 adds its split-K finalize launch. `sha` is the hash of the kernel",
-        "sources the counters were taken on (bench.py reports `traffic` only while it matches).",
+        "of each kernel; gemm_m64 adds its split-K finalize launch, gemm_m512 its row-sum pass.",
+        "`sha` is the hash of the kernel sources the counters were taken on (bench.py reports",
+        "`traffic` only while it matches).",
         "",
         "Commands:",
         "```",
