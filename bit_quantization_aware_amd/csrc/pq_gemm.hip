@@ -390,6 +390,10 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
     auto step = [&](int s, auto pc) {
         constexpr int p = decltype(pc)::value;  // s mod U
         constexpr bool code_now = ((p + 1) % C::SS) == 0;
+        // The code refill below overwrites the buffer that holds stage s's
+        // codes, read in the previous iteration: those reads (long since
+        // issued) complete before the barrier.
+        wait_lgkmcnt0();
         wait_vmcnt<tile_wait(p, P, C::SS, C::XI, NC, U)>();
         block_barrier();
         // A wave just released from the barrier issues at raised priority
