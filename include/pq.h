@@ -18,8 +18,9 @@
  * Conventions shared by every entry point
  *   Memory     Every array argument is a DEVICE pointer owned by the caller;
  *              the library keeps no pointer after the call returns.  The only
- *              memory the library allocates itself is the GEMM's split-K
- *              workspace (see pq_w2a16_gemm).  Arrays are row-major and contiguous
+ *              memory the library allocates itself is the GEMM's workspace
+ *              (split-K partial sums and activation row sums, see
+ *              pq_w2a16_gemm).  Arrays are row-major and contiguous
  *              (leading dimension = cols), except the exported codes of
  *              pq_pack_w2 / pq_pack_w4 (the export byte order below).  Weight matrices are [out, in]:
  *              a "row" is one output channel, the unit the scale alpha
@@ -262,7 +263,10 @@ pq_status pq_pack_w4(int64_t rows, int64_t cols, const float *W, const float *al
  * are too few tiles to fill the chip, K is split over blocks, each split
  * writes fp32 partial sums to a workspace of splits * M * N * 4 bytes, and a
  * second kernel on the same stream adds them in split order and writes Y.
- * The workspace is device memory owned by the library: one buffer per
+ * For large M with K >= 2048 (2-bit grids; M >= 1024, or M >= 512 when N
+ * gives at least 512 tiles of 64 x 256) a first kernel writes the sums of
+ * the activation rows to a workspace of M * 4 bytes and the GEMM kernel
+ * reads them.  The workspace is device memory owned by the library: one buffer per
  * (device, stream), allocated on first need and, when a larger one is
  * needed, replaced after the stream has been synchronized.  It lives until
  * the process ends.  Allocation failure returns PQ_ERR_HIP with nothing
