@@ -14,13 +14,16 @@
 // of a block own 64 x 128 outputs each (2 x 2 waves, 4 x 8 MFMA tiles of
 // 16 x 16), so every activation fragment read from LDS feeds 8 MFMAs instead
 // of 4 and the row sums come from a separate pass; two blocks share a CU
-// (80 KB of LDS each, 234 VGPRs per lane).  A 128 x 128 wave tile (256
+// (80 KB of LDS each, 234 VGPRs per lane).  The waves' two halves split
+// either the block's rows (128-row blocks) or K (64-row blocks, for M too
+// small to give every CU two 128-row blocks); see BigCfg.  A 128 x 128 wave
+// tile (256
 // accumulators per lane, one wave per SIMD) was slower: its accumulators
 // no longer fit beside the fragments and moved between AGPRs and VGPRs.
 //
-// Per stage of K = 64: the block's activation tile (128 rows x 128 B, 16 KB)
-// goes global -> LDS by the LDS-DMA load into a ring of four stage buffers
-// kept three stages ahead, with the same XOR swizzle of 16-byte chunks as the
+// Per iteration (one K stage of 64 over 128 rows, or two over 64 rows) the
+// block's activations (16 KB) go global -> LDS by the LDS-DMA load into a
+// ring of four slots kept three iterations ahead, with the same XOR swizzle of 16-byte chunks as the
 // tiled kernel; the codes come 32 bytes per column (two stages) per fetch
 // into a double buffer, two column tiles of the export order per 1-KB DMA.
 // One s_waitcnt plus one barrier per stage order both rings (the wait counts
@@ -171,9 +174,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, const float *r
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // LDS read addresses.  Activation fragment of row tile i, k-step T:
-    // row wm*128 + 16 i + i16, chunk 2 grp + T (swizzled); code word of the
-    // wave's column tile j at stage-in-fetch p: dword grp of column i16.
+    // LDS read addresses.  Activation fragment of row tile i, k-step T: slot
+    // row wm*64 + 16 i + i16 (the wave's half), chunk 2 grp + T (swizzled);
+    // code word of the wave's column tile j at stage-in-fetch p: dword grp of
+    // column i16.
     const int swz = xswz(i16);
     const uint8_t *xa0 = lds + XR + (wm * kWaveM + i16) * 128 + (((2 * grp) ^ swz) << 4);
     const uint8_t *xa1 = lds + XR + (wm * kWaveM + i16) * 128 + (((2 * grp + 1) ^ swz) << 4);
