@@ -17,19 +17,19 @@
 // (80 KB of LDS each, 234 VGPRs per lane).  The waves' two halves split
 // either the block's rows (128-row blocks) or K (64-row blocks, for M too
 // small to give every CU two 128-row blocks); see BigCfg.  A 128 x 128 wave
-// tile (256
-// accumulators per lane, one wave per SIMD) was slower: its accumulators
-// no longer fit beside the fragments and moved between AGPRs and VGPRs.
+// tile (256 accumulators per lane, one wave per SIMD) was slower: its
+// accumulators no longer fit beside the fragments and moved between AGPRs
+// and VGPRs.
 //
 // Per iteration (one K stage of 64 over 128 rows, or two over 64 rows) the
 // block's activations (16 KB) go global -> LDS by the LDS-DMA load into a
-// ring of four slots kept three iterations ahead, with the same XOR swizzle of 16-byte chunks as the
-// tiled kernel; the codes come 32 bytes per column (two stages) per fetch
-// into a double buffer, two column tiles of the export order per 1-KB DMA.
-// One s_waitcnt plus one barrier per stage order both rings (the wait counts
-// from the shared pipeline model).  Within a stage the wave reads the next
-// k-step's activation fragments and the next stage's code words while its
-// MFMAs on the current ones run.
+// ring of four slots kept three iterations ahead, with the tiled kernel's
+// XOR swizzle of 16-byte chunks; the codes come 32 bytes per column (two
+// stages) per fetch into a double buffer, two column tiles of the export
+// order per 1-KB DMA.  One s_waitcnt plus one barrier per iteration order
+// both rings (the wait counts from the shared pipeline model).  Within an
+// iteration the wave reads its next k-step's activation fragments and the
+// next iteration's code words while its MFMAs on the current ones run.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
