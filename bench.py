@@ -508,6 +508,14 @@ def diagnostics_measure(torch, pq, W16, a16, stream, reps=10):
         pq.pq_level_stats(md, N, K, codes, cnt, ent)
         grids[pq.MODE_NAMES[md]] = round(float(ent.mean()), 4)
     out["mean_level_entropy_bits"] = grids
+    # the forward (codes only) with and without the level statistics fused in
+    tf = b2b_ms(torch, stream, lambda i: pq.pq_quantize_fwd(mode, N, K, W16, a16, 0, None, None, codes), reps)
+    tfs = b2b_ms(torch, stream, lambda i: pq.pq_quantize_fwd_stats(mode, N, K, W16, a16, None, codes, counts, ent),
+                 reps)
+    fb = N * K * (4 + 0.25) + 4 * N
+    out["fwd_codes_ms"] = round(tf, 4)
+    out["fwd_codes_fused_stats_ms"] = round(tfs, 4)
+    out["fwd_codes_fused_stats_frac"] = round(fb / tfs / 1e6 / HBM_PEAK_GBS, 4)
     del codes, W0
     return out
 

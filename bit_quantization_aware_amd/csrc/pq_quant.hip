@@ -68,31 +68,38 @@ constexpr float kTwoThirds = static_cast<float>(2.0 / 3.0);
 template <int MODE> struct Mode;
 template <> struct Mode<PQ_W1_BINARY> {
     static constexpr int cw = 1;
+    static constexpr int levels = 2;
     static constexpr float lo = -1.0f, hi = 1.0f;
 };
 template <> struct Mode<PQ_W158_SEQ_TERNARY> {
     static constexpr int cw = 2;
+    static constexpr int levels = 3;
     static constexpr float lo = -kClip, hi = kClip;
 };
 template <> struct Mode<PQ_W2_SEQ> {
     static constexpr int cw = 2;
+    static constexpr int levels = 4;
     static constexpr float lo = -kClip, hi = kClip;
 };
 template <> struct Mode<PQ_W3_LSQ> {
     static constexpr int cw = 4;
+    static constexpr int levels = 8;
     static constexpr float lo = -4.0f, hi = 3.0f;  // LSQ grid -2^(b-1) .. 2^(b-1)-1
 };
 // The LSQ grids the pages set against SEQ at 2 and 1.58 bits ([Rebuttal]).
 template <> struct Mode<PQ_W2_LSQ> {
     static constexpr int cw = 2;
+    static constexpr int levels = 4;
     static constexpr float lo = -2.0f, hi = 1.0f;
 };
 template <> struct Mode<PQ_W158_LSQ> {
     static constexpr int cw = 2;
+    static constexpr int levels = 3;
     static constexpr float lo = -1.0f, hi = 1.0f;
 };
 template <> struct Mode<PQ_W4_LSQ> {
     static constexpr int cw = 4;
+    static constexpr int levels = 16;
     static constexpr float lo = -8.0f, hi = 7.0f;
 };
 
@@ -206,7 +213,14 @@ __device__ __forceinline__ double team_sum(double v, double *lds4)
 // before any math, to keep U * 16 bytes per lane in flight).
 constexpr int kUnroll = 4;
 
-enum : unsigned { OUT_BF16 = 1, OUT_F32 = 2, OUT_CODES = 4, OUT_ALPHA_BF16 = 8, OUT_TILED = 16 };
+enum : unsigned { OUT_BF16 = 1, OUT_F32 = 2, OUT_CODES = 4, OUT_ALPHA_BF16 = 8, OUT_TILED = 16, OUT_STATS = 32 };
+
+// Level statistics fused into the forward (OUT_STATS, single matrix): per
+// row the count of each stored code [rows, levels] and its entropy in bits.
+struct StatsOut {
+    uint32_t *counts;
+    double *entropy;
+};
 
 // Forward rows per wave: with one wave per row (launches of many short
 // rows) each wave takes two rows in turn, which halves the number of waves
@@ -250,13 +264,19 @@ __device__ __forceinline__ void store_codes(PQ_GLOBAL uint8_t *crow, int q, uint
 // Forward: optional alpha init, then per quad: quantize, emit bf16 / fp32 /
 // codes.  OUT_ALPHA_BF16 (export) also writes bf16(alpha) per row.
 template <int MODE, bool INIT, int WPR, unsigned OUTS>
-__global__ __launch_bounds__(256, PQ_QUANT_FWD_MINB) void k_quant_fwd(LaunchTable lt, void *alpha_bf16_single)
+__global__ __launch_bounds__(256, PQ_QUANT_FWD_MINB) void k_quant_fwd(LaunchTable lt, void *alpha_bf16_single,
+                                                                      StatsOut so)
 {
     constexpr int RPB = 4 / WPR;
     constexpr int TEAM = 64 * WPR;
     constexpr int CW = Mode<MODE>::cw;
+    constexpr int L = Mode<MODE>::levels;
+    constexpr bool STATS = (OUTS & OUT_STATS) != 0;
     __shared__ float lds_f[4];
     __shared__ double lds_d[4];
+    // OUT_STATS: per wave, a count of each level for each lane ([level][lane],
+    // so a wave's increments of one level fall on 64 distinct banks)
+    __shared__ uint32_t hist[STATS ? 4 * L * 64 : 1];
 
     constexpr bool TILED = (OUTS & OUT_TILED) != 0;
     static_assert(!TILED || ((OUTS & OUT_CODES) != 0 && (CW == 2 || CW == 4)), "tiled export of 2- or 4-bit codes");
@@ -342,6 +362,12 @@ __global__ __launch_bounds__(256, PQ_QUANT_FWD_MINB) void k_quant_fwd(LaunchTabl
         PQ_GLOBAL f32x4 *wq32 = (OUTS & OUT_F32) ? (PQ_GLOBAL f32x4 *)(m.wq_f32 + row * cols) : nullptr;
         PQ_GLOBAL uint8_t *crow = (OUTS & OUT_CODES) ? (PQ_GLOBAL uint8_t *)(m.codes + row * (cols * CW / 8)) : nullptr;
 
+        uint32_t *whist = hist + (STATS ? (threadIdx.x >> 6) * L * 64 + (threadIdx.x & 63) : 0);
+        if constexpr (STATS) {
+#pragma unroll
+            for (int l = 0; l < L; ++l) whist[l * 64] = 0u;
+        }
+
         // One pass: kUnroll quads per lane, loads first.  GUARD only on the last.
         auto pass = [&](int base, auto guard_c) {
             constexpr bool GUARD = decltype(guard_c)::value;
@@ -364,6 +390,14 @@ __global__ __launch_bounds__(256, PQ_QUANT_FWD_MINB) void k_quant_fwd(LaunchTabl
                 const uint32_t c2 = quant_x<MODE>(v[u].z, div_fast(v[u].z, y), l2);
                 const uint32_t c3 = quant_x<MODE>(v[u].w, div_fast(v[u].w, y), l3);
                 const float q0 = a * l0, q1 = a * l1, q2 = a * l2, q3 = a * l3;
+                if constexpr (STATS) {
+                    if (act) {
+                        __hip_atomic_fetch_add(&whist[c0 * 64], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+                        __hip_atomic_fetch_add(&whist[c1 * 64], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+                        __hip_atomic_fetch_add(&whist[c2 * 64], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+                        __hip_atomic_fetch_add(&whist[c3 * 64], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+                    }
+                }
                 if constexpr ((OUTS & OUT_BF16) != 0) {
                     if (act) wq16[q] = u32x2{pack_bf16x2(q0, q1), pack_bf16x2(q2, q3)};
                 }
@@ -393,6 +427,24 @@ __global__ __launch_bounds__(256, PQ_QUANT_FWD_MINB) void k_quant_fwd(LaunchTabl
         const int nfull = nq / STEP * STEP;
         for (int base = 0; base < nfull; base += STEP) pass(base, std::false_type{});
         if (nfull < nq) pass(nfull, std::true_type{});
+        if constexpr (STATS) {
+            // Counts of the row (lanes, then the team's waves, in a fixed
+            // order; exact in binary64) and their entropy, as the separate
+            // level-statistics kernel computes them.
+            double h = 0.0;
+#pragma unroll 1
+            for (int l = 0; l < L; ++l) {
+                const double c = team_sum<WPR>(static_cast<double>(whist[l * 64]), lds_d);
+                if (tl == 0) {
+                    so.counts[row * L + l] = static_cast<uint32_t>(c);
+                    if (c > 0.0) {
+                        const double pr = c / static_cast<double>(cols);
+                        h -= pr * log2(pr);
+                    }
+                }
+            }
+            if (tl == 0 && so.entropy) so.entropy[row] = h;
+        }
         if constexpr (TILED) {
             // zero the bytes of the last group past the row's end (< 64 bytes)
             const int64_t rb = cols * CW / 8;
@@ -771,12 +823,34 @@ pq_status launch_grouped(int count, const D *host, const D *dev, hipStream_t str
 }
 
 template <int MODE, bool INIT, unsigned OUTS>
-void launch_fwd_t(const LaunchTable &lt, int blocks, int wpr, hipStream_t s, void *abf)
+void launch_fwd_t(const LaunchTable &lt, int blocks, int wpr, hipStream_t s, void *abf, StatsOut so = {})
 {
     if (wpr == 1)
-        hipLaunchKernelGGL((k_quant_fwd<MODE, INIT, 1, OUTS>), dim3(blocks), dim3(256), 0, s, lt, abf);
+        hipLaunchKernelGGL((k_quant_fwd<MODE, INIT, 1, OUTS>), dim3(blocks), dim3(256), 0, s, lt, abf, so);
     else
-        hipLaunchKernelGGL((k_quant_fwd<MODE, INIT, 4, OUTS>), dim3(blocks), dim3(256), 0, s, lt, abf);
+        hipLaunchKernelGGL((k_quant_fwd<MODE, INIT, 4, OUTS>), dim3(blocks), dim3(256), 0, s, lt, abf, so);
+}
+
+// Forward with the fused level statistics (alpha given, codes written,
+// optionally the bf16 weights).
+template <int MODE>
+void launch_fwd_stats_mode(bool bf16, const LaunchTable &lt, int blocks, int wpr, hipStream_t s, StatsOut so)
+{
+    if (bf16) launch_fwd_t<MODE, false, OUT_STATS | OUT_CODES | OUT_BF16>(lt, blocks, wpr, s, nullptr, so);
+    else launch_fwd_t<MODE, false, OUT_STATS | OUT_CODES>(lt, blocks, wpr, s, nullptr, so);
+}
+
+void launch_fwd_stats(int mode, bool bf16, const LaunchTable &lt, int blocks, int wpr, hipStream_t s, StatsOut so)
+{
+    switch (mode) {
+    case PQ_W1_BINARY: launch_fwd_stats_mode<PQ_W1_BINARY>(bf16, lt, blocks, wpr, s, so); break;
+    case PQ_W158_SEQ_TERNARY: launch_fwd_stats_mode<PQ_W158_SEQ_TERNARY>(bf16, lt, blocks, wpr, s, so); break;
+    case PQ_W2_SEQ: launch_fwd_stats_mode<PQ_W2_SEQ>(bf16, lt, blocks, wpr, s, so); break;
+    case PQ_W3_LSQ: launch_fwd_stats_mode<PQ_W3_LSQ>(bf16, lt, blocks, wpr, s, so); break;
+    case PQ_W2_LSQ: launch_fwd_stats_mode<PQ_W2_LSQ>(bf16, lt, blocks, wpr, s, so); break;
+    case PQ_W158_LSQ: launch_fwd_stats_mode<PQ_W158_LSQ>(bf16, lt, blocks, wpr, s, so); break;
+    default: launch_fwd_stats_mode<PQ_W4_LSQ>(bf16, lt, blocks, wpr, s, so); break;
+    }
 }
 
 template <int MODE, bool INIT>
@@ -1082,6 +1156,30 @@ pq_status pq_quantize_fwd(int mode, int64_t rows, int64_t cols, const float *W, 
         1, &m, static_cast<const pq_mat *>(nullptr), static_cast<hipStream_t>(stream), true,
         [&](const LaunchTable &lt, int blocks, int wpr, hipStream_t s) { launch_fwd(mode, init, outs, lt, blocks, wpr, s); },
         (flags & PQ_CODES_EXPORT) != 0);
+}
+
+pq_status pq_quantize_fwd_stats(int mode, int64_t rows, int64_t cols, const float *W, const float *alpha,
+                                void *Wq_bf16, uint8_t *codes, uint32_t *counts, double *entropy, void *stream)
+{
+    using namespace pq;
+    pq_mat m = {};
+    m.W = W;
+    m.alpha = const_cast<float *>(alpha);
+    m.wq_bf16 = Wq_bf16;
+    m.codes = codes;
+    m.rows = rows;
+    m.cols = cols;
+    unsigned outs = 0;
+    pq_status st = check_fwd_descs(mode, 1, &m, 0u, &outs);
+    if (st != PQ_OK) return st;
+    if (rows == 0) return PQ_OK;
+    if (!codes || !counts) return PQ_ERR_NULL;
+    if (!ptr_ok(counts) || !ptr_ok(entropy)) return PQ_ERR_ALIGN;
+    const StatsOut so{counts, entropy};
+    return launch_grouped(1, &m, static_cast<const pq_mat *>(nullptr), static_cast<hipStream_t>(stream), true,
+                          [&](const LaunchTable &lt, int blocks, int wpr, hipStream_t s) {
+                              launch_fwd_stats(mode, Wq_bf16 != nullptr, lt, blocks, wpr, s, so);
+                          });
 }
 
 pq_status pq_quantize_bwd_grouped(int mode, int count, const pq_mat *descs_host,

@@ -34,7 +34,7 @@ EXPORTS = ("pq_code_row_bytes", "pq_packed_bytes", "pq_default_grad_scale", "pq_
            "pq_quantize_fwd", "pq_quantize_bwd", "pq_pack_w2", "pq_pack_w4", "pq_w2a16_gemm",
            "pq_w4a16_gemm", "pq_quantize_fwd_grouped", "pq_quantize_bwd_grouped", "pq_qat_step",
            "pq_qat_step_grouped", "pq_pack", "pq_gemm", "pq_gemm_f32a", "pq_num_levels", "pq_level_stats",
-           "pq_weight_movement")
+           "pq_quantize_fwd_stats", "pq_weight_movement")
 
 
 class PQError(RuntimeError):
@@ -93,6 +93,7 @@ def _load():
     L.pq_num_levels.argtypes = [i32]
     L.pq_num_levels.restype = i32
     L.pq_level_stats.argtypes = [i32, i64, i64, vp, vp, vp, vp]
+    L.pq_quantize_fwd_stats.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp, vp, vp]
     L.pq_weight_movement.argtypes = [i64, i64, vp, vp, vp, vp, vp]
     L.pq_quantize_fwd_grouped.argtypes = [i32, i32, vp, vp, u32, vp]
     L.pq_quantize_bwd_grouped.argtypes = [i32, i32, vp, vp, i32, vp]
@@ -207,6 +208,12 @@ def pq_num_levels(mode: int) -> int:
 def pq_level_stats(mode, rows, cols, codes, counts, entropy=None, stream=None) -> None:
     _check(lib.pq_level_stats(mode, rows, cols, _ptr(codes), _ptr(counts), _ptr(entropy), _stream(stream)),
            "pq_level_stats")
+
+
+def pq_quantize_fwd_stats(mode, rows, cols, W, alpha, Wq_bf16, codes, counts, entropy=None,
+                          stream=None) -> None:
+    _check(lib.pq_quantize_fwd_stats(mode, rows, cols, _ptr(W), _ptr(alpha), _ptr(Wq_bf16), _ptr(codes),
+                                     _ptr(counts), _ptr(entropy), _stream(stream)), "pq_quantize_fwd_stats")
 
 
 def pq_weight_movement(rows, cols, W, W0, sq_diff, sq_ref, stream=None) -> None:

@@ -420,6 +420,14 @@ pq_status pq_qat_step_grouped(int mode, int count, const pq_step_mat *descs_host
  * p_c = counts[i, c] / cols (binary64; 0 for a row on one level).  Reads
  * 1/8 .. 1/2 byte per weight.
  *
+ * pq_quantize_fwd_stats -- the forward of pq_quantize_fwd (alpha given, no
+ * init) with the level statistics of pq_level_stats taken in the same pass,
+ * from the codes as they are made: codes [rows, pq_code_row_bytes] are
+ * written (required), Wq_bf16 [rows, cols] optionally (NULL: not written),
+ * counts [rows, pq_num_levels(mode)] u32 (required) and entropy [rows] f64
+ * (optional) as pq_level_stats defines them.  All pointers 16-byte aligned.
+ * Errors as pq_quantize_fwd; codes or counts NULL -> PQ_ERR_NULL.
+ *
  * pq_weight_movement -- sq_diff[i] = sum_j (W[i,j] - W0[i,j])^2 and
  * sq_ref[i] = sum_j W0[i,j]^2 per row, each difference and square in
  * binary64, summed in a fixed order (run-to-run identical); the relative
@@ -429,6 +437,9 @@ pq_status pq_qat_step_grouped(int mode, int count, const pq_step_mat *descs_host
 int pq_num_levels(int mode);
 pq_status pq_level_stats(int mode, int64_t rows, int64_t cols, const uint8_t *codes,
                          uint32_t *counts, double *entropy, void *stream);
+pq_status pq_quantize_fwd_stats(int mode, int64_t rows, int64_t cols, const float *W,
+                                const float *alpha, void *Wq_bf16, uint8_t *codes,
+                                uint32_t *counts, double *entropy, void *stream);
 pq_status pq_weight_movement(int64_t rows, int64_t cols, const float *W, const float *W0,
                              double *sq_diff, double *sq_ref, void *stream);
 

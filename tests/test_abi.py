@@ -196,6 +196,14 @@ def test_diagnostics_argument_checks(pq):
     assert L.pq_level_stats(2, 4, 60, A, B, None, None) == 2
     assert L.pq_level_stats(2, 4, 64, None, B, None, None) == 1
     assert L.pq_level_stats(2, 0, 64, None, None, None, None) == 0               # empty
+    # pq_quantize_fwd_stats(mode, rows, cols, W, alpha, Wq_bf16, codes, counts, entropy, stream)
+    assert L.pq_quantize_fwd_stats(7, 4, 64, A, B, None, A, B, None, None) == 3
+    assert L.pq_quantize_fwd_stats(2, 4, 60, A, B, None, A, B, None, None) == 2
+    assert L.pq_quantize_fwd_stats(2, 4, 64, A, B, None, None, B, None, None) == 1   # codes required
+    assert L.pq_quantize_fwd_stats(2, 4, 64, A, B, None, A, None, None, None) == 1   # counts required
+    assert L.pq_quantize_fwd_stats(2, 4, 64, A, B, None, A, MIS, None, None) == 4
+    assert L.pq_quantize_fwd_stats(2, 4, 64, None, B, None, A, B, None, None) == 1
+    assert L.pq_quantize_fwd_stats(2, 0, 64, None, None, None, None, None, None, None) == 0  # empty
     assert L.pq_weight_movement(4, 64, A, MIS, A, B, None) == 4
     assert L.pq_weight_movement(4, 64, A, B, None, B, None) == 1
     assert L.pq_weight_movement(-1, 64, A, B, A, B, None) == 2

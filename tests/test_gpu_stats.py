@@ -1,6 +1,8 @@
 """GPU parity of the diagnostics against the oracle, through the C ABI: level
-counts bit-exact, entropy to 1e-12 (binary64, different log2), weight
-movement sums to rel 1e-12 (binary64 sums in different orders)."""
+counts bit-exact (from stored codes, and fused into the forward with its
+bf16 weights and codes bit-exact), entropy to 1e-12 (binary64, different
+log2), weight movement sums to rel 1e-12 (binary64 sums in different
+orders)."""
 import numpy as np
 import pytest
 import torch
@@ -37,6 +39,34 @@ def test_level_stats(mode, rows, cols):
     pq.pq_level_stats(mode, rows, cols, dev(codes), counts, ent)
     torch.cuda.synchronize()
     c_o, e_o = O.level_stats(mode, codes, cols)
+    assert np.array_equal(host(counts).view(np.uint32), c_o)
+    assert np.allclose(host(ent), e_o, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", [O.BINARY, O.TERNARY, O.SEQ2, O.LSQ3, O.LSQ4, O.LSQ2, O.LSQ158])
+@pytest.mark.parametrize("rows,cols,bf16", [(37, 264, True), (5, 8, False), (2, 16384, True), (4100, 64, True),
+                                            (4101, 72, False), (9, 5120, True)])
+def test_fwd_with_fused_stats(mode, rows, cols, bf16):
+    """The forward with the level statistics taken in the same pass: bf16
+    weights and codes as the oracle's forward, counts and entropy as the
+    oracle's level statistics of those codes (one wave per row and two rows
+    per wave for 4100 short rows, a team of four waves per row otherwise)."""
+    rng = np.random.default_rng(3 * rows + cols + mode)
+    W = synth.normal_f32(rng, (rows, cols), 0.02)
+    W[0] = 0.0
+    alpha = O.alpha_init(mode, W)
+    wq_o, _, codes_o = O.quantize_fwd(mode, W, alpha)
+    L = pq.pq_num_levels(mode)
+    wq = torch.empty(rows, cols, dtype=torch.bfloat16, device="cuda") if bf16 else None
+    codes = torch.empty(rows, pq.pq_code_row_bytes(mode, cols), dtype=torch.uint8, device="cuda")
+    counts = torch.empty(rows, L, dtype=torch.int32, device="cuda")
+    ent = torch.empty(rows, dtype=torch.float64, device="cuda")
+    pq.pq_quantize_fwd_stats(mode, rows, cols, dev(W), dev(alpha), wq, codes, counts, ent)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(codes), codes_o)
+    if bf16:
+        assert np.array_equal(host(wq), wq_o)
+    c_o, e_o = O.level_stats(mode, codes_o, cols)
     assert np.array_equal(host(counts).view(np.uint32), c_o)
     assert np.allclose(host(ent), e_o, rtol=0, atol=1e-12)
 
