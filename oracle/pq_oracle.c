@@ -444,10 +444,12 @@ int pqo_quantize_bwd(int mode, int64_t rows, int64_t cols, const float *W,
  * ternary is commonly held in 2-bit integers, [News] storage paragraph) or a
  * 4-bit one (3- and 4-bit LSQ).
  * ------------------------------------------------------------------------- */
+/* Widths with an export: every code container (1-bit codes eight per byte,
+ * 2-bit four per byte, 4-bit two per byte). */
 static int deployable(int mode)
 {
-    return mode == PQO_W158_SEQ_TERNARY || mode == PQO_W2_SEQ || mode == PQO_W3_LSQ || mode == PQO_W4_LSQ ||
-           mode == PQO_W2_LSQ || mode == PQO_W158_LSQ;
+    return mode == PQO_W1_BINARY || mode == PQO_W158_SEQ_TERNARY || mode == PQO_W2_SEQ || mode == PQO_W3_LSQ ||
+           mode == PQO_W4_LSQ || mode == PQO_W2_LSQ || mode == PQO_W158_LSQ;
 }
 
 int pqo_pack(int mode, int64_t rows, int64_t cols, const float *W, const float *alpha,

@@ -425,9 +425,13 @@ def test_pack_byte_layout_lsb_first():
     W4 = np.array([[-8.0, 7.0, 0.0, 1.0]], np.float32)
     p4, _ = O.pack(O.LSQ4, W4, np.ones(1, np.float32))
     assert p4.tolist() == [[0xF0, 0x98]]
+    # 1 bit: -1 -> code 0, +1 -> code 1, eight codes per byte, first code lowest
+    W1 = np.array([[-1.0, 1.0, 1.0, -1.0, 1.0, 1.0, 1.0, 1.0]], np.float32)
+    p1, _ = O.pack(O.BINARY, W1, np.ones(1, np.float32))
+    assert p1.tolist() == [[0xF6]]
 
 
-@pytest.mark.parametrize("mode", [O.SEQ2, O.LSQ4, O.TERNARY, O.LSQ3])
+@pytest.mark.parametrize("mode", [O.SEQ2, O.LSQ4, O.TERNARY, O.LSQ3, O.BINARY])
 def test_gemm_ref_is_matmul_of_dequantized_weight(mode):
     rng = np.random.default_rng(50)
     M, N, K = 5, 24, 64
@@ -437,7 +441,8 @@ def test_gemm_ref_is_matmul_of_dequantized_weight(mode):
     X = synth.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
     Y = O.gemm_ref(mode, X, packed, ab, N)
     lev = {O.SEQ2: lambda c: (c - 1.5) / 2.0, O.LSQ4: lambda c: c - 8.0,
-           O.TERNARY: lambda c: (c - 1.0) * np.float64(np.float32(2.0 / 3.0)), O.LSQ3: lambda c: c - 4.0}[mode]
+           O.TERNARY: lambda c: (c - 1.0) * np.float64(np.float32(2.0 / 3.0)), O.LSQ3: lambda c: c - 4.0,
+           O.BINARY: lambda c: 2.0 * c - 1.0}[mode]
     Wd = lev(unpack_codes(packed, mode, K).astype(np.float64)) * \
         synth.bf16_bits_to_f32(ab).astype(np.float64)[:, None]
     want = np.matmul(synth.bf16_bits_to_f32(X).astype(np.float64), Wd.T)
