@@ -184,6 +184,18 @@ struct TileCfg {
 
 
 
+// 1-bit decode: the eight codes of byte b (first code lowest) spread to the
+// eight nibbles of a word, each nibble 2 * code: the e2m1 value of the code
+// (0 or 1.0), so the fp4 -> bf16 pair converts of bytes 0..3 give codes
+// 0..7 in order.
+__device__ __forceinline__ uint32_t spread_bits_fp4(uint32_t b)
+{
+    uint32_t x = (b | (b << 12)) & 0x000F000Fu;
+    x = (x | (x << 6)) & 0x03030303u;
+    x = (x | (x << 3)) & 0x11111111u;
+    return x << 1;
+}
+
 template <int BITS, int P, int WN>
 __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
 {
@@ -287,12 +299,12 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
     // take dword grp of the stage's 16-byte piece, 4-bit lanes bytes
     // 8 (grp & 1) of piece 2 (stage) + (grp >> 1).
     const uint8_t *ca = lds + CR + (4 * w) * 1024 + i16 * 16 +
-                        (BITS == 2 ? 4 * grp : 8 * (grp & 1) + 256 * (grp >> 1));
+                        (BITS == 1 ? 2 * grp : BITS == 2 ? 4 * grp : 8 * (grp & 1) + 256 * (grp >> 1));
 
     // Fragments of one stage: A for both k-steps and the code words.
     struct Frag {
         uint4 a[2][4];
-        uint32_t d[4][BITS / 2];
+        uint32_t d[4][BITS == 4 ? 2 : 1];
     };
     // Fragments of stage st, with PH = st mod 2*SS known at compile time
     // (activation slot PH mod P, code buffer (PH / SS) & 1, stage PH mod SS).
@@ -303,8 +315,12 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
         constexpr int CST = PH % C::SS;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint8_t *p = ca + CBUF * C::CSS + j * 1024 + CST * (C::CB == 16 ? 256 : 512);
-            if constexpr (BITS == 2) {
+            // stage CST's bytes: 8, 16 or 32 per column, in the 16-byte pieces
+            const uint8_t *p = ca + CBUF * C::CSS + j * 1024 +
+                               (C::CB == 8 ? (CST >> 1) * 256 + (CST & 1) * 8 : CST * (C::CB == 16 ? 256 : 512));
+            if constexpr (BITS == 1) {
+                f.d[j][0] = *reinterpret_cast<const uint16_t *>(p);
+            } else if constexpr (BITS == 2) {
                 f.d[j][0] = *reinterpret_cast<const uint32_t *>(p);
             } else {
                 const uint2 v = *reinterpret_cast<const uint2 *>(p);
@@ -334,7 +350,13 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 uint4 b;
-                if constexpr (BITS == 2) {
+                if constexpr (BITS == 1) {
+                    const uint32_t x = spread_bits_fp4((f.d[j][0] >> (8 * T)) & 0xFFu);
+                    b.x = fp4x2_to_bf16x2<0>(x);
+                    b.y = fp4x2_to_bf16x2<1>(x);
+                    b.z = fp4x2_to_bf16x2<2>(x);
+                    b.w = fp4x2_to_bf16x2<3>(x);
+                } else if constexpr (BITS == 2) {
                     b.x = fp4x2_to_bf16x2<2 * T>(w0[j]);
                     b.y = fp4x2_to_bf16x2<2 * T>(w1[j]);
                     b.z = fp4x2_to_bf16x2<2 * T + 1>(w0[j]);
@@ -550,7 +572,7 @@ __global__ __launch_bounds__(256) void k_splitk_finalize(const float *ws, const 
 // ---------------------------------------------------------------------------
 template <int BITS>
 struct StreamGeom {
-    static constexpr int GK = BITS == 2 ? 256 : 128;  // k per group (64 bytes of a row)
+    static constexpr int GK = 512 / BITS;             // k per group (64 bytes of a row)
     static constexpr int RPL = 512 / GK;              // activation rows per 1-KB DMA
     static constexpr int XQS = 1024 + 16 * RPL;       // LDS stride of the activation DMAs
 };
@@ -641,7 +663,25 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
         }
         // chunk ch of the lane's row sits at aoff + ch * 16 * RPL
         const uint8_t *xa = sp + aoff;
-        if constexpr (BITS == 2) {
+        if constexpr (BITS == 1) {
+            // k = 128 grp + [0, 128): chunks 16 grp .. 16 grp + 15; code byte t
+            // of the lane's 16 holds k = 128 grp + 8 t + [0, 8), first lowest
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(xa + (16 * grp + t) * 16));
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const uint32_t Dw = (t >> 2) == 0 ? c[j].x : (t >> 2) == 1 ? c[j].y : (t >> 2) == 2 ? c[j].z : c[j].w;
+                    const uint32_t x = spread_bits_fp4((Dw >> (8 * (t & 3))) & 0xFFu);
+                    uint4 b;
+                    b.x = fp4x2_to_bf16x2<0>(x);
+                    b.y = fp4x2_to_bf16x2<1>(x);
+                    b.z = fp4x2_to_bf16x2<2>(x);
+                    b.w = fp4x2_to_bf16x2<3>(x);
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, b), acc[j], 0, 0, 0);
+                }
+            }
+        } else if constexpr (BITS == 2) {
             uint4 ua[8];  // k = 64 * grp + [0, 64): chunks 8 * grp .. 8 * grp + 7
 #pragma unroll
             for (int q = 0; q < 8; ++q) ua[q] = *reinterpret_cast<const uint4 *>(xa + (8 * grp + q) * 32);
@@ -779,9 +819,12 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
 // 4-bit blocks take fewer column tiles and the chip runs two per CU.
 template <int BITS, int XI>
 struct StreamCfg {
-    static constexpr int TN = BITS == 2 ? PQ_STREAM_TN : (XI == 1 ? PQ_STREAM4_TN1 : PQ_STREAM4_TN);
+    // 1 bit: 16 activation DMAs of one row each (M up to 16) leave LDS for two tiles
+    static constexpr int TN = BITS == 1 ? (XI == 16 ? 2 : PQ_STREAM_TN)
+                              : BITS == 2 ? PQ_STREAM_TN : (XI == 1 ? PQ_STREAM4_TN1 : PQ_STREAM4_TN);
     static constexpr int NW = PQ_STREAM_NW;
-    static constexpr int D = BITS == 2 ? (XI == 1 ? PQ_STREAM_D1 : XI == 2 ? PQ_STREAM_D2 : XI <= 4 ? PQ_STREAM_D4 : PQ_STREAM_D8)
+    static constexpr int D = BITS == 1 ? (XI <= 4 ? 3 : 2)
+                             : BITS == 2 ? (XI == 1 ? PQ_STREAM_D1 : XI == 2 ? PQ_STREAM_D2 : XI <= 4 ? PQ_STREAM_D4 : PQ_STREAM_D8)
                                        : (XI == 1 ? PQ_STREAM4_D1 : XI == 2 ? PQ_STREAM4_D2 : PQ_STREAM4_D4);
 };
 
@@ -913,8 +956,8 @@ pq_status launch_tile(const GemmArgs &a, hipStream_t s)
     const int sps = ((stages + splits - 1) / splits + C::SS - 1) / C::SS * C::SS;
     splits = (stages + sps - 1) / sps;
     // the tile kernel's 4-bit operand is 2 + c/8 (the stream kernel's 128 + c)
-    const float off = BITS == 2 ? a.off : 2.0f + (a.off - 128.0f) / 8.0f;
-    const float mul = BITS == 2 ? a.mul : 8.0f * a.mul;
+    const float off = BITS != 4 ? a.off : 2.0f + (a.off - 128.0f) / 8.0f;
+    const float mul = BITS != 4 ? a.mul : 8.0f * a.mul;
     TileArgs t{a.X, a.packed, a.alpha, a.Y, nullptr, a.M, a.N, a.K, mtiles, ntiles, splits, sps * kStageK,
                a.gstride, off, mul, a.alpha32};
     const int64_t total = static_cast<int64_t>(a.M) * a.N;
@@ -950,6 +993,7 @@ bool level_map(int mode, LevelMap *lm)
     case PQ_W4_LSQ: *lm = {4, 8.0f, 1.0f}; return true;
     case PQ_W2_LSQ: *lm = {2, 2.0f, 1.0f}; return true;    // the ablation grids ([Rebuttal])
     case PQ_W158_LSQ: *lm = {2, 1.0f, 1.0f}; return true;
+    case PQ_W1_BINARY: *lm = {1, 0.5f, 2.0f}; return true;  // level 2c - 1
     default: return false;
     }
 }
@@ -968,15 +1012,17 @@ pq_status gemm(int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *pa
     GemmArgs a{static_cast<const uint16_t *>(X), packed, static_cast<const uint16_t *>(alpha_bf16),
                static_cast<uint16_t *>(Y), static_cast<int>(M), static_cast<int>(N), static_cast<int>(K),
                (N + 15) / 16 * 16 * 64,
-               // the stream kernel's operand: c / 2 (2 bits), 128 + c (4 bits); all exact
-               BITS == 2 ? lm.zc / 2.0f : 128.0f + lm.zc, BITS == 2 ? 2.0f * lm.step : lm.step, alpha32};
+               // the stream kernel's operand: c (1 bit), c / 2 (2 bits), 128 + c (4 bits); all exact
+               BITS == 1 ? lm.zc : BITS == 2 ? lm.zc / 2.0f : 128.0f + lm.zc,
+               BITS == 1 ? lm.step : BITS == 2 ? 2.0f * lm.step : lm.step, alpha32};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    constexpr int GK = BITS == 2 ? 256 : 128;
+    constexpr int GK = 512 / BITS;
     constexpr int RPL = 512 / GK;
     if (M <= 16 && K % GK == 0) {
         if (M <= RPL) launch_stream<BITS, 1>(a, s);
         else if (M <= 2 * RPL) launch_stream<BITS, 2>(a, s);
         else if (M <= 4 * RPL) launch_stream<BITS, 4>(a, s);
+        else if (BITS == 1 && M <= 8) launch_stream<BITS, (BITS == 1 ? 8 : 4)>(a, s);
         else launch_stream<BITS, 16 / RPL>(a, s);
     } else if (gemm_big_takes(BITS, M, N, K)) {
         float *rsum = nullptr;
@@ -1002,6 +1048,7 @@ pq_status pq_gemm(int mode, int64_t M, int64_t N, int64_t K, const void *X, cons
 {
     pq::LevelMap lm;
     if (!pq::level_map(mode, &lm)) return PQ_ERR_MODE;
+    if (lm.bits == 1) return pq::gemm<1>(M, N, K, X, packed, alpha_bf16, Y, stream, lm);
     if (lm.bits == 2) return pq::gemm<2>(M, N, K, X, packed, alpha_bf16, Y, stream, lm);
     return pq::gemm<4>(M, N, K, X, packed, alpha_bf16, Y, stream, lm);
 }
@@ -1012,6 +1059,7 @@ pq_status pq_gemm_f32a(int mode, int64_t M, int64_t N, int64_t K, const void *X,
     pq::LevelMap lm;
     if (!pq::level_map(mode, &lm)) return PQ_ERR_MODE;
     if (!alpha) return PQ_ERR_NULL;
+    if (lm.bits == 1) return pq::gemm<1>(M, N, K, X, packed, nullptr, Y, stream, lm, alpha);
     if (lm.bits == 2) return pq::gemm<2>(M, N, K, X, packed, nullptr, Y, stream, lm, alpha);
     return pq::gemm<4>(M, N, K, X, packed, nullptr, Y, stream, lm, alpha);
 }

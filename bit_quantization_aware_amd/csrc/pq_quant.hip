@@ -279,7 +279,7 @@ __global__ __launch_bounds__(256, PQ_QUANT_FWD_MINB) void k_quant_fwd(LaunchTabl
     __shared__ uint32_t hist[STATS ? 4 * L * 64 : 1];
 
     constexpr bool TILED = (OUTS & OUT_TILED) != 0;
-    static_assert(!TILED || ((OUTS & OUT_CODES) != 0 && (CW == 2 || CW == 4)), "tiled export of 2- or 4-bit codes");
+    static_assert(!TILED || (OUTS & OUT_CODES) != 0, "tiled export writes codes");
     const int wave = threadIdx.x >> 6;
     const int tl = (wave % WPR) * 64 + (threadIdx.x & 63);
     int b = blockIdx.x;
@@ -404,7 +404,15 @@ __global__ __launch_bounds__(256, PQ_QUANT_FWD_MINB) void k_quant_fwd(LaunchTabl
                 if constexpr ((OUTS & OUT_F32) != 0) {
                     if (act) wq32[q] = f32x4{q0, q1, q2, q3};
                 }
-                if constexpr (TILED) {
+                if constexpr (TILED && CW == 1) {
+                    // 1 bit: quad q is the low or high nibble of byte q / 2 of
+                    // the row; the even lane takes its odd neighbour's nibble
+                    // (every lane shuffles, act only gates the store).
+                    const uint32_t nib = c0 | (c1 << 1) | (c2 << 2) | (c3 << 3);
+                    const uint32_t hi = __shfl_down(nib, 1);
+                    PQ_GLOBAL uint8_t *d = tbase + static_cast<int64_t>(q >> 7) * gstride + ((q >> 1) & 63);
+                    if (act && (tl & 1) == 0) *d = static_cast<uint8_t>(nib | (hi << 4));
+                } else if constexpr (TILED) {
                     // A quad is CW / 2 code bytes, and base + u * TEAM starts a
                     // whole 64-byte group g0; the lane's byte offset from there
                     // (tl or 2 tl) splits into group and byte.
@@ -768,12 +776,12 @@ constexpr int64_t kTeamColsThreshold = 4096;
 
 bool finite(double x) { return x == x && x < 1e300 && x > -1e300; }
 
-// Widths with a deployment format: a 2-bit (ternary, 2-bit SEQ) or 4-bit (3-
-// and 4-bit LSQ) code container.
+// Widths with a deployment format: every code container (binary in 1 bit,
+// ternary, 2-bit SEQ and the 2-bit LSQ grids in 2, 3- and 4-bit LSQ in 4).
 bool deployable(int mode)
 {
-    return mode == PQ_W158_SEQ_TERNARY || mode == PQ_W2_SEQ || mode == PQ_W3_LSQ || mode == PQ_W4_LSQ ||
-           mode == PQ_W2_LSQ || mode == PQ_W158_LSQ;
+    return mode == PQ_W1_BINARY || mode == PQ_W158_SEQ_TERNARY || mode == PQ_W2_SEQ || mode == PQ_W3_LSQ ||
+           mode == PQ_W4_LSQ || mode == PQ_W2_LSQ || mode == PQ_W158_LSQ;
 }
 
 int choose_wpr(int64_t total_rows, int64_t total_elems)
@@ -866,15 +874,12 @@ void launch_fwd_outs(unsigned outs, const LaunchTable &lt, int blocks, int wpr, 
     case 6: launch_fwd_t<MODE, INIT, 6>(lt, blocks, wpr, s, nullptr); break;
     case 7: launch_fwd_t<MODE, INIT, 7>(lt, blocks, wpr, s, nullptr); break;
     default:
-        // codes in the export byte order (2- and 4-bit containers only; the
-        // host rejects other modes)
-        if constexpr (Mode<MODE>::cw != 1) {
-            switch (outs) {
-            case OUT_CODES | OUT_TILED: launch_fwd_t<MODE, INIT, 20>(lt, blocks, wpr, s, nullptr); break;
-            case OUT_BF16 | OUT_CODES | OUT_TILED: launch_fwd_t<MODE, INIT, 21>(lt, blocks, wpr, s, nullptr); break;
-            case OUT_F32 | OUT_CODES | OUT_TILED: launch_fwd_t<MODE, INIT, 22>(lt, blocks, wpr, s, nullptr); break;
-            default: launch_fwd_t<MODE, INIT, 23>(lt, blocks, wpr, s, nullptr); break;
-            }
+        // codes in the export byte order
+        switch (outs) {
+        case OUT_CODES | OUT_TILED: launch_fwd_t<MODE, INIT, 20>(lt, blocks, wpr, s, nullptr); break;
+        case OUT_BF16 | OUT_CODES | OUT_TILED: launch_fwd_t<MODE, INIT, 21>(lt, blocks, wpr, s, nullptr); break;
+        case OUT_F32 | OUT_CODES | OUT_TILED: launch_fwd_t<MODE, INIT, 22>(lt, blocks, wpr, s, nullptr); break;
+        default: launch_fwd_t<MODE, INIT, 23>(lt, blocks, wpr, s, nullptr); break;
         }
         break;
     }
@@ -1251,6 +1256,7 @@ static pq_status pack_common(int mode, int64_t rows, int64_t cols, const float *
     constexpr unsigned O = OUT_CODES | OUT_TILED | OUT_ALPHA_BF16;
     const int nb = static_cast<int>(blocks);
     switch (mode) {
+    case PQ_W1_BINARY: launch_fwd_t<PQ_W1_BINARY, false, O>(lt, nb, wpr, s, alpha_bf16); break;
     case PQ_W158_SEQ_TERNARY: launch_fwd_t<PQ_W158_SEQ_TERNARY, false, O>(lt, nb, wpr, s, alpha_bf16); break;
     case PQ_W2_SEQ: launch_fwd_t<PQ_W2_SEQ, false, O>(lt, nb, wpr, s, alpha_bf16); break;
     case PQ_W3_LSQ: launch_fwd_t<PQ_W3_LSQ, false, O>(lt, nb, wpr, s, alpha_bf16); break;

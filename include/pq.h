@@ -207,11 +207,12 @@ pq_status pq_quantize_bwd(int mode, int64_t rows, int64_t cols, const float *W,
  */
 int64_t pq_packed_bytes(int mode, int64_t rows, int64_t cols);
 
-/* Widths with a deployment format ("deployable" below): PQ_W158_SEQ_TERNARY,
- * PQ_W2_SEQ, PQ_W2_LSQ and PQ_W158_LSQ in a 2-bit container, PQ_W3_LSQ and
- * PQ_W4_LSQ in a 4-bit one
+/* Widths with a deployment format ("deployable" below): PQ_W1_BINARY in a
+ * 1-bit container (eight codes per byte), PQ_W158_SEQ_TERNARY, PQ_W2_SEQ,
+ * PQ_W2_LSQ and PQ_W158_LSQ in a 2-bit container, PQ_W3_LSQ and PQ_W4_LSQ
+ * in a 4-bit one
  * (ternary is commonly held in 2-bit integers, [News] storage paragraph).
- * pq_packed_bytes returns -1 for any other mode. */
+ * pq_packed_bytes returns -1 for a bad mode. */
 
 /*
  * pq_pack_w2 -- export a 2-bit SEQ layer for deployment: the forward's codes

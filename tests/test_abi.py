@@ -46,7 +46,9 @@ def test_helpers(pq):
     assert pq.pq_packed_bytes(pq.PQ_W2_SEQ, 20, 576) == 3 * 32 * 64
     assert pq.pq_packed_bytes(pq.PQ_W4_LSQ, 1, 8) == 16 * 64
     assert pq.pq_packed_bytes(pq.PQ_W2_SEQ, 0, 64) == 0
-    assert pq.pq_packed_bytes(pq.PQ_W1_BINARY, 16, 64) == -1
+    assert pq.pq_packed_bytes(pq.PQ_W1_BINARY, 16, 64) == 16 * 64          # 8 bytes of a row: one group
+    assert pq.pq_packed_bytes(pq.PQ_W1_BINARY, 16384, 16384) == 32 * 16384 * 64
+    assert pq.pq_packed_bytes(7, 16, 64) == -1
     assert pq.pq_packed_bytes(pq.PQ_W158_SEQ_TERNARY, 16, 1024) == 16 * 256
     assert pq.pq_packed_bytes(pq.PQ_W3_LSQ, 16, 1024) == 16 * 512
     assert pq.pq_packed_bytes(pq.PQ_W2_SEQ, 16, 12) == -1
@@ -119,14 +121,14 @@ def test_pack_and_gemm_argument_checks(pq):
     assert L.pq_w2a16_gemm(0, 8, 64, A, A, B, A, None) == 0                       # empty
     assert L.pq_w2a16_gemm(1, (1 << 24) + 16, 64, A, A, B, A, None) == 2          # N bound
     assert L.pq_pack_w2(0, 64, A, A, B, A, None) == 0                             # empty
-    assert L.pq_pack(0, 4, 64, A, A, B, A, None) == 3                             # binary: no container
-    assert L.pq_gemm(0, 4, 8, 64, A, A, B, A, None) == 3
+    assert L.pq_pack(7, 4, 64, A, A, B, A, None) == 3                             # bad mode
+    assert L.pq_gemm(7, 4, 8, 64, A, A, B, A, None) == 3
     assert L.pq_gemm(1, 4, 8, 60, A, A, B, A, None) == 2                          # ternary, K % 64
     assert L.pq_pack(3, 4, 60, A, A, B, A, None) == 2
     assert L.pq_gemm_f32a(2, 4, 8, 64, A, A, None, A, None) == 1                  # alpha NULL
-    assert L.pq_gemm_f32a(0, 4, 8, 64, A, A, B, A, None) == 3
+    assert L.pq_gemm_f32a(7, 4, 8, 64, A, A, B, A, None) == 3
     # forward with codes in the export byte order: deployable widths, codes required
-    assert L.pq_quantize_fwd(0, 4, 64, A, B, 2, None, None, A, None) == 3
+    assert L.pq_quantize_fwd(7, 4, 64, A, B, 2, None, None, A, None) == 3
     assert L.pq_quantize_fwd(2, 4, 64, A, B, 2, A, None, None, None) == 1
     assert L.pq_quantize_fwd(2, 4, 64, A, B, 4, None, None, A, None) == 3         # unknown flag
 

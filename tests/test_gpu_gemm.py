@@ -70,7 +70,7 @@ def make_case(mode, seed, M, N, K, sigma=0.02):
     return X, packed, ab
 
 
-DEPLOYABLE = [O.SEQ2, O.LSQ4, O.TERNARY, O.LSQ3, O.LSQ2, O.LSQ158]
+DEPLOYABLE = [O.SEQ2, O.LSQ4, O.TERNARY, O.LSQ3, O.LSQ2, O.LSQ158, O.BINARY]
 
 
 @pytest.mark.parametrize("mode", DEPLOYABLE)
@@ -109,6 +109,18 @@ def test_gemm_zero_and_edge_values():
     Y = gpu_gemm(O.SEQ2, X, packed, ab, N)
     check(Y, O.gemm_ref(O.SEQ2, X, packed, ab, N), "edge codes")
     assert np.allclose(Y[:, 0], -0.75 * 0.5 * K) and np.allclose(Y[:, 1], 0.75 * 0.5 * K)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 96, 1024), (2, 130, 2048), (4, 64, 512), (6, 64, 512), (8, 257, 1536),
+                                   (12, 100, 1024), (16, 4100, 2048), (3, 9000, 512)])
+def test_gemm_binary_streaming_full_compare(M, N, K):
+    """1-bit codes (eight per byte) through the streaming kernel: one, two,
+    four, eight and sixteen activation DMAs per 512-k group, one to four
+    column tiles per block; every output."""
+    print(f"[gemm binary M={M} N={N} K={K}]", flush=True)
+    X, packed, ab = make_case(O.BINARY, 17 * M + N + K, M, N, K)
+    Y = gpu_gemm(O.BINARY, X, packed, ab, N)
+    check(Y, O.gemm_ref(O.BINARY, X, packed, ab, N), f"binary {M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 64, 7680), (2, 100, 8192), (2, 1000, 16384), (1, 257, 5888),

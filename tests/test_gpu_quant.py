@@ -218,7 +218,7 @@ def gpu_pack(mode, W, alpha):
     return host(packed), host(ab)
 
 
-@pytest.mark.parametrize("mode", [O.SEQ2, O.LSQ4, O.TERNARY, O.LSQ3])
+@pytest.mark.parametrize("mode", [O.SEQ2, O.LSQ4, O.TERNARY, O.LSQ3, O.BINARY])
 def test_pack_matches_forward_codes(mode):
     # 333 rows (three padding rows in the last tile), 1600 columns (a partly
     # filled last 64-byte group at both widths)
@@ -232,7 +232,7 @@ def test_pack_matches_forward_codes(mode):
     assert_bits_equal(packed, O.tile_codes(codes_fwd), "pack == fwd codes in export order")
 
 
-@pytest.mark.parametrize("mode", [O.SEQ2, O.LSQ4, O.TERNARY, O.LSQ3, O.LSQ2, O.LSQ158])
+@pytest.mark.parametrize("mode", [O.SEQ2, O.LSQ4, O.TERNARY, O.LSQ3, O.LSQ2, O.LSQ158, O.BINARY])
 @pytest.mark.parametrize("rows,cols", [(1, 8), (17, 64), (16, 1024), (4100, 264), (4096, 520), (8192, 256)])
 def test_pack_export_order_shapes(mode, rows, cols):
     """Export byte order across the launch shapes: one row per block (fewer
@@ -380,7 +380,7 @@ def test_division_at_decision_boundaries(mode):
     check_bwd(mode, W, alphas, G, f"div-boundary bwd m{mode}")
 
 
-@pytest.mark.parametrize("mode", [O.TERNARY, O.SEQ2, O.LSQ3, O.LSQ4, O.LSQ2, O.LSQ158])
+@pytest.mark.parametrize("mode", [O.TERNARY, O.SEQ2, O.LSQ3, O.LSQ4, O.LSQ2, O.LSQ158, O.BINARY])
 @pytest.mark.parametrize("rows,cols,init", [(333, 1600, True), (4100, 264, False), (17, 64, True),
                                             (64, 16384, False)])
 def test_fwd_codes_in_export_order(mode, rows, cols, init):
