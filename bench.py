@@ -719,14 +719,15 @@ def graph_ms(torch, run, reps, check=None):
 
 
 def gemm_compare(torch, pq, W16, a16, Xs, stream, reps=30):
-    """The other widths through the same kernels (ternary in the 2-bit
-    container, 3- and 4-bit LSQ in nibbles) and a hipBLASLt bf16 GEMM on the
+    """The other widths through the same kernels (binary in 1-bit codes, ternary
+    in the 2-bit container, 3- and 4-bit LSQ in nibbles) and a hipBLASLt bf16 GEMM on the
     dequantized weight, at the same shapes: each launched back to back on 8
     rotating weight copies (the 2-bit numbers are in gemm_back_to_back)."""
     N = K = GEMM_NK
     sid = stream.cuda_stream
     res = {f"m{M}": {} for M in GEMM_MS}
-    widths = (("ternary", pq.PQ_W158_SEQ_TERNARY, 2), ("w3", pq.PQ_W3_LSQ, 4), ("w4", pq.PQ_W4_LSQ, 4))
+    widths = (("w1", pq.PQ_W1_BINARY, 1), ("ternary", pq.PQ_W158_SEQ_TERNARY, 2), ("w3", pq.PQ_W3_LSQ, 4),
+              ("w4", pq.PQ_W4_LSQ, 4))
     for name, md, cbits in widths:
         a = torch.zeros(N, dtype=torch.float32, device="cuda")
         pq.pq_quantize_fwd(md, N, K, W16, a, pq.PQ_INIT_ALPHA, None, None, None)

@@ -626,7 +626,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
         reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)lds)) + w * WLDS;
     const uint8_t *wring = lds + w * WLDS;
 
-    auto issue = [&](int it, int slot) {
+    auto issue = [&](int it, int slot) __attribute__((always_inline)) {
         const uint32_t gi = static_cast<uint32_t>(w + NW * it);
         const uint32_t sb = ring + slot * SLOT;
         const uint8_t *cb = g.packed + static_cast<int64_t>(gi) * g.gstride;
@@ -648,7 +648,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
     const int mrow = i16 < M ? i16 : M - 1;
     const int aoff = TN * 1024 + (mrow / RPL) * XQS + (mrow % RPL) * 16;
 
-    auto compute = [&](int slot) {
+    auto compute = [&](int slot) __attribute__((always_inline)) {
         const uint8_t *sp = wring + slot * SLOT;
         uint4 c[TN];
 #pragma unroll
