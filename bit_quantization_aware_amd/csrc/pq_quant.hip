@@ -263,10 +263,10 @@ __device__ __forceinline__ void store_codes(PQ_GLOBAL uint8_t *crow, int q, uint
 //
 // Forward: optional alpha init, then per quad: quantize, emit bf16 / fp32 /
 // codes.  OUT_ALPHA_BF16 (export) also writes bf16(alpha) per row.
-// (The fused level statistics hold more registers: their launches ask for
-// half the blocks per CU rather than spill.)
+// (The fused level statistics and the scale init hold more registers: their
+// launches ask for half the blocks per CU rather than spill.)
 template <int MODE, bool INIT, int WPR, unsigned OUTS>
-__global__ __launch_bounds__(256, (OUTS & OUT_STATS) ? PQ_QUANT_FWD_MINB / 2 : PQ_QUANT_FWD_MINB) void k_quant_fwd(
+__global__ __launch_bounds__(256, ((OUTS & OUT_STATS) || INIT) ? PQ_QUANT_FWD_MINB / 2 : PQ_QUANT_FWD_MINB) void k_quant_fwd(
     LaunchTable lt, void *alpha_bf16_single,
                                                                       StatsOut so)
 {
