@@ -4,21 +4,24 @@
 One step = one pass of the whole path over synthetic inputs already resident
 in HBM:
   1. forward fake-quantization (2-bit SEQ, given alpha) of the whole
-     MobileLLM-125M-shaped stack -- 210 matrices, 119,439,360 weights -- in
-     one grouped launch (bf16 weights + packed codes out);
+     MobileLLM-1.5B-shaped stack -- 378 matrices, 1,473,638,400 weights with
+     0.1 % outliers -- in one grouped launch (bf16 weights + packed codes out);
   2. the straight-through backward of the same stack (dW + per-row dalpha)
      in one grouped launch;
-  3. export packing (2-bit codes + bf16 alpha) of one 16384 x 16384 weight;
-  4. the W2A16 GEMM on that packed weight at M = 1, 4, 16, 64, 512, each on
-     its own copy of the packed weight (8 copies rotate, so the 256 MB MALL
-     cannot serve repeats).
-Alpha initialisation (once per run) and the per-bit-width sweep of the stack,
-the 4-bit GEMM variant and a hipBLASLt bf16 GEMM are timed after the steps.
+  3. the packed export of the same stack (2-bit codes in the export byte
+     order + bf16 alpha) in one grouped launch;
+  4. the W2A16 GEMM on one 16384 x 16384 packed weight at M = 512, 64, 16, 4,
+     1, each on its own copy of the weight (8 copies rotate, so the 256 MB
+     MALL cannot serve repeats), each with its caller-owned workspace.
+Alpha initialisation (once per run), the MobileLLM-125M stack at every bit
+width, the Llama-3-8B projections' quantizer and GEMM, the 4-bit GEMM
+variant and a hipBLASLt bf16 GEMM are timed after the steps.
 
 Every kernel is timed with HIP events on the stream it is launched on (torch's
 current stream).  `value` is the headline metric: quantize fwd+bwd throughput
-in GB/s of algorithmic bytes on the stack.  The CPU baseline is the oracle
-(test infrastructure) on the same stack, timed on the host cores.
+in GB/s of algorithmic bytes on the 1.5B stack.  The CPU baseline is the
+oracle (test infrastructure) on a sample of the same stack and on sampled
+GEMM outputs, timed on the host cores.
 """
 import argparse
 import hashlib
@@ -74,6 +77,9 @@ def parse():
                    help="turn the two --pmc-workload counter runs into the traffic table")
     p.add_argument("--pmc-out", default=os.path.join(ROOT, "profiles", "hbm_traffic_bench_kernels.md"))
     p.add_argument("--pmc-command", default="", help="command lines recorded in the traffic table")
+    p.add_argument("--mfma-summarize", metavar="PMC_DIR",
+                   help="turn a --pmc-workload counter run of the MFMA counters into the MFMA table")
+    p.add_argument("--mfma-out", default=os.path.join(ROOT, "profiles", "mfma_util_gemm_kernels.md"))
     return p.parse_args()
 
 
@@ -112,6 +118,26 @@ def recorded_traffic(path):
             try:
                 if cells[1] == source_sha(cells[0]):
                     out[cells[0]] = int(float(cells[5]))
+            except (ValueError, OSError):
+                pass
+    return out
+
+
+def recorded_mfma(path):
+    """gemm kernel -> MFMA utilisation (fraction of the MFMA pipes' cycles
+    busy over the launch), from the MFMA counter table, for kernels whose
+    sources still match the recorded hash."""
+    out = {}
+    try:
+        lines = open(path).read().splitlines()
+    except OSError:
+        return out
+    for ln in lines:
+        cells = [c.strip() for c in ln.strip().strip("|").split("|")]
+        if len(cells) >= 4 and cells[0] in KERNEL_SOURCES:
+            try:
+                if cells[1] == source_sha(cells[0]):
+                    out[cells[0]] = float(cells[2])
             except (ValueError, OSError):
                 pass
     return out
@@ -228,10 +254,59 @@ def pmc_summarize(args):
     print("\n".join(lines))
 
 
+C3 = "mobilellm_1p5b"
+C2 = "mobilellm_125m"
+
+
+def _gen(cfg, k):
+    from bit_quantization_aware_amd import synth
+    return synth.weight(cfg, k), synth.upstream_grad(cfg, k)
+
+
+def build_stack(torch, pq, cfg, mode, dev, export=False):
+    """Upload a stacked config's W and G (generated on the host, matrix by
+    matrix from its own seed stream, 16 threads) and allocate every output of
+    the fwd, bwd (and export) launches.  Returns (mats, fwd, bwd, exp) with
+    the grouped descriptor tables."""
+    from concurrent.futures import ThreadPoolExecutor
+    from bit_quantization_aware_amd import synth
+
+    shapes = synth.SHAPES[cfg]()
+    n = len(shapes)
+    mats = []
+    with ThreadPoolExecutor(16) as ex:
+        for c0 in range(0, n, 32):
+            ks = range(c0, min(n, c0 + 32))
+            for W, G in ex.map(lambda k: _gen(cfg, k), ks):
+                r, c = W.shape
+                m = dict(W=torch.from_numpy(W).to(dev), G=torch.from_numpy(G).to(dev), rows=r, cols=c,
+                         alpha=torch.zeros(r, dtype=torch.float32, device=dev),
+                         wq_bf16=torch.empty(r, c, dtype=torch.bfloat16, device=dev),
+                         codes=torch.empty(r, pq.pq_code_row_bytes(mode, c), dtype=torch.uint8, device=dev),
+                         dW=torch.empty(r, c, dtype=torch.float32, device=dev),
+                         dalpha=torch.empty(r, dtype=torch.float32, device=dev),
+                         grad_scale=pq.pq_default_grad_scale(mode, r, c))
+                if export:
+                    m["packed"] = torch.empty(pq.pq_packed_bytes(mode, r, c), dtype=torch.uint8, device=dev)
+                    m["alpha_bf16"] = torch.empty(r, dtype=torch.bfloat16, device=dev)
+                mats.append(m)
+    ft = pq.MatTable([{k: m[k] for k in ("W", "alpha", "wq_bf16", "codes", "rows", "cols")} for m in mats])
+    bt = pq.MatTable([{k: m[k] for k in ("W", "alpha", "G", "dW", "dalpha", "grad_scale", "rows", "cols")}
+                      for m in mats])
+    et = None
+    if export:
+        et = pq.MatTable([dict(W=m["W"], alpha=m["alpha"], codes=m["packed"], alpha_bf16=m["alpha_bf16"],
+                               rows=m["rows"], cols=m["cols"]) for m in mats])
+    return mats, ft, bt, et
+
+
 def main():
     args = parse()
     if args.pmc_summarize:
         pmc_summarize(args)
+        return
+    if args.mfma_summarize:
+        mfma_summarize(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the quantizer shards "
@@ -245,34 +320,25 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs an MI355X"
     dev = "cuda"
     stream = torch.cuda.current_stream()
+    sid = stream.cuda_stream
+    mode = pq.PQ_W2_SEQ
+    cw = pq.CODE_BITS[mode]
 
     # ------------------------------------------------------------------ inputs
-    shapes = synth.mobilellm_125m_shapes()
-    mode = pq.PQ_W2_SEQ
-    stack = []
-    for k, (_, _, rows, cols) in enumerate(shapes):
-        W = torch.from_numpy(synth.weight("mobilellm_125m", k)).to(dev)
-        G = torch.from_numpy(synth.upstream_grad("mobilellm_125m", k)).to(dev)
-        stack.append(dict(W=W, G=G, rows=rows, cols=cols))
-    n_el = sum(m["rows"] * m["cols"] for m in stack)
-    n_rows = sum(m["rows"] for m in stack)
+    # the 125M stack: extras (bit-width sweep, fused step, training forward)
+    stack, ftab, btab, _ = build_stack(torch, pq, C2, mode, dev)
 
     def make_tables(md):
         for m in stack:
             r, c = m["rows"], m["cols"]
             m["alpha"] = torch.zeros(r, dtype=torch.float32, device=dev)
-            m["wq_bf16"] = torch.empty(r, c, dtype=torch.bfloat16, device=dev)
             m["codes"] = torch.empty(r, pq.pq_code_row_bytes(md, c), dtype=torch.uint8, device=dev)
-            m["dW"] = torch.empty(r, c, dtype=torch.float32, device=dev)
-            m["dalpha"] = torch.empty(r, dtype=torch.float32, device=dev)
             m["grad_scale"] = pq.pq_default_grad_scale(md, r, c)
         ft = pq.MatTable([{k: m[k] for k in ("W", "alpha", "wq_bf16", "codes", "rows", "cols")}
                           for m in stack])
         bt = pq.MatTable([{k: m[k] for k in ("W", "alpha", "G", "dW", "dalpha", "grad_scale",
                                             "rows", "cols")} for m in stack])
         return ft, bt
-
-    ftab, btab = make_tables(mode)
 
     W16 = torch.from_numpy(synth.weight("square16k", 0)).to(dev)
     a16 = torch.zeros(GEMM_NK, dtype=torch.float32, device=dev)
@@ -285,17 +351,11 @@ def main():
     Xs = {M: torch.from_numpy(synth.activations("square16k", 0, M, GEMM_NK).view(np.int16)).to(dev)
           .view(torch.bfloat16) for M in GEMM_MS}
     Ys = {M: torch.empty(M, GEMM_NK, dtype=torch.bfloat16, device=dev) for M in GEMM_MS}
+    # caller-owned GEMM workspaces, one per M (the library allocates nothing)
+    wss = {M: pq.gemm_workspace(mode, M, GEMM_NK, GEMM_NK) for M in GEMM_MS}
+    wsa = {M: ((w.data_ptr(), w.numel()) if w is not None else (0, 0)) for M, w in wss.items()}
 
-    # alpha init of the stack (once per run), timed once after a warm launch
     pq.pq_quantize_fwd_grouped(mode, ftab, pq.PQ_INIT_ALPHA)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    pq.pq_quantize_fwd_grouped(mode, ftab, pq.PQ_INIT_ALPHA)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    init_ms = e0.elapsed_time(e1)
-
     kernels = ["fwd", "bwd", "pack"] + [f"gemm_m{M}" for M in GEMM_STEP_ORDER]
 
     if args.train_fwd_only:
@@ -312,9 +372,29 @@ def main():
 
     if args.gemm_b2b_only:
         ridge = MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3
-        print(json.dumps({"gemm_back_to_back": gemm_back_to_back(torch, pq, Xs, packed, ab16, Ys, stream, ridge)}),
-              flush=True)
+        print(json.dumps({"gemm_back_to_back": gemm_back_to_back(torch, pq, Xs, packed, ab16, Ys, wsa, stream,
+                                                                 ridge)}), flush=True)
         return
+
+    # the 1.5B stack: the step's quantizer work
+    t_up = time.perf_counter()
+    big, ftab3, btab3, etab3 = build_stack(torch, pq, C3, mode, dev, export=True)
+    torch.cuda.synchronize()
+    upload_s = time.perf_counter() - t_up
+    n_el = sum(m["rows"] * m["cols"] for m in big)
+    n_rows = sum(m["rows"] for m in big)
+    print(f"bench: 1.5B stack resident ({len(big)} matrices, {n_el} weights, {upload_s:.1f} s)",
+          file=sys.stderr, flush=True)
+
+    # alpha init of the stack (once per run), timed once after a warm launch
+    pq.pq_quantize_fwd_grouped(mode, ftab3, pq.PQ_INIT_ALPHA)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    pq.pq_quantize_fwd_grouped(mode, ftab3, pq.PQ_INIT_ALPHA)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    init_ms = e0.elapsed_time(e1)
 
     if args.pmc_workload:
         src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).uniform_()
@@ -324,13 +404,14 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         launches = {
-            "fwd": lambda: pq.pq_quantize_fwd_grouped(mode, ftab, 0),
-            "bwd": lambda: pq.pq_quantize_bwd_grouped(mode, btab, pq.PQ_G_F32),
-            "pack": lambda: pq.pq_pack_w2(GEMM_NK, GEMM_NK, W16, a16, packed[0], ab16[0]),
+            "fwd": lambda: pq.pq_quantize_fwd_grouped(mode, ftab3, 0),
+            "bwd": lambda: pq.pq_quantize_bwd_grouped(mode, btab3, pq.PQ_G_F32),
+            "pack": lambda: pq.pq_pack_grouped(mode, etab3),
         }
         for j, M in enumerate(GEMM_MS):
             launches[f"gemm_m{M}"] = (lambda M=M, j=j: pq.pq_w2a16_gemm(
-                M, GEMM_NK, GEMM_NK, Xs[M], packed[1 + j % (ROTATE - 1)], ab16[1 + j % (ROTATE - 1)], Ys[M]))
+                M, GEMM_NK, GEMM_NK, Xs[M], packed[1 + j % (ROTATE - 1)], ab16[1 + j % (ROTATE - 1)], Ys[M],
+                workspace=wsa[M]))
         for k in kernels:
             for _ in range(3):
                 launches[k]()
@@ -342,16 +423,15 @@ def main():
 
     def step(it, evs):
         evs[0].record(stream)
-        pq.pq_quantize_fwd_grouped(mode, ftab, 0)
+        pq.pq_quantize_fwd_grouped(mode, ftab3, 0)
         evs[1].record(stream)
-        pq.pq_quantize_bwd_grouped(mode, btab, pq.PQ_G_F32)
+        pq.pq_quantize_bwd_grouped(mode, btab3, pq.PQ_G_F32)
         evs[2].record(stream)
-        r = it % ROTATE
-        pq.pq_pack_w2(GEMM_NK, GEMM_NK, W16, a16, packed[r], ab16[r])
+        pq.pq_pack_grouped(mode, etab3)
         evs[3].record(stream)
         for j, M in enumerate(GEMM_STEP_ORDER):
             b = (it + 1 + j) % ROTATE
-            pq.pq_w2a16_gemm(M, GEMM_NK, GEMM_NK, Xs[M], packed[b], ab16[b], Ys[M])
+            pq.pq_w2a16_gemm(M, GEMM_NK, GEMM_NK, Xs[M], packed[b], ab16[b], Ys[M], workspace=wsa[M])
             evs[4 + j].record(stream)
 
     nev = 4 + len(GEMM_STEP_ORDER)
@@ -376,10 +456,9 @@ def main():
     avg = {k: float(np.mean(v)) for k, v in per.items()}
     ms_per_step = float(np.mean(step_ms))
 
-    cw = pq.CODE_BITS[mode]
-    fb = sum(fwd_bytes(m["rows"], m["cols"], cw) for m in stack)
-    bb = sum(bwd_bytes(m["rows"], m["cols"]) for m in stack)
-    pb = pack_bytes(GEMM_NK, GEMM_NK)
+    fb = sum(fwd_bytes(m["rows"], m["cols"], cw) for m in big)
+    bb = sum(bwd_bytes(m["rows"], m["cols"]) for m in big)
+    pb = sum(pack_bytes(m["rows"], m["cols"]) for m in big)
     info = {
         "fwd": dict(bound="hbm", bytes=fb, ms=avg["fwd"]),
         "bwd": dict(bound="hbm", bytes=bb, ms=avg["bwd"]),
@@ -393,22 +472,22 @@ def main():
                                   ms=avg[f"gemm_m{M}"])
     rl = {}
     for k, d in info.items():
-        s = d["ms"] * 1e-3
+        sec = d["ms"] * 1e-3
         if d["bound"] == "hbm":
-            ach = d["bytes"] / s / 1e9
+            ach = d["bytes"] / sec / 1e9
             rl[k] = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                          frac=round(ach / HBM_PEAK_GBS, 4), ms=round(d["ms"], 5))
         else:
-            ach = d["flops"] / s / 1e12
+            ach = d["flops"] / sec / 1e12
             rl[k] = dict(bound="mfma", achieved=round(ach, 1), peak=MFMA_BF16_PEAK_TFLOPS,
                          unit="TFLOP/s", frac=round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
                          ms=round(d["ms"], 5))
         if k.startswith("gemm"):
-            rl[k]["weight_stream_GBs"] = round(d["bytes"] / s / 1e9, 1)
-            rl[k]["tflops"] = round(d["flops"] / s / 1e12, 2)
+            rl[k]["weight_stream_GBs"] = round(d["bytes"] / sec / 1e9, 1)
+            rl[k]["tflops"] = round(d["flops"] / sec / 1e12, 2)
     dominant = max(info, key=lambda k: info[k]["ms"])
-    per_launch_units = {"fwd": f"{n_el} weights", "bwd": f"{n_el} weights",
-                        "pack": f"{GEMM_NK * GEMM_NK} weights"}
+    per_launch_units = {"fwd": f"{n_el} weights (378 matrices)", "bwd": f"{n_el} weights (378 matrices)",
+                        "pack": f"{n_el} weights (378 matrices)"}
     roofline = dict(rl[dominant])
     roofline.pop("ms", None)
     roofline["kernel"] = dominant
@@ -418,9 +497,15 @@ def main():
         rl[k]["traffic"] = traffic.get(k)
     step_traffic = traffic.get("qat_step")
     roofline["units_per_launch"] = per_launch_units.get(dominant, "one GEMM call")
+    roofline["bytes_per_unit"] = {"fwd": 4 + 2 + cw / 8, "bwd": 12, "pack": 4.25}.get(dominant)
+    mfma = recorded_mfma(args.mfma_out)
+    for k in rl:
+        if k in mfma:
+            rl[k]["mfma_util"] = mfma[k]
 
     qt_ms = avg["fwd"] + avg["bwd"]
     value = (fb + bb) / (qt_ms * 1e-3) / 1e9
+    init_bytes = fb + 4 * n_rows   # the forward's bytes (alpha written besides)
 
     out = {
         "metric": "quantize fwd+bwd GB/s (% HBM peak); W2A16 GEMM TFLOP/s at 16384² (% roofline)",
@@ -436,31 +521,38 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": "MobileLLM-125M-shaped stack (30 layers x q,k,v,o 576x576, gate,up "
-                        "1536x576, down 576x1536; 210 matrices, 119,439,360 fp32 weights "
-                        "~N(0,0.02^2)), 2-bit SEQ fwd+bwd in one grouped launch each; plus "
-                        "16384x16384 2-bit export and W2A16 GEMM at M in {1,4,16,64,512}",
-            "bits": 2, "matrices": len(stack), "weights": n_el, "rows": n_rows,
+            "workload": "MobileLLM-1.5B-shaped stack (54 layers x q,o 1600x1600, k,v 400x1600, gate,up "
+                        "4352x1600, down 1600x4352; 378 matrices, 1,473,638,400 fp32 weights ~N(0,0.02^2) "
+                        "with 0.1% outliers x10), 2-bit SEQ fwd+bwd and packed export in one grouped "
+                        "launch each; plus the 16384x16384 2-bit W2A16 GEMM at M in {1,4,16,64,512}",
+            "bits": 2, "matrices": len(big), "weights": n_el, "rows": n_rows,
             "gemm_nk": GEMM_NK, "gemm_m": list(GEMM_MS), "parallelism": "single GPU"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": roofline,
         "kernels": rl,
-        "alpha_init_ms": round(init_ms, 4),
+        "alpha_init": dict(ms=round(init_ms, 4), fwd_GBs=round(init_bytes / init_ms / 1e6, 1),
+                           frac_of_fwd_bytes=round(init_bytes / init_ms / 1e6 / HBM_PEAK_GBS, 4)),
         "wall_s_timed": round(wall, 3),
+        "upload_s": round(upload_s, 2),
     }
+    del big, ftab3, btab3, etab3
+    torch.cuda.empty_cache()
 
     if not args.no_extras:
         out["diagnostics"] = diagnostics_measure(torch, pq, W16, a16, stream)
         out["train_forward"] = train_forward_measure(torch, pq, stack, stream)
         out["qat_step"] = qat_step_measure(torch, pq, stack, ftab, btab, stream)
         out["qat_step"]["traffic"] = step_traffic
-        out["gemm_back_to_back"] = gemm_back_to_back(torch, pq, Xs, packed, ab16, Ys, stream, ridge)
-        out["sweep_bits"] = sweep_bits(torch, pq, stack, make_tables, stream)
+        out["gemm_back_to_back"] = gemm_back_to_back(torch, pq, Xs, packed, ab16, Ys, wsa, stream, ridge)
+        # (the sweep re-allocates the 125M stack's alpha and codes: it runs
+        # after every measurement that uses the first tables)
+        out["mobilellm_125m"] = sweep_bits(torch, pq, stack, make_tables, stream)
+        out["llama3_8b_quantizer"] = llama_quantizer_measure(torch, pq, synth, stream)
         out["gemm_compare"] = gemm_compare(torch, pq, W16, a16, Xs, stream)
         out["llama_gemm"] = llama_gemm_measure(torch, pq, synth, stream)
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(shapes, fb + bb)
+        out["cpu_baseline"] = cpu_baseline()
 
     print(json.dumps(out), flush=True)
 
@@ -545,13 +637,19 @@ def train_forward_measure(torch, pq, stack, stream, reps=3):
             for m in stack]
     ctab = pq.MatTable([{k: d[k] for k in ("W", "alpha", "codes", "rows", "cols")} for d in mats])
     btab = pq.MatTable([{k: m[k] for k in ("W", "alpha", "wq_bf16", "rows", "cols")} for m in stack])
+    wss = {}
+    for m in stack:
+        key = (m["rows"], m["cols"])
+        if key not in wss:
+            wss[key] = pq.gemm_workspace(mode, T, m["rows"], m["cols"])
+    wsa = {k: ((w.data_ptr(), w.numel()) if w is not None else (0, 0)) for k, w in wss.items()}
     calls = [(m["rows"], m["cols"], xs[m["cols"]].data_ptr(), d["codes"].data_ptr(), m["alpha"].data_ptr(),
-              ys[m["rows"]].data_ptr()) for m, d in zip(stack, mats)]
+              ys[m["rows"]].data_ptr(), wsa[(m["rows"], m["cols"])]) for m, d in zip(stack, mats)]
 
     def codes_path():
         pq.pq_quantize_fwd_grouped(mode, ctab, pq.PQ_CODES_EXPORT)
-        for r, c, xp, cp, ap, yp in calls:
-            pq.pq_gemm_f32a(mode, T, r, c, xp, cp, ap, yp, sid)
+        for r, c, xp, cp, ap, yp, wa in calls:
+            pq.pq_gemm_f32a(mode, T, r, c, xp, cp, ap, yp, sid, workspace=wa)
 
     def bf16_path():
         pq.pq_quantize_fwd_grouped(mode, btab, 0)
@@ -616,7 +714,7 @@ def qat_step_measure(torch, pq, stack, ftab, btab, stream, reps=10):
                 speedup_vs_unfused=round((bwd + adam + fwd) / fused, 3))
 
 
-def gemm_back_to_back(torch, pq, Xs, packed, ab16, Ys, stream, ridge, reps=40):
+def gemm_back_to_back(torch, pq, Xs, packed, ab16, Ys, wsa, stream, ridge, reps=40):
     """Each GEMM of the step launched `reps` times in a row on the rotating
     weight copies, with one event pair around the run: the kernel's rate
     without the event packets and the other kernels of the step in between
@@ -632,7 +730,7 @@ def gemm_back_to_back(torch, pq, Xs, packed, ab16, Ys, stream, ridge, reps=40):
             # plain integers: the host side of a launch stays well below the
             # kernel time, so the GPU never waits for the next launch
             b = i % ROTATE
-            pq.pq_w2a16_gemm(M, GEMM_NK, GEMM_NK, xp, pk[b], ab[b], yp, sid)
+            pq.pq_w2a16_gemm(M, GEMM_NK, GEMM_NK, xp, pk[b], ab[b], yp, sid, workspace=wsa[M])
         for i in range(8):
             run(i)
         torch.cuda.synchronize()
@@ -692,8 +790,7 @@ def graph_ms(torch, run, reps, check=None):
     host's per-call cost between them.  run(i, sid) launches call i on the
     stream `sid`; `check`, if given, returns the output, which must be the
     same after the replay as after an eager call."""
-    # warm launches and capture on one stream: the library keys its
-    # workspace by stream, so nothing is allocated while capturing
+    # warm launches, then capture on a side stream
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -740,8 +837,10 @@ def gemm_compare(torch, pq, W16, a16, Xs, stream, reps=30):
             xp = Xs[M].data_ptr()
             Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
             yp = Y.data_ptr()
+            ws = pq.gemm_workspace(md, M, N, K)
+            wa = (ws.data_ptr(), ws.numel()) if ws is not None else (0, 0)
             ms = b2b_ms(torch, stream, lambda i: pq.pq_gemm(md, M, N, K, xp, pkp[i % ROTATE], abp[i % ROTATE], yp,
-                                                              sid), reps)
+                                                              sid, workspace=wa), reps)
             fl = 2.0 * M * N * K
             res[f"m{M}"].update({f"{name}_ms": round(ms, 5), f"{name}_tflops": round(fl / ms / 1e9, 2),
                                  f"{name}_weight_GBs": round(gemm_bytes(M, N, K, cbits) / ms / 1e6, 1)})
@@ -793,7 +892,10 @@ def llama_gemm_measure(torch, pq, synth, stream, reps=20):
                 .view(torch.bfloat16)
             Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
             xp, yp = X.data_ptr(), Y.data_ptr()
-            ms = graph_ms(torch, lambda i, sd: pq.pq_w2a16_gemm(M, N, K, xp, pkp[i % R], abp[i % R], yp, sd),
+            ws = pq.gemm_workspace(pq.PQ_W2_SEQ, M, N, K)
+            wa = (ws.data_ptr(), ws.numel()) if ws is not None else (0, 0)
+            ms = graph_ms(torch, lambda i, sd: pq.pq_w2a16_gemm(M, N, K, xp, pkp[i % R], abp[i % R], yp, sd,
+                                                                workspace=wa),
                           reps, check=lambda: Y)
             tb = graph_ms(torch, lambda i, sd: torch.matmul(X, wb[i % Rb].t(), out=Y), reps)
             fl, by = 2.0 * M * N * K, gemm_bytes(M, N, K, 2)
@@ -807,40 +909,105 @@ def llama_gemm_measure(torch, pq, synth, stream, reps=20):
     return res
 
 
-def cpu_baseline(shapes, alg_bytes, min_seconds=10.0, max_passes=400):
-    """The oracle (plain C, OpenMP over rows) on the same 2-bit stack: whole
-    forward + backward passes over all 210 matrices, repeated until about
-    ten seconds of CPU work have been timed."""
+def llama_quantizer_measure(torch, pq, synth, stream, reps=10):
+    """The Llama-3-8B projections' quantizer: 2-bit SEQ and ternary forward
+    (bf16 weights + codes, given alpha) and backward (dW + dalpha), one
+    matrix per launch, back to back; GB/s of algorithmic bytes and the
+    fraction of HBM peak."""
+    res = {}
+    for k, (_, name, N, K) in enumerate(synth.llama3_8b_shapes()):
+        W = torch.from_numpy(synth.weight("llama3_8b", k)).to("cuda")
+        G = torch.from_numpy(synth.upstream_grad("llama3_8b", k)).to("cuda")
+        wq = torch.empty(N, K, dtype=torch.bfloat16, device="cuda")
+        dW = torch.empty_like(W)
+        da = torch.empty(N, dtype=torch.float32, device="cuda")
+        for md, tag in ((pq.PQ_W2_SEQ, "w2_seq"), (pq.PQ_W158_SEQ_TERNARY, "ternary")):
+            a = torch.zeros(N, dtype=torch.float32, device="cuda")
+            codes = torch.empty(N, pq.pq_code_row_bytes(md, K), dtype=torch.uint8, device="cuda")
+            pq.pq_quantize_fwd(md, N, K, W, a, pq.PQ_INIT_ALPHA, None, None, None)
+            gs = pq.pq_default_grad_scale(md, N, K)
+            f = b2b_ms(torch, stream, lambda i: pq.pq_quantize_fwd(md, N, K, W, a, 0, wq, None, codes), reps)
+            b = b2b_ms(torch, stream, lambda i: pq.pq_quantize_bwd(md, N, K, W, a, G, pq.PQ_G_F32, gs, dW, da),
+                       reps)
+            fb, bb = fwd_bytes(N, K, pq.CODE_BITS[md]), bwd_bytes(N, K)
+            gbs = (fb + bb) / ((f + b) * 1e-3) / 1e9
+            res[f"{name}_{tag}"] = dict(fwd_ms=round(f, 4), bwd_ms=round(b, 4), fwd_GBs=round(fb / f / 1e6, 1),
+                                        bwd_GBs=round(bb / b / 1e6, 1), fwdbwd_GBs=round(gbs, 1),
+                                        frac=round(gbs / HBM_PEAK_GBS, 4))
+        del W, G, wq, dW
+        torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(reps=5, gemm_samples=4096):
+    """The oracle (plain C, OpenMP over rows) on a bounded sample of the
+    step's workload, on the host cores of this run:
+      * quantizer: 2-bit SEQ forward + backward over layers 0 and 1 of the
+        1.5B stack (14 matrices, 54,579,200 weights), the median of `reps`
+        whole passes at 1 thread and at every core;
+      * GEMM: the binary64 reference (the parity oracle) on `gemm_samples`
+        sampled outputs of the 16384^2 2-bit GEMM at each M, every core,
+        scaled to the whole call's flops."""
     import oracle as O
     from bit_quantization_aware_amd import synth
 
     cores = len(os.sched_getaffinity(0))
-    O.set_threads(cores)
+    shapes = synth.mobilellm_1p5b_shapes()
+    ks = [k for k, (l, _, _, _) in enumerate(shapes) if l in (0, 1)]
     data = []
-    for k in range(len(shapes)):
-        W = synth.weight("mobilellm_125m", k)
-        G = synth.upstream_grad("mobilellm_125m", k)
+    for k in ks:
+        W, G = _gen(C3, k)
         data.append((W, G, O.alpha_init(O.SEQ2, W)))
-    t, passes = 0.0, 0
-    while t < min_seconds and passes < max_passes:
-        for W, G, alpha in data:
-            t0 = time.perf_counter()
-            O.quantize_fwd(O.SEQ2, W, alpha)
-            O.quantize_bwd(O.SEQ2, W, alpha, G)
-            t += time.perf_counter() - t0
-        passes += 1
+    n_el = sum(W.size for W, _, _ in data)
+    alg = sum(fwd_bytes(W.shape[0], W.shape[1], 2) + bwd_bytes(W.shape[0], W.shape[1]) for W, _, _ in data)
+
+    def one_pass():
+        t0 = time.perf_counter()
+        for W, G, a in data:
+            O.quantize_fwd(O.SEQ2, W, a)
+            O.quantize_bwd(O.SEQ2, W, a, G)
+        return time.perf_counter() - t0
+
+    legs = {}
+    for name, th in (("one_thread", 1), ("all_cores", cores)):
+        O.set_threads(th)
+        ts = [one_pass() for _ in range(reps)]
+        med = float(np.median(ts))
+        legs[name] = dict(threads=O.max_threads(), median_s=round(med, 4), passes=reps,
+                          GBs=round(alg / med / 1e9, 3), weights_per_s=round(n_el / med, 1))
+
+    O.set_threads(cores)
+    W = synth.weight("square16k", 0)
+    a = O.alpha_init(O.SEQ2, W)
+    p, ab = O.pack(O.SEQ2, W, a)
+    del W
+    gemm = {}
+    for M in GEMM_MS:
+        X = synth.activations("square16k", 0, M, GEMM_NK)
+        rng = np.random.default_rng(M)
+        ms, ns = rng.integers(0, M, gemm_samples), rng.integers(0, GEMM_NK, gemm_samples)
+        t0 = time.perf_counter()
+        O.gemm_ref_at(O.SEQ2, X, p, ab, GEMM_NK, ms, ns)
+        dt = time.perf_counter() - t0
+        fl = 2.0 * gemm_samples * GEMM_NK
+        full = 2.0 * M * GEMM_NK * GEMM_NK
+        gemm[f"m{M}"] = dict(sampled_outputs=gemm_samples, seconds=round(dt, 4), gflops=round(fl / dt / 1e9, 3),
+                             full_call_s_est=round(dt * full / fl, 2))
     cpu = ""
     try:
         with open("/proc/cpuinfo") as f:
             cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
     except OSError:
         pass
-    return {"value": round(passes * alg_bytes / t / 1e9, 3), "unit": "GB/s", "cores": O.max_threads(),
-            "kind": "oracle", "seconds": round(t, 3), "passes": passes, "cpu": cpu,
-            "sample": f"{passes} whole 2-bit SEQ forward + backward passes over the 210 matrices of "
-                      "the MobileLLM-125M stack (the GPU workload of steps 1-2, same algorithmic "
-                      "bytes per pass); the oracle also writes fp32 values and mask bits the GPU "
-                      "step does not"}
+    return {"value": legs["all_cores"]["GBs"], "unit": "GB/s", "cores": legs["all_cores"]["threads"],
+            "kind": "oracle", "cpu": cpu, "one_thread": legs["one_thread"], "all_cores": legs["all_cores"],
+            "gemm_fp64_reference": gemm,
+            "sample": f"2-bit SEQ forward + backward over layers 0-1 of the MobileLLM-1.5B stack "
+                      f"({len(data)} matrices, {n_el} weights; same algorithmic bytes per weight as the "
+                      f"GPU step), median of {reps} whole passes at 1 thread and at {cores} threads; the "
+                      "oracle also writes fp32 values and mask bits the GPU step does not.  GEMM: the "
+                      f"binary64 reference on {gemm_samples} sampled outputs of the 16384^2 call per M, "
+                      "scaled to the call's flops"}
 
 
 if __name__ == "__main__":

@@ -33,10 +33,7 @@
 #include <stdint.h>
 
 #include <algorithm>
-#include <map>
-#include <mutex>
 #include <type_traits>
-#include <utility>
 
 #include "pq_common.hpp"
 #include "pq_gemm_common.hpp"
@@ -856,37 +853,6 @@ void launch_stream(const GemmArgs &a, hipStream_t s)
     launch_stream_tn<BITS, XI, StreamCfg<BITS, XI>::TN>(a, s);
 }
 
-// Split-K workspace: one fp32 buffer per (device, stream), grown on demand.
-// Growing waits for the stream, so a buffer in use is never freed early.
-struct Workspace {
-    void *ptr = nullptr;
-    size_t bytes = 0;
-};
-
-pq_status workspace(hipStream_t stream, size_t bytes, float **out)
-{
-    static std::mutex mu;
-    static std::map<std::pair<int, hipStream_t>, Workspace> cache;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return PQ_ERR_HIP;
-    std::lock_guard<std::mutex> lock(mu);
-    Workspace &w = cache[{dev, stream}];
-    if (w.bytes < bytes) {
-        if (w.ptr) {
-            if (hipStreamSynchronize(stream) != hipSuccess || hipFree(w.ptr) != hipSuccess) return PQ_ERR_HIP;
-            w.ptr = nullptr;
-            w.bytes = 0;
-        }
-        if (hipMalloc(&w.ptr, bytes) != hipSuccess) {
-            w.ptr = nullptr;
-            return PQ_ERR_HIP;
-        }
-        w.bytes = bytes;
-    }
-    *out = static_cast<float *>(w.ptr);
-    return PQ_OK;
-}
-
 constexpr int kNumCU = 256;  // MI355X / MI350X compute units
 
 // Sum of each activation row (bf16 -> binary32) for the large-M kernel's
@@ -932,21 +898,32 @@ double tile_cost(int64_t tiles, int stages, int splits, int64_t M, int64_t N)
     return t;
 }
 
+// How a GEMM of one shape runs, and the workspace it needs: the plan is a
+// pure function of (width, M, N, K), so the size query and the launch agree.
+struct GemmPlan {
+    enum Path { STREAM, TILE, BIG } path = STREAM;
+    int splits = 1;      // TILE: K splits
+    int sps = 0;         // TILE: stages per split (whole 64-byte groups)
+    int64_t ws = 0;      // workspace bytes (0: none)
+};
+
+constexpr int64_t kWsAlign = 256;  // workspace pieces start on 256-byte boundaries
+
 // Tiled path: the K split of least estimated time, each split keeping at
 // least PQ_TILE_MIN_STAGES stages.
 template <int BITS>
-pq_status launch_tile(const GemmArgs &a, hipStream_t s)
+void plan_tile(int64_t M, int64_t N, int64_t K, GemmPlan &p)
 {
     constexpr int kMinStages = PQ_TILE_MIN_STAGES;
-    const int mtiles = (a.M + kTileM - 1) / kTileM;
     using C = TileCfg<BITS, PQ_TILE_WN>;
-    const int ntiles = (a.N + C::TN - 1) / C::TN;
-    const int64_t tiles = static_cast<int64_t>(mtiles) * ntiles;
-    const int stages = a.K / kStageK;
+    const int64_t mtiles = (M + kTileM - 1) / kTileM;
+    const int64_t ntiles = (N + C::TN - 1) / C::TN;
+    const int64_t tiles = mtiles * ntiles;
+    const int stages = static_cast<int>(K / kStageK);
     int splits = 1;
-    double best = tile_cost(tiles, stages, 1, a.M, a.N);
+    double best = tile_cost(tiles, stages, 1, M, N);
     for (int sp = 2; sp <= std::min(64, stages / kMinStages); ++sp) {
-        const double c = tile_cost(tiles, stages, sp, a.M, a.N);
+        const double c = tile_cost(tiles, stages, sp, M, N);
         if (c < best) {
             best = c;
             splits = sp;
@@ -955,24 +932,48 @@ pq_status launch_tile(const GemmArgs &a, hipStream_t s)
     // stages per split: whole 64-byte groups, so every split starts a group
     const int sps = ((stages + splits - 1) / splits + C::SS - 1) / C::SS * C::SS;
     splits = (stages + sps - 1) / sps;
+    p.path = GemmPlan::TILE;
+    p.splits = splits;
+    p.sps = sps;
+    p.ws = splits > 1 ? static_cast<int64_t>(splits) * M * N * 4 : 0;
+}
+
+template <int BITS>
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
+{
+    constexpr int GK = 512 / BITS;
+    GemmPlan p;
+    if (M <= 16 && K % GK == 0) {
+        p.path = GemmPlan::STREAM;
+    } else if (gemm_big_takes(BITS, M, N, K)) {
+        p.path = GemmPlan::BIG;
+        p.ws = (M * 4 + kWsAlign - 1) / kWsAlign * kWsAlign;  // the activation row sums
+    } else {
+        plan_tile<BITS>(M, N, K, p);
+    }
+    return p;
+}
+
+template <int BITS>
+pq_status launch_tile(const GemmArgs &a, const GemmPlan &p, float *ws, hipStream_t s)
+{
+    using C = TileCfg<BITS, PQ_TILE_WN>;
+    const int mtiles = (a.M + kTileM - 1) / kTileM;
+    const int ntiles = (a.N + C::TN - 1) / C::TN;
     // the tile kernel's 4-bit operand is 2 + c/8 (the stream kernel's 128 + c)
     const float off = BITS != 4 ? a.off : 2.0f + (a.off - 128.0f) / 8.0f;
     const float mul = BITS != 4 ? a.mul : 8.0f * a.mul;
-    TileArgs t{a.X, a.packed, a.alpha, a.Y, nullptr, a.M, a.N, a.K, mtiles, ntiles, splits, sps * kStageK,
+    TileArgs t{a.X, a.packed, a.alpha, a.Y, ws, a.M, a.N, a.K, mtiles, ntiles, p.splits, p.sps * kStageK,
                a.gstride, off, mul, a.alpha32};
     const int64_t total = static_cast<int64_t>(a.M) * a.N;
-    if (splits > 1) {
-        pq_status st = workspace(s, static_cast<size_t>(splits) * total * sizeof(float), &t.ws);
-        if (st != PQ_OK) return st;
-    }
-    const int64_t blocks = tiles * splits;
+    const int64_t blocks = static_cast<int64_t>(mtiles) * ntiles * p.splits;
     if (blocks > INT32_MAX) return PQ_ERR_SHAPE;
     hipLaunchKernelGGL((k_gemm_tile<BITS, C::P, PQ_TILE_WN>), dim3(static_cast<unsigned>(blocks)), dim3(64 * PQ_TILE_WN),
                        0, s, t);
-    if (splits > 1) {
+    if (p.splits > 1) {
         const int64_t threads = (total + 3) / 4;
         hipLaunchKernelGGL(k_splitk_finalize, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s,
-                           t.ws, a.alpha, a.alpha32, a.Y, total, a.N, splits);
+                           t.ws, a.alpha, a.alpha32, a.Y, total, a.N, p.splits);
     }
     return PQ_OK;
 }
@@ -998,17 +999,37 @@ bool level_map(int mode, LevelMap *lm)
     }
 }
 
+bool gemm_shape_ok(int64_t M, int64_t N, int64_t K)
+{
+    return M >= 0 && N >= 0 && K > 0 && K % 64 == 0 && K <= kMaxGemmK && M <= INT32_MAX / 2 && N <= kMaxGemmN;
+}
+
+int64_t gemm_ws_bytes(int bits, int64_t M, int64_t N, int64_t K)
+{
+    if (M == 0 || N == 0) return 0;
+    if (bits == 1) return plan_gemm<1>(M, N, K).ws;
+    if (bits == 2) return plan_gemm<2>(M, N, K).ws;
+    return plan_gemm<4>(M, N, K).ws;
+}
+
 template <int BITS>
 pq_status gemm(int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *packed,
-               const void *alpha_bf16, void *Y, void *stream, const LevelMap &lm, const float *alpha32 = nullptr)
+               const void *alpha_bf16, void *Y, void *workspace, int64_t ws_bytes, void *stream,
+               const LevelMap &lm, const float *alpha32 = nullptr)
 {
     if (!X || !packed || (!alpha_bf16 && !alpha32) || !Y) return PQ_ERR_NULL;
-    if (M < 0 || N < 0 || K <= 0 || K % 64 != 0 || K > kMaxGemmK || M > INT32_MAX / 2 || N > kMaxGemmN)
-        return PQ_ERR_SHAPE;
+    if (!gemm_shape_ok(M, N, K)) return PQ_ERR_SHAPE;
     if (!aligned16(X) || !aligned16(packed) || !aligned16(Y) || (alpha_bf16 && !aligned16(alpha_bf16)) ||
         (alpha32 && !aligned16(alpha32)))
         return PQ_ERR_ALIGN;
+    if (ws_bytes < 0) return PQ_ERR_ARG;
     if (M == 0 || N == 0) return PQ_OK;
+    const GemmPlan plan = plan_gemm<BITS>(M, N, K);
+    if (plan.ws > 0) {
+        if (!workspace) return PQ_ERR_NULL;
+        if (!aligned16(workspace)) return PQ_ERR_ALIGN;
+        if (ws_bytes < plan.ws) return PQ_ERR_ARG;
+    }
     GemmArgs a{static_cast<const uint16_t *>(X), packed, static_cast<const uint16_t *>(alpha_bf16),
                static_cast<uint16_t *>(Y), static_cast<int>(M), static_cast<int>(N), static_cast<int>(K),
                (N + 15) / 16 * 16 * 64,
@@ -1018,24 +1039,33 @@ pq_status gemm(int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *pa
     hipStream_t s = static_cast<hipStream_t>(stream);
     constexpr int GK = 512 / BITS;
     constexpr int RPL = 512 / GK;
-    if (M <= 16 && K % GK == 0) {
+    if (plan.path == GemmPlan::STREAM) {
         if (M <= RPL) launch_stream<BITS, 1>(a, s);
         else if (M <= 2 * RPL) launch_stream<BITS, 2>(a, s);
         else if (M <= 4 * RPL) launch_stream<BITS, 4>(a, s);
         else if (BITS == 1 && M <= 8) launch_stream<BITS, (BITS == 1 ? 8 : 4)>(a, s);
         else launch_stream<BITS, 16 / RPL>(a, s);
-    } else if (gemm_big_takes(BITS, M, N, K)) {
-        float *rsum = nullptr;
-        const pq_status st = workspace(s, static_cast<size_t>(M) * sizeof(float), &rsum);
-        if (st != PQ_OK) return st;
+    } else if (plan.path == GemmPlan::BIG) {
+        float *rsum = static_cast<float *>(workspace);
         hipLaunchKernelGGL(k_rowsum, dim3(static_cast<unsigned>(M)), dim3(256), 0, s, a.X, a.K, rsum);
         const pq_status sb = launch_gemm_big(a, rsum, s);
         if (sb != PQ_OK) return sb;
     } else {
-        const pq_status st = launch_tile<BITS>(a, s);
+        const pq_status st = launch_tile<BITS>(a, plan, static_cast<float *>(workspace), s);
         if (st != PQ_OK) return st;
     }
     return hipGetLastError() == hipSuccess ? PQ_OK : PQ_ERR_HIP;
+}
+
+pq_status gemm_dispatch(int mode, int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *packed,
+                        const void *alpha_bf16, const float *alpha32, void *Y, void *workspace, int64_t ws_bytes,
+                        void *stream)
+{
+    LevelMap lm;
+    if (!level_map(mode, &lm)) return PQ_ERR_MODE;
+    if (lm.bits == 1) return gemm<1>(M, N, K, X, packed, alpha_bf16, Y, workspace, ws_bytes, stream, lm, alpha32);
+    if (lm.bits == 2) return gemm<2>(M, N, K, X, packed, alpha_bf16, Y, workspace, ws_bytes, stream, lm, alpha32);
+    return gemm<4>(M, N, K, X, packed, alpha_bf16, Y, workspace, ws_bytes, stream, lm, alpha32);
 }
 
 }  // namespace
@@ -1043,37 +1073,39 @@ pq_status gemm(int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *pa
 
 extern "C" {
 
-pq_status pq_gemm(int mode, int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *packed,
-                  const void *alpha_bf16, void *Y, void *stream)
+int64_t pq_gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K)
 {
     pq::LevelMap lm;
-    if (!pq::level_map(mode, &lm)) return PQ_ERR_MODE;
-    if (lm.bits == 1) return pq::gemm<1>(M, N, K, X, packed, alpha_bf16, Y, stream, lm);
-    if (lm.bits == 2) return pq::gemm<2>(M, N, K, X, packed, alpha_bf16, Y, stream, lm);
-    return pq::gemm<4>(M, N, K, X, packed, alpha_bf16, Y, stream, lm);
+    if (!pq::level_map(mode, &lm) || !pq::gemm_shape_ok(M, N, K)) return -1;
+    return pq::gemm_ws_bytes(lm.bits, M, N, K);
+}
+
+pq_status pq_gemm(int mode, int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *packed,
+                  const void *alpha_bf16, void *Y, void *workspace, int64_t workspace_bytes, void *stream)
+{
+    return pq::gemm_dispatch(mode, M, N, K, X, packed, alpha_bf16, nullptr, Y, workspace, workspace_bytes, stream);
 }
 
 pq_status pq_gemm_f32a(int mode, int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *packed,
-                       const float *alpha, void *Y, void *stream)
+                       const float *alpha, void *Y, void *workspace, int64_t workspace_bytes, void *stream)
 {
-    pq::LevelMap lm;
-    if (!pq::level_map(mode, &lm)) return PQ_ERR_MODE;
-    if (!alpha) return PQ_ERR_NULL;
-    if (lm.bits == 1) return pq::gemm<1>(M, N, K, X, packed, nullptr, Y, stream, lm, alpha);
-    if (lm.bits == 2) return pq::gemm<2>(M, N, K, X, packed, nullptr, Y, stream, lm, alpha);
-    return pq::gemm<4>(M, N, K, X, packed, nullptr, Y, stream, lm, alpha);
+    if (!alpha) {
+        pq::LevelMap lm;
+        return pq::level_map(mode, &lm) ? PQ_ERR_NULL : PQ_ERR_MODE;
+    }
+    return pq::gemm_dispatch(mode, M, N, K, X, packed, nullptr, alpha, Y, workspace, workspace_bytes, stream);
 }
 
 pq_status pq_w2a16_gemm(int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *packed,
-                        const void *alpha_bf16, void *Y, void *stream)
+                        const void *alpha_bf16, void *Y, void *workspace, int64_t workspace_bytes, void *stream)
 {
-    return pq_gemm(PQ_W2_SEQ, M, N, K, X, packed, alpha_bf16, Y, stream);
+    return pq_gemm(PQ_W2_SEQ, M, N, K, X, packed, alpha_bf16, Y, workspace, workspace_bytes, stream);
 }
 
 pq_status pq_w4a16_gemm(int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *packed,
-                        const void *alpha_bf16, void *Y, void *stream)
+                        const void *alpha_bf16, void *Y, void *workspace, int64_t workspace_bytes, void *stream)
 {
-    return pq_gemm(PQ_W4_LSQ, M, N, K, X, packed, alpha_bf16, Y, stream);
+    return pq_gemm(PQ_W4_LSQ, M, N, K, X, packed, alpha_bf16, Y, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -267,8 +267,7 @@ __device__ __forceinline__ void store_codes(PQ_GLOBAL uint8_t *crow, int q, uint
 // launches ask for half the blocks per CU rather than spill.)
 template <int MODE, bool INIT, int WPR, unsigned OUTS>
 __global__ __launch_bounds__(256, ((OUTS & OUT_STATS) || INIT) ? PQ_QUANT_FWD_MINB / 2 : PQ_QUANT_FWD_MINB) void k_quant_fwd(
-    LaunchTable lt, void *alpha_bf16_single,
-                                                                      StatsOut so)
+    LaunchTable lt, StatsOut so)
 {
     constexpr int RPB = 4 / WPR;
     constexpr int TEAM = 64 * WPR;
@@ -356,7 +355,7 @@ __global__ __launch_bounds__(256, ((OUTS & OUT_STATS) || INIT) ? PQ_QUANT_FWD_MI
         if constexpr ((OUTS & OUT_ALPHA_BF16) != 0) {
             if (tl == 0) {
                 __bf16 h = static_cast<__bf16>(alpha_raw);
-                static_cast<uint16_t *>(alpha_bf16_single)[row] = __builtin_bit_cast(uint16_t, h);
+                static_cast<uint16_t *>(m.alpha_bf16)[row] = __builtin_bit_cast(uint16_t, h);
             }
         }
 
@@ -834,12 +833,12 @@ pq_status launch_grouped(int count, const D *host, const D *dev, hipStream_t str
 }
 
 template <int MODE, bool INIT, unsigned OUTS>
-void launch_fwd_t(const LaunchTable &lt, int blocks, int wpr, hipStream_t s, void *abf, StatsOut so = {})
+void launch_fwd_t(const LaunchTable &lt, int blocks, int wpr, hipStream_t s, StatsOut so = {})
 {
     if (wpr == 1)
-        hipLaunchKernelGGL((k_quant_fwd<MODE, INIT, 1, OUTS>), dim3(blocks), dim3(256), 0, s, lt, abf, so);
+        hipLaunchKernelGGL((k_quant_fwd<MODE, INIT, 1, OUTS>), dim3(blocks), dim3(256), 0, s, lt, so);
     else
-        hipLaunchKernelGGL((k_quant_fwd<MODE, INIT, 4, OUTS>), dim3(blocks), dim3(256), 0, s, lt, abf, so);
+        hipLaunchKernelGGL((k_quant_fwd<MODE, INIT, 4, OUTS>), dim3(blocks), dim3(256), 0, s, lt, so);
 }
 
 // Forward with the fused level statistics (alpha given, codes written,
@@ -847,8 +846,8 @@ void launch_fwd_t(const LaunchTable &lt, int blocks, int wpr, hipStream_t s, voi
 template <int MODE>
 void launch_fwd_stats_mode(bool bf16, const LaunchTable &lt, int blocks, int wpr, hipStream_t s, StatsOut so)
 {
-    if (bf16) launch_fwd_t<MODE, false, OUT_STATS | OUT_CODES | OUT_BF16>(lt, blocks, wpr, s, nullptr, so);
-    else launch_fwd_t<MODE, false, OUT_STATS | OUT_CODES>(lt, blocks, wpr, s, nullptr, so);
+    if (bf16) launch_fwd_t<MODE, false, OUT_STATS | OUT_CODES | OUT_BF16>(lt, blocks, wpr, s, so);
+    else launch_fwd_t<MODE, false, OUT_STATS | OUT_CODES>(lt, blocks, wpr, s, so);
 }
 
 void launch_fwd_stats(int mode, bool bf16, const LaunchTable &lt, int blocks, int wpr, hipStream_t s, StatsOut so)
@@ -868,21 +867,21 @@ template <int MODE, bool INIT>
 void launch_fwd_outs(unsigned outs, const LaunchTable &lt, int blocks, int wpr, hipStream_t s)
 {
     switch (outs) {
-    case 0: launch_fwd_t<MODE, INIT, 0>(lt, blocks, wpr, s, nullptr); break;
-    case 1: launch_fwd_t<MODE, INIT, 1>(lt, blocks, wpr, s, nullptr); break;
-    case 2: launch_fwd_t<MODE, INIT, 2>(lt, blocks, wpr, s, nullptr); break;
-    case 3: launch_fwd_t<MODE, INIT, 3>(lt, blocks, wpr, s, nullptr); break;
-    case 4: launch_fwd_t<MODE, INIT, 4>(lt, blocks, wpr, s, nullptr); break;
-    case 5: launch_fwd_t<MODE, INIT, 5>(lt, blocks, wpr, s, nullptr); break;
-    case 6: launch_fwd_t<MODE, INIT, 6>(lt, blocks, wpr, s, nullptr); break;
-    case 7: launch_fwd_t<MODE, INIT, 7>(lt, blocks, wpr, s, nullptr); break;
+    case 0: launch_fwd_t<MODE, INIT, 0>(lt, blocks, wpr, s); break;
+    case 1: launch_fwd_t<MODE, INIT, 1>(lt, blocks, wpr, s); break;
+    case 2: launch_fwd_t<MODE, INIT, 2>(lt, blocks, wpr, s); break;
+    case 3: launch_fwd_t<MODE, INIT, 3>(lt, blocks, wpr, s); break;
+    case 4: launch_fwd_t<MODE, INIT, 4>(lt, blocks, wpr, s); break;
+    case 5: launch_fwd_t<MODE, INIT, 5>(lt, blocks, wpr, s); break;
+    case 6: launch_fwd_t<MODE, INIT, 6>(lt, blocks, wpr, s); break;
+    case 7: launch_fwd_t<MODE, INIT, 7>(lt, blocks, wpr, s); break;
     default:
         // codes in the export byte order
         switch (outs) {
-        case OUT_CODES | OUT_TILED: launch_fwd_t<MODE, INIT, 20>(lt, blocks, wpr, s, nullptr); break;
-        case OUT_BF16 | OUT_CODES | OUT_TILED: launch_fwd_t<MODE, INIT, 21>(lt, blocks, wpr, s, nullptr); break;
-        case OUT_F32 | OUT_CODES | OUT_TILED: launch_fwd_t<MODE, INIT, 22>(lt, blocks, wpr, s, nullptr); break;
-        default: launch_fwd_t<MODE, INIT, 23>(lt, blocks, wpr, s, nullptr); break;
+        case OUT_CODES | OUT_TILED: launch_fwd_t<MODE, INIT, 20>(lt, blocks, wpr, s); break;
+        case OUT_BF16 | OUT_CODES | OUT_TILED: launch_fwd_t<MODE, INIT, 21>(lt, blocks, wpr, s); break;
+        case OUT_F32 | OUT_CODES | OUT_TILED: launch_fwd_t<MODE, INIT, 22>(lt, blocks, wpr, s); break;
+        default: launch_fwd_t<MODE, INIT, 23>(lt, blocks, wpr, s); break;
         }
         break;
     }
@@ -1086,6 +1085,66 @@ pq_status check_step_descs(int mode, int count, const pq_step_mat *host, int g_d
     return PQ_OK;
 }
 
+// Export: the forward's codes in the export byte order plus bf16(alpha), one
+// launch over every matrix's rows rounded up to 16 (the padding rows of each
+// last tile are written as zeros).
+template <int MODE>
+void launch_pack_mode(const LaunchTable &lt, int blocks, int wpr, hipStream_t s)
+{
+    launch_fwd_t<MODE, false, OUT_CODES | OUT_TILED | OUT_ALPHA_BF16>(lt, blocks, wpr, s);
+}
+
+pq_status check_pack_descs(int mode, int count, const pq_mat *host)
+{
+    if (!deployable(mode)) return PQ_ERR_MODE;
+    if (count < 0) return PQ_ERR_ARG;
+    if (count > 0 && !host) return PQ_ERR_NULL;
+    for (int i = 0; i < count; ++i) {
+        const pq_mat &m = host[i];
+        if (m.rows < 0 || !valid_cols(m.cols)) return PQ_ERR_SHAPE;
+        if (m.rows == 0) continue;  // enqueues nothing; its pointers are not used
+        if (!m.W || !m.alpha || !m.codes || !m.alpha_bf16) return PQ_ERR_NULL;
+        if (!aligned16(m.W) || !aligned16(m.alpha) || !aligned16(m.codes) || !aligned16(m.alpha_bf16))
+            return PQ_ERR_ALIGN;
+    }
+    return PQ_OK;
+}
+
+pq_status pack_grouped(int mode, int count, const pq_mat *host, const pq_mat *dev, void *stream)
+{
+    return launch_grouped(
+        count, host, dev, static_cast<hipStream_t>(stream), true,
+        [&](const LaunchTable &lt, int blocks, int wpr, hipStream_t s) {
+            switch (mode) {
+            case PQ_W1_BINARY: launch_pack_mode<PQ_W1_BINARY>(lt, blocks, wpr, s); break;
+            case PQ_W158_SEQ_TERNARY: launch_pack_mode<PQ_W158_SEQ_TERNARY>(lt, blocks, wpr, s); break;
+            case PQ_W2_SEQ: launch_pack_mode<PQ_W2_SEQ>(lt, blocks, wpr, s); break;
+            case PQ_W3_LSQ: launch_pack_mode<PQ_W3_LSQ>(lt, blocks, wpr, s); break;
+            case PQ_W2_LSQ: launch_pack_mode<PQ_W2_LSQ>(lt, blocks, wpr, s); break;
+            case PQ_W158_LSQ: launch_pack_mode<PQ_W158_LSQ>(lt, blocks, wpr, s); break;
+            default: launch_pack_mode<PQ_W4_LSQ>(lt, blocks, wpr, s); break;
+            }
+        },
+        true);
+}
+
+pq_status pack_common(int mode, int64_t rows, int64_t cols, const float *W,
+                             const float *alpha, uint8_t *packed, void *alpha_bf16, void *stream)
+{
+    pq_mat m = {};
+    m.W = W;
+    m.alpha = const_cast<float *>(alpha);
+    m.codes = packed;
+    m.alpha_bf16 = alpha_bf16;
+    m.rows = rows;
+    m.cols = cols;
+    if (!deployable(mode)) return PQ_ERR_MODE;
+    if (!W || !alpha || !packed || !alpha_bf16) return PQ_ERR_NULL;
+    const pq_status st = check_pack_descs(mode, 1, &m);
+    if (st != PQ_OK) return st;
+    return pack_grouped(mode, 1, &m, nullptr, stream);
+}
+
 }  // namespace
 }  // namespace pq
 
@@ -1227,47 +1286,12 @@ pq_status pq_quantize_bwd(int mode, int64_t rows, int64_t cols, const float *W, 
                           });
 }
 
-// Export: one launch over the rows rounded up to 16 (the padding rows of the
-// last tile are written as zeros).
-static pq_status pack_common(int mode, int64_t rows, int64_t cols, const float *W,
-                             const float *alpha, uint8_t *packed, void *alpha_bf16, void *stream)
+pq_status pq_pack_grouped(int mode, int count, const pq_mat *descs_host, const pq_mat *descs_dev, void *stream)
 {
-    if (!deployable(mode)) return PQ_ERR_MODE;
-    if (!W || !alpha || !packed || !alpha_bf16) return PQ_ERR_NULL;
-    if (rows < 0 || !valid_cols(cols)) return PQ_ERR_SHAPE;
-    if (!aligned16(W) || !aligned16(alpha) || !aligned16(packed) || !aligned16(alpha_bf16))
-        return PQ_ERR_ALIGN;
-    if (rows == 0) return PQ_OK;
-    pq_mat m = {};
-    m.W = W;
-    m.alpha = const_cast<float *>(alpha);
-    m.codes = packed;
-    m.rows = rows;
-    m.cols = cols;
-    const int64_t np = (rows + 15) / 16 * 16;
-    const int wpr = choose_wpr(np, np * cols);
-    const int rpb = (4 / wpr) * fwd_rows_per_wave(wpr, true);
-    const int64_t blocks = (np + rpb - 1) / rpb;
-    if (blocks > INT32_MAX) return PQ_ERR_SHAPE;
-    LaunchTable lt;
-    lt.table = nullptr;
-    lt.single = m;
-    lt.count = 1;
-    lt.block_start[0] = 0;
-    lt.block_start[1] = static_cast<int32_t>(blocks);
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    constexpr unsigned O = OUT_CODES | OUT_TILED | OUT_ALPHA_BF16;
-    const int nb = static_cast<int>(blocks);
-    switch (mode) {
-    case PQ_W1_BINARY: launch_fwd_t<PQ_W1_BINARY, false, O>(lt, nb, wpr, s, alpha_bf16); break;
-    case PQ_W158_SEQ_TERNARY: launch_fwd_t<PQ_W158_SEQ_TERNARY, false, O>(lt, nb, wpr, s, alpha_bf16); break;
-    case PQ_W2_SEQ: launch_fwd_t<PQ_W2_SEQ, false, O>(lt, nb, wpr, s, alpha_bf16); break;
-    case PQ_W3_LSQ: launch_fwd_t<PQ_W3_LSQ, false, O>(lt, nb, wpr, s, alpha_bf16); break;
-    case PQ_W2_LSQ: launch_fwd_t<PQ_W2_LSQ, false, O>(lt, nb, wpr, s, alpha_bf16); break;
-    case PQ_W158_LSQ: launch_fwd_t<PQ_W158_LSQ, false, O>(lt, nb, wpr, s, alpha_bf16); break;
-    default: launch_fwd_t<PQ_W4_LSQ, false, O>(lt, nb, wpr, s, alpha_bf16); break;
-    }
-    return hipGetLastError() == hipSuccess ? PQ_OK : PQ_ERR_HIP;
+    const pq_status st = check_pack_descs(mode, count, descs_host);
+    if (st != PQ_OK) return st;
+    if (count > 0 && !descs_dev) return PQ_ERR_NULL;
+    return pack_grouped(mode, count, descs_host, descs_dev, stream);
 }
 
 pq_status pq_pack(int mode, int64_t rows, int64_t cols, const float *W, const float *alpha, uint8_t *packed,

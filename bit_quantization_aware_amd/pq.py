@@ -31,10 +31,11 @@ STATUS = {0: "PQ_OK", 1: "PQ_ERR_NULL", 2: "PQ_ERR_SHAPE", 3: "PQ_ERR_MODE", 4: 
 
 # Every symbol include/pq.h declares.
 EXPORTS = ("pq_code_row_bytes", "pq_packed_bytes", "pq_default_grad_scale", "pq_status_str", "pq_version",
+           "pq_gemm_workspace_bytes",
            "pq_quantize_fwd", "pq_quantize_bwd", "pq_pack_w2", "pq_pack_w4", "pq_w2a16_gemm",
            "pq_w4a16_gemm", "pq_quantize_fwd_grouped", "pq_quantize_bwd_grouped", "pq_qat_step",
            "pq_qat_step_grouped", "pq_pack", "pq_gemm", "pq_gemm_f32a", "pq_num_levels", "pq_level_stats",
-           "pq_quantize_fwd_stats", "pq_weight_movement")
+           "pq_quantize_fwd_stats", "pq_weight_movement", "pq_pack_grouped")
 
 
 class PQError(RuntimeError):
@@ -48,7 +49,8 @@ class pq_mat(ctypes.Structure):
     _fields_ = [("W", ctypes.c_void_p), ("alpha", ctypes.c_void_p), ("wq_bf16", ctypes.c_void_p),
                 ("wq_f32", ctypes.c_void_p), ("codes", ctypes.c_void_p), ("G", ctypes.c_void_p),
                 ("dW", ctypes.c_void_p), ("dalpha", ctypes.c_void_p), ("mask_bits", ctypes.c_void_p),
-                ("grad_scale", ctypes.c_double), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+                ("grad_scale", ctypes.c_double), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("alpha_bf16", ctypes.c_void_p)]
 
 
 class pq_adamw(ctypes.Structure):
@@ -85,11 +87,13 @@ def _load():
     L.pq_quantize_bwd.argtypes = [i32, i64, i64, vp, vp, vp, i32, dbl, vp, vp, vp, vp]
     L.pq_pack_w2.argtypes = [i64, i64, vp, vp, vp, vp, vp]
     L.pq_pack_w4.argtypes = [i64, i64, vp, vp, vp, vp, vp]
-    L.pq_w2a16_gemm.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp]
-    L.pq_w4a16_gemm.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp]
+    L.pq_gemm_workspace_bytes.argtypes = [i32, i64, i64, i64]
+    L.pq_gemm_workspace_bytes.restype = i64
+    L.pq_w2a16_gemm.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, i64, vp]
+    L.pq_w4a16_gemm.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, i64, vp]
     L.pq_pack.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp]
-    L.pq_gemm.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp]
-    L.pq_gemm_f32a.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp]
+    L.pq_gemm.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, i64, vp]
+    L.pq_gemm_f32a.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, i64, vp]
     L.pq_num_levels.argtypes = [i32]
     L.pq_num_levels.restype = i32
     L.pq_level_stats.argtypes = [i32, i64, i64, vp, vp, vp, vp]
@@ -97,11 +101,12 @@ def _load():
     L.pq_weight_movement.argtypes = [i64, i64, vp, vp, vp, vp, vp]
     L.pq_quantize_fwd_grouped.argtypes = [i32, i32, vp, vp, u32, vp]
     L.pq_quantize_bwd_grouped.argtypes = [i32, i32, vp, vp, i32, vp]
+    L.pq_pack_grouped.argtypes = [i32, i32, vp, vp, vp]
     L.pq_qat_step.argtypes = [i32, i64, i64, vp, vp, vp, i32, dbl, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.pq_qat_step_grouped.argtypes = [i32, i32, vp, vp, i32, vp, vp]
     for name in EXPORTS:
         if name not in ("pq_code_row_bytes", "pq_packed_bytes", "pq_default_grad_scale", "pq_status_str",
-                        "pq_version", "pq_num_levels"):
+                        "pq_version", "pq_num_levels", "pq_gemm_workspace_bytes"):
             getattr(L, name).restype = i32
     return L
 
@@ -173,13 +178,46 @@ def pq_pack_w4(rows, cols, W, alpha, packed, alpha_bf16, stream=None) -> None:
                           _stream(stream)), "pq_pack_w4")
 
 
-def pq_w2a16_gemm(M, N, K, X, packed, alpha_bf16, Y, stream=None) -> None:
-    _check(lib.pq_w2a16_gemm(M, N, K, _ptr(X), _ptr(packed), _ptr(alpha_bf16), _ptr(Y),
+def pq_gemm_workspace_bytes(mode: int, M: int, N: int, K: int) -> int:
+    return int(lib.pq_gemm_workspace_bytes(mode, M, N, K))
+
+
+def gemm_workspace(mode: int, M: int, N: int, K: int, device="cuda") -> Optional[torch.Tensor]:
+    """A device buffer of pq_gemm_workspace_bytes(mode, M, N, K) bytes (None
+    when the shape needs none), allocated by torch for the caller to keep."""
+    n = pq_gemm_workspace_bytes(mode, M, N, K)
+    if n < 0:
+        raise PQError(2, "pq_gemm_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device) if n > 0 else None
+
+
+def _ws(mode, M, N, K, X, workspace, stream):
+    """(pointer, size, tensor) of the caller's workspace, or of one allocated
+    here from torch's caching allocator.  A buffer allocated here is marked
+    as used by the launch stream, so torch hands it out again only after the
+    GEMM on that stream is done with it."""
+    if workspace is None:
+        dev = X.device if isinstance(X, torch.Tensor) else "cuda"
+        workspace = gemm_workspace(mode, M, N, K, dev)
+        if workspace is None:
+            return None, 0, None
+        if stream is not None:
+            s = torch.cuda.ExternalStream(stream) if isinstance(stream, int) else stream
+            workspace.record_stream(s)
+    if isinstance(workspace, tuple):        # (pointer, bytes) from a caller that keeps its own buffer
+        return workspace[0], int(workspace[1]), None
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size(), workspace
+
+
+def pq_w2a16_gemm(M, N, K, X, packed, alpha_bf16, Y, stream=None, workspace=None) -> None:
+    wp, wb, _keep = _ws(PQ_W2_SEQ, M, N, K, X, workspace, stream)
+    _check(lib.pq_w2a16_gemm(M, N, K, _ptr(X), _ptr(packed), _ptr(alpha_bf16), _ptr(Y), wp, wb,
                              _stream(stream)), "pq_w2a16_gemm")
 
 
-def pq_w4a16_gemm(M, N, K, X, packed, alpha_bf16, Y, stream=None) -> None:
-    _check(lib.pq_w4a16_gemm(M, N, K, _ptr(X), _ptr(packed), _ptr(alpha_bf16), _ptr(Y),
+def pq_w4a16_gemm(M, N, K, X, packed, alpha_bf16, Y, stream=None, workspace=None) -> None:
+    wp, wb, _keep = _ws(PQ_W4_LSQ, M, N, K, X, workspace, stream)
+    _check(lib.pq_w4a16_gemm(M, N, K, _ptr(X), _ptr(packed), _ptr(alpha_bf16), _ptr(Y), wp, wb,
                              _stream(stream)), "pq_w4a16_gemm")
 
 
@@ -188,13 +226,15 @@ def pq_pack(mode, rows, cols, W, alpha, packed, alpha_bf16, stream=None) -> None
                        _stream(stream)), "pq_pack")
 
 
-def pq_gemm(mode, M, N, K, X, packed, alpha_bf16, Y, stream=None) -> None:
-    _check(lib.pq_gemm(mode, M, N, K, _ptr(X), _ptr(packed), _ptr(alpha_bf16), _ptr(Y),
+def pq_gemm(mode, M, N, K, X, packed, alpha_bf16, Y, stream=None, workspace=None) -> None:
+    wp, wb, _keep = _ws(mode, M, N, K, X, workspace, stream)
+    _check(lib.pq_gemm(mode, M, N, K, _ptr(X), _ptr(packed), _ptr(alpha_bf16), _ptr(Y), wp, wb,
                        _stream(stream)), "pq_gemm")
 
 
-def pq_gemm_f32a(mode, M, N, K, X, packed, alpha, Y, stream=None) -> None:
-    _check(lib.pq_gemm_f32a(mode, M, N, K, _ptr(X), _ptr(packed), _ptr(alpha), _ptr(Y),
+def pq_gemm_f32a(mode, M, N, K, X, packed, alpha, Y, stream=None, workspace=None) -> None:
+    wp, wb, _keep = _ws(mode, M, N, K, X, workspace, stream)
+    _check(lib.pq_gemm_f32a(mode, M, N, K, _ptr(X), _ptr(packed), _ptr(alpha), _ptr(Y), wp, wb,
                             _stream(stream)), "pq_gemm_f32a")
 
 
@@ -228,7 +268,7 @@ class MatTable:
     it keeps the device copy (a torch uint8 tensor) alive."""
 
     STRUCT = pq_mat
-    POINTERS = ("W", "alpha", "wq_bf16", "wq_f32", "codes", "G", "dW", "dalpha", "mask_bits")
+    POINTERS = ("W", "alpha", "wq_bf16", "wq_f32", "codes", "G", "dW", "dalpha", "mask_bits", "alpha_bf16")
 
     def __init__(self, mats: Sequence[dict], device="cuda"):
         n = len(mats)
@@ -261,6 +301,11 @@ def pq_quantize_fwd_grouped(mode, table: MatTable, flags=0, stream=None) -> None
 def pq_quantize_bwd_grouped(mode, table: MatTable, g_dtype=PQ_G_F32, stream=None) -> None:
     _check(lib.pq_quantize_bwd_grouped(mode, table.count, table.host_ptr, table.dev_ptr, g_dtype,
                                        _stream(stream)), "pq_quantize_bwd_grouped")
+
+
+def pq_pack_grouped(mode, table: MatTable, stream=None) -> None:
+    _check(lib.pq_pack_grouped(mode, table.count, table.host_ptr, table.dev_ptr, _stream(stream)),
+           "pq_pack_grouped")
 
 
 class StepTable(MatTable):

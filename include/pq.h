@@ -17,20 +17,22 @@
  *
  * Conventions shared by every entry point
  *   Memory     Every array argument is a DEVICE pointer owned by the caller;
- *              the library keeps no pointer after the call returns.  The only
- *              memory the library allocates itself is the GEMM's workspace
- *              (split-K partial sums and activation row sums, see
- *              pq_w2a16_gemm).  Arrays are row-major and contiguous
+ *              the library keeps no pointer after the call returns and never
+ *              allocates or frees device memory: the GEMM's scratch (split-K
+ *              partial sums, activation row sums) is a caller-owned
+ *              workspace sized by pq_gemm_workspace_bytes.  Arrays are
+ *              row-major and contiguous
  *              (leading dimension = cols), except the exported codes of
  *              pq_pack_w2 / pq_pack_w4 (the export byte order below).  Weight matrices are [out, in]:
  *              a "row" is one output channel, the unit the scale alpha
  *              belongs to ([Note] "Paper vs. code": one learned scale per
  *              row, shape (rows, 1)).
  *   Streams    `stream` is a hipStream_t (NULL = the null stream).  Calls only
- *              enqueue work on it and return; results are ready when the
- *              stream is.  The only global state is the workspace cache,
- *              guarded by a mutex, so calls from several host threads are
- *              safe.
+ *              enqueue work on it and return, without waiting on the host;
+ *              results are ready when the stream is.  The library holds no
+ *              global mutable state, so calls from several host threads are
+ *              safe, and every call can be captured into a HIP graph
+ *              (including its first call).
  *   bf16       bf16 arrays are passed as void* and hold IEEE bfloat16 bit
  *              patterns; every cast to bf16 rounds to nearest-even.
  *   Errors     Arguments are checked on the host before anything is enqueued:
@@ -173,6 +175,15 @@ pq_status pq_quantize_fwd(int mode, int64_t rows, int64_t cols, const float *W,
  *            and s = the boundary level outside (clipped weights still feed
  *            the scale), accumulated in binary64 and rounded once ([Note]
  *            "Paper vs. code", LSQ-gradient row).
+ *   The boundary level is +-0.75 at 2-bit SEQ, +-fl32(2/3) for ternary (the
+ *   level of the clipped value), Qn or Qp for the LSQ grids.  For 1 bit,
+ *   sign(w) plays the part of the rounding, so the same rule reads
+ *   s = sign(w) - x inside |x| <= 1 and s = sign(w) outside (sign(+-0) = +1).
+ *   The pages name no binary gradient; this uniform reading is the library's
+ *   own, and an alternative (s = sign(w) everywhere, the derivative of
+ *   q = alpha * sign(w)) would change dalpha on every binary row.  The
+ *   ternary outside value and the default grad_scale carry readings the
+ *   pages do not pin either.
  *
  *   W, alpha   in   as in the forward (alpha is the value the forward used)
  *   G          in   [rows, cols] dL/dWq, fp32 (PQ_G_F32) or bf16 (PQ_G_BF16)
@@ -244,6 +255,23 @@ pq_status pq_pack_w4(int64_t rows, int64_t cols, const float *W, const float *al
                      uint8_t *packed, void *alpha_bf16, void *stream);
 
 /*
+ * pq_gemm_workspace_bytes -- device workspace, in bytes, that the GEMM entry
+ * points below need for this width and shape: 0 when the kernels chosen for
+ * the shape use none, -1 for an unknown mode or a shape they reject.  The
+ * kernel choice is a fixed function of (mode, M, N, K), so the value is the
+ * same for every call with these arguments:
+ *   M <= 16 (weight streaming): none;
+ *   larger M with 64 x 256 output tiles: when there are too few tiles to
+ *     fill the chip, K is split over blocks, each split writes fp32 partial
+ *     sums [splits, M, N] and a second kernel adds them in split order --
+ *     splits * M * N * 4 bytes; otherwise none;
+ *   large M at 2-bit widths (K >= 2048; M >= 1024, or M >= 512 when N gives
+ *     at least 512 tiles of 64 x 256): the fp32 sums of the activation rows,
+ *     M * 4 bytes rounded up to 256.
+ */
+int64_t pq_gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
+
+/*
  * pq_w2a16_gemm -- deployment GEMM with packed 2-bit SEQ weights and bf16
  * activations ([News] speed paragraph: 2-bit-weight kernel against FP16 and
  * 4-bit weights at a 16384 x 16384 weight; the layer has no bias, [Note]
@@ -260,37 +288,37 @@ pq_status pq_pack_w4(int64_t rows, int64_t cols, const float *W, const float *al
  *                   (export byte order; the padding bytes are never used)
  *   alpha_bf16 in   [N] bf16
  *   Y          out  [M, N] bf16
- * Workspace.  For M > 16 the output is cut into 64 x 256 tiles; when there
- * are too few tiles to fill the chip, K is split over blocks, each split
- * writes fp32 partial sums to a workspace of splits * M * N * 4 bytes, and a
- * second kernel on the same stream adds them in split order and writes Y.
- * For large M with K >= 2048 (2-bit grids; M >= 1024, or M >= 512 when N
- * gives at least 512 tiles of 64 x 256) a first kernel writes the sums of
- * the activation rows to a workspace of M * 4 bytes and the GEMM kernel
- * reads them.  The workspace is device memory owned by the library: one buffer per
- * (device, stream), allocated on first need and, when a larger one is
- * needed, replaced after the stream has been synchronized.  It lives until
- * the process ends.  Allocation failure returns PQ_ERR_HIP with nothing
- * enqueued.
+ *   workspace  scratch device memory of at least
+ *              pq_gemm_workspace_bytes(PQ_W2_SEQ, M, N, K) bytes, 16-byte
+ *              aligned, owned by the caller; its contents on entry do not
+ *              matter and on return are unspecified.  May be NULL when that
+ *              size is 0.  Two calls in flight at once (on different
+ *              streams) need different workspaces.
+ *   workspace_bytes  the size of `workspace` (>= 0)
+ * Errors as above, and: workspace needed but NULL -> PQ_ERR_NULL; not
+ * 16-byte aligned -> PQ_ERR_ALIGN; workspace_bytes too small or negative ->
+ * PQ_ERR_ARG.
  */
 pq_status pq_w2a16_gemm(int64_t M, int64_t N, int64_t K, const void *X,
                         const uint8_t *packed, const void *alpha_bf16, void *Y,
-                        void *stream);
+                        void *workspace, int64_t workspace_bytes, void *stream);
 
 /* pq_w4a16_gemm -- the same GEMM on pq_pack_w4 weights
  * (pq_packed_bytes(PQ_W4_LSQ, N, K) bytes), level(c) = c - 8. */
 pq_status pq_w4a16_gemm(int64_t M, int64_t N, int64_t K, const void *X,
                         const uint8_t *packed, const void *alpha_bf16, void *Y,
-                        void *stream);
+                        void *workspace, int64_t workspace_bytes, void *stream);
 
 /* pq_gemm -- the same GEMM for any deployable width, on pq_pack(mode, ...)
  * weights, with the width's levels ([Note] "Finding 3"): ternary
  * (c - 1) * fl32(2/3), 2-bit SEQ (c - 1.5) / 2, 3-bit LSQ c - 4, 4-bit LSQ
  * c - 8, and the ablation grids c - 2 (2-bit LSQ) and c - 1 (1.58-bit LSQ);
  * an other mode -> PQ_ERR_MODE.  These are the widths whose accuracy
- * and storage the pages compare ([News] speed and storage paragraphs). */
+ * and storage the pages compare ([News] speed and storage paragraphs).
+ * Workspace as pq_w2a16_gemm, sized by pq_gemm_workspace_bytes(mode, ...). */
 pq_status pq_gemm(int mode, int64_t M, int64_t N, int64_t K, const void *X,
-                  const uint8_t *packed, const void *alpha_bf16, void *Y, void *stream);
+                  const uint8_t *packed, const void *alpha_bf16, void *Y,
+                  void *workspace, int64_t workspace_bytes, void *stream);
 
 /* pq_gemm_f32a -- pq_gemm with the binary32 scale of training (alpha [N]
  * fp32, as pq_quantize_fwd keeps it) instead of the exported bf16 one: the
@@ -299,10 +327,11 @@ pq_status pq_gemm(int mode, int64_t M, int64_t N, int64_t K, const void *X,
  * pq_quantize_fwd(..., PQ_CODES_EXPORT, ...).  It reads 1/8 or 1/4 of the
  * bytes of the fake-quantized bf16 weights and never materialises them; the
  * forward's own Wq = bf16(alpha * level) rounds each weight to bf16 first,
- * so the two differ by that rounding (relative 2^-9 per weight).  Errors as
- * pq_gemm; alpha NULL -> PQ_ERR_NULL. */
+ * so the two differ by that rounding (relative 2^-9 per weight).  Errors
+ * and workspace as pq_gemm; alpha NULL -> PQ_ERR_NULL. */
 pq_status pq_gemm_f32a(int mode, int64_t M, int64_t N, int64_t K, const void *X,
-                       const uint8_t *packed, const float *alpha, void *Y, void *stream);
+                       const uint8_t *packed, const float *alpha, void *Y,
+                       void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
  * Grouped launches: one kernel launch over a whole stack of matrices (for
@@ -328,6 +357,7 @@ typedef struct pq_mat {
     double grad_scale;    /* bwd alpha-gradient scale for this matrix      */
     int64_t rows;
     int64_t cols;         /* positive multiple of 8                        */
+    void *alpha_bf16;     /* export out [rows] bf16 (pq_pack_grouped)      */
 } pq_mat;
 
 /* Forward over `count` matrices; per matrix exactly pq_quantize_fwd.
@@ -339,6 +369,14 @@ pq_status pq_quantize_fwd_grouped(int mode, int count, const pq_mat *descs_host,
  * that entry's grad_scale. */
 pq_status pq_quantize_bwd_grouped(int mode, int count, const pq_mat *descs_host,
                                   const pq_mat *descs_dev, int g_dtype, void *stream);
+
+/* Export over `count` matrices in one launch; per matrix exactly
+ * pq_pack(mode, rows, cols, W, alpha, codes, alpha_bf16): `codes` receives
+ * pq_packed_bytes(mode, rows, cols) bytes in the export byte order and
+ * `alpha_bf16` the [rows] bf16 scales (the export of a whole model, [Note]
+ * "Paper vs. code", last bullet: savings exist only after export). */
+pq_status pq_pack_grouped(int mode, int count, const pq_mat *descs_host,
+                          const pq_mat *descs_dev, void *stream);
 
 /*
  * Fused QAT step: the straight-through backward of the current forward,

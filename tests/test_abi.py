@@ -31,7 +31,8 @@ def test_every_declared_symbol_is_exported(pq):
 
 
 def test_struct_layout(pq):
-    assert ctypes.sizeof(pq.pq_mat) == 96
+    assert ctypes.sizeof(pq.pq_mat) == 104
+    assert pq.pq_mat.alpha_bf16.offset == 96
     assert ctypes.sizeof(pq.pq_step_mat) == 104
     assert ctypes.sizeof(pq.pq_adamw) == 48
 
@@ -113,24 +114,71 @@ def test_pack_and_gemm_argument_checks(pq):
     assert L.pq_pack_w2(4, 64, None, A, B, A, None) == 1
     assert L.pq_pack_w2(4, 12, A, A, B, A, None) == 2
     assert L.pq_pack_w4(4, 64, A, A, MIS, A, None) == 4
-    assert L.pq_w2a16_gemm(4, 8, 64, None, A, B, A, None) == 1
-    assert L.pq_w2a16_gemm(4, 8, 60, A, A, B, A, None) == 2
-    assert L.pq_w2a16_gemm(4, 8, 72, A, A, B, A, None) == 2                       # K % 64
-    assert L.pq_w2a16_gemm(-1, 8, 64, A, A, B, A, None) == 2
-    assert L.pq_w4a16_gemm(4, 8, 64, A, MIS, B, A, None) == 4
-    assert L.pq_w2a16_gemm(0, 8, 64, A, A, B, A, None) == 0                       # empty
-    assert L.pq_w2a16_gemm(1, (1 << 24) + 16, 64, A, A, B, A, None) == 2          # N bound
-    assert L.pq_pack_w2(0, 64, A, A, B, A, None) == 0                             # empty
-    assert L.pq_pack(7, 4, 64, A, A, B, A, None) == 3                             # bad mode
-    assert L.pq_gemm(7, 4, 8, 64, A, A, B, A, None) == 3
-    assert L.pq_gemm(1, 4, 8, 60, A, A, B, A, None) == 2                          # ternary, K % 64
+    # pq_w2a16_gemm(M, N, K, X, packed, alpha_bf16, Y, workspace, workspace_bytes, stream)
+    assert L.pq_w2a16_gemm(4, 8, 64, None, A, B, A, None, 0, None) == 1
+    assert L.pq_w2a16_gemm(4, 8, 60, A, A, B, A, None, 0, None) == 2
+    assert L.pq_w2a16_gemm(4, 8, 72, A, A, B, A, None, 0, None) == 2                 # K % 64
+    assert L.pq_w2a16_gemm(-1, 8, 64, A, A, B, A, None, 0, None) == 2
+    assert L.pq_w4a16_gemm(4, 8, 64, A, MIS, B, A, None, 0, None) == 4
+    assert L.pq_w2a16_gemm(0, 8, 64, A, A, B, A, None, 0, None) == 0                 # empty
+    assert L.pq_w2a16_gemm(1, (1 << 24) + 16, 64, A, A, B, A, None, 0, None) == 2    # N bound
+    assert L.pq_w2a16_gemm(4, 8, 64, A, A, B, A, None, -1, None) == 7                # negative size
+    assert L.pq_pack_w2(0, 64, A, A, B, A, None) == 0                                # empty
+    assert L.pq_pack(7, 4, 64, A, A, B, A, None) == 3                                # bad mode
+    assert L.pq_gemm(7, 4, 8, 64, A, A, B, A, None, 0, None) == 3
+    assert L.pq_gemm(1, 4, 8, 60, A, A, B, A, None, 0, None) == 2                    # ternary, K % 64
     assert L.pq_pack(3, 4, 60, A, A, B, A, None) == 2
-    assert L.pq_gemm_f32a(2, 4, 8, 64, A, A, None, A, None) == 1                  # alpha NULL
-    assert L.pq_gemm_f32a(7, 4, 8, 64, A, A, B, A, None) == 3
+    assert L.pq_gemm_f32a(2, 4, 8, 64, A, A, None, A, None, 0, None) == 1            # alpha NULL
+    assert L.pq_gemm_f32a(7, 4, 8, 64, A, A, B, A, None, 0, None) == 3
     # forward with codes in the export byte order: deployable widths, codes required
     assert L.pq_quantize_fwd(7, 4, 64, A, B, 2, None, None, A, None) == 3
     assert L.pq_quantize_fwd(2, 4, 64, A, B, 2, A, None, None, None) == 1
-    assert L.pq_quantize_fwd(2, 4, 64, A, B, 4, None, None, A, None) == 3         # unknown flag
+    assert L.pq_quantize_fwd(2, 4, 64, A, B, 4, None, None, A, None) == 3            # unknown flag
+
+
+def test_gemm_workspace_size_query(pq):
+    """The size query follows the kernel choice: none for the weight-streaming
+    path (M <= 16), split-K partials when the tiled path splits K, the
+    activation row sums for the large-M 2-bit path; -1 for bad arguments."""
+    q = pq.pq_gemm_workspace_bytes
+    for mode in range(7):
+        for M in (1, 4, 16):
+            assert q(mode, M, 16384, 16384) == 0
+    assert q(7, 1, 64, 64) == -1 and q(2, 1, 64, 60) == -1 and q(2, -1, 64, 64) == -1
+    assert q(2, 0, 64, 64) == 0 and q(2, 64, 0, 64) == 0
+    # 64 x 16384 output: 64 tiles of 64 x 256 do not fill the chip, so K is split
+    ws = q(2, 64, 16384, 16384)
+    assert ws > 0 and ws % (64 * 16384 * 4) == 0
+    # 1024 rows at K >= 2048: the large-M path's row sums, M * 4 rounded to 256
+    assert q(2, 1024, 8192, 2048) == 4096
+    assert q(2, 1100, 8200, 2112) == (1100 * 4 + 255) // 256 * 256
+    # a chip-filling tiled grid needs nothing
+    assert q(4, 4096, 16384, 256) == 0
+
+
+def test_gemm_workspace_checks(pq):
+    """A shape that needs a workspace rejects a missing, misaligned or short
+    one before anything is enqueued."""
+    L = pq.lib
+    M, N, K = 64, 16384, 16384
+    ws = pq.pq_gemm_workspace_bytes(2, M, N, K)
+    assert ws > 0
+    assert L.pq_w2a16_gemm(M, N, K, A, A, B, A, None, 0, None) == 1                  # missing
+    assert L.pq_w2a16_gemm(M, N, K, A, A, B, A, None, ws, None) == 1
+    assert L.pq_w2a16_gemm(M, N, K, A, A, B, A, MIS, ws, None) == 4                  # misaligned
+    assert L.pq_w2a16_gemm(M, N, K, A, A, B, A, B, ws - 16, None) == 7               # too small
+    assert L.pq_gemm_f32a(2, M, N, K, A, A, B, A, None, 0, None) == 1
+    assert L.pq_gemm(2, 1024, 8192, 2048, A, A, B, A, None, 0, None) == 1            # row sums
+    assert L.pq_gemm(2, 1024, 8192, 2048, A, A, B, A, B, 4095, None) == 7
+
+
+def test_library_holds_no_allocator():
+    """The GEMM sources call no device allocator and keep no per-stream cache."""
+    csrc = os.path.join(ROOT, "bit_quantization_aware_amd", "csrc")
+    for f in os.listdir(csrc):
+        src = open(os.path.join(csrc, f)).read()
+        for word in ("hipMalloc", "hipFree", "hipStreamSynchronize", "std::map", "std::mutex"):
+            assert word not in src, (f, word)
 
 
 def test_grouped_argument_checks(pq):
@@ -148,6 +196,17 @@ def test_grouped_argument_checks(pq):
     assert L.pq_quantize_fwd_grouped(2, -1, h, A, 0, None) == 7
     assert L.pq_quantize_fwd_grouped(2, 0, None, None, 0, None) == 0              # empty stack
     assert L.pq_quantize_bwd_grouped(2, 2, h, A, 0, None) == 1                    # G NULL
+    # grouped export: codes and alpha_bf16 required per matrix
+    assert L.pq_pack_grouped(2, 2, h, A, None) == 1
+    for m in mats:
+        m.codes, m.alpha_bf16 = A, B
+    assert L.pq_pack_grouped(7, 2, h, A, None) == 3                               # not deployable
+    assert L.pq_pack_grouped(2, 2, h, None, None) == 1                            # no device table
+    mats[1].alpha_bf16 = MIS
+    assert L.pq_pack_grouped(2, 2, h, A, None) == 4
+    mats[1].cols = 12
+    assert L.pq_pack_grouped(2, 2, h, A, None) == 2
+    assert L.pq_pack_grouped(2, 0, None, None, None) == 0                         # empty stack
 
 
 def test_qat_step_argument_checks(pq):
@@ -209,3 +268,18 @@ def test_diagnostics_argument_checks(pq):
     assert L.pq_weight_movement(4, 64, A, MIS, A, B, None) == 4
     assert L.pq_weight_movement(4, 64, A, B, None, B, None) == 1
     assert L.pq_weight_movement(-1, 64, A, B, A, B, None) == 2
+
+
+def test_launch_failure_reports_pq_err_hip(pq):
+    """With no usable device the launch itself fails, and every entry point
+    reports PQ_ERR_HIP instead of pretending success.  Runs only where no GPU
+    is visible: the fake addresses below would otherwise reach a kernel."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible: this check needs a host without one")
+    L = pq.lib
+    assert L.pq_quantize_fwd(2, 4, 64, A, B, 0, B, None, None, None) == 6
+    assert L.pq_quantize_bwd(2, 4, 64, A, B, A, 0, 1.0, B, B, None, None) == 6
+    assert L.pq_pack_w2(4, 64, A, A, B, A, None) == 6
+    assert L.pq_w2a16_gemm(1, 64, 64, A, A, B, A, None, 0, None) == 6
+    assert L.pq_w2a16_gemm(64, 16384, 16384, A, A, B, A, B, 1 << 30, None) == 6

@@ -425,3 +425,142 @@ def test_grouped_fwd_codes_in_export_order():
         _, _, codes_o = O.quantize_fwd(mode, W, a_o)
         assert_bits_equal(host(m["alpha"]), a_o, "alpha")
         assert_bits_equal(host(m["codes"]), O.tile_codes(codes_o), f"codes {W.shape}")
+
+
+# ----------------------------------------------------------------------------
+# The MobileLLM-1.5B stack at full size, the split of very large stacks, and
+# canary guards around every output
+# ----------------------------------------------------------------------------
+def _gen_1p5b(k):
+    return synth.weight("mobilellm_1p5b", k), synth.upstream_grad("mobilellm_1p5b", k)
+
+
+@pytest.mark.timeout(900)
+def test_mobilellm_1p5b_full_stack():
+    """All 378 matrices of the MobileLLM-1.5B-shaped stack (1,473,638,400
+    weights, 0.1 % outliers x10) through one grouped 2-bit fwd launch (alpha
+    init), one grouped bwd launch and one grouped export launch -- the
+    benchmark's launch configuration -- with every output of every matrix
+    checked against the oracle.  The inputs are regenerated on the host from
+    each matrix's seed stream for the comparison, so host memory holds one
+    chunk of matrices at a time."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    mode = O.SEQ2
+    shapes = synth.mobilellm_1p5b_shapes()
+    n = len(shapes)
+    assert n == 378 and sum(r * c for _, _, r, c in shapes) == 1473638400
+    print(f"[1.5B full stack: {n} matrices, upload]", flush=True)
+    mats = []
+    with ThreadPoolExecutor(16) as ex:
+        for c0 in range(0, n, 32):
+            for k, (W, G) in zip(range(c0, min(n, c0 + 32)), ex.map(_gen_1p5b, range(c0, min(n, c0 + 32)))):
+                rows, cols = W.shape
+                mats.append(dict(
+                    W=dev(W), G=dev(G), alpha=torch.zeros(rows, dtype=torch.float32, device="cuda"),
+                    wq_bf16=empty_bf16(rows, cols),
+                    codes=torch.empty(rows, cols // 4, dtype=torch.uint8, device="cuda"),
+                    dW=torch.empty(rows, cols, dtype=torch.float32, device="cuda"),
+                    dalpha=torch.empty(rows, dtype=torch.float32, device="cuda"),
+                    mask_bits=torch.empty(rows, cols // 8, dtype=torch.uint8, device="cuda"),
+                    packed=torch.full((pq.pq_packed_bytes(mode, rows, cols),), 0xA5, dtype=torch.uint8,
+                                      device="cuda"),
+                    alpha_bf16=empty_bf16(rows), grad_scale=pq.pq_default_grad_scale(mode, rows, cols),
+                    rows=rows, cols=cols))
+    fwd_t = pq.MatTable([{k: d[k] for k in ("W", "alpha", "wq_bf16", "codes", "rows", "cols")} for d in mats])
+    bwd_t = pq.MatTable([{k: d[k] for k in ("W", "alpha", "G", "dW", "dalpha", "mask_bits", "grad_scale",
+                                            "rows", "cols")} for d in mats])
+    exp_t = pq.MatTable([dict(W=d["W"], alpha=d["alpha"], codes=d["packed"], alpha_bf16=d["alpha_bf16"],
+                              rows=d["rows"], cols=d["cols"]) for d in mats])
+    print("[1.5B full stack: grouped fwd (init) + bwd + export]", flush=True)
+    pq.pq_quantize_fwd_grouped(mode, fwd_t, pq.PQ_INIT_ALPHA)
+    pq.pq_quantize_bwd_grouped(mode, bwd_t, pq.PQ_G_F32)
+    pq.pq_pack_grouped(mode, exp_t)
+    torch.cuda.synchronize()
+    print("[1.5B full stack: checking]", flush=True)
+    with ThreadPoolExecutor(4) as ex:
+        for c0 in range(0, n, 16):
+            ks = list(range(c0, min(n, c0 + 16)))
+            for k, (W, G) in zip(ks, ex.map(_gen_1p5b, ks)):
+                d = mats[k]
+                a_o = O.alpha_init(mode, W)
+                assert_bits_equal(host(d["alpha"]), a_o, f"1.5B[{k}] alpha")
+                wq_o, _, codes_o = O.quantize_fwd(mode, W, a_o)
+                assert_bits_equal(host(d["codes"]), codes_o, f"1.5B[{k}] codes")
+                assert_bits_equal(host(d["wq_bf16"]), wq_o, f"1.5B[{k}] wq")
+                dW_o, da_o, m_o = O.quantize_bwd(mode, W, a_o, G)
+                assert_bits_equal(host(d["mask_bits"]), m_o, f"1.5B[{k}] mask")
+                assert_bits_equal(host(d["dW"]), dW_o, f"1.5B[{k}] dW")
+                assert_rel(host(d["dalpha"]), da_o, 1e-5, np.float64(1e-35), f"1.5B[{k}] dalpha")
+                p_o, ab_o = O.pack(mode, W, a_o)
+                assert_bits_equal(host(d["packed"]), O.tile_codes(p_o), f"1.5B[{k}] packed")
+                assert_bits_equal(host(d["alpha_bf16"]), ab_o, f"1.5B[{k}] alpha bf16")
+            if c0 % 64 == 0:
+                print(f"[1.5B full stack: {min(n, c0 + 16)} of {n} checked]", flush=True)
+
+
+@pytest.mark.parametrize("mode", [O.SEQ2, O.BINARY, O.LSQ4])
+def test_grouped_stack_beyond_one_launch(mode):
+    """A stack of 1000 matrices: more than one launch table holds (448 per
+    launch), so the grouped calls split it into three launches; every output
+    of every matrix checked, fwd with alpha init, bwd and export."""
+    shapes = [(16, 64), (3, 8), (40, 136), (1, 8), (17, 72), (64, 256), (5, 16), (33, 40)]
+    mats = [synth.random_case(5000 + i, *shapes[i % len(shapes)]) for i in range(1000)]
+    print(f"[grouped 1000 matrices mode={mode}]", flush=True)
+    outs = run_grouped(mode, mats, init=True)
+    check_grouped(mode, mats, outs, f"1000-stack m{mode}")
+    # the same stack through the grouped export
+    dmats = []
+    for W, _ in mats:
+        rows, cols = W.shape
+        dmats.append(dict(W=dev(W), alpha=dev(O.alpha_init(mode, W)),
+                          codes=torch.full((pq.pq_packed_bytes(mode, rows, cols),), 0xA5, dtype=torch.uint8,
+                                           device="cuda"), alpha_bf16=empty_bf16(rows), rows=rows, cols=cols))
+    pq.pq_pack_grouped(mode, pq.MatTable(dmats))
+    torch.cuda.synchronize()
+    for i, ((W, _), d) in enumerate(zip(mats, dmats)):
+        p_o, ab_o = O.pack(mode, W, O.alpha_init(mode, W))
+        assert_bits_equal(host(d["codes"]), O.tile_codes(p_o), f"1000-stack[{i}] packed")
+        assert_bits_equal(host(d["alpha_bf16"]), ab_o, f"1000-stack[{i}] alpha bf16")
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("shape", [(37, 72), (5, 8), (4100, 24), (1, 16384), (70, 4352)])
+def test_outputs_stay_inside_their_buffers(mode, shape):
+    """Every fwd / bwd / export output sits between 256-byte canary guards
+    (0xA5); after the calls the guards are intact and the outputs match the
+    oracle (ragged rows, one row, many short rows, long rows)."""
+    from gpu_util import Guarded
+
+    rows, cols = shape
+    W, G = synth.random_case(6000 + rows + cols + mode, rows, cols)
+    a_o = O.alpha_init(mode, W)
+    alpha = Guarded((rows,), torch.float32)
+    wq = Guarded((rows, cols), torch.bfloat16)
+    wq32 = Guarded((rows, cols), torch.float32)
+    codes = Guarded((rows, pq.pq_code_row_bytes(mode, cols)), torch.uint8)
+    pq.pq_quantize_fwd(mode, rows, cols, dev(W), alpha.t, pq.PQ_INIT_ALPHA, wq.t, wq32.t, codes.t)
+    dW = Guarded((rows, cols), torch.float32)
+    da = Guarded((rows,), torch.float32)
+    mask = Guarded((rows, cols // 8), torch.uint8)
+    pq.pq_quantize_bwd(mode, rows, cols, dev(W), dev(a_o), dev(G), pq.PQ_G_F32,
+                       pq.pq_default_grad_scale(mode, rows, cols), dW.t, da.t, mask.t)
+    packed = Guarded((pq.pq_packed_bytes(mode, rows, cols),), torch.uint8)
+    ab = Guarded((rows,), torch.bfloat16)
+    pq.pq_pack(mode, rows, cols, dev(W), dev(a_o), packed.t, ab.t)
+    torch.cuda.synchronize()
+    for name, g in (("alpha", alpha), ("wq_bf16", wq), ("wq_f32", wq32), ("codes", codes), ("dW", dW),
+                    ("dalpha", da), ("mask", mask), ("packed", packed), ("alpha_bf16", ab)):
+        g.check(f"m{mode} {shape} {name}")
+    wq_o, wq32_o, codes_o = O.quantize_fwd(mode, W, a_o)
+    assert_bits_equal(host(alpha.t), a_o, "alpha")
+    assert_bits_equal(host(codes.t), codes_o, "codes")
+    assert_bits_equal(host(wq.t), wq_o, "wq")
+    assert_bits_equal(host(wq32.t), wq32_o, "wq32")
+    dW_o, da_o, m_o = O.quantize_bwd(mode, W, a_o, G)
+    assert_bits_equal(host(dW.t), dW_o, "dW")
+    assert_bits_equal(host(mask.t), m_o, "mask")
+    assert_rel(host(da.t), da_o, 1e-5, np.float64(1e-35), "dalpha")
+    p_o, ab_o = O.pack(mode, W, a_o)
+    assert_bits_equal(host(packed.t), O.tile_codes(p_o), "packed")
+    assert_bits_equal(host(ab.t), ab_o, "alpha bf16")
