@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpq.so")
-SOURCES = ["pq_quant.hip", "pq_gemm.hip", "pq_gemm_big.hip", "pq_stats.hip"]
+SOURCES = ["pq_quant.hip", "pq_gemm.hip", "pq_gemm_big.hip", "pq_stats.hip", "pq_noalloc.hip"]
 ARCH = "gfx950"
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -1069,6 +1069,20 @@ pq_status gemm_dispatch(int mode, int64_t M, int64_t N, int64_t K, const void *X
 }
 
 }  // namespace
+
+int64_t gemm_workspace_need(int mode, int64_t M, int64_t N, int64_t K)
+{
+    LevelMap lm;
+    if (!level_map(mode, &lm) || !gemm_shape_ok(M, N, K)) return -1;
+    return gemm_ws_bytes(lm.bits, M, N, K);
+}
+
+pq_status gemm_run(int mode, int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *packed,
+                   const void *alpha_bf16, void *Y, void *workspace, int64_t workspace_bytes, void *stream)
+{
+    return gemm_dispatch(mode, M, N, K, X, packed, alpha_bf16, nullptr, Y, workspace, workspace_bytes, stream);
+}
+
 }  // namespace pq
 
 extern "C" {

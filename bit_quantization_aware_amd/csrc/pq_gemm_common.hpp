@@ -148,6 +148,12 @@ __device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w)
 
 }  // namespace
 
+// pq_gemm with a given workspace (pq_gemm.hip), and the workspace bytes a
+// shape needs (-1 for an unknown mode or a rejected shape).
+pq_status gemm_run(int mode, int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *packed,
+                   const void *alpha_bf16, void *Y, void *workspace, int64_t workspace_bytes, void *stream);
+int64_t gemm_workspace_need(int mode, int64_t M, int64_t N, int64_t K);
+
 // Large-M 2-bit path (pq_gemm_big.hip): whether it takes a GEMM of this
 // shape, and its launch (rowsum: the [M] activation row sums).
 bool gemm_big_takes(int bits, int64_t M, int64_t N, int64_t K);

@@ -35,7 +35,7 @@ EXPORTS = ("pq_code_row_bytes", "pq_packed_bytes", "pq_default_grad_scale", "pq_
            "pq_quantize_fwd", "pq_quantize_bwd", "pq_pack_w2", "pq_pack_w4", "pq_w2a16_gemm",
            "pq_w4a16_gemm", "pq_quantize_fwd_grouped", "pq_quantize_bwd_grouped", "pq_qat_step",
            "pq_qat_step_grouped", "pq_pack", "pq_gemm", "pq_gemm_f32a", "pq_num_levels", "pq_level_stats",
-           "pq_quantize_fwd_stats", "pq_weight_movement", "pq_pack_grouped")
+           "pq_quantize_fwd_stats", "pq_weight_movement", "pq_pack_grouped", "pq_gemm_noalloc")
 
 
 class PQError(RuntimeError):
@@ -94,6 +94,7 @@ def _load():
     L.pq_pack.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp]
     L.pq_gemm.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, i64, vp]
     L.pq_gemm_f32a.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, i64, vp]
+    L.pq_gemm_noalloc.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp]
     L.pq_num_levels.argtypes = [i32]
     L.pq_num_levels.restype = i32
     L.pq_level_stats.argtypes = [i32, i64, i64, vp, vp, vp, vp]
@@ -236,6 +237,15 @@ def pq_gemm_f32a(mode, M, N, K, X, packed, alpha, Y, stream=None, workspace=None
     wp, wb, _keep = _ws(mode, M, N, K, X, workspace, stream)
     _check(lib.pq_gemm_f32a(mode, M, N, K, _ptr(X), _ptr(packed), _ptr(alpha), _ptr(Y), wp, wb,
                             _stream(stream)), "pq_gemm_f32a")
+
+
+PQ_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def pq_gemm_noalloc(mode, M, N, K, X, packed, alpha_bf16, Y, stream=None) -> None:
+    """pq_gemm with the library's fixed scratch instead of a workspace."""
+    _check(lib.pq_gemm_noalloc(mode, M, N, K, _ptr(X), _ptr(packed), _ptr(alpha_bf16), _ptr(Y),
+                               _stream(stream)), "pq_gemm_noalloc")
 
 
 PQ_CODES_EXPORT = 2

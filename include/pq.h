@@ -20,8 +20,10 @@
  *              the library keeps no pointer after the call returns and never
  *              allocates or frees device memory: the GEMM's scratch (split-K
  *              partial sums, activation row sums) is a caller-owned
- *              workspace sized by pq_gemm_workspace_bytes.  Arrays are
- *              row-major and contiguous
+ *              workspace sized by pq_gemm_workspace_bytes.  The one
+ *              exception is pq_gemm_noalloc, whose scratch is a fixed array
+ *              inside the library (see there).  Arrays are row-major and
+ *              contiguous
  *              (leading dimension = cols), except the exported codes of
  *              pq_pack_w2 / pq_pack_w4 (the export byte order below).  Weight matrices are [out, in]:
  *              a "row" is one output channel, the unit the scale alpha
@@ -29,10 +31,11 @@
  *              row, shape (rows, 1)).
  *   Streams    `stream` is a hipStream_t (NULL = the null stream).  Calls only
  *              enqueue work on it and return, without waiting on the host;
- *              results are ready when the stream is.  The library holds no
- *              global mutable state, so calls from several host threads are
- *              safe, and every call can be captured into a HIP graph
- *              (including its first call).
+ *              results are ready when the stream is.  Apart from
+ *              pq_gemm_noalloc's scratch the library holds no global mutable
+ *              state, so calls from several host threads are safe, and every
+ *              call can be captured into a HIP graph (including its first
+ *              call).
  *   bf16       bf16 arrays are passed as void* and hold IEEE bfloat16 bit
  *              patterns; every cast to bf16 rounds to nearest-even.
  *   Errors     Arguments are checked on the host before anything is enqueued:
@@ -332,6 +335,27 @@ pq_status pq_gemm(int mode, int64_t M, int64_t N, int64_t K, const void *X,
 pq_status pq_gemm_f32a(int mode, int64_t M, int64_t N, int64_t K, const void *X,
                        const uint8_t *packed, const float *alpha, void *Y,
                        void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * pq_gemm_noalloc -- pq_gemm for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, kernels and results as pq_gemm, without the
+ * workspace: the scratch the kernels need (split-K partial sums, activation
+ * row sums; pq_gemm_workspace_bytes of the shape) is a fixed array of
+ * PQ_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, looked up
+ * on the first call made on that GPU and held until the process ends.  The
+ * call allocates nothing and never waits on the host.
+ *   A shape whose scratch need exceeds PQ_NOALLOC_SCRATCH_BYTES ->
+ *   PQ_ERR_UNSUPPORTED, with nothing enqueued (use pq_gemm with a workspace).
+ *   Other errors as pq_gemm.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (no part of it needs to start at zero): calls that overlap on one
+ * GPU (on different streams, or from different host threads) race on it and
+ * must be serialised by the caller.
+ */
+#define PQ_NOALLOC_SCRATCH_BYTES (((int64_t)32) << 20)
+pq_status pq_gemm_noalloc(int mode, int64_t M, int64_t N, int64_t K, const void *X,
+                          const uint8_t *packed, const void *alpha_bf16, void *Y, void *stream);
 
 /*
  * Grouped launches: one kernel launch over a whole stack of matrices (for

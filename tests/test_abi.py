@@ -283,3 +283,18 @@ def test_launch_failure_reports_pq_err_hip(pq):
     assert L.pq_pack_w2(4, 64, A, A, B, A, None) == 6
     assert L.pq_w2a16_gemm(1, 64, 64, A, A, B, A, None, 0, None) == 6
     assert L.pq_w2a16_gemm(64, 16384, 16384, A, A, B, A, B, 1 << 30, None) == 6
+
+
+def test_gemm_noalloc_argument_checks(pq):
+    """pq_gemm_noalloc validates like pq_gemm and rejects, before anything
+    is enqueued, a shape whose scratch need exceeds the library's array."""
+    L = pq.lib
+    assert pq.PQ_NOALLOC_SCRATCH_BYTES == 32 << 20
+    assert L.pq_gemm_noalloc(7, 4, 8, 64, A, A, B, A, None) == 3                    # mode
+    assert L.pq_gemm_noalloc(2, 4, 8, 60, A, A, B, A, None) == 2                    # K % 64
+    assert L.pq_gemm_noalloc(2, 4, 8, 64, None, A, B, A, None) == 1                 # X NULL
+    assert L.pq_gemm_noalloc(2, 4, 8, 64, A, MIS, B, A, None) == 4                  # align
+    assert L.pq_gemm_noalloc(2, 0, 8, 64, A, A, B, A, None) == 0                    # empty
+    assert pq.pq_gemm_workspace_bytes(2, 300, 16384, 16384) > pq.PQ_NOALLOC_SCRATCH_BYTES
+    assert L.pq_gemm_noalloc(2, 300, 16384, 16384, A, A, B, A, None) == 5           # scratch too small
+    assert pq.pq_gemm_workspace_bytes(2, 64, 16384, 16384) <= pq.PQ_NOALLOC_SCRATCH_BYTES

@@ -1,0 +1,106 @@
+"""pq_gemm_noalloc -- the GEMM entry point that allocates nothing (its
+scratch is the library's fixed per-GPU array) -- against pq_gemm with a
+caller's workspace on the same inputs, through the C ABI: bit for bit (the
+same kernels), and within the GEMM bar of the binary64 oracle.  Two calls in
+a row, the second with a smaller input, for each path that uses scratch
+(split-K partials; activation row sums) and one that uses none; and a call
+captured into a HIP graph with no warm-up."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from bit_quantization_aware_amd import synth
+
+from gpu_util import dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pq():
+    from bit_quantization_aware_amd import pq as _pq
+    assert torch.cuda.is_available()
+    O.set_threads(16)
+    return _pq
+
+
+def case(mode, seed, M, N, K):
+    rng = np.random.default_rng(seed)
+    W = synth.normal_f32(rng, (N, K), 0.02)
+    alpha = O.alpha_init(mode, W)
+    packed, ab = O.pack(mode, W, alpha)
+    X = synth.to_bf16_bits(synth.normal_f32(rng, (M, K)))
+    return X, packed, ab
+
+
+def both(pq, mode, X, packed, ab, N):
+    M, K = X.shape
+    Xd, Pd, Ad = dev(X), dev(O.tile_codes(packed)), dev(ab)
+    Y1 = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    Y2 = torch.full((M, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    pq.pq_gemm(mode, M, N, K, Xd, Pd, Ad, Y1)
+    rc = pq.lib.pq_gemm_noalloc(mode, M, N, K, Xd.data_ptr(), Pd.data_ptr(), Ad.data_ptr(), Y2.data_ptr(),
+                                torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, pq.pq_status_str(rc)
+    torch.cuda.synchronize()
+    return host(Y1), host(Y2)
+
+
+def check_ref(Yb, X, packed, ab, N, mode, what):
+    Y = synth.bf16_bits_to_f32(Yb).astype(np.float64)
+    M = Y.shape[0]
+    rng = np.random.default_rng(M + N)
+    ms = np.concatenate([[0, M - 1], rng.integers(0, M, 1500)])
+    ns = np.concatenate([[0, N - 1], rng.integers(0, N, 1500)])
+    ref = O.gemm_ref_at(mode, X, packed, ab, N, ms, ns)
+    rms = np.sqrt(np.mean(ref ** 2))
+    for rel in (2e-2, 4e-3):
+        assert np.all(np.abs(Y[ms, ns] - ref) <= rel * np.maximum(np.abs(ref), rms)), f"{what}: outside {rel}"
+
+
+@pytest.mark.parametrize("mode,first,second", [
+    (O.SEQ2, (64, 16384, 16384), (64, 2048, 2048)),        # split-K partials: 32 MiB, then a smaller split
+    (O.SEQ2, (1024, 8192, 2048), (520, 16202, 2048)),      # activation row sums
+    (O.LSQ4, (100, 4096, 4096), (33, 512, 1024)),          # 4-bit tiles with and without a split
+    (O.SEQ2, (16, 8192, 4096), (1, 1000, 1024)),           # weight streaming: no scratch
+])
+def test_noalloc_matches_workspace_gemm_twice(pq, mode, first, second):
+    for k, (M, N, K) in enumerate((first, second)):
+        print(f"[noalloc mode={mode} M={M} N={N} K={K}]", flush=True)
+        assert pq.pq_gemm_workspace_bytes(mode, M, N, K) <= pq.PQ_NOALLOC_SCRATCH_BYTES
+        X, packed, ab = case(mode, 40 + 3 * k + M, M, N, K)
+        Y1, Y2 = both(pq, mode, X, packed, ab, N)
+        assert np.array_equal(Y1, Y2), f"call {k}: noalloc differs from the workspace GEMM"
+        check_ref(Y2, X, packed, ab, N, mode, f"noalloc call {k}")
+
+
+def test_noalloc_graph_capture_first_call(pq):
+    """A pq_gemm_noalloc call captured before any eager call, replayed with
+    eager work between replays, equals the eager result every time."""
+    M, N, K = 64, 2048, 2048
+    X, packed, ab = case(O.SEQ2, 77, M, N, K)
+    Xd, Pd, Ad = dev(X), dev(O.tile_codes(packed)), dev(ab)
+    Yg = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        rc = pq.lib.pq_gemm_noalloc(O.SEQ2, M, N, K, Xd.data_ptr(), Pd.data_ptr(), Ad.data_ptr(), Yg.data_ptr(),
+                                    side.cuda_stream)
+    assert rc == 0
+    Ye = torch.empty_like(Yg)
+    pq.pq_gemm(O.SEQ2, M, N, K, Xd, Pd, Ad, Ye)
+    torch.cuda.synchronize()
+    for r in range(3):
+        Yg.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Yg.view(torch.int16), Ye.view(torch.int16)), f"replay {r}"
+        torch.randn(1 << 20, device="cuda").mul_(3.0)
+        torch.cuda.synchronize()
+    check_ref(host(Ye), X, packed, ab, N, O.SEQ2, "graph")
+    del g
