@@ -85,15 +85,29 @@ def parse():
 
 # Sources whose kernels each bench kernel runs: the traffic recorded for a
 # kernel is reported only while these files are unchanged.
-KERNEL_SOURCES = {
-    "fwd": ("pq_quant.hip", "pq_common.hpp"),
-    "bwd": ("pq_quant.hip", "pq_common.hpp"),
-    "pack": ("pq_quant.hip", "pq_common.hpp"),
-    "qat_step": ("pq_quant.hip", "pq_common.hpp"),
-}
+_QUANT_SOURCES = ("pq_quant.hip", "pq_quant_kernels.hpp", "pq_quant_mode.hip", "pq_common.hpp")
+KERNEL_SOURCES = {"fwd": _QUANT_SOURCES, "bwd": _QUANT_SOURCES, "pack": _QUANT_SOURCES, "qat_step": _QUANT_SOURCES}
 for _m in (1, 4, 16, 64, 512):
     KERNEL_SOURCES[f"gemm_m{_m}"] = ("pq_gemm.hip", "pq_gemm_big.hip", "pq_gemm_common.hpp", "pq_common.hpp")
 CALIB_BYTES = 1 << 30   # the calibration copy reads and writes 1 GiB
+# --pmc-workload: the step entries in this order, each called PMC_CALLS times
+# between marker launches
+PMC_KEYS = ("fwd", "bwd", "pack") + tuple(f"gemm_m{M}" for M in (512, 64, 16, 4, 1))
+PMC_CALLS = 3
+MARKER = "k_weight_movement"
+
+
+def pmc_segments(dispatches):
+    """Split [(name, counters)] of a --pmc-workload run at the marker
+    launches: {key: [counters of every launch of that key's calls]}, and the
+    launches before the first marker (the fused step's and the calibration
+    copies)."""
+    idx = [i for i, (n, _) in enumerate(dispatches) if MARKER in n]
+    if len(idx) < len(PMC_KEYS) + 1:
+        raise SystemExit(f"expected {len(PMC_KEYS) + 1} marker launches, found {len(idx)}")
+    idx = idx[-(len(PMC_KEYS) + 1):]
+    seg = {k: [c for _, c in dispatches[idx[j] + 1:idx[j + 1]]] for j, k in enumerate(PMC_KEYS)}
+    return seg, dispatches[:idx[0]]
 
 
 def source_sha(kernel):
@@ -165,74 +179,65 @@ def gemm_bytes(M, N, K, bits):
     return N * K * bits / 8 + 2 * N + 2 * M * K + 2 * M * N
 
 
-def pmc_summarize(args):
-    """Per-kernel HBM bytes from the FETCH_SIZE and WRITE_SIZE passes of
-    --pmc-workload, scaled by what each counter reads for the 1 GiB copy."""
+def load_pmc(d, counters):
+    """[(kernel name, {counter: value summed over the dispatch's rows})] in
+    dispatch order, from a rocprofv3 --pmc csv run under directory d."""
     import csv
     import glob
 
-    def load(d, counter):
-        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
-        if not f:
-            raise SystemExit(f"no counter_collection.csv under {d}")
-        rows = [r for r in csv.DictReader(open(f[0])) if r["Counter_Name"] == counter]
-        per = {}
-        for r in rows:
-            key = int(r["Dispatch_Id"])
-            e = per.setdefault(key, [r["Kernel_Name"], 0.0])
-            e[1] += float(r["Counter_Value"])
-        return [per[k] for k in sorted(per)]
+    f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not f:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    per = {}
+    for r in csv.DictReader(open(f[0])):
+        if r["Counter_Name"] not in counters:
+            continue
+        e = per.setdefault(int(r["Dispatch_Id"]), (r["Kernel_Name"], {}))
+        e[1][r["Counter_Name"]] = e[1].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return [per[k] for k in sorted(per)]
 
-    fetch = load(args.pmc_summarize[0], "FETCH_SIZE")
-    write = load(args.pmc_summarize[1], "WRITE_SIZE")
 
-    def last(seq, pred, n):
-        hits = [v for name, v in seq if pred(name)]
-        return hits[-n:] if len(hits) >= n else None
+def pmc_summarize(args):
+    """HBM bytes per call of each step entry from the FETCH_SIZE and
+    WRITE_SIZE passes of --pmc-workload (every launch of the call summed:
+    the quantizer's launches per team class, the M = 64 split-K finalize,
+    the M = 512 row-sum pass), each counter scaled by what it reads for the
+    1 GiB copy; and the fused step's."""
+    fetch = load_pmc(args.pmc_summarize[0], ("FETCH_SIZE",))
+    write = load_pmc(args.pmc_summarize[1], ("WRITE_SIZE",))
+    fseg, fpre = pmc_segments(fetch)
+    wseg, wpre = pmc_segments(write)
 
-    copy_pred = lambda n: "copy" in n.lower() and "pq::" not in n
-    groups = {
-        "fwd": lambda n: "k_quant_fwd<2, false, 1, 5u>" in n,
-        "bwd": lambda n: "k_quant_bwd<2, 1, false, true, false>" in n,
-        "pack": lambda n: re.search(r"k_quant_fwd<2, false, \d, 28u>", n) is not None,
-        # k_gemm_stream<BITS, TN, NW, D, XI>: M = 1, 4, 16 use XI = 1, 2, 8
-        "gemm_m1": lambda n: re.search(r"k_gemm_stream<2, \d+, \d+, \d+, 1>", n) is not None,
-        "gemm_m4": lambda n: re.search(r"k_gemm_stream<2, \d+, \d+, \d+, 2>", n) is not None,
-        "gemm_m16": lambda n: re.search(r"k_gemm_stream<2, \d+, \d+, \d+, 8>", n) is not None,
-        "qat_step": lambda n: "k_qat_step<2, 1, false>" in n,
-    }
-    # the calibration copies: the three largest copy dispatches (the fused
-    # step measurement also clones tensors)
-    def calib(seq):
-        vals = sorted((v for name, v in seq if copy_pred(name)), reverse=True)
+    # the calibration copies: the three largest copy dispatches before the
+    # first marker (the fused step measurement also clones tensors)
+    def calib(seq, c):
+        vals = sorted((v[c] for name, v in seq if "copy" in name.lower() and "pq::" not in name), reverse=True)
         return vals[:3] if len(vals) >= 3 else None
 
-    cf, cw_ = calib(fetch), calib(write)
+    cf, cw_ = calib(fpre, "FETCH_SIZE"), calib(wpre, "WRITE_SIZE")
     if not cf or not cw_:
         raise SystemExit("calibration copy dispatches not found")
     fscale = CALIB_BYTES / (np.mean(cf) * 1024.0)
     wscale = CALIB_BYTES / (np.mean(cw_) * 1024.0)
     res = {}
-    for k, pred in groups.items():
-        f, w = last(fetch, pred, 3), last(write, pred, 3)
-        if f and w:
-            res[k] = (np.mean(f), np.mean(w))
-    # M = 64: the tiled kernel and its split-K finalize; M = 512: the
-    # large-M kernel and its row-sum pass
-    for key, parts in (("gemm_m64", ("k_gemm_tile<2,", "k_splitk_finalize")),
-                       ("gemm_m512", ("k_gemm_big2<2>", "k_rowsum"))):
-        f = [last(fetch, lambda n, t=t: t in n, 3) for t in parts]
-        w = [last(write, lambda n, t=t: t in n, 3) for t in parts]
-        if all(f) and all(w):
-            res[key] = (sum(np.mean(x) for x in f), sum(np.mean(x) for x in w))
+    for k in PMC_KEYS:
+        res[k] = (sum(c["FETCH_SIZE"] for c in fseg[k]) / PMC_CALLS,
+                  sum(c["WRITE_SIZE"] for c in wseg[k]) / PMC_CALLS)
+    # the fused step: its last three launches before the calibration
+    sf = [v["FETCH_SIZE"] for n, v in fpre if "k_qat_step<2," in n][-3:]
+    sw = [v["WRITE_SIZE"] for n, v in wpre if "k_qat_step<2," in n][-3:]
+    if len(sf) == 3 and len(sw) == 3:
+        res["qat_step"] = (float(np.mean(sf)), float(np.mean(sw)))
     lines = [
         "# HBM traffic per launch of the bench.py step kernels (rocprofv3 PMC)",
         "",
         "Counters: `FETCH_SIZE` and `WRITE_SIZE` (KiB per dispatch), each collected in its own",
         "rocprofv3 pass over `bench.py --pmc-workload` (one MI355X). Each counter is scaled by what",
         "it reads for a plain 1 GiB device copy in the same run (1 GiB read, 1 GiB written):",
-        f"FETCH scale = {fscale:.4f}, WRITE scale = {wscale:.4f}. Means over the last three launches",
-        "of each kernel; gemm_m64 adds its split-K finalize launch, gemm_m512 its row-sum pass.",
+        f"FETCH scale = {fscale:.4f}, WRITE scale = {wscale:.4f}. Per call of each step entry (the mean of",
+        "three calls): every launch of the call summed -- the quantizer's launch per team class, the M = 64",
+        "split-K finalize, the M = 512 row-sum pass. fwd, bwd and pack are the 1.5B stack's; qat_step the",
+        "125M stack's fused step.",
         "`sha` is the hash of the kernel sources the counters were taken on (bench.py reports",
         "`traffic` only while it matches).",
         "",
@@ -298,6 +303,79 @@ def build_stack(torch, pq, cfg, mode, dev, export=False):
         et = pq.MatTable([dict(W=m["W"], alpha=m["alpha"], codes=m["packed"], alpha_bf16=m["alpha_bf16"],
                                rows=m["rows"], cols=m["cols"]) for m in mats])
     return mats, ft, bt, et
+
+
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU",
+                 "SQ_INSTS_MFMA", "SQ_BUSY_CYCLES", "SQ_INSTS_LDS", "SQ_ACTIVE_INST_VALU")
+SIMD_NUM = 1024   # 256 CUs x 4 SIMDs
+XCDS = 8          # GRBM_GUI_ACTIVE comes summed over the 8 XCDs
+# kernel-name parts of each GEMM of the step (M = 64 adds its split-K finalize,
+# M = 512 its row-sum pass)
+GEMM_PARTS = {
+    "gemm_m1": (r"k_gemm_stream<2, \d+, \d+, \d+, 1>",),
+    "gemm_m4": (r"k_gemm_stream<2, \d+, \d+, \d+, 2>",),
+    "gemm_m16": (r"k_gemm_stream<2, \d+, \d+, \d+, 8>",),
+    "gemm_m64": (r"k_gemm_tile<2,", r"k_splitk_finalize"),
+    "gemm_m512": (r"k_gemm_big2<2>", r"k_rowsum"),
+}
+
+
+def mfma_summarize(args):
+    """MFMA utilisation of the step's GEMMs from one rocprofv3 --pmc pass of
+    MFMA_COUNTERS over --pmc-workload: MfmaUtil = sum over SIMDs of
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDS * SIMD_NUM), the
+    counter tool's definition (its max over XCDs taken as the per-XCD mean
+    of the summed value); flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512."""
+    disp = load_pmc(args.mfma_summarize, MFMA_COUNTERS)
+    seg, _ = pmc_segments(disp)
+    rows = {}
+    for key in PMC_KEYS:
+        if not key.startswith("gemm"):
+            continue
+        tot = {c: sum(d.get(c, 0.0) for d in seg[key]) / PMC_CALLS for c in MFMA_COUNTERS}
+        M = int(key.split("m")[-1])
+        busy, gui = tot["SQ_VALU_MFMA_BUSY_CYCLES"], tot["GRBM_GUI_ACTIVE"] / XCDS
+        mfma = tot["SQ_INSTS_MFMA"]
+        rows[key] = dict(
+            util=busy / (gui * SIMD_NUM) if gui else 0.0,
+            flops_counted=tot["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512,
+            flops_needed=2.0 * M * GEMM_NK * GEMM_NK,
+            valu_per_mfma=(tot["SQ_INSTS_VALU"] - mfma) / mfma if mfma else 0.0,
+            lds_per_mfma=tot["SQ_INSTS_LDS"] / mfma if mfma else 0.0,
+            valu_active=tot["SQ_ACTIVE_INST_VALU"] / (gui * SIMD_NUM) if gui else 0.0,
+            gui=gui)
+    lines = [
+        "# MFMA utilisation of the bench.py step GEMMs (16384 x 16384, 2-bit; rocprofv3 PMC)",
+        "",
+        "One rocprofv3 `--pmc` pass of the counters below over `bench.py --pmc-workload` (one MI355X),",
+        "per call (mean of three; M = 64 adds its split-K finalize, M = 512 its row-sum pass).",
+        "`util` = sum over SIMDs of SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x",
+        f"{SIMD_NUM} SIMDs) -- the counter tool's MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES counts 16 cycles per",
+        "16x16x32 bf16 MFMA); GRBM_GUI_ACTIVE includes the launch's ramp, so short launches read low;",
+        "`flops counted` = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512,",
+        "`flops needed` = 2 M N K (the kernels pad M to 16-row MFMA tiles, so small M counts more);",
+        "`VALU/MFMA` = (SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA, the decode and bookkeeping",
+        "issued per MFMA; `LDS/MFMA` likewise; `VALU active` = SQ_ACTIVE_INST_VALU per SIMD-cycle;",
+        "`GUI cycles` = GRBM_GUI_ACTIVE / 8.",
+        "`sha` is the hash of the GEMM sources the counters were taken on (bench.py reports",
+        "`mfma_util` per GEMM only while it matches).",
+        "",
+        "Command:",
+        "```",
+    ] + [c for c in args.pmc_command.split(";;") if c] + [
+        "```",
+        "",
+        "| kernel | sha | util | flops counted | flops needed | VALU/MFMA | LDS/MFMA | VALU active | GUI cycles |",
+        "|---|---|---|---|---|---|---|---|---|",
+    ]
+    for k, r in rows.items():
+        lines.append(f"| {k} | {source_sha(k)} | {r['util']:.4f} | {r['flops_counted']:.4g} | "
+                     f"{r['flops_needed']:.4g} | {r['valu_per_mfma']:.2f} | {r['lds_per_mfma']:.2f} | "
+                     f"{r['valu_active']:.3f} | {r['gui']:.0f} |")
+    os.makedirs(os.path.dirname(args.mfma_out), exist_ok=True)
+    with open(args.mfma_out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def main():
@@ -397,12 +475,23 @@ def main():
     init_ms = e0.elapsed_time(e1)
 
     if args.pmc_workload:
+        # the fused step's own launches first (it runs unfused comparisons
+        # too), then a 1 GiB copy for the counter calibration, then every
+        # step entry three times, each entry's launches between two marker
+        # launches (k_weight_movement on 64 weights, used nowhere else here)
+        qat = qat_step_measure(torch, pq, stack, ftab, btab, stream, reps=3)
+        print("pmc workload: qat_step", flush=True)
         src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).uniform_()
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+        mk = torch.zeros(64, device=dev)
+        mk2 = torch.zeros(8, dtype=torch.float64, device=dev)
+
+        def marker():
+            pq.pq_weight_movement(8, 8, mk, mk, mk2, mk2)
         launches = {
             "fwd": lambda: pq.pq_quantize_fwd_grouped(mode, ftab3, 0),
             "bwd": lambda: pq.pq_quantize_bwd_grouped(mode, btab3, pq.PQ_G_F32),
@@ -412,13 +501,13 @@ def main():
             launches[f"gemm_m{M}"] = (lambda M=M, j=j: pq.pq_w2a16_gemm(
                 M, GEMM_NK, GEMM_NK, Xs[M], packed[1 + j % (ROTATE - 1)], ab16[1 + j % (ROTATE - 1)], Ys[M],
                 workspace=wsa[M]))
-        for k in kernels:
-            for _ in range(3):
+        marker()
+        for k in PMC_KEYS:
+            for _ in range(PMC_CALLS):
                 launches[k]()
+            marker()
             torch.cuda.synchronize()
-            print(f"pmc workload: {k} x3", flush=True)
-        qat_step_measure(torch, pq, stack, ftab, btab, stream, reps=3)
-        print("pmc workload: qat_step", flush=True)
+            print(f"pmc workload: {k} x{PMC_CALLS}", flush=True)
         return
 
     def step(it, evs):

@@ -20,6 +20,9 @@ CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpq.so")
 SOURCES = ["pq_quant.hip", "pq_gemm.hip", "pq_gemm_big.hip", "pq_stats.hip", "pq_noalloc.hip"]
+# the quantizer's kernels, one translation unit per mode (PQ_W1_BINARY .. PQ_W158_LSQ)
+MODE_SOURCE = "pq_quant_mode.hip"
+NUM_MODES = 7
 ARCH = "gfx950"
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -34,16 +37,17 @@ def _hipcc() -> str:
     return "hipcc"
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(unit, verbose: bool) -> str:
+    src, defines, tag = unit
+    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + tag + ".o")
+    cmd = [_hipcc(), *CFLAGS, *defines, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass warns that it does not know the packed-fp32-ops feature
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {src}:\n{err}")
+        raise RuntimeError(f"hipcc failed on {src} {' '.join(defines)}:\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
     return obj
@@ -51,8 +55,11 @@ def _compile(src: str, verbose: bool) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    units = [(s, [], "") for s in SOURCES]
+    units += [(MODE_SOURCE, [f"-DPQ_QUANT_MODE={m}"], f"_{m}") for m in range(NUM_MODES)]
+    workers = max(1, min(len(units), os.cpu_count() or 1))
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        objs = list(ex.map(lambda u: _compile(u, verbose), units))
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

@@ -53,8 +53,9 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16)
 }
 
 // Launch table for the quantizer kernels: one launch covers `count` matrices;
-// matrix k owns blocks [block_start[k], block_start[k+1]).  It travels in the
-// kernel-argument segment, so the per-block lookup is a few scalar-cache hits.
+// launch entry k is descriptor idx[k] of the table and owns blocks
+// [block_start[k], block_start[k+1]).  It travels in the kernel-argument
+// segment, so the per-block lookup is a few scalar-cache hits.
 constexpr int kMaxGroup = 448;
 
 template <typename D>
@@ -63,6 +64,8 @@ struct LaunchTableT {
     D single;
     int count;
     int32_t block_start[kMaxGroup + 1];
+    int16_t idx[kMaxGroup];
+    int nt_out;      // forward: write the outputs with nontemporal stores
 };
 using LaunchTable = LaunchTableT<pq_mat>;
 using StepTable = LaunchTableT<pq_step_mat>;

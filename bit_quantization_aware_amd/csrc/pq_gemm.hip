@@ -59,6 +59,14 @@
 #ifndef PQ_STREAM_NW
 #define PQ_STREAM_NW 4
 #endif
+// 2-bit streaming configurations with at most this many activation DMAs per
+// group (M <= 4) use eight waves per block, two per SIMD, so that one wave's
+// decode overlaps the other's MFMAs and DMA waits (measured at 16384^2:
+// M = 1 16.0 -> 14.7 us, M = 4 17.4 -> 16.1 us, with two stages in flight
+// per wave instead of three); 0: none do.
+#ifndef PQ_STREAM_NW8_XI
+#define PQ_STREAM_NW8_XI 2
+#endif
 #ifndef PQ_STREAM_TN
 #define PQ_STREAM_TN 4
 #endif
@@ -819,9 +827,10 @@ struct StreamCfg {
     // 1 bit: 16 activation DMAs of one row each (M up to 16) leave LDS for two tiles
     static constexpr int TN = BITS == 1 ? (XI == 16 ? 2 : PQ_STREAM_TN)
                               : BITS == 2 ? PQ_STREAM_TN : (XI == 1 ? PQ_STREAM4_TN1 : PQ_STREAM4_TN);
-    static constexpr int NW = PQ_STREAM_NW;
+    static constexpr bool NW8 = BITS == 2 && XI <= PQ_STREAM_NW8_XI;
+    static constexpr int NW = NW8 ? 8 : PQ_STREAM_NW;
     static constexpr int D = BITS == 1 ? (XI <= 4 ? 3 : 2)
-                             : BITS == 2 ? (XI == 1 ? PQ_STREAM_D1 : XI == 2 ? PQ_STREAM_D2 : XI <= 4 ? PQ_STREAM_D4 : PQ_STREAM_D8)
+                             : BITS == 2 ? (NW8 ? 2 : XI == 1 ? PQ_STREAM_D1 : XI == 2 ? PQ_STREAM_D2 : XI <= 4 ? PQ_STREAM_D4 : PQ_STREAM_D8)
                                        : (XI == 1 ? PQ_STREAM4_D1 : XI == 2 ? PQ_STREAM4_D2 : PQ_STREAM4_D4);
 };
 

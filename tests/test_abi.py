@@ -146,9 +146,11 @@ def test_gemm_workspace_size_query(pq):
             assert q(mode, M, 16384, 16384) == 0
     assert q(7, 1, 64, 64) == -1 and q(2, 1, 64, 60) == -1 and q(2, -1, 64, 64) == -1
     assert q(2, 0, 64, 64) == 0 and q(2, 64, 0, 64) == 0
-    # 64 x 16384 output: 64 tiles of 64 x 256 do not fill the chip, so K is split
-    ws = q(2, 64, 16384, 16384)
-    assert ws > 0 and ws % (64 * 16384 * 4) == 0
+    # 64 x 16384 output: 64 tiles of 64 x 256 do not fill the chip, so K is
+    # split over blocks, each split writing fp32 partials [M, N]
+    for mode in (2, 4):
+        ws = q(mode, 64, 16384, 16384)
+        assert ws > 0 and ws % (64 * 16384 * 4) == 0 and ws // (64 * 16384 * 4) >= 2
     # 1024 rows at K >= 2048: the large-M path's row sums, M * 4 rounded to 256
     assert q(2, 1024, 8192, 2048) == 4096
     assert q(2, 1100, 8200, 2112) == (1100 * 4 + 255) // 256 * 256
