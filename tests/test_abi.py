@@ -30,6 +30,16 @@ def test_every_declared_symbol_is_exported(pq):
     assert set(names) == set(pq.EXPORTS)
 
 
+def test_header_constants_match_binding(pq):
+    """The sizes pq.h defines are the ones the binding uses."""
+    src = open(os.path.join(ROOT, "include", "pq.h")).read()
+    for name, value in {"PQ_NOALLOC_SCRATCH_BYTES": pq.PQ_NOALLOC_SCRATCH_BYTES}.items():
+        m = re.search(r"#define\s+" + name + r"\s+(.+)", src)
+        assert m, name
+        expr = re.sub(r"\(\s*int64_t\s*\)", "", m.group(1))
+        assert eval(expr, {}) == value, name
+
+
 def test_struct_layout(pq):
     assert ctypes.sizeof(pq.pq_mat) == 104
     assert pq.pq_mat.alpha_bf16.offset == 96

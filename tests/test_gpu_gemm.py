@@ -296,6 +296,32 @@ def test_gemm_caller_workspace_and_guards(M, N, K):
         check(Yg[ms, ns], O.gemm_ref_at(O.SEQ2, X, packed, ab, N, ms, ns), f"caller workspace {M}x{N}x{K}")
 
 
+def test_gemm_workspace_reused_across_shapes():
+    """One workspace, sized for the largest of the shapes, through a sequence
+    of GEMMs that use it differently (split-K partials of several sizes,
+    activation row sums, none), twice over: every result matches the
+    reference, whatever the previous call left in it."""
+    shapes = [(64, 2048, 2048), (1024, 8192, 2048), (1, 1024, 4096), (256, 1536, 4096), (100, 1000, 2048),
+              (4, 4096, 4096)]
+    need = max(pq.pq_gemm_workspace_bytes(O.SEQ2, *sh) for sh in shapes)
+    ws = torch.full((need,), 0x5A, dtype=torch.uint8, device="cuda")
+    cases = {sh: make_case(O.SEQ2, 700 + sum(sh), *sh) for sh in shapes}
+    for rnd in range(2):
+        for (M, N, K) in shapes:
+            print(f"[gemm ws reuse round={rnd} M={M} N={N} K={K}]", flush=True)
+            X, packed, ab = cases[(M, N, K)]
+            Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+            pq.pq_w2a16_gemm(M, N, K, dev(X), dev(O.tile_codes(packed)), dev(ab), Y, workspace=(ws.data_ptr(), need))
+            torch.cuda.synchronize()
+            Yg = synth.bf16_bits_to_f32(host(Y)).astype(np.float64)
+            if M * N <= 1 << 20:
+                check(Yg, O.gemm_ref(O.SEQ2, X, packed, ab, N), f"reuse {M}x{N}x{K}")
+            else:
+                rng = np.random.default_rng(M + rnd)
+                ms, ns = sample_points(rng, M, N, 2000)
+                check(Yg[ms, ns], O.gemm_ref_at(O.SEQ2, X, packed, ab, N, ms, ns), f"reuse {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("M,N,K", [(64, 2048, 2048), (1024, 8192, 2048), (16, 4096, 4096)])
 def test_gemm_graph_capture_without_warmup(M, N, K):
     """The first call of a shape can be captured into a HIP graph (nothing is
