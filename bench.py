@@ -18,7 +18,8 @@ width, the Llama-3-8B projections' quantizer and GEMM, the 4-bit GEMM
 variant and a hipBLASLt bf16 GEMM are timed after the steps.
 
 Every kernel is timed with HIP events on the stream it is launched on (torch's
-current stream).  `value` is the headline metric: quantize fwd+bwd throughput
+current stream); the step's events are timing-only events without the
+system-scope cache fence a default event record adds (TimingEvent).  `value` is the headline metric: quantize fwd+bwd throughput
 in GB/s of algorithmic bytes on the 1.5B stack.  The CPU baseline is the
 oracle (test infrastructure) on a sample of the same stack and on sampled
 GEMM outputs, timed on the host cores.
@@ -155,6 +156,62 @@ def recorded_mfma(path):
             except (ValueError, OSError):
                 pass
     return out
+
+
+class TimingEvent:
+    """A HIP event for timing only, created with hipEventDisableSystemFence:
+    recording it writes a timestamp without the system-scope cache write-back
+    and invalidate that a default event adds (HIP documents the flag for
+    this: the fence costs time and disturbs the following work, so kernels
+    timed between default events look slower than they run).  Made through
+    the HIP runtime this process already uses (torch's), found by its mapped
+    path, so that torch's streams are valid handles for it."""
+    FLAGS = 0x20000000  # hipEventDisableSystemFence
+    _lib = None
+
+    @classmethod
+    def hip(cls):
+        if cls._lib is None:
+            import ctypes
+            path = None
+            with open("/proc/self/maps") as f:
+                for line in f:
+                    if "libamdhip64.so" in line:
+                        path = line.split()[-1]
+                        break
+            if path is None:
+                raise RuntimeError("the HIP runtime is not loaded")
+            L = ctypes.CDLL(path)
+            L.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._lib = L
+        return cls._lib
+
+    def __init__(self):
+        import ctypes
+        self._c = ctypes
+        self.e = ctypes.c_void_p()
+        rc = self.hip().hipEventCreateWithFlags(ctypes.byref(self.e), self.FLAGS)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags: {rc}")
+
+    def record(self, stream):
+        rc = self.hip().hipEventRecord(self.e, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord: {rc}")
+
+    def elapsed_time(self, end):
+        ms = self._c.c_float()
+        rc = self.hip().hipEventElapsedTime(self._c.byref(ms), self.e, end.e)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime: {rc}")
+        return float(ms.value)
+
+    def __del__(self):
+        if self._lib is not None and self.e:
+            self._lib.hipEventDestroy(self.e)
 
 
 def fwd_bytes(rows, cols, cw):
@@ -525,10 +582,10 @@ def main():
 
     nev = 4 + len(GEMM_STEP_ORDER)
     for it in range(args.warmup):
-        step(it, [torch.cuda.Event(enable_timing=True) for _ in range(nev)])
+        step(it, [TimingEvent() for _ in range(nev)])
     torch.cuda.synchronize()
 
-    all_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    all_evs = [[TimingEvent() for _ in range(nev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for it in range(args.steps):
