@@ -130,10 +130,11 @@ namespace {
 // Lane (i16, grp) takes k = 16 * grp + 8 * t + [0, 8) of the stage at k-step
 // t, so its codes for a stage are one dword (2-bit) or two (4-bit), and the
 // decode yields the eight codes in natural k order:
-//   2-bit: w0 = (d & 0x03030303) | ((d << 2) & 0x30303030) holds codes
-//          (4q, 4q+1) as fp4 nibbles in byte q, w1 the same of d >> 4 holds
-//          (4q+2, 4q+3); the fp4 -> bf16 pair convert of bytes (w0.0, w1.0,
-//          w0.1, w1.1) gives codes 0..7 as c/2, bytes 2 and 3 give 8..15.
+//   2-bit: the export orders each code word so that w0 = d & 0x33333333
+//          holds codes 0..7 as fp4 nibbles in k order (low nibble of each
+//          byte first) and w1 = (d >> 2) & 0x33333333 codes 8..15; the
+//          fp4 -> bf16 pair converts of w0's four bytes give k-step 0 as c/2,
+//          those of w1 k-step 1.
 //   4-bit: byte p of d & 0x0F0F0F0F and of (d >> 4) & 0x0F0F0F0F hold codes
 //          2p and 2p+1; a byte permute places them in the two bf16 halves and
 //          (q << 3) | 0x40004000 makes 2 + c/8.
@@ -340,14 +341,15 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
                 f.a[T][i] = *reinterpret_cast<const uint4 *>(xa[i][T] + SLOT * C::XBYTES);
     };
     auto mma = [&](const Frag &f, auto &&between) {
+        // 2 bits: the code word's masked nibbles are its codes 0..7 (w0)
+        // and 8..15 (w1) in k order, one k-step each (the export's word order)
         uint32_t w0[4], w1[4];
         if constexpr (BITS == 2) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint32_t x = f.d[j][0];
-                const uint32_t y = x >> 4;
-                w0[j] = (x & 0x03030303u) | ((x << 2) & 0x30303030u);
-                w1[j] = (y & 0x03030303u) | ((y << 2) & 0x30303030u);
+                w0[j] = x & 0x33333333u;
+                w1[j] = (x >> 2) & 0x33333333u;
             }
         }
         static_for<0, 2>([&](auto tc) {
@@ -362,10 +364,11 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
                     b.z = fp4x2_to_bf16x2<2>(x);
                     b.w = fp4x2_to_bf16x2<3>(x);
                 } else if constexpr (BITS == 2) {
-                    b.x = fp4x2_to_bf16x2<2 * T>(w0[j]);
-                    b.y = fp4x2_to_bf16x2<2 * T>(w1[j]);
-                    b.z = fp4x2_to_bf16x2<2 * T + 1>(w0[j]);
-                    b.w = fp4x2_to_bf16x2<2 * T + 1>(w1[j]);
+                    const uint32_t wt = T == 0 ? w0[j] : w1[j];
+                    b.x = fp4x2_to_bf16x2<0>(wt);
+                    b.y = fp4x2_to_bf16x2<1>(wt);
+                    b.z = fp4x2_to_bf16x2<2>(wt);
+                    b.w = fp4x2_to_bf16x2<3>(wt);
                 } else {
                     const uint32_t x = f.d[j][T];
                     const uint32_t lo = x & 0x0F0F0F0Fu;
@@ -567,11 +570,13 @@ __global__ __launch_bounds__(256) void k_splitk_finalize(const float *ws, const 
 //
 // Decode.  2-bit: with D & 0x33333333 every nibble holds one code in its low
 // two bits, the e2m1 value c/2; v_cvt_scalef32_pk_bf16_fp4 turns each byte
-// into two exact bf16 (codes 4b and 4b+2), and (D >> 2) & 0x33333333 gives
-// codes 4b+1, 4b+3.  level = (c - 1.5)/2 = v - 0.75.  4-bit: nibbles are
-// spread into bytes and completed to bf16 128 + c (exact); level = v - 136.
-// The activations are put in the matching k order (evens, then odds, of each
-// 16- or 8-wide block) by byte permutes.  The row sums of X needed by the
+// into two exact bf16, and the export's word order makes the four bytes
+// codes 0..7 of the word in k order and those of (D >> 2) & 0x33333333
+// codes 8..15, so the activation chunks are used as loaded.
+// level = (c - 1.5)/2 = v - 0.75.  4-bit: nibbles are spread into bytes and
+// completed to bf16 128 + c (exact); level = v - 136, and the activations
+// are put in the matching k order (evens, then odds, of each 8-wide block)
+// by byte permutes.  The row sums of X needed by the
 // offsets are taken with v_dot2 on the chunk each lane fetched.  The NW
 // partial sums are combined in LDS in a fixed order.
 // ---------------------------------------------------------------------------
@@ -692,21 +697,11 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
             for (int q = 0; q < 8; ++q) ua[q] = *reinterpret_cast<const uint4 *>(xa + (8 * grp + q) * 32);
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                const uint4 u0 = ua[2 * d];
-                const uint4 u1 = ua[2 * d + 1];
-                const uint32_t r[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-                // even / odd bf16 halves of each dword pair, one byte permute each
-                uint4 ae, ao;
-                ae.x = __builtin_amdgcn_perm(r[1], r[0], 0x05040100u);
-                ae.y = __builtin_amdgcn_perm(r[3], r[2], 0x05040100u);
-                ae.z = __builtin_amdgcn_perm(r[5], r[4], 0x05040100u);
-                ae.w = __builtin_amdgcn_perm(r[7], r[6], 0x05040100u);
-                ao.x = __builtin_amdgcn_perm(r[1], r[0], 0x07060302u);
-                ao.y = __builtin_amdgcn_perm(r[3], r[2], 0x07060302u);
-                ao.z = __builtin_amdgcn_perm(r[5], r[4], 0x07060302u);
-                ao.w = __builtin_amdgcn_perm(r[7], r[6], 0x07060302u);
-                const bf16x8 a_e = __builtin_bit_cast(bf16x8, ae);
-                const bf16x8 a_o = __builtin_bit_cast(bf16x8, ao);
+                // code word d holds k = 64 grp + 16 d + [0, 16): its low
+                // nibbles k .. k + 7, its high ones k + 8 .. k + 15, in k
+                // order (the export's word order), matching chunks 2d, 2d + 1
+                const bf16x8 a_e = __builtin_bit_cast(bf16x8, ua[2 * d]);
+                const bf16x8 a_o = __builtin_bit_cast(bf16x8, ua[2 * d + 1]);
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     const uint32_t Dw = d == 0 ? c[j].x : d == 1 ? c[j].y : d == 2 ? c[j].z : c[j].w;

@@ -204,15 +204,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, const float *r
         constexpr int T = decltype(t_c)::value;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const uint32_t x = d[j];
-            const uint32_t y = x >> 4;
-            const uint32_t w0 = (x & 0x03030303u) | ((x << 2) & 0x30303030u);
-            const uint32_t w1 = (y & 0x03030303u) | ((y << 2) & 0x30303030u);
+            // the code word's masked nibbles: codes 0..7 (k-step 0) and
+            // 8..15 (k-step 1) in k order (the export's word order)
+            const uint32_t wt = T == 0 ? d[j] & 0x33333333u : (d[j] >> 2) & 0x33333333u;
             uint4 b;
-            b.x = fp4x2_to_bf16x2<2 * T>(w0);
-            b.y = fp4x2_to_bf16x2<2 * T>(w1);
-            b.z = fp4x2_to_bf16x2<2 * T + 1>(w0);
-            b.w = fp4x2_to_bf16x2<2 * T + 1>(w1);
+            b.x = fp4x2_to_bf16x2<0>(wt);
+            b.y = fp4x2_to_bf16x2<1>(wt);
+            b.z = fp4x2_to_bf16x2<2>(wt);
+            b.w = fp4x2_to_bf16x2<3>(wt);
             const bf16x8 bv = __builtin_bit_cast(bf16x8, b);
 #pragma unroll
             for (int i = 0; i < kRT; ++i)

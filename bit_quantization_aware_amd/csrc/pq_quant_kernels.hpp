@@ -402,8 +402,9 @@ __global__ __launch_bounds__(256, fwd_waves_per_eu(MODE, IQ, OUTS, U)) void k_qu
                 if (tl == 0 && so.entropy) so.entropy[row] = h;
             }
             if constexpr (TILED) {
-                // zero the bytes of the last group past the row's end (< 64 bytes)
-                const int64_t rb = cols * CW / 8;
+                // zero the bytes of the last group past the row's end (< 64
+                // bytes); 2-bit rows end on a whole word of the export
+                const int64_t rb = CW == 2 ? (cols * CW / 8 + 3) / 4 * 4 : cols * CW / 8;
                 const int64_t kb = rb + tl;
                 if (kb < gbytes) tbase[(kb >> 6) * gstride + (kb & 63)] = 0;
             }
@@ -468,8 +469,25 @@ __global__ __launch_bounds__(256, fwd_waves_per_eu(MODE, IQ, OUTS, U)) void k_qu
                 // (tl or 2 tl) splits into group and byte.
                 const int64_t g0 = (static_cast<int64_t>(sbase) * (CW / 2)) >> 6;
                 if constexpr (CW == 2) {
-                    PQ_GLOBAL uint8_t *d = tbase + (g0 + (tl >> 6)) * gstride + (tl & 63);
-                    if (act) *d = static_cast<uint8_t>(c0 | (c1 << 2) | (c2 << 4) | (c3 << 6));
+                    // Four lanes' quads are one 4-byte word of the export,
+                    // whose byte j holds codes 2j, 8+2j, 2j+1, 9+2j of the
+                    // word's 16 (bits 0-1, 2-3, 4-5, 6-7).  Quads 0 and 2 make
+                    // bytes 0-1, quads 1 and 3 bytes 2-3: each lane spreads
+                    // its codes over a halfword (the word's second half one
+                    // bit pair higher), adds its partner's (lane tl ^ 2) and
+                    // writes byte 2 (qq & 1) + (qq >> 1).  Quads past the row
+                    // end add zeros; a word holding any code of the row is
+                    // written whole.
+                    const int qq = tl & 3;
+                    uint32_t h = act ? (c0 | (c1 << 4) | (c2 << 8) | (c3 << 12)) : 0u;
+                    h <<= 2 * (qq >> 1);
+                    h |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(h), 2));
+                    const int wq0 = sbase + (tl & ~3);  // the word's first quad in the row
+                    if (wq0 * 4 < cols) {
+                        PQ_GLOBAL uint8_t *d =
+                            tbase + (g0 + (tl >> 6)) * gstride + ((tl & 60) + 2 * (qq & 1) + (qq >> 1));
+                        *d = static_cast<uint8_t>(h >> (8 * (qq >> 1)));
+                    }
                 } else {
                     PQ_GLOBAL uint8_t *d = tbase + (g0 + (tl >> 5)) * gstride + ((2 * tl) & 63);
                     if (act) *(PQ_GLOBAL uint16_t *)d = static_cast<uint16_t>(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));

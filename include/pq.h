@@ -205,19 +205,27 @@ pq_status pq_quantize_bwd(int mode, int64_t rows, int64_t cols, const float *W,
                           uint8_t *mask_bits, void *stream);
 
 /*
- * Export byte order.  The exported codes hold the same bytes as the
- * forward's code rows (pq_quantize_fwd `codes`: rb = cols * b / 8 bytes per
- * row, four 2-bit or two 4-bit codes per byte, first code lowest), reordered
- * for the deployment GEMM, which reads 16 rows x 64 bytes as one MFMA operand
+ * Export byte order.  The exported codes are the forward's code rows
+ * (pq_quantize_fwd `codes`: rb = cols * b / 8 bytes per row, eight 1-bit,
+ * four 2-bit or two 4-bit codes per byte, first code lowest), reordered for
+ * the deployment GEMM, which reads 16 rows x 64 bytes as one MFMA operand
  * ([News] speed paragraph: the 2-bit kernel consumes packed weights; the
- * pages fix four codes per byte and a bf16 scale per row, not a byte order).
- * With Np = rows rounded up to a multiple of 16 and G = ceil(rb / 64):
- *   byte c of row n (c < rb, n < rows) is stored at
- *     (c / 64) * Np * 64 + (n / 16) * 1024 + (n % 16) * 64 + c % 64,
- * i.e. group-major runs of 64 bytes of every row, each 16-row tile 1 KB
- * ordered [row][64 bytes].  Every other byte (rows rows .. Np - 1,
- * bytes rb .. 64 G - 1 of a row) is written as 0.  Total size
- * G * Np * 64 bytes = pq_packed_bytes(mode, rows, cols).
+ * pages fix four codes per byte and a bf16 scale per row, not a byte order):
+ * 1. 2-bit codes only: each 4-byte word of a row (16 codes k0 .. k15, code
+ *    ki in bits 2i .. 2i+1 of the little-endian word; the row zero-padded to
+ *    whole words, rbw = rb rounded up to 4) is rewritten so that its byte j
+ *    holds k(2j) in bits 0-1, k(8+2j) in bits 2-3, k(2j+1) in bits 4-5 and
+ *    k(9+2j) in bits 6-7: masked with 0x33333333 the word's nibbles are
+ *    codes k0 .. k7 in order (low nibble of each byte first), and shifted
+ *    right by 2 and masked, k8 .. k15.  1- and 4-bit rows keep their bytes
+ *    (rbw = rb).
+ * 2. With Np = rows rounded up to a multiple of 16 and G = ceil(rb / 64):
+ *    byte c of row n (c < rbw, n < rows) is stored at
+ *      (c / 64) * Np * 64 + (n / 16) * 1024 + (n % 16) * 64 + c % 64,
+ *    i.e. group-major runs of 64 bytes of every row, each 16-row tile 1 KB
+ *    ordered [row][64 bytes].  Every other byte (rows rows .. Np - 1,
+ *    bytes rbw .. 64 G - 1 of a row) is written as 0.  Total size
+ *    G * Np * 64 bytes = pq_packed_bytes(mode, rows, cols).
  */
 int64_t pq_packed_bytes(int mode, int64_t rows, int64_t cols);
 

@@ -52,7 +52,7 @@ def lib():
                                       _i64p, _i64p, _i64, _f64p]
         L.pqo_tiled_bytes.argtypes = [_i64, _i64]
         L.pqo_tiled_bytes.restype = _i64
-        L.pqo_tile_codes.argtypes = [_i64, _i64, _u8p, _u8p]
+        L.pqo_tile_codes.argtypes = [ctypes.c_int, _i64, _i64, _u8p, _u8p]
         L.pqo_adamw.argtypes = [_i64, _f32p, _f32p, _f32p, _f32p] + [ctypes.c_double] * 5 + [_i64]
         L.pqo_qat_step.argtypes = ([ctypes.c_int, _i64, _i64, _f32p, _f32p, ctypes.c_void_p, ctypes.c_int,
                                     ctypes.c_double, _f32p, _f32p, _f32p, _f32p] + [ctypes.c_double] * 5 +
@@ -242,19 +242,20 @@ def tiled_bytes(rows: int, row_bytes: int) -> int:
     return int(lib().pqo_tiled_bytes(rows, row_bytes))
 
 
-def tile_codes(packed: np.ndarray) -> np.ndarray:
-    """Deployment byte order (flat uint8) of row-major code rows [rows, rb]."""
+def tile_codes(packed: np.ndarray, cw: int) -> np.ndarray:
+    """Deployment byte order (flat uint8) of row-major rows [rows, rb] of
+    cw-bit codes (2-bit codes are also reordered inside each 4-byte word)."""
     packed = _c(packed, np.uint8)
     rows, rb = packed.shape
     out = np.empty(tiled_bytes(rows, rb), np.uint8)
-    _check(lib().pqo_tile_codes(rows, rb, _p(packed, _u8p), _p(out, _u8p)))
+    _check(lib().pqo_tile_codes(cw, rows, rb, _p(packed, _u8p), _p(out, _u8p)))
     return out
 
 
 def pack_tiled(mode: int, W: np.ndarray, alpha: np.ndarray):
     """Export in the deployment byte order: (tiled codes uint8 flat, alpha bf16 bits)."""
     packed, ab = pack(mode, W, alpha)
-    return tile_codes(packed), ab
+    return tile_codes(packed, CODE_BITS[mode]), ab
 
 
 def gemm_ref(mode: int, X_bf16: np.ndarray, packed: np.ndarray, alpha_bf16: np.ndarray, N: int):

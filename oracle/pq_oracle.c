@@ -631,13 +631,26 @@ int pqo_weight_movement(int64_t rows, int64_t cols, const float *W, const float 
  * 2-bit weight holds (four codes per byte and a bf16 scale per row, [News]
  * storage and speed paragraphs); the byte order the deployed GEMM reads is
  * this library's own, defined here from the row-major code rows that the
- * forward emits (rb bytes per row):
- *   groups   g = 0 .. G-1,  G  = ceil(rb / 64)   (64 bytes of every row)
- *   tiles    t = 0 .. Np/16-1, Np = rows rounded up to a multiple of 16
- *   row r = 0 .. 15 of the tile, byte e = 0 .. 63 of the row's group
- *   tiled[((g * (Np/16) + t) * 16 + r) * 64 + e]
- *       = rowmajor[(16 t + r) * rb + 64 g + e]
- *   when the row 16 t + r < rows and the byte 64 g + e < rb, else 0.
+ * forward emits (rb bytes per row, cw-bit codes, first code lowest):
+ *
+ * 1. (2-bit codes only) inside each 4-byte word of a row -- 16 codes
+ *    k0 .. k15, code ki in bits 2i .. 2i+1 of the little-endian word, the
+ *    row's bytes zero-padded to a whole word -- byte j (j = 0 .. 3) of the
+ *    export word holds
+ *        k(2j) in bits 0-1, k(8+2j) in bits 2-3,
+ *        k(2j+1) in bits 4-5, k(9+2j) in bits 6-7,
+ *    so that masking the word with 0x33333333 leaves codes k0 .. k7 in its
+ *    eight nibbles in k order (low nibble of each byte first), and masking
+ *    it shifted right by 2 leaves k8 .. k15.  1- and 4-bit codes keep the
+ *    row-major bytes.
+ * 2. the bytes are then placed group by group:
+ *    groups   g = 0 .. G-1,  G  = ceil(rb / 64)   (64 bytes of every row)
+ *    tiles    t = 0 .. Np/16-1, Np = rows rounded up to a multiple of 16
+ *    row r = 0 .. 15 of the tile, byte e = 0 .. 63 of the row's group
+ *    tiled[((g * (Np/16) + t) * 16 + r) * 64 + e]
+ *        = row[16 t + r] byte 64 g + e  (after step 1)
+ *    when the row 16 t + r < rows and the byte lies within the row (rb
+ *    bytes; for 2-bit codes rb rounded up to a whole word), else 0.
  * So every 64-byte group of all rows is one contiguous run (group-major),
  * inside it each tile of 16 rows is 1 KB, and inside a tile each row's 64
  * bytes are contiguous.  Size: G * Np * 64 bytes.
@@ -648,18 +661,46 @@ int64_t pqo_tiled_bytes(int64_t rows, int64_t rb)
     return ((rb + 63) / 64) * ((rows + 15) / 16 * 16) * 64;
 }
 
-int pqo_tile_codes(int64_t rows, int64_t rb, const uint8_t *rowmajor, uint8_t *tiled)
+/* Step 1 for one word of 2-bit codes. */
+static uint32_t export_word2(uint32_t w)
 {
-    if (rows < 0 || rb < 0) return -1;
+    uint32_t out = 0;
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t b = ((w >> (2 * (2 * j))) & 3u) | (((w >> (2 * (8 + 2 * j))) & 3u) << 2) |
+                           (((w >> (2 * (2 * j + 1))) & 3u) << 4) | (((w >> (2 * (9 + 2 * j))) & 3u) << 6);
+        out |= b << (8 * j);
+    }
+    return out;
+}
+
+int pqo_tile_codes(int cw, int64_t rows, int64_t rb, const uint8_t *rowmajor, uint8_t *tiled)
+{
+    if (rows < 0 || rb < 0 || (cw != 1 && cw != 2 && cw != 4)) return -1;
     const int64_t G = (rb + 63) / 64, T = (rows + 15) / 16;
-    for (int64_t g = 0; g < G; ++g)
-        for (int64_t t = 0; t < T; ++t)
-            for (int r = 0; r < 16; ++r)
+    const int64_t rbw = cw == 2 ? (rb + 3) / 4 * 4 : rb;  /* bytes the row covers in the export */
+    uint8_t *row = (uint8_t *)calloc((size_t)(G * 64 > 0 ? G * 64 : 1), 1);
+    if (!row) return -1;
+    for (int64_t t = 0; t < T; ++t)
+        for (int r = 0; r < 16; ++r) {
+            const int64_t n = 16 * t + r;
+            memset(row, 0, (size_t)(G * 64));
+            if (n < rows) {
+                memcpy(row, rowmajor + n * rb, (size_t)rb);
+                if (cw == 2)
+                    for (int64_t c = 0; c < rbw; c += 4) {
+                        const uint32_t w = (uint32_t)row[c] | ((uint32_t)row[c + 1] << 8) |
+                                           ((uint32_t)row[c + 2] << 16) | ((uint32_t)row[c + 3] << 24);
+                        const uint32_t e = export_word2(w);
+                        for (int b = 0; b < 4; ++b) row[c + b] = (uint8_t)(e >> (8 * b));
+                    }
+            }
+            for (int64_t g = 0; g < G; ++g)
                 for (int e = 0; e < 64; ++e) {
-                    const int64_t dst = ((g * T + t) * 16 + r) * 64 + e;
-                    const int64_t n = 16 * t + r, c = 64 * g + e;
-                    tiled[dst] = (n < rows && c < rb) ? rowmajor[n * rb + c] : 0;
+                    const int64_t c = 64 * g + e;
+                    tiled[((g * T + t) * 16 + r) * 64 + e] = c < rbw ? row[c] : 0;
                 }
+        }
+    free(row);
     return 0;
 }
 

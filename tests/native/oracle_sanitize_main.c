@@ -29,7 +29,7 @@ int pqo_level_stats(int mode, int64_t rows, int64_t cols, const uint8_t *codes, 
 int pqo_weight_movement(int64_t rows, int64_t cols, const float *W, const float *W0, double *sq_diff,
                         double *sq_ref);
 int64_t pqo_tiled_bytes(int64_t rows, int64_t rb);
-int pqo_tile_codes(int64_t rows, int64_t rb, const uint8_t *rowmajor, uint8_t *tiled);
+int pqo_tile_codes(int cw, int64_t rows, int64_t rb, const uint8_t *rowmajor, uint8_t *tiled);
 int pqo_gemm_ref(int mode, int64_t M, int64_t N, int64_t K, const uint16_t *X, const uint8_t *packed,
                  const uint16_t *alpha_bf16, double *Y);
 int pqo_gemm_ref_f32a(int mode, int64_t M, int64_t N, int64_t K, const uint16_t *X,
@@ -94,7 +94,7 @@ static int one_case(int mode, int64_t rows, int64_t cols, int g_bf16)
     CHECK(pqo_pack(mode, rows, cols, W, alpha, codes, ab));
     const int64_t tb = pqo_tiled_bytes(rows, rb);
     uint8_t *tiled = ALLOC(uint8_t, tb);
-    CHECK(pqo_tile_codes(rows, rb, codes, tiled));
+    CHECK(pqo_tile_codes(pqo_code_bits(mode), rows, rb, codes, tiled));
     const int64_t M = 3;
     uint16_t *X = ALLOC(uint16_t, M * cols);
     for (int64_t i = 0; i < M * cols; ++i) X[i] = Gh[i % (n > 0 ? n : 1)];

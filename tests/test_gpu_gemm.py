@@ -52,7 +52,7 @@ def gpu_gemm(mode, X, packed, ab, N):
     the export byte order (the oracle's tile_codes)."""
     M, K = X.shape
     Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-    tiled = O.tile_codes(packed)
+    tiled = O.tile_codes(packed, O.CODE_BITS[mode])
     assert tiled.size == pq.pq_packed_bytes(mode, N, K)
     if mode == O.SEQ2:
         pq.pq_w2a16_gemm(M, N, K, dev(X), dev(tiled), dev(ab), Y)
@@ -230,7 +230,7 @@ def test_gemm_large_m_full_compare():
     alpha = O.alpha_init(O.SEQ2, W)
     packed, _ = O.pack(O.SEQ2, W, alpha)
     Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-    pq.pq_gemm_f32a(O.SEQ2, M, N, K, dev(X), dev(O.tile_codes(packed)), dev(alpha), Y)
+    pq.pq_gemm_f32a(O.SEQ2, M, N, K, dev(X), dev(O.tile_codes(packed, O.CODE_BITS[O.SEQ2])), dev(alpha), Y)
     torch.cuda.synchronize()
     Yg = synth.bf16_bits_to_f32(host(Y)).astype(np.float64)
     check(Yg, O.gemm_ref_f32a(O.SEQ2, X, packed, alpha, N), "large-M f32a full")
@@ -263,7 +263,7 @@ def test_gemm_f32_alpha(mode, M, N, K):
     packed, _ = O.pack(mode, W, alpha)
     X = synth.to_bf16_bits(synth.normal_f32(rng, (M, K)))
     Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-    pq.pq_gemm_f32a(mode, M, N, K, dev(X), dev(O.tile_codes(packed)), dev(alpha), Y)
+    pq.pq_gemm_f32a(mode, M, N, K, dev(X), dev(O.tile_codes(packed, O.CODE_BITS[mode])), dev(alpha), Y)
     torch.cuda.synchronize()
     Yg = synth.bf16_bits_to_f32(host(Y)).astype(np.float64)
     check(Yg, O.gemm_ref_f32a(mode, X, packed, alpha, N), f"f32a m{mode} {M}x{N}x{K}")
@@ -282,7 +282,7 @@ def test_gemm_caller_workspace_and_guards(M, N, K):
     assert nbytes >= 0
     ws = Guarded((nbytes,), torch.uint8)
     Y = Guarded((M, N), torch.bfloat16)
-    tiled = dev(O.tile_codes(packed))
+    tiled = dev(O.tile_codes(packed, O.CODE_BITS[O.SEQ2]))
     pq.pq_w2a16_gemm(M, N, K, dev(X), tiled, dev(ab), Y.t, workspace=(ws.t.data_ptr() if nbytes else 0, nbytes))
     torch.cuda.synchronize()
     ws.check("workspace")
@@ -311,7 +311,7 @@ def test_gemm_workspace_reused_across_shapes():
             print(f"[gemm ws reuse round={rnd} M={M} N={N} K={K}]", flush=True)
             X, packed, ab = cases[(M, N, K)]
             Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-            pq.pq_w2a16_gemm(M, N, K, dev(X), dev(O.tile_codes(packed)), dev(ab), Y, workspace=(ws.data_ptr(), need))
+            pq.pq_w2a16_gemm(M, N, K, dev(X), dev(O.tile_codes(packed, O.CODE_BITS[O.SEQ2])), dev(ab), Y, workspace=(ws.data_ptr(), need))
             torch.cuda.synchronize()
             Yg = synth.bf16_bits_to_f32(host(Y)).astype(np.float64)
             if M * N <= 1 << 20:
@@ -329,7 +329,7 @@ def test_gemm_graph_capture_without_warmup(M, N, K):
     call, replayed three times with eager work in between, every replay
     equal bit for bit to the eager result, which matches the reference."""
     X, packed, ab = make_case(O.SEQ2, 900 + M + N, M, N, K)
-    Xd, tiled, abd = dev(X), dev(O.tile_codes(packed)), dev(ab)
+    Xd, tiled, abd = dev(X), dev(O.tile_codes(packed, O.CODE_BITS[O.SEQ2])), dev(ab)
     ws = pq.gemm_workspace(O.SEQ2, M, N, K)
     wsa = (ws.data_ptr(), ws.numel()) if ws is not None else (0, 0)
     Yg = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")

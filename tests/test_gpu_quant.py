@@ -226,10 +226,10 @@ def test_pack_matches_forward_codes(mode):
     alpha = O.alpha_init(mode, W)
     packed, ab = gpu_pack(mode, W, alpha)
     p_o, ab_o = O.pack(mode, W, alpha)
-    assert_bits_equal(packed, O.tile_codes(p_o), "packed")
+    assert_bits_equal(packed, O.tile_codes(p_o, O.CODE_BITS[mode]), "packed")
     assert_bits_equal(ab, ab_o, "alpha bf16")
     _, _, _, codes_fwd = gpu_fwd(mode, W, alpha, False, want_f32=False)
-    assert_bits_equal(packed, O.tile_codes(codes_fwd), "pack == fwd codes in export order")
+    assert_bits_equal(packed, O.tile_codes(codes_fwd, O.CODE_BITS[mode]), "pack == fwd codes in export order")
 
 
 @pytest.mark.parametrize("mode", [O.SEQ2, O.LSQ4, O.TERNARY, O.LSQ3, O.LSQ2, O.LSQ158, O.BINARY])
@@ -243,7 +243,7 @@ def test_pack_export_order_shapes(mode, rows, cols):
     alpha = O.alpha_init(mode, W)
     packed, ab = gpu_pack(mode, W, alpha)
     p_o, ab_o = O.pack(mode, W, alpha)
-    assert_bits_equal(packed, O.tile_codes(p_o), f"packed {rows}x{cols}")
+    assert_bits_equal(packed, O.tile_codes(p_o, O.CODE_BITS[mode]), f"packed {rows}x{cols}")
     assert_bits_equal(ab, ab_o, "alpha bf16")
 
 
@@ -328,7 +328,7 @@ def test_mobilellm_1p5b_layers_with_outliers():
         rows, cols = W.shape
         packed, ab = gpu_pack(O.SEQ2, W, o["alpha"])
         p_o, ab_o = O.pack(O.SEQ2, W, o["alpha"])
-        assert_bits_equal(packed, O.tile_codes(p_o), f"1.5B[{i}] packed")
+        assert_bits_equal(packed, O.tile_codes(p_o, O.CODE_BITS[O.SEQ2]), f"1.5B[{i}] packed")
         assert_bits_equal(ab, ab_o, f"1.5B[{i}] alpha bf16")
 
 
@@ -399,7 +399,7 @@ def test_fwd_codes_in_export_order(mode, rows, cols, init):
     wq_o, _, codes_o = O.quantize_fwd(mode, W, a_o)
     assert_bits_equal(host(ad), a_o, "alpha")
     assert_bits_equal(host(wq), wq_o, "wq")
-    assert_bits_equal(host(codes), O.tile_codes(codes_o), "codes (export order)")
+    assert_bits_equal(host(codes), O.tile_codes(codes_o, O.CODE_BITS[mode]), "codes (export order)")
 
 
 def test_grouped_fwd_codes_in_export_order():
@@ -424,7 +424,7 @@ def test_grouped_fwd_codes_in_export_order():
         a_o = O.alpha_init(mode, W)
         _, _, codes_o = O.quantize_fwd(mode, W, a_o)
         assert_bits_equal(host(m["alpha"]), a_o, "alpha")
-        assert_bits_equal(host(m["codes"]), O.tile_codes(codes_o), f"codes {W.shape}")
+        assert_bits_equal(host(m["codes"]), O.tile_codes(codes_o, O.CODE_BITS[mode]), f"codes {W.shape}")
 
 
 # ----------------------------------------------------------------------------
@@ -493,7 +493,7 @@ def test_mobilellm_1p5b_full_stack():
                 assert_bits_equal(host(d["dW"]), dW_o, f"1.5B[{k}] dW")
                 assert_rel(host(d["dalpha"]), da_o, 1e-5, np.float64(1e-35), f"1.5B[{k}] dalpha")
                 p_o, ab_o = O.pack(mode, W, a_o)
-                assert_bits_equal(host(d["packed"]), O.tile_codes(p_o), f"1.5B[{k}] packed")
+                assert_bits_equal(host(d["packed"]), O.tile_codes(p_o, O.CODE_BITS[mode]), f"1.5B[{k}] packed")
                 assert_bits_equal(host(d["alpha_bf16"]), ab_o, f"1.5B[{k}] alpha bf16")
             if c0 % 64 == 0:
                 print(f"[1.5B full stack: {min(n, c0 + 16)} of {n} checked]", flush=True)
@@ -520,7 +520,7 @@ def test_grouped_stack_beyond_one_launch(mode):
     torch.cuda.synchronize()
     for i, ((W, _), d) in enumerate(zip(mats, dmats)):
         p_o, ab_o = O.pack(mode, W, O.alpha_init(mode, W))
-        assert_bits_equal(host(d["codes"]), O.tile_codes(p_o), f"1000-stack[{i}] packed")
+        assert_bits_equal(host(d["codes"]), O.tile_codes(p_o, O.CODE_BITS[mode]), f"1000-stack[{i}] packed")
         assert_bits_equal(host(d["alpha_bf16"]), ab_o, f"1000-stack[{i}] alpha bf16")
 
 
@@ -562,5 +562,5 @@ def test_outputs_stay_inside_their_buffers(mode, shape):
     assert_bits_equal(host(mask.t), m_o, "mask")
     assert_rel(host(da.t), da_o, 1e-5, np.float64(1e-35), "dalpha")
     p_o, ab_o = O.pack(mode, W, a_o)
-    assert_bits_equal(host(packed.t), O.tile_codes(p_o), "packed")
+    assert_bits_equal(host(packed.t), O.tile_codes(p_o, O.CODE_BITS[mode]), "packed")
     assert_bits_equal(host(ab.t), ab_o, "alpha bf16")

@@ -456,9 +456,29 @@ def test_gemm_ref_is_matmul_of_dequantized_weight(mode):
     assert np.allclose(O.gemm_ref_f32a(mode, X, packed, alpha, N), want32, rtol=1e-12, atol=1e-12)
 
 
-def _tile_by_reshape(P):
-    """The deployment byte order as a numpy index shuffle: pad to whole tiles
-    and groups, then order the axes (group, tile, row, byte)."""
+def _word_order_2bit(P):
+    """The 2-bit export's reorder inside each 4-byte word, in numpy: the row
+    zero-padded to whole words, its 16 codes per word split out (code i in
+    bits 2i..2i+1), and byte j rebuilt from codes 2j, 8+2j, 2j+1, 9+2j."""
+    rows, rb = P.shape
+    rbw = -(-rb // 4) * 4
+    pad = np.zeros((rows, rbw), np.uint8)
+    pad[:, :rb] = P
+    words = pad.reshape(rows, rbw // 4, 4).astype(np.uint32)
+    w = words[..., 0] | (words[..., 1] << 8) | (words[..., 2] << 16) | (words[..., 3] << 24)
+    k = [(w >> (2 * i)) & 3 for i in range(16)]
+    out = np.zeros((rows, rbw // 4, 4), np.uint8)
+    for j in range(4):
+        out[..., j] = (k[2 * j] | (k[8 + 2 * j] << 2) | (k[2 * j + 1] << 4) | (k[9 + 2 * j] << 6)).astype(np.uint8)
+    return out.reshape(rows, rbw)
+
+
+def _tile_by_reshape(P, cw):
+    """The deployment byte order as a numpy index shuffle: (2-bit codes:
+    reorder inside each word,) pad to whole tiles and groups, then order the
+    axes (group, tile, row, byte)."""
+    if cw == 2:
+        P = _word_order_2bit(P)
     rows, rb = P.shape
     Np, G = -(-rows // 16) * 16, -(-rb // 64)
     pad = np.zeros((Np, G * 64), np.uint8)
@@ -466,20 +486,66 @@ def _tile_by_reshape(P):
     return pad.reshape(Np // 16, 16, G, 64).transpose(2, 0, 1, 3).reshape(-1)
 
 
+@pytest.mark.parametrize("cw", [1, 2, 4])
 @pytest.mark.parametrize("rows,rb", [(16, 64), (20, 144), (1, 2), (33, 16), (48, 256), (7, 200),
-                                     (0, 64), (5, 0)])
-def test_tile_codes_matches_axis_shuffle(rows, rb):
+                                     (0, 64), (5, 0), (3, 25), (17, 66)])
+def test_tile_codes_matches_axis_shuffle(rows, rb, cw):
     rng = np.random.default_rng(rows * 1000 + rb)
     P = rng.integers(0, 256, (rows, rb), dtype=np.uint8)
-    T = O.tile_codes(P)
+    T = O.tile_codes(P, cw)
     assert T.size == O.tiled_bytes(rows, rb) == -(-rb // 64) * (-(-rows // 16) * 16) * 64
-    assert np.array_equal(T, _tile_by_reshape(P))
+    assert np.array_equal(T, _tile_by_reshape(P, cw))
+
+
+def test_tile_codes_2bit_word_by_hand():
+    """One row of 16 2-bit codes k_i = i mod 4 (row-major bytes 0xE4 each):
+    export byte j holds k(2j), k(8+2j), k(2j+1), k(9+2j) in bits 0-1, 2-3,
+    4-5, 6-7, so bytes 0..3 are 0x50, 0xFA, 0x50, 0xFA (worked out by hand:
+    0x50 = 0 | 0 << 2 | 1 << 4 | 1 << 6, 0xFA = 2 | 2 << 2 | 3 << 4 | 3 << 6);
+    the rest of the 64-byte group and the 15 padding rows are zero."""
+    P = np.full((1, 4), 0xE4, np.uint8)
+    T = O.tile_codes(P, 2)
+    assert T.size == 16 * 64
+    assert list(T[:4]) == [0x50, 0xFA, 0x50, 0xFA]
+    assert not T[4:].any()
+    # 1- and 4-bit codes keep the row-major bytes
+    assert list(O.tile_codes(P, 4)[:4]) == [0xE4] * 4 and list(O.tile_codes(P, 1)[:4]) == [0xE4] * 4
+
+
+def _e2m1(nib):
+    """Value of an e2m1 nibble from the format's definition: sign bit 3,
+    exponent bits 2-1 (bias 1), mantissa bit 0; exponent 0 is subnormal."""
+    s = -1.0 if nib & 8 else 1.0
+    e, m = (nib >> 1) & 3, nib & 1
+    return s * (m * 0.5 if e == 0 else (1 + m / 2) * 2.0 ** (e - 1))
+
+
+def test_tile_codes_2bit_nibbles_decode_in_k_order():
+    """What the export order is for: in each word, the nibbles of
+    word & 0x33333333 (low nibble of each byte first) are the e2m1 values
+    c/2 of codes k0..k7 in order, and those of (word >> 2) & 0x33333333 the
+    codes k8..k15 -- checked on random rows through the oracle's tiling."""
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 4, (16, 64))
+    P = np.zeros((16, 16), np.uint8)
+    for i in range(64):
+        P[:, i // 4] |= (codes[:, i] << (2 * (i % 4))).astype(np.uint8)
+    T = O.tile_codes(P, 2)
+    for r in range(16):
+        row = T[r * 64:r * 64 + 16]
+        for wi in range(4):
+            w = int.from_bytes(bytes(row[4 * wi:4 * wi + 4]), "little")
+            got = []
+            for m in (w & 0x33333333, (w >> 2) & 0x33333333):
+                for n in range(8):
+                    got.append(_e2m1((m >> (4 * n)) & 0xF))
+            assert got == [c / 2 for c in codes[r, 16 * wi:16 * wi + 16]]
 
 
 def test_tile_codes_hand_positions():
-    # 20 rows of 144 bytes (2-bit codes of 576 weights): 32 padded rows, 3 groups.
+    # 20 rows of 144 bytes (4-bit codes of 288 weights): 32 padded rows, 3 groups.
     P = (np.arange(20 * 144) % 251 + 1).astype(np.uint8).reshape(20, 144)
-    T = O.tile_codes(P)
+    T = O.tile_codes(P, 4)
     assert T.size == 3 * 32 * 64
     # row 17, byte 70: group 1, tile 1, tile row 1, byte 6 of the group
     assert T[((1 * 2 + 1) * 16 + 1) * 64 + 6] == P[17, 70]

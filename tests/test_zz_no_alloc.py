@@ -38,7 +38,7 @@ def case(mode, seed, M, N, K):
 
 def both(pq, mode, X, packed, ab, N):
     M, K = X.shape
-    Xd, Pd, Ad = dev(X), dev(O.tile_codes(packed)), dev(ab)
+    Xd, Pd, Ad = dev(X), dev(O.tile_codes(packed, O.CODE_BITS[mode])), dev(ab)
     Y1 = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
     Y2 = torch.full((M, N), 7.0, dtype=torch.bfloat16, device="cuda")
     pq.pq_gemm(mode, M, N, K, Xd, Pd, Ad, Y1)
@@ -82,7 +82,7 @@ def test_noalloc_graph_capture_first_call(pq):
     eager work between replays, equals the eager result every time."""
     M, N, K = 64, 2048, 2048
     X, packed, ab = case(O.SEQ2, 77, M, N, K)
-    Xd, Pd, Ad = dev(X), dev(O.tile_codes(packed)), dev(ab)
+    Xd, Pd, Ad = dev(X), dev(O.tile_codes(packed, O.CODE_BITS[O.SEQ2])), dev(ab)
     Yg = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
