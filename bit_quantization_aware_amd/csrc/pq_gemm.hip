@@ -56,6 +56,12 @@
 #ifndef PQ_TILE_MIN_STAGES
 #define PQ_TILE_MIN_STAGES 4
 #endif
+// Blocks of a tiled launch with more output tiles x splits than this many
+// (a multiple of 8; two per CU): each block then takes several in turn
+// (0: one block per item).
+#ifndef PQ_TILE_PERSIST
+#define PQ_TILE_PERSIST 512
+#endif
 #ifndef PQ_STREAM_NW
 #define PQ_STREAM_NW 4
 #endif
@@ -218,47 +224,56 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int i16 = lane & 15, grp = lane >> 4;
 
-    // Block -> (m-tile, n-tile, split), consecutive indices on one XCD.
-    int t = blockIdx.x;
+    // Work items (m-tile, n-tile, split); the block takes items blockIdx.x,
+    // blockIdx.x + gridDim.x, ...  With the item count and the grid multiples
+    // of 8, item i is remapped so that consecutive indices -- the m-tiles
+    // sharing a weight tile -- fall to one XCD (the eight XCDs take
+    // workgroups round robin, so all of a block's items stay on its XCD).
+    const int nitems = g.mtiles * g.ntiles * g.splits;
     const int nb = gridDim.x;
-    if ((nb & 7) == 0) t = (t & 7) * (nb >> 3) + (t >> 3);
-    const int mt = t % g.mtiles;
-    t /= g.mtiles;
-    const int nt = t % g.ntiles;
-    const int split = t / g.ntiles;
-
+    const bool remap = (nitems & 7) == 0 && (nb & 7) == 0;
     const int M = g.M, N = g.N, K = g.K;
-    const int m0 = mt * kTileM, n0 = nt * C::TN;
-    const int kbeg = split * g.kps;
-    const int kend = min(K, kbeg + g.kps);
-    const int ns = (kend - kbeg) / kStageK;
-
-    // DMA sources: a wave-uniform base (advanced per stage) plus a fixed
-    // per-lane byte offset.  Rows >= M and columns >= N read row M-1 / N-1.
-    const uint8_t *xbase = reinterpret_cast<const uint8_t *>(g.X + static_cast<int64_t>(m0) * K + kbeg);
-    uint32_t xoff[C::XI];
-#pragma unroll
-    for (int q = 0; q < C::XI; ++q) {
-        const int r = 8 * (C::XI * w + q) + (lane >> 3);
-        const int c = (lane & 7) ^ xswz(r);
-        xoff[q] = static_cast<uint32_t>(static_cast<int64_t>(min(m0 + r, M - 1) - m0) * K * 2 + 16 * c);
-    }
-    // Code DMAs: one fetch covers SS stages of the block's columns, one
-    // 64-byte group of each.  DMA i of wave w brings columns 16 (NC w + i) ..
-    // +15, which is one 1-KB tile of the export order: lane l reads the
-    // 16-byte piece l >> 4 of column l & 15 (tile offset 64 (l & 15) +
-    // 16 (l >> 4)) and it lands as [piece][16 columns][16 B] in LDS.
     constexpr int NC = C::NC;
     constexpr int SS = C::SS;
-    uint32_t ccol[NC];
     const int cpiece = lane >> 4;
     const int cstage = (16 * cpiece) / C::CB, cwithin = (16 * cpiece) % C::CB;
+
+    // The current item: its tile, K range and DMA sources (a wave-uniform
+    // base, advanced per stage, plus a fixed per-lane byte offset; rows >= M
+    // and columns >= N read row M-1 / N-1).  Code DMAs: one fetch covers SS
+    // stages of the block's columns, one 64-byte group of each.  DMA i of
+    // wave w brings columns 16 (NC w + i) .. +15, which is one 1-KB tile of
+    // the export order: lane l reads the 16-byte piece l >> 4 of column
+    // l & 15 (tile offset 64 (l & 15) + 16 (l >> 4)) and it lands as
+    // [piece][16 columns][16 B] in LDS.
+    int m0 = 0, n0 = 0, split = 0, kbeg = 0, ns = 0;
+    int64_t g_first = 0;
+    const uint8_t *xbase = nullptr;
+    uint32_t xoff[C::XI], ccol[NC];
+    auto setup = [&](int item) {
+        int t = remap ? (item & 7) * (nitems >> 3) + (item >> 3) : item;
+        const int mt = t % g.mtiles;
+        t /= g.mtiles;
+        const int nt = t % g.ntiles;
+        split = t / g.ntiles;
+        m0 = mt * kTileM;
+        n0 = nt * C::TN;
+        kbeg = split * g.kps;
+        ns = (min(K, kbeg + g.kps) - kbeg) / kStageK;
+        xbase = reinterpret_cast<const uint8_t *>(g.X + static_cast<int64_t>(m0) * K + kbeg);
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
-        const int cl = min(n0 + 16 * (NC * w + i) + (lane & 15), N - 1);
-        ccol[i] = static_cast<uint32_t>((cl >> 4) * 1024 + (cl & 15) * 64);
-    }
-    const int64_t g_first = kbeg / (SS * kStageK);  // the split starts a group
+        for (int q = 0; q < C::XI; ++q) {
+            const int r = 8 * (C::XI * w + q) + (lane >> 3);
+            const int c = (lane & 7) ^ xswz(r);
+            xoff[q] = static_cast<uint32_t>(static_cast<int64_t>(min(m0 + r, M - 1) - m0) * K * 2 + 16 * c);
+        }
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            const int cl = min(n0 + 16 * (NC * w + i) + (lane & 15), N - 1);
+            ccol[i] = static_cast<uint32_t>((cl >> 4) * 1024 + (cl & 15) * 64);
+        }
+        g_first = kbeg / (SS * kStageK);  // the split starts a group
+    };
     const uint32_t lds_base = static_cast<uint32_t>(
         reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)lds));
 
@@ -284,10 +299,6 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
     };
 
     floatx4 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
     float rs = 0.f;
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     const bf16x2_t ones2 = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
@@ -406,14 +417,33 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
     // s + 1's fragments and multiplies stage s.  The wait count of each
     // unrolled phase comes from tile_wait: the DMAs issued after the newer of
     // the two it needs may stay in flight.
+    //
+    // A block with several items issues the next item's prologue DMAs as soon
+    // as the current item's ring is free (after the row-sum barrier), then
+    // writes the current item's outputs, so the next item's first loads are
+    // in flight during the epilogue.  The prologue wait stays correct with
+    // those stores outstanding: the loads retire in order among themselves,
+    // so at most (P - 2) XI + NC operations outstanding still means that
+    // code fetch 0 and activation stage 0 have landed.
     constexpr int U = 2 * C::SS > P ? 2 * C::SS : P;   // unroll: phases of slots and buffers
     static_assert(U % P == 0 && U % (2 * C::SS) == 0, "unroll covers both rings");
     Frag fr[2];
-    issue_c(0);
+    auto prologue = [&]() {
+        issue_c(0);
 #pragma unroll
-    for (int st = 0; st < P - 1; ++st) issue_x(st, st);
-    issue_c(1);
-    // prologue: activation stage 0 and code fetch 0 landed
+        for (int st = 0; st < P - 1; ++st) issue_x(st, st);
+        issue_c(1);
+    };
+    int item = blockIdx.x;
+    setup(item);
+    prologue();
+    for (;;) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    rs = 0.f;
+    // activation stage 0 and code fetch 0 landed
     wait_vmcnt<(P - 2) * C::XI + NC>();
     block_barrier();
     read_frags(std::integral_constant<int, 0>{}, fr[0]);
@@ -459,6 +489,7 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
         if (s + decltype(pc)::value < ns) step(s + decltype(pc)::value, pc);
     });
     wait_vmcnt<0>();
+    wait_lgkmcnt0();
 
     // Row sums: combine the four k-groups, publish row 16w + i16.
     rs += __shfl_xor(rs, 16);
@@ -466,12 +497,20 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
     if (grp == 0 && w < 4) ssum[16 * w + i16] = rs;
     __syncthreads();
 
-    // Epilogue: acc[i][j][e] is row m0 + 16 * ((i + w) & 3) + i16, column
-    // n0 + 64w + 16j + 4grp + e.
+    // The next item's prologue, into the ring every wave is done with.
+    const int e_m0 = m0, e_n0 = n0, e_split = split;
+    const int next = item + nb;
+    if (next < nitems) {
+        setup(next);
+        prologue();
+    }
+
+    // Epilogue: acc[i][j][e] is row e_m0 + 16 * ((i + w) & 3) + i16, column
+    // e_n0 + 64w + 16j + 4grp + e.
     const bool vec = (N & 3) == 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int n = n0 + 64 * w + 16 * j + 4 * grp;
+        const int n = e_n0 + 64 * w + 16 * j + 4 * grp;
         if (n >= N) continue;
         float al[4] = {1.f, 1.f, 1.f, 1.f};
         if (g.splits == 1) {
@@ -481,7 +520,7 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int rl = 16 * ((i + w) & 3) + i16;
-            const int m = m0 + rl;
+            const int m = e_m0 + rl;
             if (m >= M) continue;
             const float sr = g.off * ssum[rl];
             float v[4];
@@ -498,7 +537,7 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
                         if (n + e < N) g.Y[o + e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(al[e] * v[e]));
                 }
             } else {
-                float *dst = g.ws + static_cast<int64_t>(split) * M * N + o;
+                float *dst = g.ws + static_cast<int64_t>(e_split) * M * N + o;
                 if (vec) {
                     *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
                 } else {
@@ -508,6 +547,9 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
                 }
             }
         }
+    }
+    if (next >= nitems) break;
+    item = next;
     }
 }
 
@@ -970,8 +1012,11 @@ pq_status launch_tile(const GemmArgs &a, const GemmPlan &p, float *ws, hipStream
     TileArgs t{a.X, a.packed, a.alpha, a.Y, ws, a.M, a.N, a.K, mtiles, ntiles, p.splits, p.sps * kStageK,
                a.gstride, off, mul, a.alpha32};
     const int64_t total = static_cast<int64_t>(a.M) * a.N;
-    const int64_t blocks = static_cast<int64_t>(mtiles) * ntiles * p.splits;
-    if (blocks > INT32_MAX) return PQ_ERR_SHAPE;
+    const int64_t items = static_cast<int64_t>(mtiles) * ntiles * p.splits;
+    if (items > INT32_MAX) return PQ_ERR_SHAPE;
+    // More items than two blocks per CU: persistent blocks, each taking
+    // items in turn with the next item's first loads under the epilogue.
+    const int64_t blocks = PQ_TILE_PERSIST > 0 && items > PQ_TILE_PERSIST ? PQ_TILE_PERSIST : items;
     hipLaunchKernelGGL((k_gemm_tile<BITS, C::P, PQ_TILE_WN>), dim3(static_cast<unsigned>(blocks)), dim3(64 * PQ_TILE_WN),
                        0, s, t);
     if (p.splits > 1) {
