@@ -296,6 +296,47 @@ def test_gemm_caller_workspace_and_guards(M, N, K):
         check(Yg[ms, ns], O.gemm_ref_at(O.SEQ2, X, packed, ab, N, ms, ns), f"caller workspace {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("mode", [O.SEQ2, O.LSQ4, O.BINARY])
+@pytest.mark.parametrize("M,N,K", [(2100, 4000, 256), (1030, 7700, 512)])
+def test_gemm_persistent_tiles_full_compare(mode, M, N, K):
+    """More output tiles than the tiled launch has blocks (528 and 527
+    items of 64 x 256 for 512 blocks): blocks take several tiles in turn,
+    with and without the XCD order (item count a multiple of 8 or not),
+    ragged last row and column tiles; every output."""
+    print(f"[gemm persistent mode={mode} M={M} N={N} K={K}]", flush=True)
+    assert -(-M // 64) * -(-N // 256) > 512
+    X, packed, ab = make_case(mode, 31 * M + N + K + mode, M, N, K)
+    Y = gpu_gemm(mode, X, packed, ab, N)
+    check(Y, O.gemm_ref(mode, X, packed, ab, N), f"persistent m{mode} {M}x{N}x{K}")
+
+
+def test_gemm_training_forward_shape_sampled():
+    """The MobileLLM training forward's up projection at 16384 tokens
+    (1536 tiles for 512 persistent blocks) from codes with the binary32
+    scale, sampled outputs against the binary64 reference."""
+    M, N, K = 16384, 1536, 576
+    rng = np.random.default_rng(4242)
+    W = synth.normal_f32(rng, (N, K), 0.02)
+    alpha = O.alpha_init(O.SEQ2, W)
+    packed, _ = O.pack(O.SEQ2, W, alpha)
+    X = synth.to_bf16_bits(synth.normal_f32(rng, (M, K)))
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    pq.pq_gemm_f32a(O.SEQ2, M, N, K, dev(X), dev(O.tile_codes(packed, 2)), dev(alpha), Y)
+    torch.cuda.synchronize()
+    Yg = synth.bf16_bits_to_f32(host(Y)).astype(np.float64)
+    ms, ns = sample_points(rng, M, N, 4000)
+    # every output of the first and the last 64-row tile too
+    edge_m = np.repeat(np.r_[0:64, M - 64:M], N)
+    edge_n = np.tile(np.arange(N), 128)
+    ms, ns = np.concatenate([ms, edge_m]), np.concatenate([ns, edge_n])
+    # binary64 reference with the binary32 scale, on the sampled rows only
+    rows = np.unique(ms)
+    Yr = O.gemm_ref_f32a(O.SEQ2, X[rows], packed, alpha, N)
+    pos = {r: i for i, r in enumerate(rows)}
+    ref = Yr[[pos[m] for m in ms], ns]
+    check(Yg[ms, ns], ref, "training forward 16384x1536x576")
+
+
 def test_gemm_workspace_reused_across_shapes():
     """One workspace, sized for the largest of the shapes, through a sequence
     of GEMMs that use it differently (split-K partials of several sizes,
