@@ -62,6 +62,11 @@
 #ifndef PQ_TILE_PERSIST
 #define PQ_TILE_PERSIST 512
 #endif
+// 1: the tiled kernel takes its row sums on the matrix unit (one MFMA per
+// k-step with an all-ones A operand) instead of 4 v_dot2 per k-step.
+#ifndef PQ_TILE_RS_MFMA
+#define PQ_TILE_RS_MFMA 0
+#endif
 #ifndef PQ_STREAM_NW
 #define PQ_STREAM_NW 4
 #endif
@@ -75,6 +80,15 @@
 #endif
 #ifndef PQ_STREAM_TN
 #define PQ_STREAM_TN 4
+#endif
+// 2-bit streaming configurations with at least this many activation DMAs
+// per group (M >= 3) take the activation row sums on the matrix unit, one
+// MFMA per k-step against an all-ones operand, instead of 4 v_dot2 per DMA
+// on the VALU, which bounds these launches (16384^2 back to back: M = 16
+// 21.8 -> 19.1 us, M = 8 18.0 -> 16.4, M = 4 15.6 -> 15.1; M <= 2, with one
+// DMA per group, keeps the 4 v_dot2).
+#ifndef PQ_STREAM_RS_MFMA_XI
+#define PQ_STREAM_RS_MFMA_XI 2
 #endif
 // 4-bit streaming kernel: column tiles per block (with one activation DMA
 // per group, and with more), stages for 1, 2, 4 DMAs
@@ -300,6 +314,8 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
 
     floatx4 acc[4][4];
     float rs = 0.f;
+    floatx4 accrs = floatx4{0.f, 0.f, 0.f, 0.f};
+    const bf16x8 ones8 = __builtin_bit_cast(bf16x8, uint4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     const bf16x2_t ones2 = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
 
@@ -398,10 +414,15 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
                                                                          acc[i][j], 0, 0, 0);
             }
             const uint4 aw = f.a[T][0];
-            rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, aw.x), ones2, rs, false);
-            rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, aw.y), ones2, rs, false);
-            rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, aw.z), ones2, rs, false);
-            rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, aw.w), ones2, rs, false);
+            if constexpr (PQ_TILE_RS_MFMA != 0) {
+                // row m = 16 w + i16 of the tile, summed over the k-step
+                accrs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, __builtin_bit_cast(bf16x8, aw), accrs, 0, 0, 0);
+            } else {
+                rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, aw.x), ones2, rs, false);
+                rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, aw.y), ones2, rs, false);
+                rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, aw.z), ones2, rs, false);
+                rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, aw.w), ones2, rs, false);
+            }
             if constexpr (T == 0) {
                 __builtin_amdgcn_sched_barrier(0);
                 between();
@@ -443,6 +464,7 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
     rs = 0.f;
+    accrs = floatx4{0.f, 0.f, 0.f, 0.f};
     // activation stage 0 and code fetch 0 landed
     wait_vmcnt<(P - 2) * C::XI + NC>();
     block_barrier();
@@ -491,9 +513,14 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
     wait_vmcnt<0>();
     wait_lgkmcnt0();
 
-    // Row sums: combine the four k-groups, publish row 16w + i16.
-    rs += __shfl_xor(rs, 16);
-    rs += __shfl_xor(rs, 32);
+    // Row sums: combine the four k-groups, publish row 16w + i16 (from the
+    // matrix unit every lane of column i16 holds the whole sum).
+    if constexpr (PQ_TILE_RS_MFMA != 0) {
+        rs = accrs[0];
+    } else {
+        rs += __shfl_xor(rs, 16);
+        rs += __shfl_xor(rs, 32);
+    }
     if (grp == 0 && w < 4) ssum[16 * w + i16] = rs;
     __syncthreads();
 
@@ -696,6 +723,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
     float rsx[XI];
 #pragma unroll
     for (int q = 0; q < XI; ++q) rsx[q] = 0.f;
+    constexpr bool RSM = BITS == 2 && XI >= PQ_STREAM_RS_MFMA_XI;  // row sums on the matrix unit
+    floatx4 accr = floatx4{0.f, 0.f, 0.f, 0.f};
+    const bf16x8 ones8 = __builtin_bit_cast(bf16x8, uint4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
     // A-operand row of this lane; rows >= M repeat row M - 1 (an LDS broadcast).
     const int mrow = i16 < M ? i16 : M - 1;
     const int aoff = TN * 1024 + (mrow / RPL) * XQS + (mrow % RPL) * 16;
@@ -706,7 +736,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
 #pragma unroll
         for (int j = 0; j < TN; ++j) c[j] = *reinterpret_cast<const uint4 *>(sp + j * 1024 + lane * 16);
 #pragma unroll
-        for (int q = 0; q < XI; ++q) {
+        for (int q = 0; q < (RSM ? 0 : XI); ++q) {
             const uint4 v = *reinterpret_cast<const uint4 *>(sp + TN * 1024 + q * XQS + lane * 16);
             rsx[q] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.x), ones2, rsx[q], false);
             rsx[q] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.y), ones2, rsx[q], false);
@@ -744,6 +774,10 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
                 // order (the export's word order), matching chunks 2d, 2d + 1
                 const bf16x8 a_e = __builtin_bit_cast(bf16x8, ua[2 * d]);
                 const bf16x8 a_o = __builtin_bit_cast(bf16x8, ua[2 * d + 1]);
+                if constexpr (RSM) {
+                    accr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_e, ones8, accr, 0, 0, 0);
+                    accr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_o, ones8, accr, 0, 0, 0);
+                }
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     const uint32_t Dw = d == 0 ? c[j].x : d == 1 ? c[j].y : d == 2 ? c[j].z : c[j].w;
@@ -822,9 +856,16 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
     for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) red[(w * NACC + 4 * j + e) * 64 + lane] = acc[j][e];
-    // Row sums: reduce over the lanes that fetched chunks of the same row.
+    // Row sums: reduce over the lanes that fetched chunks of the same row
+    // (on the matrix unit: lane (0, grp) holds rows 4 grp .. 4 grp + 3).
+    if constexpr (RSM) {
+        if (i16 == 0) {
 #pragma unroll
-    for (int q = 0; q < XI; ++q) {
+            for (int e = 0; e < 4; ++e) rsum[w][4 * grp + e] = accr[e];
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < (RSM ? 0 : XI); ++q) {
         float v = rsx[q];
 #pragma unroll
         for (int o = RPL; o < 64; o <<= 1) v += __shfl_xor(v, o);
