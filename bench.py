@@ -257,8 +257,8 @@ def load_pmc(d, counters):
 def pmc_summarize(args):
     """HBM bytes per call of each step entry from the FETCH_SIZE and
     WRITE_SIZE passes of --pmc-workload (every launch of the call summed:
-    the quantizer's launches per team class, the M = 64 split-K finalize,
-    the M = 512 row-sum pass), each counter scaled by what it reads for the
+    the quantizer's launches per team class, the M = 64 split-K finalize),
+    each counter scaled by what it reads for the
     1 GiB copy; and the fused step's."""
     fetch = load_pmc(args.pmc_summarize[0], ("FETCH_SIZE",))
     write = load_pmc(args.pmc_summarize[1], ("WRITE_SIZE",))
@@ -293,7 +293,7 @@ def pmc_summarize(args):
         "it reads for a plain 1 GiB device copy in the same run (1 GiB read, 1 GiB written):",
         f"FETCH scale = {fscale:.4f}, WRITE scale = {wscale:.4f}. Per call of each step entry (the mean of",
         "three calls): every launch of the call summed -- the quantizer's launch per team class, the M = 64",
-        "split-K finalize, the M = 512 row-sum pass. fwd, bwd and pack are the 1.5B stack's; qat_step the",
+        "split-K finalize. fwd, bwd and pack are the 1.5B stack's; qat_step the",
         "125M stack's fused step.",
         "`sha` is the hash of the kernel sources the counters were taken on (bench.py reports",
         "`traffic` only while it matches).",
@@ -366,14 +366,13 @@ MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_M
                  "SQ_INSTS_MFMA", "SQ_BUSY_CYCLES", "SQ_INSTS_LDS", "SQ_ACTIVE_INST_VALU")
 SIMD_NUM = 1024   # 256 CUs x 4 SIMDs
 XCDS = 8          # GRBM_GUI_ACTIVE comes summed over the 8 XCDs
-# kernel-name parts of each GEMM of the step (M = 64 adds its split-K finalize,
-# M = 512 its row-sum pass)
+# kernel-name parts of each GEMM of the step (M = 64 adds its split-K finalize)
 GEMM_PARTS = {
     "gemm_m1": (r"k_gemm_stream<2, \d+, \d+, \d+, 1>",),
     "gemm_m4": (r"k_gemm_stream<2, \d+, \d+, \d+, 2>",),
     "gemm_m16": (r"k_gemm_stream<2, \d+, \d+, \d+, 8>",),
     "gemm_m64": (r"k_gemm_tile<2,", r"k_splitk_finalize"),
-    "gemm_m512": (r"k_gemm_big2<2>", r"k_rowsum"),
+    "gemm_m512": (r"k_gemm_big2<2>",),
 }
 
 
@@ -405,7 +404,7 @@ def mfma_summarize(args):
         "# MFMA utilisation of the bench.py step GEMMs (16384 x 16384, 2-bit; rocprofv3 PMC)",
         "",
         "One rocprofv3 `--pmc` pass of the counters below over `bench.py --pmc-workload` (one MI355X),",
-        "per call (mean of three; M = 64 adds its split-K finalize, M = 512 its row-sum pass).",
+        "per call (mean of three; M = 64 adds its split-K finalize).",
         "`util` = sum over SIMDs of SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x",
         f"{SIMD_NUM} SIMDs) -- the counter tool's MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES counts 16 cycles per",
         "16x16x32 bf16 MFMA); GRBM_GUI_ACTIVE includes the launch's ramp, so short launches read low;",

@@ -944,32 +944,6 @@ void launch_stream(const GemmArgs &a, hipStream_t s)
 
 constexpr int kNumCU = 256;  // MI355X / MI350X compute units
 
-// Sum of each activation row (bf16 -> binary32) for the large-M kernel's
-// level offset, one block of 256 threads per row: thread t adds the
-// 8-element chunks t, t + 256, ... in order, then the block combines its
-// lanes in a fixed butterfly and its waves in order.
-__global__ __launch_bounds__(256) void k_rowsum(const uint16_t *X, int K, float *rowsum)
-{
-    __shared__ float part[4];
-    const int64_t row = blockIdx.x;
-    const u32x4 *x = reinterpret_cast<const u32x4 *>(X + row * K);
-    const int nq = K / 8;
-    float acc = 0.f;
-    for (int q = threadIdx.x; q < nq; q += 256) {
-        const u32x4 v = __builtin_nontemporal_load(&x[q]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            acc += __builtin_bit_cast(float, v[e] << 16);
-            acc += __builtin_bit_cast(float, v[e] & 0xFFFF0000u);
-        }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
-    __syncthreads();
-    if (threadIdx.x == 0) rowsum[row] = ((part[0] + part[1]) + part[2]) + part[3];
-}
-
 // Estimated time (us) of a tiled launch with `splits` K splits, from
 // measurements at 16384^2 and the Llama-3-8B shapes: blocks run in rounds of
 // up to two per CU; one stage of a block takes about 0.56 us alone on its CU
@@ -996,7 +970,6 @@ struct GemmPlan {
     int64_t ws = 0;      // workspace bytes (0: none)
 };
 
-constexpr int64_t kWsAlign = 256;  // workspace pieces start on 256-byte boundaries
 
 // Tiled path: the K split of least estimated time, each split keeping at
 // least PQ_TILE_MIN_STAGES stages.
@@ -1036,7 +1009,6 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
         p.path = GemmPlan::STREAM;
     } else if (gemm_big_takes(BITS, M, N, K)) {
         p.path = GemmPlan::BIG;
-        p.ws = (M * 4 + kWsAlign - 1) / kWsAlign * kWsAlign;  // the activation row sums
     } else {
         plan_tile<BITS>(M, N, K, p);
     }
@@ -1138,9 +1110,7 @@ pq_status gemm(int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *pa
         else if (BITS == 1 && M <= 8) launch_stream<BITS, (BITS == 1 ? 8 : 4)>(a, s);
         else launch_stream<BITS, 16 / RPL>(a, s);
     } else if (plan.path == GemmPlan::BIG) {
-        float *rsum = static_cast<float *>(workspace);
-        hipLaunchKernelGGL(k_rowsum, dim3(static_cast<unsigned>(M)), dim3(256), 0, s, a.X, a.K, rsum);
-        const pq_status sb = launch_gemm_big(a, rsum, s);
+        const pq_status sb = launch_gemm_big(a, s);
         if (sb != PQ_OK) return sb;
     } else {
         const pq_status st = launch_tile<BITS>(a, plan, static_cast<float *>(workspace), s);

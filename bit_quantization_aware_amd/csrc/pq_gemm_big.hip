@@ -13,7 +13,8 @@
 // thousands there are enough output tiles for wider ones: here the 4 waves
 // of a block own 64 x 128 outputs each (2 x 2 waves, 4 x 8 MFMA tiles of
 // 16 x 16), so every activation fragment read from LDS feeds 8 MFMAs instead
-// of 4 and the row sums come from a separate pass; two blocks share a CU
+// of 4, and the activation row sums come from 4 extra MFMAs per stage
+// against an all-ones operand; two blocks share a CU
 // (80 KB of LDS each, 234 VGPRs per lane).  The waves' two halves split
 // either the block's rows (128-row blocks) or K (64-row blocks, for M too
 // small to give every CU two 128-row blocks); see BigCfg.  A 128 x 128 wave
@@ -92,7 +93,7 @@ struct BigCfg {
 constexpr int64_t kBigMaxK = int64_t(1) << 22;
 
 template <int KH>
-__global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, const float *rowsum, int mtiles)
+__global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, int mtiles)
 {
     using C = BigCfg<KH>;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kBigLds];
@@ -198,10 +199,25 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, const float *r
         for (int j = 0; j < 8; ++j)
             d[j] = *reinterpret_cast<const uint32_t *>(ca + BUF * kBigCBytes + j * 512 + P * 256);
     };
+    // Activation row sums for the level offset, on the matrix unit: of the
+    // two waves sharing a row half, column half WN sums row tiles 2 WN and
+    // 2 WN + 1 of every k-step with an all-ones A operand (4 MFMAs per stage
+    // beside 64); accrs[ii] is row tile 2 WN + ii of the wave's rows.
+    floatx4 accrs[2];
+    accrs[0] = accrs[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const bf16x8 ones8 = __builtin_bit_cast(bf16x8, uint4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+
     // MFMAs of one k-step: weights (16 columns) as the A operand, so each
     // lane ends with four consecutive columns of one row.
-    auto mma = [&](auto t_c, const uint4 (&a)[kRT], const uint32_t (&d)[8]) __attribute__((always_inline)) {
+    auto mma = [&](auto t_c, const uint4 (&a)[kRT], const uint32_t (&d)[8], auto wn_c) __attribute__((always_inline)) {
         constexpr int T = decltype(t_c)::value;
+        {
+            constexpr int WN = decltype(wn_c)::value;
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii)
+                accrs[ii] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, __builtin_bit_cast(bf16x8, a[2 * WN + ii]),
+                                                                    accrs[ii], 0, 0, 0);
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             // the code word's masked nibbles: codes 0..7 (k-step 0) and
@@ -220,6 +236,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, const float *r
         }
     };
 
+    // The pipeline, instantiated once per column half (the row tiles a wave
+    // sums are then a compile-time choice and its MFMA sequence stays
+    // unbranched).
+    auto pipeline = [&](auto wn_c) __attribute__((always_inline)) {
     // Prologue: code fetch 0, activation stages 0 .. P - 2, code fetch 1
     // (the issue order the wait model assumes); stage 0 and fetch 0 landed.
     issue_c(0);
@@ -250,14 +270,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, const float *r
         // k-step 0 of stage s (a0), reading k-step 1 (a1)
         read_a(std::integral_constant<int, p % kBigP>{}, std::integral_constant<int, 1>{}, a1);
         __builtin_amdgcn_sched_barrier(0);
-        mma(std::integral_constant<int, 0>{}, a0, dc[p & 1]);
+        mma(std::integral_constant<int, 0>{}, a0, dc[p & 1], wn_c);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
         // k-step 1 of stage s (a1), reading stage s + 1's k-step 0 and codes
         read_a(std::integral_constant<int, (p + 1) % kBigP>{}, std::integral_constant<int, 0>{}, a0);
         read_c(std::integral_constant<int, (p + 1) % kBigU>{}, dc[(p + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
-        mma(std::integral_constant<int, 1>{}, a1, dc[p & 1]);
+        mma(std::integral_constant<int, 1>{}, a1, dc[p & 1], wn_c);
         __builtin_amdgcn_sched_barrier(0);
     };
     int s = 0;
@@ -267,7 +287,19 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, const float *r
     static_for<0, kBigU - 1>([&](auto pc) __attribute__((always_inline)) {
         if (s + decltype(pc)::value < nit) step(s + decltype(pc)::value, pc);
     });
+    };
+    if (wn == 0) pipeline(std::integral_constant<int, 0>{});
+    else pipeline(std::integral_constant<int, 1>{});
     wait_vmcnt<0>();
+    // The row sums to LDS, past the K-half buffer below (the ring is free
+    // once every wave is here).
+    float *rsl = reinterpret_cast<float *>(lds) + 2 * (kRT * 8 * 4 * 64);
+    __syncthreads();
+    if (grp == 0) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) rsl[w * kWaveM + 16 * (2 * wn + ii) + i16] = accrs[ii][0];
+    }
+    if constexpr (KH == 1) __syncthreads();
     if constexpr (KH == 2) {
         // Add the second K half's sums to the first's through LDS (the ring
         // is free: every DMA has landed and, after the barrier, every read).
@@ -305,7 +337,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, const float *r
         for (int i = 0; i < kRT; ++i) {
             const int m = m0 + (KH == 1 ? wm * kWaveM : 0) + 16 * i + i16;
             if (m >= M) continue;
-            const float sr = g.off * rowsum[m];
+            const int r = 16 * i + i16;
+            // the row's sum: from the wave of its row half that owns row tile
+            // i (KH = 1), or the two K halves' owners added (KH = 2)
+            const float rsum = KH == 1 ? rsl[(2 * wm + (i >> 1)) * kWaveM + r]
+                                       : rsl[(i >> 1) * kWaveM + r] + rsl[(2 + (i >> 1)) * kWaveM + r];
+            const float sr = g.off * rsum;
             float v[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = al[e] * (g.mul * (acc[i][j][e] - sr));
@@ -337,18 +374,16 @@ int big_form(int bits, int64_t M, int64_t N, int64_t K)
 
 bool gemm_big_takes(int bits, int64_t M, int64_t N, int64_t K) { return big_form(bits, M, N, K) != 0; }
 
-pq_status launch_gemm_big(const GemmArgs &a, const float *rowsum, hipStream_t s)
+pq_status launch_gemm_big(const GemmArgs &a, hipStream_t s)
 {
     const int form = big_form(2, a.M, a.N, a.K);
     const int ntiles = (a.N + kBigN - 1) / kBigN;
     if (form == 1) {
         const int mtiles = (a.M + BigCfg<1>::BM - 1) / BigCfg<1>::BM;
-        hipLaunchKernelGGL(k_gemm_big2<1>, dim3(static_cast<unsigned>(mtiles * ntiles)), dim3(256), 0, s, a, rowsum,
-                           mtiles);
+        hipLaunchKernelGGL(k_gemm_big2<1>, dim3(static_cast<unsigned>(mtiles * ntiles)), dim3(256), 0, s, a, mtiles);
     } else if (form == 2) {
         const int mtiles = (a.M + BigCfg<2>::BM - 1) / BigCfg<2>::BM;
-        hipLaunchKernelGGL(k_gemm_big2<2>, dim3(static_cast<unsigned>(mtiles * ntiles)), dim3(256), 0, s, a, rowsum,
-                           mtiles);
+        hipLaunchKernelGGL(k_gemm_big2<2>, dim3(static_cast<unsigned>(mtiles * ntiles)), dim3(256), 0, s, a, mtiles);
     } else {
         return PQ_ERR_SHAPE;
     }

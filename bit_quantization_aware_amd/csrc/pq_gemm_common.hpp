@@ -155,8 +155,8 @@ pq_status gemm_run(int mode, int64_t M, int64_t N, int64_t K, const void *X, con
 int64_t gemm_workspace_need(int mode, int64_t M, int64_t N, int64_t K);
 
 // Large-M 2-bit path (pq_gemm_big.hip): whether it takes a GEMM of this
-// shape, and its launch (rowsum: the [M] activation row sums).
+// shape, and its launch (no workspace).
 bool gemm_big_takes(int bits, int64_t M, int64_t N, int64_t K);
-pq_status launch_gemm_big(const GemmArgs &a, const float *rowsum, hipStream_t s);
+pq_status launch_gemm_big(const GemmArgs &a, hipStream_t s);
 
 }  // namespace pq

@@ -1,7 +1,7 @@
 // pq_noalloc.hip -- pq_gemm_noalloc: the packed-weight GEMM for callers that
 // cannot allocate device memory (code under HIP graph capture, tight serving
 // loops, harnesses that forbid device allocation).  The GEMM kernels that need
-// scratch -- split-K partial sums, activation row sums -- use a fixed array
+// scratch -- split-K partial sums -- use a fixed array
 // inside the library instead of a caller's workspace.
 //
 // The array lives in this file as a device variable.  Its host-side name is

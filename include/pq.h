@@ -19,7 +19,7 @@
  *   Memory     Every array argument is a DEVICE pointer owned by the caller;
  *              the library keeps no pointer after the call returns and never
  *              allocates or frees device memory: the GEMM's scratch (split-K
- *              partial sums, activation row sums) is a caller-owned
+ *              partial sums) is a caller-owned
  *              workspace sized by pq_gemm_workspace_bytes.  The one
  *              exception is pq_gemm_noalloc, whose scratch is a fixed array
  *              inside the library (see there).  Arrays are row-major and
@@ -277,8 +277,8 @@ pq_status pq_pack_w4(int64_t rows, int64_t cols, const float *W, const float *al
  *     sums [splits, M, N] and a second kernel adds them in split order --
  *     splits * M * N * 4 bytes; otherwise none;
  *   large M at 2-bit widths (K >= 2048; M >= 1024, or M >= 512 when N gives
- *     at least 512 tiles of 64 x 256): the fp32 sums of the activation rows,
- *     M * 4 bytes rounded up to 256.
+ *     at least 512 tiles of 64 x 256): none (the kernel sums the activation
+ *     rows for the level offset itself).
  */
 int64_t pq_gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
 
@@ -348,8 +348,8 @@ pq_status pq_gemm_f32a(int mode, int64_t M, int64_t N, int64_t K, const void *X,
  * pq_gemm_noalloc -- pq_gemm for callers that cannot allocate device memory:
  * code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  Same arguments, kernels and results as pq_gemm, without the
- * workspace: the scratch the kernels need (split-K partial sums, activation
- * row sums; pq_gemm_workspace_bytes of the shape) is a fixed array of
+ * workspace: the scratch the kernels need (split-K partial sums;
+ * pq_gemm_workspace_bytes of the shape) is a fixed array of
  * PQ_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, looked up
  * on the first call made on that GPU and held until the process ends.  The
  * call allocates nothing and never waits on the host.

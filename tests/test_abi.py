@@ -149,7 +149,7 @@ def test_pack_and_gemm_argument_checks(pq):
 def test_gemm_workspace_size_query(pq):
     """The size query follows the kernel choice: none for the weight-streaming
     path (M <= 16), split-K partials when the tiled path splits K, the
-    activation row sums for the large-M 2-bit path; -1 for bad arguments."""
+    none for the large-M 2-bit path; -1 for bad arguments."""
     q = pq.pq_gemm_workspace_bytes
     for mode in range(7):
         for M in (1, 4, 16):
@@ -161,9 +161,9 @@ def test_gemm_workspace_size_query(pq):
     for mode in (2, 4):
         ws = q(mode, 64, 16384, 16384)
         assert ws > 0 and ws % (64 * 16384 * 4) == 0 and ws // (64 * 16384 * 4) >= 2
-    # 1024 rows at K >= 2048: the large-M path's row sums, M * 4 rounded to 256
-    assert q(2, 1024, 8192, 2048) == 4096
-    assert q(2, 1100, 8200, 2112) == (1100 * 4 + 255) // 256 * 256
+    # 1024 rows at K >= 2048: the large-M path sums the activation rows itself
+    assert q(2, 1024, 8192, 2048) == 0
+    assert q(2, 1100, 8200, 2112) == 0
     # a chip-filling tiled grid needs nothing
     assert q(4, 4096, 16384, 256) == 0
 
@@ -180,8 +180,9 @@ def test_gemm_workspace_checks(pq):
     assert L.pq_w2a16_gemm(M, N, K, A, A, B, A, MIS, ws, None) == 4                  # misaligned
     assert L.pq_w2a16_gemm(M, N, K, A, A, B, A, B, ws - 16, None) == 7               # too small
     assert L.pq_gemm_f32a(2, M, N, K, A, A, B, A, None, 0, None) == 1
-    assert L.pq_gemm(2, 1024, 8192, 2048, A, A, B, A, None, 0, None) == 1            # row sums
-    assert L.pq_gemm(2, 1024, 8192, 2048, A, A, B, A, B, 4095, None) == 7
+    assert L.pq_gemm(2, 256, 4096, 4096, A, A, B, A, None, 0, None) == 1             # tiled split-K
+    assert L.pq_gemm(2, 256, 4096, 4096, A, A, B, A, B, pq.pq_gemm_workspace_bytes(2, 256, 4096, 4096) - 16,
+                     None) == 7
 
 
 def test_library_holds_no_allocator():

@@ -201,8 +201,8 @@ def test_gemm_16384_sampled(mode, M):
 @pytest.mark.parametrize("M,N,K", [(1024, 8192, 2048), (1100, 8200, 2112), (1030, 8202, 2240),
                                    (512, 16384, 2048), (600, 16200, 2176), (520, 16202, 2048)])
 def test_gemm_large_m_sampled(mode, M, N, K):
-    """The large-M path (64 x 128 outputs per wave, row sums from a separate
-    pass), both forms: 128-row blocks (M >= 1024) and 64-row blocks whose
+    """The large-M path (64 x 128 outputs per wave, the activation row sums
+    taken inside the kernel on the matrix unit), both forms: 128-row blocks (M >= 1024) and 64-row blocks whose
     two wave pairs split K (the M = 512..600 cases); ragged M and N, N not a
     multiple of 4, K with a partial last 64-byte group and, for the first
     form, an odd number of 64-k stages; 4000 sampled outputs
@@ -273,8 +273,8 @@ def test_gemm_f32_alpha(mode, M, N, K):
 def test_gemm_caller_workspace_and_guards(M, N, K):
     """The workspace is the caller's: exactly pq_gemm_workspace_bytes bytes
     between canary guards, as is the output; the guards stay intact and the
-    result matches the reference (split-K partials, activation row sums, and
-    a shape that needs no workspace)."""
+    result matches the reference (split-K partials, and shapes that need no
+    workspace: the large-M path and weight streaming)."""
     from gpu_util import Guarded
 
     X, packed, ab = make_case(O.SEQ2, 500 + M + N, M, N, K)
@@ -339,8 +339,8 @@ def test_gemm_training_forward_shape_sampled():
 
 def test_gemm_workspace_reused_across_shapes():
     """One workspace, sized for the largest of the shapes, through a sequence
-    of GEMMs that use it differently (split-K partials of several sizes,
-    activation row sums, none), twice over: every result matches the
+    of GEMMs that use it differently (split-K partials of several sizes, and
+    paths that use none), twice over: every result matches the
     reference, whatever the previous call left in it."""
     shapes = [(64, 2048, 2048), (1024, 8192, 2048), (1, 1024, 4096), (256, 1536, 4096), (100, 1000, 2048),
               (4, 4096, 4096)]

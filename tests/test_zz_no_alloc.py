@@ -3,7 +3,7 @@ scratch is the library's fixed per-GPU array) -- against pq_gemm with a
 caller's workspace on the same inputs, through the C ABI: bit for bit (the
 same kernels), and within the GEMM bar of the binary64 oracle.  Two calls in
 a row, the second with a smaller input, for each path that uses scratch
-(split-K partials; activation row sums) and one that uses none; and a call
+(split-K partials) and paths that use none (large M, weight streaming); and a call
 captured into a HIP graph with no warm-up."""
 import ctypes
 
@@ -63,7 +63,7 @@ def check_ref(Yb, X, packed, ab, N, mode, what):
 
 @pytest.mark.parametrize("mode,first,second", [
     (O.SEQ2, (64, 16384, 16384), (64, 2048, 2048)),        # split-K partials: 32 MiB, then a smaller split
-    (O.SEQ2, (1024, 8192, 2048), (520, 16202, 2048)),      # activation row sums
+    (O.SEQ2, (1024, 8192, 2048), (520, 16202, 2048)),      # large-M path: no scratch
     (O.LSQ4, (100, 4096, 4096), (33, 512, 1024)),          # 4-bit tiles with and without a split
     (O.SEQ2, (16, 8192, 4096), (1, 1000, 1024)),           # weight streaming: no scratch
 ])
