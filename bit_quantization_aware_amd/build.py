@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpq.so")
-SOURCES = ["pq_quant.hip", "pq_gemm.hip", "pq_gemm_big.hip", "pq_stats.hip", "pq_noalloc.hip"]
+SOURCES = ["pq_quant.hip", "pq_gemm.hip", "pq_gemm_big.hip", "pq_gemm_wres.hip", "pq_stats.hip", "pq_noalloc.hip"]
 # the quantizer's kernels, one translation unit per mode (PQ_W1_BINARY .. PQ_W158_LSQ)
 MODE_SOURCE = "pq_quant_mode.hip"
 NUM_MODES = 7

@@ -52,6 +52,11 @@
 #ifndef PQ_TILE_P4
 #define PQ_TILE_P4 4
 #endif
+// Code fetches in the tiled kernel's LDS ring (2- and 4-bit; 1-bit keeps 2):
+// with 3, two fetches of weight codes are in flight behind the one in use.
+#ifndef PQ_TILE_NCB
+#define PQ_TILE_NCB 2
+#endif
 // Fewest K stages per split of the tiled kernel's K split.
 #ifndef PQ_TILE_MIN_STAGES
 #define PQ_TILE_MIN_STAGES 4
@@ -189,6 +194,7 @@ struct TileArgs {
     int64_t gstride;         // bytes per 64-byte group of all rows
     float off, mul;          // level = mul * (v - off) for the decoded operand v
     const float *alpha32;    // [N] binary32 scale, or nullptr (use alpha)
+    int nfast;               // item order: column tile fastest (1) or row tile fastest (0)
 };
 
 
@@ -204,10 +210,12 @@ struct TileCfg {
     static constexpr int P = BITS == 2 ? PQ_TILE_P2 : PQ_TILE_P4;  // activation ring depth
     static constexpr int XI = 8 / WN;                    // activation DMAs per wave per stage
     static constexpr int NC = 4;                         // code DMAs per wave per fetch
-    static constexpr int LDS = P * XBYTES + 2 * CSS;
+    static constexpr int NCB = BITS == 1 ? 2 : PQ_TILE_NCB;  // code fetches in the ring
+    static constexpr int LDS = P * XBYTES + NCB * CSS;
     static_assert(WN == 4 || WN == 8, "block width");
     static_assert(NC * WN * 1024 == CSS, "one fetch is NC 1-KB DMAs per wave");
     static_assert(P >= 3, "activation ring depth");
+    static_assert(NCB == 2 || NCB == 3, "code ring depth");
 };
 
 
@@ -229,11 +237,16 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
 {
     using C = TileCfg<BITS, WN>;
     static_assert(P >= 3, "ring depth");
-    // LDS: P activation stages, then two code fetches (double buffer).
+    // LDS: P activation stages, then NCB code fetches.  Between items,
+    // activation slot P - 1 stages the outputs: the next item's prologue
+    // fills slots 0 .. P-2 only, and its first refill of slot P - 1 comes
+    // after a barrier that every wave reaches past its epilogue.
     __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
     __shared__ float ssum[kTileM];
     constexpr int XR = 0;                 // activation region
     constexpr int CR = P * C::XBYTES;     // code region
+    constexpr int NCB = C::NCB;
+    static_assert(C::LDS + kTileM * 4 <= 80 * 1024, "two blocks per CU");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -243,8 +256,9 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
     // Work items (m-tile, n-tile, split); the block takes items blockIdx.x,
     // blockIdx.x + gridDim.x, ...  With the item count and the grid multiples
     // of 8, item i is remapped so that consecutive indices -- the m-tiles
-    // sharing a weight tile -- fall to one XCD (the eight XCDs take
-    // workgroups round robin, so all of a block's items stay on its XCD).
+    // sharing a weight tile, or with g.nfast the n-tiles sharing a row
+    // tile -- fall to one XCD (the eight XCDs take workgroups round robin, so
+    // all of a block's items stay on its XCD).
     const int nitems = g.mtiles * g.ntiles * g.splits;
     const int nb = gridDim.x;
     const bool remap = (nitems & 7) == 0 && (nb & 7) == 0;
@@ -268,10 +282,18 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
     uint32_t xoff[C::XI], ccol[NC];
     auto setup = [&](int item) {
         int t = remap ? (item & 7) * (nitems >> 3) + (item >> 3) : item;
-        const int mt = t % g.mtiles;
-        t /= g.mtiles;
-        const int nt = t % g.ntiles;
-        split = t / g.ntiles;
+        int mt, nt;
+        if (g.nfast) {
+            nt = t % g.ntiles;
+            t /= g.ntiles;
+            mt = t % g.mtiles;
+            split = t / g.mtiles;
+        } else {
+            mt = t % g.mtiles;
+            t /= g.mtiles;
+            nt = t % g.ntiles;
+            split = t / g.ntiles;
+        }
         m0 = mt * kTileM;
         n0 = nt * C::TN;
         kbeg = split * g.kps;
@@ -301,17 +323,17 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
         for (int q = 0; q < C::XI; ++q)
             dma16(xs, xoff[q], lds_base + XR + slot * C::XBYTES + (C::XI * w + q) * 1024);
     };
-    // Code DMA of fetch G (group g_first + G) into buffer G & 1; a lane
-    // whose stage lies past the split's end re-reads the last stage (in
-    // bounds, never used), which lies in the same group or, for a fetch
+    // Code DMA of fetch G (group g_first + G) into buffer `buf` (G mod NCB);
+    // a lane whose stage lies past the split's end re-reads the last stage
+    // (in bounds, never used), which lies in the same group or, for a fetch
     // wholly past the end, in the split's last group.
-    auto issue_c = [&](int G) {
+    auto issue_c = [&](int G, int buf) {
         const int st = min(G * SS + cstage, ns - 1);
         const uint8_t *cb = g.packed + (g_first + min(G, (ns - 1) / SS)) * g.gstride;
         const uint32_t po = static_cast<uint32_t>((((st % SS) * C::CB + cwithin) >> 4) * 16);
 #pragma unroll
         for (int i = 0; i < NC; ++i)
-            dma16(cb, ccol[i] + po, lds_base + CR + (G & 1) * C::CSS + (NC * w + i) * 1024);
+            dma16(cb, ccol[i] + po, lds_base + CR + buf * C::CSS + (NC * w + i) * 1024);
     };
 
     floatx4 acc[4][4];
@@ -341,12 +363,12 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
         uint4 a[2][4];
         uint32_t d[4][BITS == 4 ? 2 : 1];
     };
-    // Fragments of stage st, with PH = st mod 2*SS known at compile time
-    // (activation slot PH mod P, code buffer (PH / SS) & 1, stage PH mod SS).
+    // Fragments of stage st, with PH = st mod U known at compile time
+    // (activation slot PH mod P, code buffer (PH / SS) mod NCB, stage PH mod SS).
     auto read_frags = [&](auto ph_c, Frag &f) {
         constexpr int PH = decltype(ph_c)::value;
         constexpr int SLOT = PH % P;
-        constexpr int CBUF = (PH / C::SS) & 1;
+        constexpr int CBUF = (PH / C::SS) % NCB;
         constexpr int CST = PH % C::SS;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -433,9 +455,9 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
         });
     };
 
-    // Pipeline.  Activation DMAs run P - 1 stages ahead; code fetch G + 2 is
-    // issued in the last iteration that reads fetch G's buffer (after its
-    // barrier), SS stages before it is needed.  Iteration s waits for
+    // Pipeline.  Activation DMAs run P - 1 stages ahead; code fetch G + NCB
+    // is issued in the last iteration that reads fetch G's buffer (after its
+    // barrier), (NCB - 1) SS stages before it is needed.  Iteration s waits for
     // stage s + 1 (and its codes), passes the barrier, refills, reads stage
     // s + 1's fragments and multiplies stage s.  The wait count of each
     // unrolled phase comes from tile_wait: the DMAs issued after the newer of
@@ -446,16 +468,17 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
     // writes the current item's outputs, so the next item's first loads are
     // in flight during the epilogue.  The prologue wait stays correct with
     // those stores outstanding: the loads retire in order among themselves,
-    // so at most (P - 2) XI + NC operations outstanding still means that
-    // code fetch 0 and activation stage 0 have landed.
-    constexpr int U = 2 * C::SS > P ? 2 * C::SS : P;   // unroll: phases of slots and buffers
-    static_assert(U % P == 0 && U % (2 * C::SS) == 0, "unroll covers both rings");
+    // so at most (P - 2) XI + (NCB - 1) NC operations outstanding still
+    // means that code fetch 0 and activation stage 0 have landed.
+    constexpr int U = lcm_int(P, NCB * C::SS);   // unroll: phases of slots and buffers
+    static_assert(U % P == 0 && U % (NCB * C::SS) == 0, "unroll covers both rings");
     Frag fr[2];
     auto prologue = [&]() {
-        issue_c(0);
+        issue_c(0, 0);
 #pragma unroll
         for (int st = 0; st < P - 1; ++st) issue_x(st, st);
-        issue_c(1);
+#pragma unroll
+        for (int G = 1; G < NCB; ++G) issue_c(G, G);
     };
     int item = blockIdx.x;
     setup(item);
@@ -468,7 +491,7 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
     rs = 0.f;
     accrs = floatx4{0.f, 0.f, 0.f, 0.f};
     // activation stage 0 and code fetch 0 landed
-    wait_vmcnt<(P - 2) * C::XI + NC>();
+    wait_vmcnt<(P - 2) * C::XI + (NCB - 1) * NC>();
     block_barrier();
     read_frags(std::integral_constant<int, 0>{}, fr[0]);
     auto step = [&](int s, auto pc) {
@@ -478,7 +501,7 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
         // codes, read in the previous iteration: those reads (long since
         // issued) complete before the barrier.
         wait_lgkmcnt0();
-        wait_vmcnt<tile_wait(p, P, C::SS, C::XI, NC, U)>();
+        wait_vmcnt<tile_wait(p, P, C::SS, C::XI, NC, U, NCB)>();
         block_barrier();
         // A wave just released from the barrier issues at raised priority
         // until its refill is out: its fragment reads, first MFMAs and DMAs
@@ -488,7 +511,7 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
         __builtin_amdgcn_s_setprio(1);
         auto refill = [&]() {
             issue_x(s + P - 1, (p + P - 1) % P);
-            if constexpr (code_now) issue_c((s + 1) / C::SS + 1);
+            if constexpr (code_now) issue_c((s + 1) / C::SS + NCB - 1, ((p + 1) / C::SS + NCB - 1) % NCB);
         };
         if (PQ_TILE_DMA_MID == 0) refill();
         read_frags(std::integral_constant<int, (p + 1) % U>{}, fr[(p + 1) & 1]);
@@ -514,6 +537,8 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
     });
     wait_vmcnt<0>();
     wait_lgkmcnt0();
+    // every wave's DMAs have landed and its reads are done: slot P - 1 is free
+    block_barrier();
 
     // Row sums: combine the four k-groups, publish row 16w + i16 (from the
     // matrix unit every lane of column i16 holds the whole sum).
@@ -535,38 +560,71 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
     }
 
     // Epilogue: acc[i][j][e] is row e_m0 + 16 * ((i + w) & 3) + i16, column
-    // e_n0 + 64w + 16j + 4grp + e.
-    const bool vec = (N & 3) == 0;
+    // e_n0 + 64w + 16j + 4grp + e; four lanes hold a row's 64 columns in
+    // 8-byte pieces.  One split: each wave passes its rows through 2 KB of
+    // slot P - 1, 16 rows at a time, so that every store instruction writes
+    // 16 bytes per lane and eight whole 128-byte row segments (16-byte
+    // chunks XOR-swizzled by row for the LDS banks).  Several splits: fp32
+    // partials, 16 bytes per lane as held.
+    if (g.splits == 1) {
+        uint8_t *stg = lds + XR + (P - 1) * C::XBYTES + w * 2048;
+        const int nw = e_n0 + 64 * w + 8 * (lane & 7);   // this lane's 8 output columns
+        const bool vec8 = (N & 7) == 0;
+        float al[4][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int n = e_n0 + 64 * w + 16 * j + 4 * grp;
-        if (n >= N) continue;
-        float al[4] = {1.f, 1.f, 1.f, 1.f};
-        if (g.splits == 1) {
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) al[e] = n + e < N ? col_scale(g.alpha, g.alpha32, n + e) : 0.f;
-        }
+            for (int e = 0; e < 4; ++e) {
+                const int n = e_n0 + 64 * w + 16 * j + 4 * grp + e;
+                al[j][e] = n < N ? col_scale(g.alpha, g.alpha32, n) : 0.f;
+            }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int rl = 16 * ((i + w) & 3) + i16;
-            const int m = e_m0 + rl;
-            if (m >= M) continue;
-            const float sr = g.off * ssum[rl];
-            float v[4];
+            const int rt = (i + w) & 3;
+            const float sr = g.off * ssum[16 * rt + i16];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = g.mul * (acc[i][j][e] - sr);
-            const int64_t o = static_cast<int64_t>(m) * N + n;
-            if (g.splits == 1) {
-                if (vec) {
-                    *reinterpret_cast<u32x2 *>(g.Y + o) =
-                        u32x2{pack_bf16x2(al[0] * v[0], al[1] * v[1]), pack_bf16x2(al[2] * v[2], al[3] * v[3])};
-                } else {
+            for (int j = 0; j < 4; ++j) {
+                float v[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n + e < N) g.Y[o + e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(al[e] * v[e]));
+                for (int e = 0; e < 4; ++e) v[e] = g.mul * (acc[i][j][e] - sr);
+                const int ch = (2 * j + (grp >> 1)) ^ (i16 & 7);
+                *reinterpret_cast<u32x2 *>(stg + i16 * 128 + ch * 16 + (grp & 1) * 8) =
+                    u32x2{pack_bf16x2(al[j][0] * v[0], al[j][1] * v[1]), pack_bf16x2(al[j][2] * v[2], al[j][3] * v[3])};
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int r = (lane >> 3) + 8 * h;
+                const uint4 d = *reinterpret_cast<const uint4 *>(stg + r * 128 + (((lane & 7) ^ (r & 7)) << 4));
+                const int m = e_m0 + 16 * rt + r;
+                if (m < M && nw < N) {
+                    uint16_t *y = g.Y + static_cast<int64_t>(m) * N + nw;
+                    if (vec8) {
+                        *reinterpret_cast<uint4 *>(y) = d;
+                    } else {
+                        const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (nw + e < N) y[e] = static_cast<uint16_t>(dw[e >> 1] >> (16 * (e & 1)));
+                    }
                 }
-            } else {
-                float *dst = g.ws + static_cast<int64_t>(e_split) * M * N + o;
+            }
+        }
+    } else {
+        const bool vec = (N & 3) == 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = e_n0 + 64 * w + 16 * j + 4 * grp;
+            if (n >= N) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rl = 16 * ((i + w) & 3) + i16;
+                const int m = e_m0 + rl;
+                if (m >= M) continue;
+                const float sr = g.off * ssum[rl];
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = g.mul * (acc[i][j][e] - sr);
+                float *dst = g.ws + static_cast<int64_t>(e_split) * M * N + static_cast<int64_t>(m) * N + n;
                 if (vec) {
                     *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
                 } else {
@@ -964,7 +1022,7 @@ double tile_cost(int64_t tiles, int stages, int splits, int64_t M, int64_t N)
 // How a GEMM of one shape runs, and the workspace it needs: the plan is a
 // pure function of (width, M, N, K), so the size query and the launch agree.
 struct GemmPlan {
-    enum Path { STREAM, TILE, BIG } path = STREAM;
+    enum Path { STREAM, TILE, BIG, WRES } path = STREAM;
     int splits = 1;      // TILE: K splits
     int sps = 0;         // TILE: stages per split (whole 64-byte groups)
     int64_t ws = 0;      // workspace bytes (0: none)
@@ -1009,6 +1067,8 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
         p.path = GemmPlan::STREAM;
     } else if (gemm_big_takes(BITS, M, N, K)) {
         p.path = GemmPlan::BIG;
+    } else if (gemm_wres_takes(BITS, M, N, K)) {
+        p.path = GemmPlan::WRES;
     } else {
         plan_tile<BITS>(M, N, K, p);
     }
@@ -1024,8 +1084,15 @@ pq_status launch_tile(const GemmArgs &a, const GemmPlan &p, float *ws, hipStream
     // the tile kernel's 4-bit operand is 2 + c/8 (the stream kernel's 128 + c)
     const float off = BITS != 4 ? a.off : 2.0f + (a.off - 128.0f) / 8.0f;
     const float mul = BITS != 4 ? a.mul : 8.0f * a.mul;
+    // Item order: the blocks of one XCD take consecutive items and share its
+    // L2.  Row tile fastest, each XCD reads the activations of all rows
+    // (up to 8 copies, one per XCD, or one per column tile if fewer) and a
+    // share of the codes; column tile fastest, the other way round.  Take
+    // the order of fewer HBM bytes.
+    const double xb = 2.0 * a.M * a.K, cb = static_cast<double>(a.N) * a.K * BITS / 8.0;
+    const int nfast = std::min(8, mtiles) * cb + xb < cb + std::min(8, ntiles) * xb;
     TileArgs t{a.X, a.packed, a.alpha, a.Y, ws, a.M, a.N, a.K, mtiles, ntiles, p.splits, p.sps * kStageK,
-               a.gstride, off, mul, a.alpha32};
+               a.gstride, off, mul, a.alpha32, nfast};
     const int64_t total = static_cast<int64_t>(a.M) * a.N;
     const int64_t items = static_cast<int64_t>(mtiles) * ntiles * p.splits;
     if (items > INT32_MAX) return PQ_ERR_SHAPE;
@@ -1112,6 +1179,9 @@ pq_status gemm(int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *pa
     } else if (plan.path == GemmPlan::BIG) {
         const pq_status sb = launch_gemm_big(a, s);
         if (sb != PQ_OK) return sb;
+    } else if (plan.path == GemmPlan::WRES) {
+        const pq_status sw = launch_gemm_wres(a, s);
+        if (sw != PQ_OK) return sw;
     } else {
         const pq_status st = launch_tile<BITS>(a, plan, static_cast<float *>(workspace), s);
         if (st != PQ_OK) return st;

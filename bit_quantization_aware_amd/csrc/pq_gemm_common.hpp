@@ -49,43 +49,54 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 // K per pipeline stage of the tiled kernels.
 constexpr int kStageK = 64;
 
+constexpr int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
+constexpr int lcm_int(int a, int b) { return a / gcd_int(a, b) * b; }
+
 // Activation LDS swizzle: chunk c of tile row r sits in slot c ^ xswz(r).
 // Rows 0-7 (and 8-15) get distinct slots and rows r, r + 8 differ in the
 // slot's low bit, so the 16 rows one A-operand read touches are spread over
 // all banks whether the LDS serves 8 or 16 lanes of a 16-byte read per clock.
 __device__ __forceinline__ int xswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-// DMA bookkeeping of the tiled kernel's pipeline, evaluated at compile time.
-// Issue order: code fetch 0, activation stages 0 .. P-2, code fetch 1; then
-// iteration j issues activation stage j + P - 1 and, when (j + 1) % SS == 0,
-// code fetch (j + 1) / SS + 1.  Iteration s needs activation stage s + 1 and
-// code fetch (s + 1) / SS landed; loads retire in order, so the largest safe
-// vmcnt is the number of DMA instructions issued after the newer of the two.
-// Issue "times" only order the events.
-constexpr int tile_t_x(int k, int P) { return k <= P - 2 ? 1 + k : P + 1 + 2 * (k - P + 1); }
-constexpr int tile_t_c(int F, int P, int SS) { return F == 0 ? 0 : F == 1 ? P : P + 2 + 2 * ((F - 1) * SS - 1); }
-constexpr int tile_wait_at(int s, int P, int SS, int XI, int NC)
+// DMA bookkeeping of the tiled kernels' pipelines, evaluated at compile
+// time, for a ring of P activation stages and NCB code fetches of SS stages.
+// Issue order: code fetch 0, activation stages 0 .. P-2, code fetches
+// 1 .. NCB-1; then iteration j issues activation stage j + P - 1 and, when
+// (j + 1) % SS == 0, code fetch (j + 1) / SS + NCB - 1.  Iteration s needs
+// activation stage s + 1 and code fetch (s + 1) / SS landed; loads retire in
+// order, so the largest safe vmcnt is the number of DMA instructions issued
+// after the newer of the two.  Issue "times" only order the events.
+constexpr int tile_t_x(int k, int P, int NCB)
 {
-    const int a = tile_t_x(s + 1, P), b = tile_t_c((s + 1) / SS, P, SS);
+    return k <= P - 2 ? 1 + k : P + NCB - 1 + 2 * (k - P + 1);
+}
+constexpr int tile_t_c(int F, int P, int SS, int NCB)
+{
+    return F == 0 ? 0 : F < NCB ? P + F - 1 : P + NCB + 2 * ((F - NCB + 1) * SS - 1);
+}
+constexpr int tile_wait_at(int s, int P, int SS, int XI, int NC, int NCB)
+{
+    const int a = tile_t_x(s + 1, P, NCB), b = tile_t_c((s + 1) / SS, P, SS, NCB);
     const int newest = a > b ? a : b;
     int n = 0;
     for (int st = 0; st < P - 1; ++st)
         if (1 + st > newest) n += XI;
-    if (P > newest) n += NC;
+    for (int F = 1; F < NCB; ++F)
+        if (P + F - 1 > newest) n += NC;
     for (int j = 0; j < s; ++j) {
-        if (P + 1 + 2 * j > newest) n += XI;
-        if ((j + 1) % SS == 0 && P + 2 + 2 * j > newest) n += NC;
+        if (P + NCB - 1 + 2 * j > newest) n += XI;
+        if ((j + 1) % SS == 0 && P + NCB + 2 * j > newest) n += NC;
     }
     return n;
 }
 // The wait of unrolled phase p: the smallest safe count over the iterations
 // s = p, p + U, ... (the first ones included; steady state is reached well
 // within the range scanned).
-constexpr int tile_wait(int p, int P, int SS, int XI, int NC, int U)
+constexpr int tile_wait(int p, int P, int SS, int XI, int NC, int U, int NCB = 2)
 {
     int best = 1 << 30;
-    for (int s = p; s < 4 * U + 2 * P + 2 * SS; s += U) {
-        const int w = tile_wait_at(s, P, SS, XI, NC);
+    for (int s = p; s < 4 * U + 2 * P + 2 * NCB * SS; s += U) {
+        const int w = tile_wait_at(s, P, SS, XI, NC, NCB);
         best = w < best ? w : best;
     }
     return best;
@@ -158,5 +169,10 @@ int64_t gemm_workspace_need(int mode, int64_t M, int64_t N, int64_t K);
 // shape, and its launch (no workspace).
 bool gemm_big_takes(int bits, int64_t M, int64_t N, int64_t K);
 pq_status launch_gemm_big(const GemmArgs &a, hipStream_t s);
+
+// Short-K, many-row 2-bit path with resident codes (pq_gemm_wres.hip):
+// whether it takes a GEMM of this shape, and its launch (no workspace).
+bool gemm_wres_takes(int bits, int64_t M, int64_t N, int64_t K);
+pq_status launch_gemm_wres(const GemmArgs &a, hipStream_t s);
 
 }  // namespace pq

@@ -253,7 +253,7 @@ def test_gemm_llama3_8b_sampled(M):
 
 @pytest.mark.parametrize("mode", DEPLOYABLE)
 @pytest.mark.parametrize("M,N,K", [(1, 96, 1024), (16, 257, 512), (64, 576, 576), (256, 1536, 576),
-                                   (512, 576, 1536)])
+                                   (512, 576, 1536), (2048, 576, 576)])
 def test_gemm_f32_alpha(mode, M, N, K):
     """The training forward's product: codes + the binary32 alpha (no bf16
     rounding of the scale), every output against the binary64 reference."""
@@ -311,9 +311,10 @@ def test_gemm_persistent_tiles_full_compare(mode, M, N, K):
 
 
 def test_gemm_training_forward_shape_sampled():
-    """The MobileLLM training forward's up projection at 16384 tokens
-    (1536 tiles for 512 persistent blocks) from codes with the binary32
-    scale, sampled outputs against the binary64 reference."""
+    """The MobileLLM training forward's up projection at 16384 tokens from
+    codes with the binary32 scale (1536 tiles of 64 x 256, runs of four row
+    tiles per block of the resident-code kernel), sampled outputs against
+    the binary64 reference."""
     M, N, K = 16384, 1536, 576
     rng = np.random.default_rng(4242)
     W = synth.normal_f32(rng, (N, K), 0.02)
@@ -335,6 +336,34 @@ def test_gemm_training_forward_shape_sampled():
     pos = {r: i for i, r in enumerate(rows)}
     ref = Yr[[pos[m] for m in ms], ns]
     check(Yg[ms, ns], ref, "training forward 16384x1536x576")
+
+
+def _wres_runs(M, N):
+    """(row tiles, blocks) of the resident-code launch: 64 x 256 tiles; per
+    column tile as many runs of row tiles as 512 blocks allow, then as few as
+    give the same longest run."""
+    mt, nt = -(-M // 64), -(-N // 256)
+    rmax = max(1, min(mt, 512 // nt))
+    runlen = -(-mt // rmax)
+    return mt * nt, nt * -(-mt // runlen)
+
+
+@pytest.mark.parametrize("mode,M,N,K", [(O.SEQ2, 1030, 600, 576), (O.TERNARY, 1030, 600, 576),
+                                        (O.LSQ2, 1030, 600, 576), (O.LSQ158, 1030, 600, 576),
+                                        (O.SEQ2, 8380, 1102, 192), (O.SEQ2, 2100, 200, 704),
+                                        (O.SEQ2, 1024, 256, 64), (O.LSQ2, 3000, 515, 640)])
+def test_gemm_short_k_resident_codes_full_compare(mode, M, N, K):
+    """2-bit GEMMs with K <= 704 and M >= 1024 (the resident-code kernel):
+    ragged last row tile, N not a multiple of 256, 16, 8 or 4 (the
+    element-wise store), one K stage, the largest K, and 655 tiles on 330
+    blocks (runs of one and two row tiles); every output."""
+    print(f"[gemm resident codes mode={mode} M={M} N={N} K={K}]", flush=True)
+    tiles, nb = _wres_runs(M, N)
+    if (M, N) == (8380, 1102):
+        assert tiles > nb
+    X, packed, ab = make_case(mode, 13 * M + N + K + mode, M, N, K)
+    Y = gpu_gemm(mode, X, packed, ab, N)
+    check(Y, O.gemm_ref(mode, X, packed, ab, N), f"resident codes m{mode} {M}x{N}x{K}")
 
 
 def test_gemm_workspace_reused_across_shapes():
