@@ -324,35 +324,59 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, int mtiles)
     }
 
     // Epilogue: acc[i][j][e] is row m0 + wm*kWaveM (KH = 1) + 16 i + i16, column
-    // n0 + wn*128 + 16 j + 4 grp + e.
-    const bool vec = (N & 3) == 0;
+    // n0 + wn*128 + 16 j + 4 grp + e; four lanes hold a row's 128 columns in
+    // 8-byte pieces.  Each wave writes its 64 x 128 outputs to 16 KB of LDS
+    // and reads them back by rows, so that every store instruction writes 16
+    // bytes per lane and four whole 256-byte row segments (16-byte chunks
+    // XOR-swizzled by row for the LDS banks).  The staging area is the ring
+    // below the row sums (KH = 1), or the wave's own K-half buffer, already
+    // read (KH = 2).
+    uint8_t *stg = lds + (KH == 1 ? w * 16384 : wn * (kRT * 8 * 4 * 64 * 4));
+    float sr[kRT];
+#pragma unroll
+    for (int i = 0; i < kRT; ++i) {
+        const int r = 16 * i + i16;
+        // the row's sum: from the wave of its row half that owns row tile
+        // i (KH = 1), or the two K halves' owners added (KH = 2)
+        const float rsum = KH == 1 ? rsl[(2 * wm + (i >> 1)) * kWaveM + r]
+                                   : rsl[(i >> 1) * kWaveM + r] + rsl[(2 + (i >> 1)) * kWaveM + r];
+        sr[i] = g.off * rsum;
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const int n = n0 + wn * 128 + 16 * j + 4 * grp;
-        if (n >= N) continue;
         float al[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) al[e] = n + e < N ? col_scale(g.alpha, g.alpha32, n + e) : 0.f;
+        for (int e = 0; e < 4; ++e) {
+            const int n = n0 + wn * 128 + 16 * j + 4 * grp + e;
+            al[e] = n < N ? col_scale(g.alpha, g.alpha32, n) : 0.f;
+        }
 #pragma unroll
         for (int i = 0; i < kRT; ++i) {
-            const int m = m0 + (KH == 1 ? wm * kWaveM : 0) + 16 * i + i16;
-            if (m >= M) continue;
-            const int r = 16 * i + i16;
-            // the row's sum: from the wave of its row half that owns row tile
-            // i (KH = 1), or the two K halves' owners added (KH = 2)
-            const float rsum = KH == 1 ? rsl[(2 * wm + (i >> 1)) * kWaveM + r]
-                                       : rsl[(i >> 1) * kWaveM + r] + rsl[(2 + (i >> 1)) * kWaveM + r];
-            const float sr = g.off * rsum;
             float v[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = al[e] * (g.mul * (acc[i][j][e] - sr));
-            const int64_t o = static_cast<int64_t>(m) * N + n;
-            if (vec) {
-                *reinterpret_cast<u32x2 *>(g.Y + o) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-            } else {
+            for (int e = 0; e < 4; ++e) v[e] = al[e] * (g.mul * (acc[i][j][e] - sr[i]));
+            const int r = 16 * i + i16;
+            const int ch = (2 * j + (grp >> 1)) ^ i16;
+            *reinterpret_cast<u32x2 *>(stg + r * 256 + ch * 16 + (grp & 1) * 8) =
+                u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        }
+    }
+    const int nw = n0 + wn * 128 + 8 * (lane & 15);   // this lane's 8 output columns
+    const bool vec8 = (N & 7) == 0;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (n + e < N) g.Y[o + e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[e]));
+    for (int h = 0; h < 16; ++h) {
+        const int r = (lane >> 4) + 4 * h;
+        const uint4 d = *reinterpret_cast<const uint4 *>(stg + r * 256 + (((lane & 15) ^ (r & 15)) << 4));
+        const int m = m0 + (KH == 1 ? wm * kWaveM : 0) + r;
+        if (m < M && nw < N) {
+            uint16_t *y = g.Y + static_cast<int64_t>(m) * N + nw;
+            if (vec8) {
+                *reinterpret_cast<uint4 *>(y) = d;
+            } else {
+                const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (nw + e < N) y[e] = static_cast<uint16_t>(dw[e >> 1] >> (16 * (e & 1)));
             }
         }
     }
