@@ -409,7 +409,8 @@ def mfma_summarize(args):
         f"{SIMD_NUM} SIMDs) -- the counter tool's MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES counts 16 cycles per",
         "16x16x32 bf16 MFMA); GRBM_GUI_ACTIVE includes the launch's ramp, so short launches read low;",
         "`flops counted` = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512,",
-        "`flops needed` = 2 M N K (the kernels pad M to 16-row MFMA tiles, so small M counts more);",
+        "`flops needed` = 2 M N K (the counted flops also hold the row sums' all-ones MFMAs, and the",
+        "kernels pad M to 16-row MFMA tiles, so small M counts more);",
         "`VALU/MFMA` = (SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA, the decode and bookkeeping",
         "issued per MFMA; `LDS/MFMA` likewise; `VALU active` = SQ_ACTIVE_INST_VALU per SIMD-cycle;",
         "`GUI cycles` = GRBM_GUI_ACTIVE / 8.",
