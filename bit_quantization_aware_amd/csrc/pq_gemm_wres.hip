@@ -44,6 +44,10 @@
 #ifndef PQ_WRES_MAX_STAGES
 #define PQ_WRES_MAX_STAGES 11
 #endif
+// 1: 192-column blocks (four waves of 48 columns) where they pad N less.
+#ifndef PQ_WRES_NARROW
+#define PQ_WRES_NARROW 1
+#endif
 // Fewest rows for which this kernel takes a 2-bit GEMM.
 #ifndef PQ_WRES_MIN_M
 #define PQ_WRES_MIN_M 1024
@@ -53,7 +57,7 @@ namespace pq {
 namespace {
 
 constexpr int kWresTM = 64;                          // rows per tile
-constexpr int kWresN = 256;                          // block columns: 4 waves x 64
+constexpr int kWresN = 256;                          // block columns: 4 waves x 64 (or x 48)
 constexpr int kWresP = 4;                            // activation ring slots
 constexpr int kWresXBytes = kWresTM * kStageK * 2;   // 8 KB per slot
 constexpr int kWresXI = kWresXBytes / (4 * 1024);    // activation DMAs per wave per stage
@@ -64,9 +68,13 @@ constexpr int kWresBlocks = 512;                     // two per CU
 static_assert(kWresXI * 4 * 1024 == kWresXBytes, "one slot is XI 1-KB DMAs per wave");
 static_assert(kWresLds + kWresTM * 4 <= 80 * 1024, "two blocks per CU");
 
+// JW: 16-column MFMA tiles per wave, 4 (256-column blocks) or 3 (192).
+template <int JW>
 __global__ __launch_bounds__(256, 2) void k_gemm_wres(GemmArgs g, int mtiles, int ntiles)
 {
+    static_assert(JW == 3 || JW == 4, "48 or 64 columns per wave");
     constexpr int P = kWresP, XI = kWresXI;
+    constexpr int WC = 16 * JW, TN = 4 * WC;   // columns per wave, per block
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kWresLds];
     __shared__ float ssum[kWresTM];
     constexpr int XR = 0;                   // activation ring
@@ -106,8 +114,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wres(GemmArgs g, int mtiles, in
     }
 
     // LDS read addresses.  a[i] is row tile (i + w) & 3, so a[0] is the tile
-    // whose row sums this wave keeps; the code word of column 64 w + 16 j +
-    // i16 at stage st is dword grp of its 16 bytes.
+    // whose row sums this wave keeps; the code word of the wave's column
+    // 16 j + i16 at stage st is dword grp of its 16 bytes (1 KB per wave and
+    // stage, the last 16 columns unused when JW = 3).
     const int swz = xswz(i16);
     const uint8_t *xa[4][2];
 #pragma unroll
@@ -115,17 +124,17 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wres(GemmArgs g, int mtiles, in
 #pragma unroll
         for (int T = 0; T < 2; ++T)
             xa[i][T] = lds + XR + (16 * ((i + w) & 3) + i16) * 128 + (((2 * grp + T) ^ swz) << 4);
-    const uint8_t *ca = lds + CR + (64 * w + i16) * 16 + 4 * grp;
+    const uint8_t *ca = lds + CR + w * 1024 + i16 * 16 + 4 * grp;
 
     struct Frag {
         uint4 a[2][4];
-        uint32_t d[4];
+        uint32_t d[JW];
     };
     auto read_frags = [&](auto slot_c, int kst, Frag &f) __attribute__((always_inline)) {
         constexpr int SLOT = decltype(slot_c)::value;
         const uint8_t *cp = ca + kst * kWresCStage;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) f.d[j] = *reinterpret_cast<const uint32_t *>(cp + j * 256);
+        for (int j = 0; j < JW; ++j) f.d[j] = *reinterpret_cast<const uint32_t *>(cp + j * 256);
 #pragma unroll
         for (int T = 0; T < 2; ++T)
 #pragma unroll
@@ -133,14 +142,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wres(GemmArgs g, int mtiles, in
                 f.a[T][i] = *reinterpret_cast<const uint4 *>(xa[i][T] + SLOT * kWresXBytes);
     };
 
-    floatx4 acc[4][4];
+    floatx4 acc[4][JW];
     floatx4 accrs;
     const bf16x8 ones8 = __builtin_bit_cast(bf16x8, uint4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
     auto clear_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < JW; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
         accrs = floatx4{0.f, 0.f, 0.f, 0.f};
     };
     // One stage: the code word's masked nibbles are its codes 0..7 (k-step 0)
@@ -148,16 +157,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wres(GemmArgs g, int mtiles, in
     // are the MFMA A operand, so a lane's outputs are four consecutive
     // columns of one row.
     auto mma = [&](const Frag &f, auto &&between) __attribute__((always_inline)) {
-        uint32_t w0[4], w1[4];
+        uint32_t w0[JW], w1[JW];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < JW; ++j) {
             w0[j] = f.d[j] & 0x33333333u;
             w1[j] = (f.d[j] >> 2) & 0x33333333u;
         }
         static_for<0, 2>([&](auto tc) {
             constexpr int T = decltype(tc)::value;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < JW; ++j) {
                 const uint32_t wt = T == 0 ? w0[j] : w1[j];
                 uint4 bw;
                 bw.x = fp4x2_to_bf16x2<0>(wt);
@@ -182,13 +191,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wres(GemmArgs g, int mtiles, in
 
     {
         const int T = nseg * ns;
-        const int n0 = nt * kWresN;
+        const int n0 = nt * TN;
 
         // Resident codes: per stage one DMA per wave, lane l fetching the
-        // stage's 16 bytes of column 64 w + l (piece st & 3 of group st >> 2
-        // of its export tile).  Columns >= N re-read column N - 1.
+        // stage's 16 bytes of the wave's column l (piece st & 3 of group
+        // st >> 2 of its export tile).  Columns >= N re-read column N - 1;
+        // with JW = 3 lanes 48..63 fetch unused pieces.
         {
-            const int cl = min(n0 + 64 * w + lane, N - 1);
+            const int cl = min(n0 + WC * w + lane, N - 1);
             const uint32_t coff = static_cast<uint32_t>((cl >> 4) * 1024 + (cl & 15) * 64);
             for (int st = 0; st < ns; ++st)
                 dma16(g.packed + static_cast<int64_t>(st >> 2) * g.gstride, coff + (st & 3) * 16,
@@ -232,12 +242,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wres(GemmArgs g, int mtiles, in
         for (int st = 0; st < P - 1; ++st) issue_x(st);
 
         // Per-column scales of the tile, the same for all its row tiles.
-        float al[4][4];
+        float al[JW][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < JW; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int n = n0 + 64 * w + 16 * j + 4 * grp + e;
+                const int n = n0 + WC * w + 16 * j + 4 * grp + e;
                 al[j][e] = n < N ? col_scale(g.alpha, g.alpha32, n) : 0.f;
             }
 
@@ -252,8 +262,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wres(GemmArgs g, int mtiles, in
         int mc = 0, kc = 0;
         // Row tile mc is complete: publish its row sums, write its outputs,
         // clear the accumulators.  acc[i][j][e] is row 16 ((i + w) & 3) + i16
-        // of the tile, column 64 w + 16 j + 4 grp + e: four lanes hold a
-        // row's 64 columns in 8-byte pieces.  Each wave passes its rows
+        // of the tile, the wave's column 16 j + 4 grp + e: four lanes hold a
+        // row's WC columns in 8-byte pieces.  Each wave passes its rows
         // through 2 KB of the slot of the stage just multiplied (free until
         // the next step refills it), 16 rows at a time, so that every store
         // instruction writes 16 bytes per lane and eight whole 128-byte row
@@ -265,14 +275,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wres(GemmArgs g, int mtiles, in
             __syncthreads();
             const int m0 = (mt0 + mc) * kWresTM;
             uint8_t *stg = lds + XR + SLOT * kWresXBytes + w * 2048;
-            const int nw = n0 + 64 * w + 8 * (lane & 7);   // this lane's 8 output columns
+            const int nw = n0 + WC * w + 8 * (lane & 7);   // this lane's 8 output columns
+            const bool lane_cols = (lane & 7) < 2 * JW;
             const bool vec = (N & 7) == 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int rt = (i + w) & 3;
                 const float sr = g.off * ssum[16 * rt + i16];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < JW; ++j) {
                     float v[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] = al[j][e] * (g.mul * (acc[i][j][e] - sr));
@@ -285,7 +296,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wres(GemmArgs g, int mtiles, in
                     const int r = (lane >> 3) + 8 * h;
                     const uint4 d = *reinterpret_cast<const uint4 *>(stg + r * 128 + (((lane & 7) ^ (r & 7)) << 4));
                     const int m = m0 + 16 * rt + r;
-                    if (m < M && nw < N) {
+                    if (lane_cols && m < M && nw < N) {
                         uint16_t *y = g.Y + static_cast<int64_t>(m) * N + nw;
                         if (vec) {
                             *reinterpret_cast<uint4 *>(y) = d;
@@ -343,7 +354,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wres(GemmArgs g, int mtiles, in
 bool gemm_wres_takes(int bits, int64_t M, int64_t N, int64_t K)
 {
     if (bits != 2 || M < PQ_WRES_MIN_M || K > static_cast<int64_t>(kWresMaxStages) * kStageK) return false;
-    const int64_t items = (M + kWresTM - 1) / kWresTM * ((N + kWresN - 1) / kWresN);
+    const int64_t items = (M + kWresTM - 1) / kWresTM * ((N + 191) / 192);
     return items <= INT32_MAX;
 }
 
@@ -351,14 +362,21 @@ pq_status launch_gemm_wres(const GemmArgs &a, hipStream_t s)
 {
     if (!gemm_wres_takes(2, a.M, a.N, a.K)) return PQ_ERR_SHAPE;
     const int mtiles = (a.M + kWresTM - 1) / kWresTM;
-    const int ntiles = (a.N + kWresN - 1) / kWresN;
+    // 192-column blocks where they pad N less than 256-column ones (N = 576:
+    // three tiles either way, no idle columns)
+    const bool narrow = PQ_WRES_NARROW && (a.N + 191) / 192 * 192 < (a.N + kWresN - 1) / kWresN * kWresN;
+    const int tn = narrow ? 192 : kWresN;
+    const int ntiles = (a.N + tn - 1) / tn;
     // Runs per column tile: as many as two blocks per CU allow, then as few
     // as give the same longest run (the runs differ by at most a row tile).
     const int64_t rmax = std::max<int64_t>(1, std::min<int64_t>(mtiles, kWresBlocks / ntiles));
     const int64_t runlen = (mtiles + rmax - 1) / rmax;
     const int64_t blocks = ntiles * ((mtiles + runlen - 1) / runlen);
     if (blocks > INT32_MAX) return PQ_ERR_SHAPE;
-    hipLaunchKernelGGL(k_gemm_wres, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a, mtiles, ntiles);
+    if (narrow)
+        hipLaunchKernelGGL(k_gemm_wres<3>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a, mtiles, ntiles);
+    else
+        hipLaunchKernelGGL(k_gemm_wres<4>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a, mtiles, ntiles);
     return hipGetLastError() == hipSuccess ? PQ_OK : PQ_ERR_HIP;
 }
 

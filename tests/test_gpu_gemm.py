@@ -339,10 +339,11 @@ def test_gemm_training_forward_shape_sampled():
 
 
 def _wres_runs(M, N):
-    """(row tiles, blocks) of the resident-code launch: 64 x 256 tiles; per
-    column tile as many runs of row tiles as 512 blocks allow, then as few as
-    give the same longest run."""
-    mt, nt = -(-M // 64), -(-N // 256)
+    """(row tiles, blocks) of the resident-code launch: 64 x 256 tiles, or
+    64 x 192 where those pad N less; per column tile as many runs of row
+    tiles as 512 blocks allow, then as few as give the same longest run."""
+    tn = 192 if -(-N // 192) * 192 < -(-N // 256) * 256 else 256
+    mt, nt = -(-M // 64), -(-N // tn)
     rmax = max(1, min(mt, 512 // nt))
     runlen = -(-mt // rmax)
     return mt * nt, nt * -(-mt // runlen)
@@ -351,12 +352,17 @@ def _wres_runs(M, N):
 @pytest.mark.parametrize("mode,M,N,K", [(O.SEQ2, 1030, 600, 576), (O.TERNARY, 1030, 600, 576),
                                         (O.LSQ2, 1030, 600, 576), (O.LSQ158, 1030, 600, 576),
                                         (O.SEQ2, 8380, 1102, 192), (O.SEQ2, 2100, 200, 704),
-                                        (O.SEQ2, 1024, 256, 64), (O.LSQ2, 3000, 515, 640)])
+                                        (O.SEQ2, 1024, 256, 64), (O.LSQ2, 3000, 515, 640),
+                                        (O.SEQ2, 2048, 576, 576), (O.TERNARY, 1100, 192, 320),
+                                        (O.LSQ158, 1500, 380, 704), (O.SEQ2, 1090, 190, 64),
+                                        (O.LSQ2, 8300, 1150, 192)])
 def test_gemm_short_k_resident_codes_full_compare(mode, M, N, K):
     """2-bit GEMMs with K <= 704 and M >= 1024 (the resident-code kernel):
     ragged last row tile, N not a multiple of 256, 16, 8 or 4 (the
-    element-wise store), one K stage, the largest K, and 655 tiles on 330
-    blocks (runs of one and two row tiles); every output."""
+    element-wise store), one K stage, the largest K, 655 tiles on 330
+    blocks (runs of one and two row tiles), and the 192-column blocks of
+    48-column waves (N = 576, 192, 380, 190, 1150, where they pad N less
+    than 256-column ones); every output."""
     print(f"[gemm resident codes mode={mode} M={M} N={N} K={K}]", flush=True)
     tiles, nb = _wres_runs(M, N)
     if (M, N) == (8380, 1102):
