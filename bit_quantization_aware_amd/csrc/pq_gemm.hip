@@ -54,6 +54,11 @@
 #endif
 // Code fetches in the tiled kernel's LDS ring (2- and 4-bit; 1-bit keeps 2):
 // with 3, two fetches of weight codes are in flight behind the one in use.
+// 1: 192-column tiled blocks (four waves of 48 columns) where they pad N
+// less than 256-column ones.
+#ifndef PQ_TILE_NARROW
+#define PQ_TILE_NARROW 1
+#endif
 #ifndef PQ_TILE_NCB
 #define PQ_TILE_NCB 2
 #endif
@@ -139,7 +144,9 @@ namespace {
 //
 // A block owns a 64 x 256 output tile; its four waves each own 64 columns
 // (4 x 4 MFMA tiles of 16 x 16), so every wave reads the whole 64-row
-// activation tile and every decoded weight fragment feeds four MFMAs.  K runs
+// activation tile and every decoded weight fragment feeds four MFMAs.  Where
+// 192-column tiles pad N less (N = 576), the waves own 48 columns (4 x 3
+// MFMA tiles) and the code fetches shrink to match.  K runs
 // in stages of 64.  Each stage's activation tile (64 rows x 128 B) is copied
 // global -> LDS by the gfx950 LDS-DMA load (global_load_lds_dwordx4), with no
 // register or VALU traffic, into a ring of four stage buffers kept three
@@ -198,10 +205,12 @@ struct TileArgs {
 };
 
 
-// Tile of WN waves along N (64 columns each): 64 x 64*WN outputs per block.
-template <int BITS, int WN>
+// Tile of WN waves along N (16 JW columns each: JW = 4, or 3 where 192-column
+// blocks pad N less): 64 x 16*JW*WN outputs per block.
+template <int BITS, int WN, int JW = 4>
 struct TileCfg {
-    static constexpr int TN = 64 * WN;                   // columns per block
+    static constexpr int WC = 16 * JW;                   // columns per wave
+    static constexpr int TN = WC * WN;                   // columns per block
     static constexpr int CB = 8 * BITS;                  // code bytes per column per stage
     static constexpr int XBYTES = kTileM * kStageK * 2;  // 8 KB
     static constexpr int CBYTES = TN * CB;               // codes of one stage
@@ -209,10 +218,11 @@ struct TileCfg {
     static constexpr int CSS = SS * CBYTES;              // codes of one fetch
     static constexpr int P = BITS == 2 ? PQ_TILE_P2 : PQ_TILE_P4;  // activation ring depth
     static constexpr int XI = 8 / WN;                    // activation DMAs per wave per stage
-    static constexpr int NC = 4;                         // code DMAs per wave per fetch
+    static constexpr int NC = JW;                        // code DMAs per wave per fetch
     static constexpr int NCB = BITS == 1 ? 2 : PQ_TILE_NCB;  // code fetches in the ring
     static constexpr int LDS = P * XBYTES + NCB * CSS;
-    static_assert(WN == 4 || WN == 8, "block width");
+    static_assert(WN == 4, "block width: the epilogue stages 2 KB per wave in one 8-KB slot");
+    static_assert(JW == 3 || JW == 4, "48 or 64 columns per wave");
     static_assert(NC * WN * 1024 == CSS, "one fetch is NC 1-KB DMAs per wave");
     static_assert(P >= 3, "activation ring depth");
     static_assert(NCB == 2 || NCB == 3, "code ring depth");
@@ -232,10 +242,11 @@ __device__ __forceinline__ uint32_t spread_bits_fp4(uint32_t b)
     return x << 1;
 }
 
-template <int BITS, int P, int WN>
+template <int BITS, int P, int WN, int JW>
 __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
 {
-    using C = TileCfg<BITS, WN>;
+    using C = TileCfg<BITS, WN, JW>;
+    constexpr int WC = C::WC;
     static_assert(P >= 3, "ring depth");
     // LDS: P activation stages, then NCB code fetches.  Between items,
     // activation slot P - 1 stages the outputs: the next item's prologue
@@ -336,7 +347,7 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
             dma16(cb, ccol[i] + po, lds_base + CR + buf * C::CSS + (NC * w + i) * 1024);
     };
 
-    floatx4 acc[4][4];
+    floatx4 acc[4][JW];
     float rs = 0.f;
     floatx4 accrs = floatx4{0.f, 0.f, 0.f, 0.f};
     const bf16x8 ones8 = __builtin_bit_cast(bf16x8, uint4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
@@ -352,16 +363,16 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
 #pragma unroll
         for (int T = 0; T < 2; ++T)
             xa[i][T] = lds + XR + (16 * ((i + w) & 3) + i16) * 128 + (((2 * grp + T) ^ swz) << 4);
-    // Code reads: column 64w + 16j + i16 is in DMA block 4w + j; 2-bit lanes
-    // take dword grp of the stage's 16-byte piece, 4-bit lanes bytes
+    // Code reads: the wave's column 16j + i16 is in DMA block NC w + j; 2-bit
+    // lanes take dword grp of the stage's 16-byte piece, 4-bit lanes bytes
     // 8 (grp & 1) of piece 2 (stage) + (grp >> 1).
-    const uint8_t *ca = lds + CR + (4 * w) * 1024 + i16 * 16 +
+    const uint8_t *ca = lds + CR + (NC * w) * 1024 + i16 * 16 +
                         (BITS == 1 ? 2 * grp : BITS == 2 ? 4 * grp : 8 * (grp & 1) + 256 * (grp >> 1));
 
     // Fragments of one stage: A for both k-steps and the code words.
     struct Frag {
         uint4 a[2][4];
-        uint32_t d[4][BITS == 4 ? 2 : 1];
+        uint32_t d[JW][BITS == 4 ? 2 : 1];
     };
     // Fragments of stage st, with PH = st mod U known at compile time
     // (activation slot PH mod P, code buffer (PH / SS) mod NCB, stage PH mod SS).
@@ -371,7 +382,7 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
         constexpr int CBUF = (PH / C::SS) % NCB;
         constexpr int CST = PH % C::SS;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < JW; ++j) {
             // stage CST's bytes: 8, 16 or 32 per column, in the 16-byte pieces
             const uint8_t *p = ca + CBUF * C::CSS + j * 1024 +
                                (C::CB == 8 ? (CST >> 1) * 256 + (CST & 1) * 8 : CST * (C::CB == 16 ? 256 : 512));
@@ -394,10 +405,10 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
     auto mma = [&](const Frag &f, auto &&between) {
         // 2 bits: the code word's masked nibbles are its codes 0..7 (w0)
         // and 8..15 (w1) in k order, one k-step each (the export's word order)
-        uint32_t w0[4], w1[4];
+        uint32_t w0[JW], w1[JW];
         if constexpr (BITS == 2) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < JW; ++j) {
                 const uint32_t x = f.d[j][0];
                 w0[j] = x & 0x33333333u;
                 w1[j] = (x >> 2) & 0x33333333u;
@@ -406,7 +417,7 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
         static_for<0, 2>([&](auto tc) {
             constexpr int T = decltype(tc)::value;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < JW; ++j) {
                 uint4 b;
                 if constexpr (BITS == 1) {
                     const uint32_t x = spread_bits_fp4((f.d[j][0] >> (8 * T)) & 0xFFu);
@@ -487,7 +498,7 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < JW; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
     rs = 0.f;
     accrs = floatx4{0.f, 0.f, 0.f, 0.f};
     // activation stage 0 and code fetch 0 landed
@@ -560,7 +571,7 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
     }
 
     // Epilogue: acc[i][j][e] is row e_m0 + 16 * ((i + w) & 3) + i16, column
-    // e_n0 + 64w + 16j + 4grp + e; four lanes hold a row's 64 columns in
+    // e_n0 + WC w + 16j + 4grp + e; four lanes hold a row's WC columns in
     // 8-byte pieces.  One split: each wave passes its rows through 2 KB of
     // slot P - 1, 16 rows at a time, so that every store instruction writes
     // 16 bytes per lane and eight whole 128-byte row segments (16-byte
@@ -568,14 +579,15 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
     // partials, 16 bytes per lane as held.
     if (g.splits == 1) {
         uint8_t *stg = lds + XR + (P - 1) * C::XBYTES + w * 2048;
-        const int nw = e_n0 + 64 * w + 8 * (lane & 7);   // this lane's 8 output columns
+        const int nw = e_n0 + WC * w + 8 * (lane & 7);   // this lane's 8 output columns
+        const bool lane_cols = (lane & 7) < 2 * JW;
         const bool vec8 = (N & 7) == 0;
-        float al[4][4];
+        float al[JW][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < JW; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int n = e_n0 + 64 * w + 16 * j + 4 * grp + e;
+                const int n = e_n0 + WC * w + 16 * j + 4 * grp + e;
                 al[j][e] = n < N ? col_scale(g.alpha, g.alpha32, n) : 0.f;
             }
 #pragma unroll
@@ -583,7 +595,7 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
             const int rt = (i + w) & 3;
             const float sr = g.off * ssum[16 * rt + i16];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < JW; ++j) {
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = g.mul * (acc[i][j][e] - sr);
@@ -596,7 +608,7 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
                 const int r = (lane >> 3) + 8 * h;
                 const uint4 d = *reinterpret_cast<const uint4 *>(stg + r * 128 + (((lane & 7) ^ (r & 7)) << 4));
                 const int m = e_m0 + 16 * rt + r;
-                if (m < M && nw < N) {
+                if (lane_cols && m < M && nw < N) {
                     uint16_t *y = g.Y + static_cast<int64_t>(m) * N + nw;
                     if (vec8) {
                         *reinterpret_cast<uint4 *>(y) = d;
@@ -612,8 +624,8 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
     } else {
         const bool vec = (N & 3) == 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int n = e_n0 + 64 * w + 16 * j + 4 * grp;
+        for (int j = 0; j < JW; ++j) {
+            const int n = e_n0 + WC * w + 16 * j + 4 * grp;
             if (n >= N) continue;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -1023,6 +1035,7 @@ double tile_cost(int64_t tiles, int stages, int splits, int64_t M, int64_t N)
 // pure function of (width, M, N, K), so the size query and the launch agree.
 struct GemmPlan {
     enum Path { STREAM, TILE, BIG, WRES } path = STREAM;
+    int jw = 4;          // TILE: 16-column tiles per wave (3: 192-column blocks)
     int splits = 1;      // TILE: K splits
     int sps = 0;         // TILE: stages per split (whole 64-byte groups)
     int64_t ws = 0;      // workspace bytes (0: none)
@@ -1036,8 +1049,11 @@ void plan_tile(int64_t M, int64_t N, int64_t K, GemmPlan &p)
 {
     constexpr int kMinStages = PQ_TILE_MIN_STAGES;
     using C = TileCfg<BITS, PQ_TILE_WN>;
+    // 192-column blocks where they pad N less than 256-column ones
+    p.jw = PQ_TILE_NARROW && (N + 191) / 192 * 192 < (N + C::TN - 1) / C::TN * C::TN ? 3 : 4;
+    const int64_t tn = 16 * p.jw * PQ_TILE_WN;
     const int64_t mtiles = (M + kTileM - 1) / kTileM;
-    const int64_t ntiles = (N + C::TN - 1) / C::TN;
+    const int64_t ntiles = (N + tn - 1) / tn;
     const int64_t tiles = mtiles * ntiles;
     const int stages = static_cast<int>(K / kStageK);
     int splits = 1;
@@ -1075,10 +1091,10 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
     return p;
 }
 
-template <int BITS>
+template <int BITS, int JW>
 pq_status launch_tile(const GemmArgs &a, const GemmPlan &p, float *ws, hipStream_t s)
 {
-    using C = TileCfg<BITS, PQ_TILE_WN>;
+    using C = TileCfg<BITS, PQ_TILE_WN, JW>;
     const int mtiles = (a.M + kTileM - 1) / kTileM;
     const int ntiles = (a.N + C::TN - 1) / C::TN;
     // the tile kernel's 4-bit operand is 2 + c/8 (the stream kernel's 128 + c)
@@ -1099,7 +1115,7 @@ pq_status launch_tile(const GemmArgs &a, const GemmPlan &p, float *ws, hipStream
     // More items than two blocks per CU: persistent blocks, each taking
     // items in turn with the next item's first loads under the epilogue.
     const int64_t blocks = PQ_TILE_PERSIST > 0 && items > PQ_TILE_PERSIST ? PQ_TILE_PERSIST : items;
-    hipLaunchKernelGGL((k_gemm_tile<BITS, C::P, PQ_TILE_WN>), dim3(static_cast<unsigned>(blocks)), dim3(64 * PQ_TILE_WN),
+    hipLaunchKernelGGL((k_gemm_tile<BITS, C::P, PQ_TILE_WN, JW>), dim3(static_cast<unsigned>(blocks)), dim3(64 * PQ_TILE_WN),
                        0, s, t);
     if (p.splits > 1) {
         const int64_t threads = (total + 3) / 4;
@@ -1183,7 +1199,8 @@ pq_status gemm(int64_t M, int64_t N, int64_t K, const void *X, const uint8_t *pa
         const pq_status sw = launch_gemm_wres(a, s);
         if (sw != PQ_OK) return sw;
     } else {
-        const pq_status st = launch_tile<BITS>(a, plan, static_cast<float *>(workspace), s);
+        const pq_status st = plan.jw == 3 ? launch_tile<BITS, 3>(a, plan, static_cast<float *>(workspace), s)
+                                          : launch_tile<BITS, 4>(a, plan, static_cast<float *>(workspace), s);
         if (st != PQ_OK) return st;
     }
     return hipGetLastError() == hipSuccess ? PQ_OK : PQ_ERR_HIP;
