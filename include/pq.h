@@ -272,13 +272,15 @@ pq_status pq_pack_w4(int64_t rows, int64_t cols, const float *W, const float *al
  * kernel choice is a fixed function of (mode, M, N, K), so the value is the
  * same for every call with these arguments:
  *   M <= 16 (weight streaming): none;
- *   larger M with 64 x 256 output tiles: when there are too few tiles to
- *     fill the chip, K is split over blocks, each split writes fp32 partial
- *     sums [splits, M, N] and a second kernel adds them in split order --
- *     splits * M * N * 4 bytes; otherwise none;
+ *   larger M with 64 x 256 (or 64 x 192) output tiles: when there are too
+ *     few tiles to fill the chip, K is split over blocks, each split writes
+ *     fp32 partial sums [splits, M, N] and a second kernel adds them in
+ *     split order -- splits * M * N * 4 bytes; otherwise none;
  *   large M at 2-bit widths (K >= 2048; M >= 1024, or M >= 512 when N gives
  *     at least 512 tiles of 64 x 256): none (the kernel sums the activation
- *     rows for the level offset itself).
+ *     rows for the level offset itself);
+ *   short K at 2-bit widths (K <= 704, M >= 1024; the codes of a column
+ *     tile stay in LDS): none.
  */
 int64_t pq_gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
 
