@@ -562,6 +562,15 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
     if (grp == 0 && w < 4) ssum[16 * w + i16] = rs;
     __syncthreads();
 
+    // One split: this item's per-column scales, loaded and waited for while
+    // no DMA is in flight (a wait for them later would also wait for the
+    // next item's first loads).
+    float al[JW][4];
+    if (g.splits == 1) {
+        load_col_scales<JW>(g.alpha, g.alpha32, n0 + WC * w + 4 * grp, N, al);
+        wait_vmcnt<0>();
+    }
+
     // The next item's prologue, into the ring every wave is done with.
     const int e_m0 = m0, e_n0 = n0, e_split = split;
     const int next = item + nb;
@@ -582,14 +591,6 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
         const int nw = e_n0 + WC * w + 8 * (lane & 7);   // this lane's 8 output columns
         const bool lane_cols = (lane & 7) < 2 * JW;
         const bool vec8 = (N & 7) == 0;
-        float al[JW][4];
-#pragma unroll
-        for (int j = 0; j < JW; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int n = e_n0 + WC * w + 16 * j + 4 * grp + e;
-                al[j][e] = n < N ? col_scale(g.alpha, g.alpha32, n) : 0.f;
-            }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int rt = (i + w) & 3;

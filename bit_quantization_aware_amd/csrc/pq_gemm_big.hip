@@ -342,19 +342,17 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, int mtiles)
                                    : rsl[(i >> 1) * kWaveM + r] + rsl[(2 + (i >> 1)) * kWaveM + r];
         sr[i] = g.off * rsum;
     }
+    // the per-column scales of each column tile, its four loads issued
+    // before any of them is used
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        float al[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int n = n0 + wn * 128 + 16 * j + 4 * grp + e;
-            al[e] = n < N ? col_scale(g.alpha, g.alpha32, n) : 0.f;
-        }
+        float al[1][4];
+        load_col_scales<1>(g.alpha, g.alpha32, n0 + wn * 128 + 16 * j + 4 * grp, N, al);
 #pragma unroll
         for (int i = 0; i < kRT; ++i) {
             float v[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = al[e] * (g.mul * (acc[i][j][e] - sr[i]));
+            for (int e = 0; e < 4; ++e) v[e] = al[0][e] * (g.mul * (acc[i][j][e] - sr[i]));
             const int r = 16 * i + i16;
             const int ch = (2 * j + (grp >> 1)) ^ i16;
             *reinterpret_cast<u32x2 *>(stg + r * 256 + ch * 16 + (grp & 1) * 8) =

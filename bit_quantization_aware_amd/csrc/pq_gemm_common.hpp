@@ -34,6 +34,32 @@ __device__ __forceinline__ float col_scale(const uint16_t *a16, const float *a32
     return a32 ? a32[n] : bf16_to_f32(a16[n]);
 }
 
+// Per-column scales of a lane's output columns: out[j][e] for column
+// n0 + 16 j + e (j < J, e < 4), 0 past N.  All loads are issued, from the
+// binary32 or the bf16 array (a uniform choice), before any is used, so
+// they cost one round trip instead of one each.
+template <int J>
+__device__ __forceinline__ void load_col_scales(const uint16_t *a16, const float *a32, int n0, int N,
+                                                float (&out)[J][4])
+{
+    if (a32) {
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[j][e] = a32[min(n0 + 16 * j + e, N - 1)];
+    } else {
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[j][e] = bf16_to_f32(a16[min(n0 + 16 * j + e, N - 1)]);
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (n0 + 16 * j + e >= N) out[j][e] = 0.f;
+}
+
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F &&f)

@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wres(GemmArgs g, int mtiles, in
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kWresLds];
     __shared__ float ssum[kWresTM];
     constexpr int XR = 0;                   // activation ring
-    constexpr int CR = P * kWresXBytes;     // resident codes, [stage][256 columns][16 B]
+    constexpr int CR = P * kWresXBytes;     // resident codes, [stage][wave][64 columns][16 B]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -193,6 +193,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wres(GemmArgs g, int mtiles, in
         const int T = nseg * ns;
         const int n0 = nt * TN;
 
+        // Per-column scales of the tile, the same for all its row tiles:
+        // loaded before any DMA and waited for here, so that no wait for
+        // them (which would also wait for every DMA in flight) lands in the
+        // stream.  Columns >= N read column N - 1 and get 0.
+        float al[JW][4];
+        load_col_scales<JW>(g.alpha, g.alpha32, n0 + WC * w + 4 * grp, N, al);
+        wait_vmcnt<0>();
+
         // Resident codes: per stage one DMA per wave, lane l fetching the
         // stage's 16 bytes of the wave's column l (piece st & 3 of group
         // st >> 2 of its export tile).  Columns >= N re-read column N - 1;
@@ -240,16 +248,6 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wres(GemmArgs g, int mtiles, in
         };
 #pragma unroll
         for (int st = 0; st < P - 1; ++st) issue_x(st);
-
-        // Per-column scales of the tile, the same for all its row tiles.
-        float al[JW][4];
-#pragma unroll
-        for (int j = 0; j < JW; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int n = n0 + WC * w + 16 * j + 4 * grp + e;
-                al[j][e] = n < N ? col_scale(g.alpha, g.alpha32, n) : 0.f;
-            }
 
         clear_acc();
         // the codes and activation stage 0 landed
