@@ -242,11 +242,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, int mtiles)
     auto pipeline = [&](auto wn_c) __attribute__((always_inline)) {
     // Prologue: code fetch 0, activation stages 0 .. P - 2, code fetch 1
     // (the issue order the wait model assumes); stage 0 and fetch 0 landed.
+    // code fetches first when each iteration has its own (KH = 2; see the
+    // step below), so that the wait model's order holds from the start
+    constexpr int CF = C::SS == 1 ? 1 : 0;
     issue_c(0);
+    if constexpr (CF) issue_c(1);
 #pragma unroll
     for (int it = 0; it < kBigP - 1; ++it) issue_x(it, it);
-    issue_c(1);
-    wait_vmcnt<(kBigP - 2) * kBigXI + kBigNC>();
+    if constexpr (!CF) issue_c(1);
+    // activation stage 0 and code fetch 0 landed: the DMAs issued after stage
+    // 0 may stay in flight (stages 1 .. P-2, and code fetch 1 unless it went
+    // first)
+    wait_vmcnt<(kBigP - 2) * kBigXI + (CF ? 0 : kBigNC)>();
     block_barrier();
     uint4 a0[kRT], a1[kRT];
     uint32_t dc[2][8];
@@ -258,15 +265,22 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, int mtiles)
     // fetch before last; then the two k-steps of stage s, each reading the
     // next k-step's fragments first.  Every LDS read of a ring slot or code
     // buffer is complete before the barrier that precedes its refill.
+    //
+    // With one code fetch per iteration (KH = 2) the fetch an iteration
+    // needs is issued one iteration ahead; issued after that iteration's
+    // activation stage it would be the newest DMA, and every wait would be
+    // for all of them (vmcnt 0).  Issued before it, one activation stage
+    // stays in flight across each wait.
     auto step = [&](int s, auto pc) __attribute__((always_inline)) {
         constexpr int p = decltype(pc)::value;  // s mod U
         constexpr bool code_now = ((p + 1) % C::SS) == 0;
         wait_lgkmcnt0();
-        wait_vmcnt<tile_wait(p, kBigP, C::SS, kBigXI, kBigNC, kBigU)>();
+        wait_vmcnt<tile_wait(p, kBigP, C::SS, kBigXI, kBigNC, kBigU, 2, CF)>();
         block_barrier();
         __builtin_amdgcn_s_setprio(1);
+        if constexpr (code_now && CF) issue_c((s + 1) / C::SS + 1);
         issue_x(s + kBigP - 1, (p + kBigP - 1) % kBigP);
-        if constexpr (code_now) issue_c((s + 1) / C::SS + 1);
+        if constexpr (code_now && !CF) issue_c((s + 1) / C::SS + 1);
         // k-step 0 of stage s (a0), reading k-step 1 (a1)
         read_a(std::integral_constant<int, p % kBigP>{}, std::integral_constant<int, 1>{}, a1);
         __builtin_amdgcn_sched_barrier(0);

@@ -87,42 +87,44 @@ __device__ __forceinline__ int xswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 // DMA bookkeeping of the tiled kernels' pipelines, evaluated at compile
 // time, for a ring of P activation stages and NCB code fetches of SS stages.
 // Issue order: code fetch 0, activation stages 0 .. P-2, code fetches
-// 1 .. NCB-1; then iteration j issues activation stage j + P - 1 and, when
-// (j + 1) % SS == 0, code fetch (j + 1) / SS + NCB - 1.  Iteration s needs
-// activation stage s + 1 and code fetch (s + 1) / SS landed; loads retire in
-// order, so the largest safe vmcnt is the number of DMA instructions issued
-// after the newer of the two.  Issue "times" only order the events.
-constexpr int tile_t_x(int k, int P, int NCB)
+// 1 .. NCB-1 (with CF = 1: all code fetches first); then iteration j issues
+// activation stage j + P - 1 and, when (j + 1) % SS == 0, code fetch
+// (j + 1) / SS + NCB - 1 (after the activation stage, or before it when
+// CF = 1).  Iteration s needs activation stage
+// s + 1 and code fetch (s + 1) / SS landed; loads retire in order, so the
+// largest safe vmcnt is the number of DMA instructions issued after the
+// newer of the two.  Issue "times" only order the events.
+constexpr int tile_t_x(int k, int P, int NCB, int CF = 0)
 {
-    return k <= P - 2 ? 1 + k : P + NCB - 1 + 2 * (k - P + 1);
+    return k <= P - 2 ? (CF ? NCB + k : 1 + k) : P + NCB - 1 + 2 * (k - P + 1) + CF;
 }
-constexpr int tile_t_c(int F, int P, int SS, int NCB)
+constexpr int tile_t_c(int F, int P, int SS, int NCB, int CF = 0)
 {
-    return F == 0 ? 0 : F < NCB ? P + F - 1 : P + NCB + 2 * ((F - NCB + 1) * SS - 1);
+    return F == 0 ? 0 : F < NCB ? (CF ? F : P + F - 1) : P + NCB + 2 * ((F - NCB + 1) * SS - 1) - CF;
 }
-constexpr int tile_wait_at(int s, int P, int SS, int XI, int NC, int NCB)
+constexpr int tile_wait_at(int s, int P, int SS, int XI, int NC, int NCB, int CF = 0)
 {
-    const int a = tile_t_x(s + 1, P, NCB), b = tile_t_c((s + 1) / SS, P, SS, NCB);
+    const int a = tile_t_x(s + 1, P, NCB, CF), b = tile_t_c((s + 1) / SS, P, SS, NCB, CF);
     const int newest = a > b ? a : b;
     int n = 0;
     for (int st = 0; st < P - 1; ++st)
-        if (1 + st > newest) n += XI;
+        if ((CF ? NCB + st : 1 + st) > newest) n += XI;
     for (int F = 1; F < NCB; ++F)
-        if (P + F - 1 > newest) n += NC;
+        if ((CF ? F : P + F - 1) > newest) n += NC;
     for (int j = 0; j < s; ++j) {
-        if (P + NCB - 1 + 2 * j > newest) n += XI;
-        if ((j + 1) % SS == 0 && P + NCB + 2 * j > newest) n += NC;
+        if (P + NCB - 1 + 2 * j + CF > newest) n += XI;
+        if ((j + 1) % SS == 0 && P + NCB + 2 * j - CF > newest) n += NC;
     }
     return n;
 }
 // The wait of unrolled phase p: the smallest safe count over the iterations
 // s = p, p + U, ... (the first ones included; steady state is reached well
 // within the range scanned).
-constexpr int tile_wait(int p, int P, int SS, int XI, int NC, int U, int NCB = 2)
+constexpr int tile_wait(int p, int P, int SS, int XI, int NC, int U, int NCB = 2, int CF = 0)
 {
     int best = 1 << 30;
     for (int s = p; s < 4 * U + 2 * P + 2 * NCB * SS; s += U) {
-        const int w = tile_wait_at(s, P, SS, XI, NC, NCB);
+        const int w = tile_wait_at(s, P, SS, XI, NC, NCB, CF);
         best = w < best ? w : best;
     }
     return best;
