@@ -344,7 +344,7 @@ __global__ __launch_bounds__(64 * WN, 8 / WN) void k_gemm_tile(TileArgs g)
         const uint32_t po = static_cast<uint32_t>((((st % SS) * C::CB + cwithin) >> 4) * 16);
 #pragma unroll
         for (int i = 0; i < NC; ++i)
-            dma16(cb, ccol[i] + po, lds_base + CR + buf * C::CSS + (NC * w + i) * 1024);
+            dma16<PQ_NT_TILE>(cb, ccol[i] + po, lds_base + CR + buf * C::CSS + (NC * w + i) * 1024);
     };
 
     floatx4 acc[4][JW];
@@ -783,7 +783,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_stream(GemmArgs g)
         const uint32_t sb = ring + slot * SLOT;
         const uint8_t *cb = g.packed + static_cast<int64_t>(gi) * g.gstride;
 #pragma unroll
-        for (int j = 0; j < TN; ++j) dma16(cb, coff[j], sb + j * 1024);
+        for (int j = 0; j < TN; ++j) dma16<PQ_NT_STREAM>(cb, coff[j], sb + j * 1024);
 #pragma unroll
         for (int q = 0; q < XI; ++q) dma16(g.X, xoff[q] + gi * (GK * 2), sb + TN * 1024 + q * XQS);
     };

@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big2(GemmArgs g, int mtiles)
         const uint32_t po = static_cast<uint32_t>((st & 3) * 16);
 #pragma unroll
         for (int i = 0; i < kBigNC; ++i)
-            dma16(cb, ccol[i] + po, lds_base + CR + (F & 1) * kBigCBytes + (kBigNC * w + i) * 1024);
+            dma16<PQ_NT_BIG>(cb, ccol[i] + po, lds_base + CR + (F & 1) * kBigCBytes + (kBigNC * w + i) * 1024);
     };
 
     floatx4 acc[kRT][8];

@@ -136,21 +136,61 @@ constexpr int tile_wait(int p, int P, int SS, int XI, int NC, int U, int NCB = 2
 // which cannot tell the ring slots apart, does not wait for every DMA before
 // each LDS read; the kernel orders the ring itself with s_waitcnt vmcnt and
 // s_barrier.  The instruction writes no VGPRs.
+//
+// NT marks the load non-temporal: the weight codes, which a GEMM reads once,
+// then take no room in the caches from data that is reused.  Above all they
+// do not displace dirty lines that earlier kernels left in the memory-side
+// last-level cache, which would have to be written back to HBM during the
+// GEMM.  After a 1 GB copy, a 16384^2 GEMM with one activation row took
+// 20.3 us with plain loads and 15.1 us with non-temporal ones (14.4-14.5 us
+// in both cases back to back, with nothing dirty); with 16 rows 23.1 and
+// 20.6 us.
+// Non-temporal code loads, per GEMM kernel (1: on).  On in the streaming
+// kernel only.  The other kernels measured slower with them, 3-8 % back to
+// back, and no faster after a large write: 16384^2 at 512 rows 201 us
+// against 187; 4096 x 4096 x 4096 100 against 95; 16384 rows of K = 576,
+// N = 576 through the resident-code kernel 21.6 against 20.4.
+#ifndef PQ_NT_STREAM
+#define PQ_NT_STREAM 1
+#endif
+#ifndef PQ_NT_TILE
+#define PQ_NT_TILE 0
+#endif
+#ifndef PQ_NT_BIG
+#define PQ_NT_BIG 0
+#endif
+#ifndef PQ_NT_WRES
+#define PQ_NT_WRES 0
+#endif
+
+template <bool NT = false>
 __device__ __forceinline__ void dma16(const void *base, uint32_t off, uint32_t lds_addr)
 {
     // M0 is saved and restored around the load, so the compiler's own use
     // of it (if any) is undisturbed; one wait state separates the M0 write
     // from the LDS-DMA that reads it.
     uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, %2\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(off), "s"(base), "s"(lds_addr)
-        : "memory");
+    if constexpr (NT) {
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %3\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %1, %2 nt\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "v"(off), "s"(base), "s"(lds_addr)
+            : "memory");
+    } else {
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %3\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %1, %2\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "v"(off), "s"(base), "s"(lds_addr)
+            : "memory");
+    }
 }
 
 __device__ __forceinline__ void block_barrier()

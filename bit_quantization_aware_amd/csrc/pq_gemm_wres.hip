@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wres(GemmArgs g, int mtiles, in
             const int cl = min(n0 + WC * w + lane, N - 1);
             const uint32_t coff = static_cast<uint32_t>((cl >> 4) * 1024 + (cl & 15) * 64);
             for (int st = 0; st < ns; ++st)
-                dma16(g.packed + static_cast<int64_t>(st >> 2) * g.gstride, coff + (st & 3) * 16,
+                dma16<PQ_NT_WRES>(g.packed + static_cast<int64_t>(st >> 2) * g.gstride, coff + (st & 3) * 16,
                       lds_base + CR + st * kWresCStage + w * 1024);
         }
 
