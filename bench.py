@@ -29,6 +29,7 @@ import hashlib
 import json
 import re
 import os
+import statistics
 import sys
 import time
 
@@ -766,7 +767,8 @@ def train_forward_measure(torch, pq, stack, stream, reps=3):
     8 x 2048 tokens: (a) this library's forward writing only the codes in the
     export byte order, then pq_gemm_f32a per matrix (codes + fp32 alpha);
     (b) the forward writing bf16 weights, then hipBLASLt (torch.matmul) per
-    matrix on them."""
+    matrix on them.  Three alternating passes of each; the medians are
+    reported."""
     mode = pq.PQ_W2_SEQ
     dev = stack[0]["W"].device
     T = TRAIN_TOKENS
@@ -802,8 +804,8 @@ def train_forward_measure(torch, pq, stack, stream, reps=3):
         for m in stack:
             torch.matmul(xs[m["cols"]], m["wq_bf16"].t(), out=ys[m["rows"]])
 
-    a = b2b_ms(torch, stream, lambda i: codes_path(), reps)
-    b = b2b_ms(torch, stream, lambda i: bf16_path(), reps)
+    a, b, pa, pb = paired_ms(lambda: b2b_ms(torch, stream, lambda i: codes_path(), reps),
+                             lambda: b2b_ms(torch, stream, lambda i: bf16_path(), reps))
     fwd_c = b2b_ms(torch, stream, lambda i: pq.pq_quantize_fwd_grouped(mode, ctab, pq.PQ_CODES_EXPORT), reps)
     fwd_b = b2b_ms(torch, stream, lambda i: pq.pq_quantize_fwd_grouped(mode, btab, 0), reps)
     fl = 2.0 * T * sum(m["rows"] * m["cols"] for m in stack)
@@ -811,7 +813,8 @@ def train_forward_measure(torch, pq, stack, stream, reps=3):
                 bf16_path_ms=round(b, 4), bf16_path_tflops=round(fl / b / 1e9, 1),
                 fwd_codes_only_ms=round(fwd_c, 4), fwd_bf16_codes_ms=round(fwd_b, 4),
                 gemm="codes: pq_gemm_f32a per matrix; bf16: torch.matmul (hipBLASLt) per matrix",
-                speedup=round(b / a, 3))
+                speedup=round(b / a, 3), codes_passes_ms=[round(t, 4) for t in pa],
+                bf16_passes_ms=[round(t, 4) for t in pb])
 
 
 def qat_step_measure(torch, pq, stack, ftab, btab, stream, reps=10):
@@ -915,6 +918,17 @@ def sweep_bits(torch, pq, stack, make_tables, stream):
     return res
 
 
+def paired_ms(fa, fb, passes=3):
+    """Two timings taken in alternating passes (a, b, a, b, ...): the medians
+    and every pass.  The first pass of a shape runs on cold clocks and caches
+    for both sides; the median keeps it from deciding the comparison."""
+    ta, tb = [], []
+    for _ in range(passes):
+        ta.append(fa())
+        tb.append(fb())
+    return statistics.median(ta), statistics.median(tb), ta, tb
+
+
 def b2b_ms(torch, stream, run, reps):
     """Mean time per launch of `reps` launches in a row, one event pair
     around them (after a few warm launches)."""
@@ -1013,9 +1027,9 @@ def llama_gemm_measure(torch, pq, synth, stream, reps=20):
     GEMM at M in {1, 16, 256, 4096}, next to a hipBLASLt bf16 GEMM on the
     dequantized weight.  Both rotate weight copies (ROTATE_BYTES) and run
     back to back inside one HIP graph (so that launches of a few microseconds
-    are not bound by the host's per-call cost); frac is against the
-    weight-stream roofline below the ridge point and the bf16 MFMA peak
-    above it."""
+    are not bound by the host's per-call cost), in three alternating passes
+    whose medians are reported; frac is against the weight-stream roofline
+    below the ridge point and the bf16 MFMA peak above it."""
     res = {}
     ridge = MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3
     for k, (_, name, N, K) in enumerate(synth.llama3_8b_shapes()):
@@ -1040,16 +1054,19 @@ def llama_gemm_measure(torch, pq, synth, stream, reps=20):
             xp, yp = X.data_ptr(), Y.data_ptr()
             ws = pq.gemm_workspace(pq.PQ_W2_SEQ, M, N, K)
             wa = (ws.data_ptr(), ws.numel()) if ws is not None else (0, 0)
-            ms = graph_ms(torch, lambda i, sd: pq.pq_w2a16_gemm(M, N, K, xp, pkp[i % R], abp[i % R], yp, sd,
-                                                                workspace=wa),
-                          reps, check=lambda: Y)
-            tb = graph_ms(torch, lambda i, sd: torch.matmul(X, wb[i % Rb].t(), out=Y), reps)
+            ms, tb, pa, pb = paired_ms(
+                lambda: graph_ms(torch, lambda i, sd: pq.pq_w2a16_gemm(M, N, K, xp, pkp[i % R], abp[i % R], yp,
+                                                                       sd, workspace=wa),
+                                 reps, check=lambda: Y),
+                lambda: graph_ms(torch, lambda i, sd: torch.matmul(X, wb[i % Rb].t(), out=Y), reps))
             fl, by = 2.0 * M * N * K, gemm_bytes(M, N, K, 2)
             gbs, tf = by / ms / 1e6, fl / ms / 1e9
             frac = gbs / HBM_PEAK_GBS if fl / by < ridge else tf / MFMA_BF16_PEAK_TFLOPS
             res[f"{name}_m{M}"] = dict(ms=round(ms, 5), tflops=round(tf, 2), weight_stream_GBs=round(gbs, 1),
                                        frac=round(frac, 4), bf16_hipblaslt_ms=round(tb, 5),
-                                       speedup_vs_bf16=round(tb / ms, 2))
+                                       speedup_vs_bf16=round(tb / ms, 2),
+                                       passes_ms=[round(t, 5) for t in pa],
+                                       bf16_passes_ms=[round(t, 5) for t in pb])
         del pk, ab, wb, wq
         torch.cuda.empty_cache()
     return res
