@@ -311,10 +311,10 @@ int64_t pq_gemm_workspace_bytes(int mode, int64_t M, int64_t N, int64_t K);
  * Errors as above, and: workspace needed but NULL -> PQ_ERR_NULL; not
  * 16-byte aligned -> PQ_ERR_ALIGN; workspace_bytes too small or negative ->
  * PQ_ERR_ARG.
- * Caches: with M <= 16 the weight codes are read non-temporally (they do not
- * displace other data or dirty lines from the last-level cache, and a second
- * call on the same weight reads them from HBM again); larger M reads them
- * through the caches.
+ * Caches: with M <= 16 the weight codes are read as non-temporal (streaming)
+ * loads, so that they neither displace other data nor force dirty lines out
+ * of the last-level cache; a later call on the same weight should not count
+ * on finding them cached.  Larger M reads them with ordinary loads.
  */
 pq_status pq_w2a16_gemm(int64_t M, int64_t N, int64_t K, const void *X,
                         const uint8_t *packed, const void *alpha_bf16, void *Y,
